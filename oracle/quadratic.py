@@ -1,0 +1,67 @@
+"""F1: the quadratic masked (parallel) form, fp64, numpy.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Per sequence of n tokens with decay lam (the glossary page "Lightning
+Attention", features list, parallel form for training):
+    D[i, j] = lam^(i-j) if i >= j else 0
+    P = (Q K^T) * D,  O = P V  [+ diag(lam^(t+1)) Q S0]
+    S_final = lam^n S0 + sum_j lam^(n-1-j) k_j v_j^T
+Backward of L = <dO, O> with S0 constant:
+    G = (dO V^T) * D,  dQ = G K [+ diag(lam^(t+1)) dO S0^T],  dK = G^T Q,  dV = P^T dO.
+The n x n matrices make this form usable for n up to a few thousand only.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def decay_matrix(n: int, lam: float) -> np.ndarray:
+    """D[i, j] = lam^(i-j) for i >= j, 0 above the diagonal (lam^0 = 1, also for lam = 0)."""
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    e = np.where(i >= j, i - j, 0).astype(np.float64)
+    return np.where(i >= j, np.power(np.float64(lam), e), 0.0)
+
+
+def _powers(lam: float, exps: np.ndarray) -> np.ndarray:
+    return np.power(np.float64(lam), exps.astype(np.float64))
+
+
+def fwd_quadratic(q, k, v, lam, s_init=None):
+    """One sequence: q, k, v [n, d]; returns (O [n, d], S_final [d, d])."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n = q.shape[0]
+    lam = float(np.float64(lam))
+    D = decay_matrix(n, lam)
+    P = (q @ k.T) * D
+    o = P @ v
+    w = _powers(lam, np.arange(n - 1, -1, -1))  # lam^(n-1-j)
+    s_final = (k * w[:, None]).T @ v
+    if s_init is not None:
+        s0 = np.asarray(s_init, dtype=np.float64)
+        o = o + _powers(lam, np.arange(1, n + 1))[:, None] * (q @ s0)
+        s_final = s_final + (lam ** n) * s0
+    return o, s_final
+
+
+def bwd_quadratic(q, k, v, dout, lam, s_init=None):
+    """One sequence: returns (dQ, dK, dV) of L = <dO, O>."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(dout, dtype=np.float64)
+    n = q.shape[0]
+    lam = float(np.float64(lam))
+    D = decay_matrix(n, lam)
+    G = (g @ v.T) * D
+    P = (q @ k.T) * D
+    dq = G @ k
+    if s_init is not None:
+        s0 = np.asarray(s_init, dtype=np.float64)
+        dq = dq + _powers(lam, np.arange(1, n + 1))[:, None] * (g @ s0.T)
+    dk = G.T @ q
+    dv = P.T @ g
+    return dq, dk, dv

@@ -1,0 +1,350 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+* exact rational brute force of the definition on tiny inputs, including exact
+  gradients obtained from the forward definition by linearity;
+* hand-worked examples (tests/golden/hand_examples.json);
+* closed forms for constant inputs (forward, final state and backward);
+* a library routine at lam = 1: ((Q K^T).tril()) V in torch float64;
+* invariants: the two forms agree, split-and-continue, decode steps == forward;
+* planted mistakes in a copy of the quadratic form are caught by these pins.
+
+The definition is causal linear attention with per-head decay,
+O_t = sum_{j<=t} lam^(t-j) (q_t . k_j) v_j, as reorganised by Lightning
+Attention-2 (Tiling paragraph, mechanism field) and as in the recurrent and
+parallel forms the glossary page "Lightning Attention" lists.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import quadratic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+
+
+# ----------------------------------------------------------------- exact brute force
+def exact_forward(q, k, v, lam, s0=None):
+    """Direct sums of the definition in exact rationals. Returns (O, S_final)."""
+    n, d = len(q), len(q[0])
+    lam = Fraction(lam)
+    O = []
+    for t in range(n):
+        row = [Fraction(0)] * d
+        for j in range(t + 1):
+            w = lam ** (t - j) * sum(Fraction(q[t][a]) * Fraction(k[j][a]) for a in range(d))
+            for c in range(d):
+                row[c] += w * Fraction(v[j][c])
+        if s0 is not None:
+            for c in range(d):
+                row[c] += lam ** (t + 1) * sum(Fraction(q[t][a]) * Fraction(s0[a][c]) for a in range(d))
+        O.append(row)
+    S = [[Fraction(0)] * d for _ in range(d)]
+    for j in range(n):
+        w = lam ** (n - 1 - j)
+        for a in range(d):
+            for c in range(d):
+                S[a][c] += w * Fraction(k[j][a]) * Fraction(v[j][c])
+    if s0 is not None:
+        for a in range(d):
+            for c in range(d):
+                S[a][c] += lam ** n * Fraction(s0[a][c])
+    return O, S
+
+
+def exact_loss(q, k, v, g, lam, s0=None):
+    O, _ = exact_forward(q, k, v, lam, s0)
+    return sum(O[t][c] * Fraction(g[t][c]) for t in range(len(O)) for c in range(len(O[0])))
+
+
+def exact_grads(q, k, v, g, lam, s0=None):
+    """Exact dL/dQ, dL/dK, dL/dV of L = <dO, O>.
+
+    L is affine in each of Q, K, V separately, so each partial derivative is an
+    exact difference of two loss evaluations of the forward definition."""
+    n, d = len(q), len(q[0])
+    zero = [[0] * d for _ in range(n)]
+
+    def unit(t, a):
+        m = [[0] * d for _ in range(n)]
+        m[t][a] = 1
+        return m
+
+    base_q = exact_loss(zero, k, v, g, lam, s0)
+    base_k = exact_loss(q, zero, v, g, lam, s0)
+    base_v = exact_loss(q, k, zero, g, lam, s0)
+    dq = [[exact_loss(unit(t, a), k, v, g, lam, s0) - base_q for a in range(d)] for t in range(n)]
+    dk = [[exact_loss(q, unit(t, a), v, g, lam, s0) - base_k for a in range(d)] for t in range(n)]
+    dv = [[exact_loss(q, k, unit(t, a), g, lam, s0) - base_v for a in range(d)] for t in range(n)]
+    return dq, dk, dv
+
+
+def as_f64(m):
+    return np.array([[float(x) for x in row] for row in m], dtype=np.float64)
+
+
+LAMS = [Fraction(0), Fraction(1, 2), Fraction(3, 4), Fraction(1)]
+
+
+@pytest.mark.parametrize("lam", LAMS)
+@pytest.mark.parametrize("n,d,seed,with_s0", [(1, 1, 0, False), (5, 2, 1, False), (9, 3, 2, True),
+                                              (16, 4, 3, False), (12, 2, 4, True)])
+def test_forward_matches_exact_rationals(lam, n, d, seed, with_s0):
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.integers(-3, 4, size=(n, d)).tolist() for _ in range(3))
+    s0 = rng.integers(-3, 4, size=(d, d)).tolist() if with_s0 else None
+    O_ex, S_ex = exact_forward(q, k, v, lam, s0)
+    O_ex, S_ex = as_f64(O_ex), as_f64(S_ex)
+    lamf = float(lam)
+    o2, s2 = oracle.fwd_recurrent(np.array(q), np.array(k), np.array(v), lamf,
+                                  None if s0 is None else np.array(s0))
+    # Small integers and dyadic lam keep every intermediate exact in binary64.
+    assert np.array_equal(o2, O_ex)
+    assert np.array_equal(s2, S_ex)
+    o1, s1 = oracle.fwd_quadratic(q, k, v, lamf, s0)
+    np.testing.assert_allclose(o1, O_ex, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(s1, S_ex, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("lam", LAMS)
+@pytest.mark.parametrize("n,d,seed,with_s0", [(4, 2, 10, False), (7, 3, 11, True), (10, 2, 12, False)])
+def test_backward_matches_exact_gradients(lam, n, d, seed, with_s0):
+    rng = np.random.default_rng(seed)
+    q, k, v, g = (rng.integers(-3, 4, size=(n, d)).tolist() for _ in range(4))
+    s0 = rng.integers(-3, 4, size=(d, d)).tolist() if with_s0 else None
+    dq_ex, dk_ex, dv_ex = (as_f64(m) for m in exact_grads(q, k, v, g, lam, s0))
+    lamf = float(lam)
+    s0a = None if s0 is None else np.array(s0)
+    dq, dk, dv = oracle.bwd_recurrent(np.array(q), np.array(k), np.array(v), np.array(g), lamf, s0a)
+    assert np.array_equal(dq, dq_ex)
+    assert np.array_equal(dk, dk_ex)
+    assert np.array_equal(dv, dv_ex)
+    dq1, dk1, dv1 = oracle.bwd_quadratic(q, k, v, g, lamf, s0)
+    for a, b in ((dq1, dq_ex), (dk1, dk_ex), (dv1, dv_ex)):
+        np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("lam", LAMS)
+def test_decode_matches_exact_rationals(lam):
+    rng = np.random.default_rng(7)
+    n, d = 8, 3
+    q, k, v = (rng.integers(-3, 4, size=(n, d)).tolist() for _ in range(3))
+    O_ex, S_ex = exact_forward(q, k, v, lam)
+    S = np.zeros((d, d))
+    for t in range(n):
+        o, S = oracle.decode_step(S, np.array(q[t], float), np.array(k[t], float), np.array(v[t], float),
+                                  float(lam))
+        assert np.array_equal(o, as_f64([O_ex[t]])[0])
+    assert np.array_equal(S, as_f64(S_ex))
+
+
+# ----------------------------------------------------------------- hand-worked golden values
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("ex", _golden()["examples"], ids=lambda e: e["name"])
+def test_hand_worked_examples(ex):
+    q, k, v, g = (np.array(ex[key], dtype=np.float64) for key in ("q", "k", "v", "dO"))
+    s0 = np.array(ex["S0"], dtype=np.float64) if "S0" in ex else None
+    lam = ex["lam"]
+    for o, s in (oracle.fwd_recurrent(q, k, v, lam, s0), oracle.fwd_quadratic(q, k, v, lam, s0)):
+        np.testing.assert_allclose(o, ex["O"], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(s, ex["S_final"], rtol=0, atol=1e-14)
+    for grads in (oracle.bwd_recurrent(q, k, v, g, lam, s0), oracle.bwd_quadratic(q, k, v, g, lam, s0)):
+        for got, key in zip(grads, ("dQ", "dK", "dV")):
+            np.testing.assert_allclose(got, ex[key], rtol=0, atol=1e-14, err_msg=key)
+
+
+@pytest.mark.parametrize("ex", _golden()["decode"], ids=lambda e: e["name"])
+def test_hand_worked_decode(ex):
+    o, s = oracle.decode_step(np.array(ex["S"], float), np.array(ex["q"], float),
+                              np.array(ex["k"], float), np.array(ex["v"], float), ex["lam"])
+    np.testing.assert_array_equal(o, ex["o"])
+    np.testing.assert_array_equal(s, ex["S_new"])
+
+
+# ----------------------------------------------------------------- closed forms
+@pytest.mark.parametrize("lam", [1.0, 0.9375, 0.5, 0.0])
+def test_closed_forms_all_ones(lam):
+    n, d = 1000, 16
+    ones = np.ones((n, d))
+    t = np.arange(n, dtype=np.float64)
+    if lam == 1.0:
+        geo_t = t + 1                      # sum_{m=0}^{t} lam^m
+        geo_rev = n - t                    # sum_{m=0}^{n-1-t} lam^m
+        geo_n = float(n)
+    else:
+        geo_t = (1 - lam ** (t + 1)) / (1 - lam)
+        geo_rev = (1 - lam ** (n - t)) / (1 - lam)
+        geo_n = (1 - lam ** n) / (1 - lam)
+    o_exp = d * geo_t[:, None] * ones
+    s_exp = geo_n * np.ones((d, d))
+    for o, s in (oracle.fwd_recurrent(ones, ones, ones, lam), oracle.fwd_quadratic(ones, ones, ones, lam)):
+        np.testing.assert_allclose(o, o_exp, rtol=1e-12)
+        np.testing.assert_allclose(s, s_exp, rtol=1e-12)
+    dq_exp = d * geo_t[:, None] * ones
+    dkv_exp = d * geo_rev[:, None] * ones
+    for dq, dk, dv in (oracle.bwd_recurrent(ones, ones, ones, ones, lam),
+                       oracle.bwd_quadratic(ones, ones, ones, ones, lam)):
+        np.testing.assert_allclose(dq, dq_exp, rtol=1e-12)
+        np.testing.assert_allclose(dk, dkv_exp, rtol=1e-12)
+        np.testing.assert_allclose(dv, dkv_exp, rtol=1e-12)
+
+
+def test_no_decay_is_one_based_i_d_v():
+    """lam = 1 and all-ones q, k, v: the 1-based position i gives O_i = i * d * v."""
+    n, d = 300, 8
+    ones = np.ones((n, d))
+    o, _ = oracle.fwd_recurrent(ones, ones, ones, 1.0)
+    i = np.arange(1, n + 1, dtype=np.float64)
+    np.testing.assert_array_equal(o, (i * d)[:, None] * ones)
+
+
+def test_d1_n2_by_hand():
+    q = np.array([[1.5], [-2.0]]); k = np.array([[3.0], [0.25]]); v = np.array([[2.0], [4.0]])
+    lam = 0.75
+    o, s = oracle.fwd_recurrent(q, k, v, lam)
+    assert o[0, 0] == 1.5 * 3.0 * 2.0
+    assert o[1, 0] == -2.0 * (lam * 3.0 * 2.0 + 0.25 * 4.0)
+    assert s[0, 0] == lam * 6.0 + 1.0
+
+
+# ----------------------------------------------------------------- library special case
+def test_no_decay_equals_library_masked_product():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(5)
+    n, d = 512, 32
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    ref = (torch.matmul(tq, tk.T.contiguous()).tril() @ tv).numpy()
+    o, s = oracle.fwd_recurrent(q, k, v, 1.0)
+    np.testing.assert_allclose(o, ref, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(s, (tk.T.contiguous() @ tv).numpy(), rtol=1e-10, atol=1e-10)
+
+
+# ----------------------------------------------------------------- invariants
+@pytest.mark.parametrize("lam", [0.0, 0.5, 0.97, 1.0])
+def test_two_forms_agree_random(lam):
+    rng = np.random.default_rng(int(lam * 100) + 3)
+    n, d = 700, 16
+    q, k, v, g = (rng.standard_normal((n, d)) / 4 for _ in range(4))
+    s0 = rng.standard_normal((d, d))
+    o1, s1 = oracle.fwd_quadratic(q, k, v, lam, s0)
+    o2, s2 = oracle.fwd_recurrent(q, k, v, lam, s0)
+    assert oracle.rel_l2(o2, o1) < 1e-12 and oracle.rel_l2(s2, s1) < 1e-12
+    for a, b in zip(oracle.bwd_recurrent(q, k, v, g, lam, s0), oracle.bwd_quadratic(q, k, v, g, lam, s0)):
+        assert oracle.rel_l2(a, b) < 1e-12
+
+
+def test_two_forms_agree_per_decay_head():
+    import synth
+    H, n, d = 16, 1024, 32
+    lams = synth.decay_schedule(H).astype(np.float64)
+    q, k, v = (synth.normal(0, i, (H, n, d), d ** -0.5, "f64") for i in (1, 2, 3))
+    o2, s2 = oracle.fwd_recurrent(q, k, v, lams)
+    for h in range(H):
+        o1, s1 = oracle.fwd_quadratic(q[h], k[h], v[h], lams[h])
+        assert oracle.rel_l2(o2[h], o1) < 1e-12
+        assert oracle.rel_l2(s2[h], s1) < 1e-12
+
+
+@pytest.mark.parametrize("m", [1, 63, 64, 65, 200])
+def test_split_and_continue(m):
+    rng = np.random.default_rng(m)
+    n, d, lam = 257, 8, 0.9
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    o, s = oracle.fwd_recurrent(q, k, v, lam)
+    oa, sa = oracle.fwd_recurrent(q[:m], k[:m], v[:m], lam)
+    ob, sb = oracle.fwd_recurrent(q[m:], k[m:], v[m:], lam, sa)
+    np.testing.assert_allclose(np.concatenate([oa, ob]), o, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(sb, s, rtol=1e-12, atol=1e-12)
+
+
+def test_block_states_are_prefix_states():
+    rng = np.random.default_rng(9)
+    n, d, lam, bk = 200, 4, 0.8, 64
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    _, _, sb = oracle.fwd_recurrent(q, k, v, lam, block=bk)
+    assert sb.shape == (4, d, d)
+    assert np.all(sb[0] == 0)
+    for b in range(1, 4):
+        _, s = oracle.fwd_recurrent(q[:b * bk], k[:b * bk], v[:b * bk], lam)
+        np.testing.assert_allclose(sb[b], s, rtol=1e-13, atol=1e-13)
+
+
+def test_linear_in_v_and_q():
+    rng = np.random.default_rng(11)
+    n, d, lam = 100, 6, 0.7
+    q, k, v, v2, q2 = (rng.standard_normal((n, d)) for _ in range(5))
+    o_a, _ = oracle.fwd_recurrent(q, k, v, lam)
+    o_b, _ = oracle.fwd_recurrent(q, k, v2, lam)
+    o_ab, _ = oracle.fwd_recurrent(q, k, 2 * v - 3 * v2, lam)
+    np.testing.assert_allclose(o_ab, 2 * o_a - 3 * o_b, rtol=1e-11, atol=1e-11)
+    o_c, _ = oracle.fwd_recurrent(q2, k, v, lam)
+    o_ac, _ = oracle.fwd_recurrent(q + q2, k, v, lam)
+    np.testing.assert_allclose(o_ac, o_a + o_c, rtol=1e-11, atol=1e-11)
+
+
+def test_adjoint_identity_random():
+    """<dO, J dX> == <J^T dO, dX> for the exact linear maps X -> O (each of Q, K, V)."""
+    rng = np.random.default_rng(13)
+    n, d, lam = 64, 5, 0.85
+    q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+    dq, dk, dv = oracle.bwd_recurrent(q, k, v, g, lam)
+    dX = rng.standard_normal((n, d))
+    # O is linear in Q and in V, so J dX is O evaluated with dX in that slot.
+    lhs_q = np.sum(g * oracle.fwd_recurrent(dX, k, v, lam)[0])
+    lhs_v = np.sum(g * oracle.fwd_recurrent(q, k, dX, lam)[0])
+    lhs_k = np.sum(g * oracle.fwd_recurrent(q, dX, v, lam)[0])
+    assert abs(lhs_q - np.sum(dq * dX)) < 1e-10 * (1 + abs(lhs_q))
+    assert abs(lhs_v - np.sum(dv * dX)) < 1e-10 * (1 + abs(lhs_v))
+    assert abs(lhs_k - np.sum(dk * dX)) < 1e-10 * (1 + abs(lhs_k))
+
+
+def test_decode_equals_forward_random():
+    rng = np.random.default_rng(17)
+    P, n, d = 6, 40, 8
+    lams = np.linspace(0.3, 1.0, P)
+    q, k, v = (rng.standard_normal((P, n, d)) for _ in range(3))
+    o_ref, s_ref = oracle.fwd_recurrent(q, k, v, lams)
+    S = np.zeros((P, d, d))
+    for t in range(n):
+        o, S = oracle.decode_step(S, q[:, t], k[:, t], v[:, t], lams)
+        np.testing.assert_allclose(o, o_ref[:, t], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S, s_ref, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------- the pins catch planted mistakes
+def _brute_force_fails(fwd):
+    rng = np.random.default_rng(21)
+    q, k, v = (rng.integers(-3, 4, size=(9, 3)).tolist() for _ in range(3))
+    O_ex, _ = exact_forward(q, k, v, Fraction(1, 2))
+    o, _ = fwd(q, k, v, 0.5)
+    return not np.allclose(o, as_f64(O_ex), rtol=1e-12, atol=1e-12)
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    orig = quadratic.decay_matrix
+    assert not _brute_force_fails(quadratic.fwd_quadratic)
+    # decay exponent off by one
+    monkeypatch.setattr(quadratic, "decay_matrix", lambda n, lam: orig(n, lam) * lam)
+    assert _brute_force_fails(quadratic.fwd_quadratic)
+    # diagonal dropped (strictly causal)
+    monkeypatch.setattr(quadratic, "decay_matrix", lambda n, lam: np.tril(orig(n, lam), -1))
+    assert _brute_force_fails(quadratic.fwd_quadratic)
+    # anti-causal mask (transposed decay matrix)
+    monkeypatch.setattr(quadratic, "decay_matrix", lambda n, lam: orig(n, lam).T)
+    assert _brute_force_fails(quadratic.fwd_quadratic)
+    monkeypatch.setattr(quadratic, "decay_matrix", orig)
+
+    # q and k swapped in the score (P = K Q^T): caught by the brute force
+    def swapped(q, k, v, lam):
+        q, k, v = (np.asarray(x, float) for x in (q, k, v))
+        D = orig(len(q), lam)
+        return ((k @ q.T) * D) @ v, None
+    assert _brute_force_fails(swapped)
