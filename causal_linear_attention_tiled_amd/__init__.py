@@ -1,0 +1,209 @@
+"""Python binding of liblinattn (tiled causal linear attention with per-head decay, gfx950).
+
+Argument marshalling only: every function here checks tensor types, takes device
+pointers and the current HIP stream from PyTorch, and calls the C entry point of
+the same name in ``liblinattn.so`` (declared in ``include/liblinattn.h``).  All
+arithmetic runs in the library's HIP kernels; there is no fallback.  If the
+shared library is missing or fails to load, importing this package raises.
+
+Layouts: Q, K, V, O, dO, dQ, dK, dV are contiguous [B, H, N, D] tensors of
+dtype float32 or bfloat16 on one GPU; states are contiguous [B, H, D, D]
+float32; ``lam`` is a sequence (or CPU tensor / array) of H floats in [0, 1].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblinattn.so")
+
+LA_F32, LA_BF16 = 0, 1
+LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EALIGN, LA_EWORKSPACE, LA_EHIP, LA_ENODEV = range(7)
+
+
+class LaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: status {code}: {la_strerror(code)}")
+
+
+class la_prof_entry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"liblinattn.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.la_fwd.argtypes = [vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.la_fwd.restype = ctypes.c_int
+    lib.la_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
+    lib.la_fwd_workspace_bytes.restype = sz
+    lib.la_bwd.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.la_bwd.restype = ctypes.c_int
+    lib.la_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
+    lib.la_bwd_workspace_bytes.restype = sz
+    lib.la_decode_step.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i32, vp, vp]
+    lib.la_decode_step.restype = ctypes.c_int
+    lib.la_strerror.argtypes = [ctypes.c_int]
+    lib.la_strerror.restype = ctypes.c_char_p
+    lib.la_version.restype = ctypes.c_int
+    lib.la_prof_enable.argtypes = [ctypes.c_int]
+    lib.la_prof_collect.argtypes = [ctypes.POINTER(la_prof_entry), ctypes.c_int]
+    return lib
+
+
+lib = _load()
+
+EXPORTS = ("la_fwd", "la_fwd_workspace_bytes", "la_bwd", "la_bwd_workspace_bytes", "la_decode_step",
+           "la_strerror", "la_version", "la_prof_enable", "la_prof_collect")
+
+
+def la_strerror(code: int) -> str:
+    return lib.la_strerror(code).decode()
+
+
+def la_version() -> int:
+    return lib.la_version()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LA_F32
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _lam_array(lam, H: int):
+    vals = [float(x) for x in (lam.tolist() if hasattr(lam, "tolist") else lam)]
+    if len(vals) != H:
+        raise ValueError(f"lam has {len(vals)} values, expected H={H}")
+    return (ctypes.c_float * H)(*vals)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_seq(name, t, ref=None):
+    if t.dim() != 4 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [B, H, N, D] tensor")
+    if ref is not None and (t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device):
+        raise ValueError(f"{name} must match Q in shape, dtype and device")
+
+
+def _check_state(name, t, B, H, D, device):
+    if t is None:
+        return
+    if t.dtype != torch.float32 or tuple(t.shape) != (B, H, D, D) or not t.is_contiguous() \
+            or t.device != device:
+        raise ValueError(f"{name} must be a contiguous float32 [B, H, D, D] tensor on {device}")
+
+
+def la_fwd_workspace_bytes(B, H, N, D, Bk, dtype_code) -> int:
+    return int(lib.la_fwd_workspace_bytes(B, H, N, D, Bk, dtype_code))
+
+
+def la_bwd_workspace_bytes(B, H, N, D, Bk, dtype_code) -> int:
+    return int(lib.la_bwd_workspace_bytes(B, H, N, D, Bk, dtype_code))
+
+
+def _workspace(nbytes, device, ws):
+    if nbytes == 0:
+        return ws
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return ws
+
+
+def la_fwd(q, k, v, lam, Bk: int = 64, kv_in=None, out=None, kv_out=None, want_state: bool = True,
+           ws=None):
+    """O (and the final float32 state) of causal linear attention with per-head decay.
+
+    Returns (O, kv_out); kv_out is None when ``want_state`` is False and none is given."""
+    _check_seq("Q", q)
+    _check_seq("K", k, q)
+    _check_seq("V", v, q)
+    B, H, N, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check_seq("O", out, q)
+    if kv_out is None and want_state:
+        kv_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    _check_state("kv_in", kv_in, B, H, D, q.device)
+    _check_state("kv_out", kv_out, B, H, D, q.device)
+    code = _dtype_code(q)
+    nbytes = la_fwd_workspace_bytes(B, H, N, D, Bk, code)
+    ws = _workspace(nbytes, q.device, ws)
+    rc = lib.la_fwd(_ptr(q), _ptr(k), _ptr(v), _lam_array(lam, H), B, H, N, D, Bk, code, _ptr(kv_in),
+                    _ptr(out), _ptr(kv_out), _ptr(ws), nbytes if ws is not None else 0, _stream(q.device))
+    if rc != LA_OK:
+        raise LaError(rc, "la_fwd")
+    return out, kv_out
+
+
+def la_bwd(q, k, v, dout, lam, Bk: int = 64, kv_in=None, dq=None, dk=None, dv=None, ws=None):
+    """dQ, dK, dV of L = <dO, O> for la_fwd (kv_in held constant)."""
+    for name, t in (("Q", q), ("K", k), ("V", v), ("dO", dout)):
+        _check_seq(name, t, q)
+    B, H, N, D = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        _check_seq(name, t, q)
+    _check_state("kv_in", kv_in, B, H, D, q.device)
+    code = _dtype_code(q)
+    nbytes = la_bwd_workspace_bytes(B, H, N, D, Bk, code)
+    ws = _workspace(nbytes, q.device, ws)
+    rc = lib.la_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _lam_array(lam, H), B, H, N, D, Bk, code,
+                    _ptr(kv_in), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), nbytes if ws is not None else 0,
+                    _stream(q.device))
+    if rc != LA_OK:
+        raise LaError(rc, "la_bwd")
+    return dq, dk, dv
+
+
+def la_decode_step(state, q, k, v, lam, out=None):
+    """One recurrent step S <- lam S + k v^T, o = q S; ``state`` [Bs, H, D, D] float32 is updated in place.
+
+    q, k, v are [Bs, H, D]; returns o."""
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [Bs, H, D] tensor")
+    Bs, H, D = q.shape
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must match q")
+    if state.dtype != torch.float32 or tuple(state.shape) != (Bs, H, D, D) or not state.is_contiguous():
+        raise ValueError("state must be a contiguous float32 [Bs, H, D, D] tensor")
+    out = torch.empty_like(q) if out is None else out
+    rc = lib.la_decode_step(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _lam_array(lam, H), Bs, H, D,
+                            _dtype_code(q), _ptr(out), _stream(q.device))
+    if rc != LA_OK:
+        raise LaError(rc, "la_decode_step")
+    return out
+
+
+def la_prof_enable(on: bool = True) -> None:
+    lib.la_prof_enable(1 if on else 0)
+
+
+def la_prof_collect(max_entries: int = 64) -> dict:
+    """{kernel name: (launches, total milliseconds)} since the last collect."""
+    arr = (la_prof_entry * max_entries)()
+    n = lib.la_prof_collect(arr, max_entries)
+    if n < 0:
+        raise LaError(-n, "la_prof_collect")
+    return {arr[i].name.decode(): (int(arr[i].launches), float(arr[i].total_ms)) for i in range(n)}

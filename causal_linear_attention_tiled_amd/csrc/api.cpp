@@ -1,0 +1,399 @@
+// Host side of liblinattn: argument validation, the chunk plan, kernel
+// dispatch and optional per-kernel profiling.  See include/liblinattn.h for
+// the contract of every exported call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/liblinattn.h"
+#include "la_internal.h"
+
+namespace {
+
+using la::LamArgs;
+
+// Target workgroup count for the chunk plan: two per compute unit of an
+// MI355X (256 CUs), so that a launch fills the chip with some slack.
+constexpr int64_t kTargetWorkgroups = 512;
+// A chunk should span at least this many blocks, so the per-chunk state
+// traffic (a few D x D float32 matrices) stays small next to its tokens.
+constexpr int64_t kMinBlocksPerChunk = 4;
+
+thread_local char g_err[256];
+
+int hip_fail(hipError_t e, const char* where) {
+    std::snprintf(g_err, sizeof(g_err), "%s: %s", where, hipGetErrorString(e));
+    return LA_EHIP;
+}
+
+// ------------------------------------------------------------------ profiling
+struct ProfRec {
+    const char* name;
+    hipEvent_t start, stop;
+};
+std::atomic<int> g_prof_on{0};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof;
+
+// Enqueue one kernel through `fn`, bracketed by events when profiling.
+template <typename Fn>
+int launch(const char* name, hipStream_t s, Fn&& fn) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    const bool prof = g_prof_on.load(std::memory_order_relaxed) != 0;
+    if (prof) {
+        if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)
+            return hip_fail(hipGetLastError(), "hipEventCreate");
+        hipError_t er = hipEventRecord(e0, s);
+        if (er != hipSuccess) return hip_fail(er, "hipEventRecord");
+    }
+    fn();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, name);
+    if (prof) {
+        hipError_t er = hipEventRecord(e1, s);
+        if (er != hipSuccess) return hip_fail(er, "hipEventRecord");
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        g_prof.push_back({name, e0, e1});
+    }
+    return LA_OK;
+}
+
+// ------------------------------------------------------------------ validation
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    const void* p;
+    size_t bytes;
+};
+
+bool overlap(const Range& a, const Range& b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    auto a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a <= 0 || b <= 0) return false;
+    if (a > INT64_MAX / b) return false;
+    *out = a * b;
+    return true;
+}
+
+bool supported_D(int64_t D) { return D == 16 || D == 32 || D == 64 || D == 128; }
+bool supported_Bk(int64_t Bk) { return Bk == 16 || Bk == 32 || Bk == 64 || Bk == 128; }
+
+// Shape checks common to la_fwd / la_bwd and their size queries.
+int check_shape(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype, int64_t* elems) {
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_EINVAL;
+    if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || Bk <= 0) return LA_EINVAL;
+    if (!supported_D(D) || !supported_Bk(Bk) || H > la::kMaxHeads) return LA_EUNSUPPORTED;
+    int64_t t;
+    if (!mul_ok(B, H, &t) || !mul_ok(t, N, &t) || !mul_ok(t, D, &t) || t > (INT64_MAX / 8)) return LA_EINVAL;
+    *elems = t;
+    return LA_OK;
+}
+
+int load_lambda(const float* lambda, int64_t H, LamArgs* out) {
+    if (!lambda) return LA_EINVAL;
+    std::memset(out, 0, sizeof(*out));
+    for (int64_t h = 0; h < H; ++h) {
+        const float x = lambda[h];
+        if (!(x >= 0.f && x <= 1.f)) return LA_EINVAL;  // also rejects NaN
+        out->lam[h] = x;
+    }
+    return LA_OK;
+}
+
+// ------------------------------------------------------------------ plan
+struct Plan {
+    int chunks;
+    int64_t L;     // chunk length in tokens (multiple of Bk)
+    bool mfma;
+};
+
+bool force_generic() {
+    const char* e = std::getenv("LA_KERNEL");
+    return e && std::strcmp(e, "generic") == 0;
+}
+
+Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype) {
+    Plan p;
+    const int64_t pairs = B * H;
+    const int64_t nb = (N + Bk - 1) / Bk;
+    int64_t C = 1;
+    const char* env = std::getenv("LA_CHUNKS");
+    if (env && std::atoll(env) > 0) {
+        C = std::atoll(env);
+    } else if (pairs < kTargetWorkgroups) {
+        C = (kTargetWorkgroups + pairs - 1) / pairs;
+        C = std::min<int64_t>(C, std::max<int64_t>(1, nb / kMinBlocksPerChunk));
+    }
+    C = std::max<int64_t>(1, std::min<int64_t>(C, nb));
+    const int64_t bpc = (nb + C - 1) / C;
+    p.L = bpc * Bk;
+    p.chunks = static_cast<int>((nb + bpc - 1) / bpc);
+    p.mfma = dtype == LA_BF16 && la::mfma_supported(static_cast<int>(D), Bk) && !force_generic();
+    return p;
+}
+
+size_t slot_bytes(int64_t pairs, const Plan& p, int64_t D) {
+    if (p.chunks <= 1) return 0;
+    return static_cast<size_t>(pairs) * static_cast<size_t>(p.chunks - 1) * static_cast<size_t>(D * D) *
+           sizeof(float);
+}
+
+size_t round_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// ------------------------------------------------------------------ sweeps
+// Forward-direction sweep (O of la_fwd, or dQ of la_bwd with operands
+// (dO, V, K) and the transposed initial state).
+int run_forward_sweep(const void* q, const void* k, const void* v, void* out, const float* kv_in,
+                      int kv_in_t, float* kv_out, float* slots, int64_t pairs, int64_t N, int64_t D,
+                      int32_t Bk, int32_t H, int bf16, const Plan& p, const LamArgs& lam, hipStream_t s,
+                      const char* tag) {
+    int rc;
+    if (p.chunks > 1) {
+        la::ChunkStateArgs cs{k, v, slots, N, p.L, static_cast<int>(D), Bk, H, p.chunks, pairs, 0};
+        if (p.mfma)
+            rc = launch("chunk_state_mfma", s, [&] { la::launch_chunk_state_mfma(cs, lam, s); });
+        else
+            rc = launch("chunk_state_generic", s, [&] { la::launch_chunk_state_generic(cs, lam, bf16, s); });
+        if (rc) return rc;
+        la::ScanArgs sc{slots, kv_in, kv_in_t, p.L, static_cast<int>(D), H, p.chunks, pairs, 0};
+        rc = launch("state_scan", s, [&] { la::launch_scan(sc, lam, s); });
+        if (rc) return rc;
+    }
+    la::SweepArgs a{};
+    a.a = q;
+    a.b = k;
+    a.c = v;
+    a.out0 = out;
+    a.slots = slots;
+    a.kv_in = kv_in;
+    a.kv_in_transposed = kv_in_t;
+    a.kv_out = kv_out;
+    a.N = N;
+    a.L = p.L;
+    a.D = static_cast<int>(D);
+    a.Bk = Bk;
+    a.H = H;
+    a.chunks = p.chunks;
+    a.pairs = pairs;
+    if (p.mfma) return launch(tag[0] == 'd' ? "dq_mfma" : "fwd_mfma", s, [&] { la::launch_fwd_mfma(a, lam, s); });
+    return launch(tag[0] == 'd' ? "dq_generic" : "fwd_generic", s, [&] { la::launch_fwd_generic(a, lam, bf16, s); });
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+extern "C" {
+
+int la_version(void) { return 10000; }
+
+const char* la_strerror(int code) {
+    switch (code) {
+        case LA_OK: return "ok";
+        case LA_EINVAL: return "invalid argument";
+        case LA_EUNSUPPORTED: return "unsupported shape (D in {16,32,64,128}, Bk in {16,32,64,128}, H <= 256)";
+        case LA_EALIGN: return "device pointer not 16-byte aligned";
+        case LA_EWORKSPACE: return "workspace missing or too small";
+        case LA_EHIP: {
+            static thread_local char buf[320];
+            std::snprintf(buf, sizeof(buf), "HIP error: %s", g_err);
+            return buf;
+        }
+        case LA_ENODEV: return "no HIP device";
+        default: return "unknown status";
+    }
+}
+
+size_t la_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype) {
+    int64_t elems;
+    if (check_shape(B, H, N, D, Bk, dtype, &elems) != LA_OK) return 0;
+    const Plan p = make_plan(B, H, N, D, Bk, dtype);
+    return slot_bytes(B * H, p, D);
+}
+
+size_t la_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype) {
+    int64_t elems;
+    if (check_shape(B, H, N, D, Bk, dtype, &elems) != LA_OK) return 0;
+    const Plan p = make_plan(B, H, N, D, Bk, dtype);
+    const size_t one = slot_bytes(B * H, p, D);
+    return one ? 2 * round_up(one) : 0;
+}
+
+int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int64_t B, int64_t H,
+           int64_t N, int64_t D, int32_t Bk, int32_t dtype, const float* kv_in, void* O, float* kv_out,
+           void* ws, size_t ws_bytes, void* hip_stream) {
+    int64_t elems;
+    int rc = check_shape(B, H, N, D, Bk, dtype, &elems);
+    if (rc) return rc;
+    if (!Q || !K || !V || !O) return LA_EINVAL;
+    LamArgs lam;
+    if ((rc = load_lambda(lambda, H, &lam))) return rc;
+    for (const void* p : {Q, K, V, static_cast<const void*>(O), static_cast<const void*>(kv_in),
+                          static_cast<const void*>(kv_out), static_cast<const void*>(ws)})
+        if (p && !aligned16(p)) return LA_EALIGN;
+    const size_t tb = static_cast<size_t>(elems) * (dtype == LA_BF16 ? 2 : 4);
+    const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
+    const Plan p = make_plan(B, H, N, D, Bk, dtype);
+    const size_t need = slot_bytes(B * H, p, D);
+    if (need && (!ws || ws_bytes < need)) return LA_EWORKSPACE;
+    const Range rq{Q, tb}, rk{K, tb}, rv{V, tb}, ro{O, tb}, rin{kv_in, kv_in ? sb : 0},
+        rout{kv_out, kv_out ? sb : 0}, rws{ws, need};
+    for (const Range& r : {rq, rk, rv, rin})
+        if (overlap(ro, r) || overlap(rout, r) || overlap(rws, r)) return LA_EINVAL;
+    if (overlap(ro, rout) || overlap(ro, rws) || overlap(rout, rws)) return LA_EINVAL;
+
+    int dev_count = 0;
+    if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count == 0) return LA_ENODEV;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    return run_forward_sweep(Q, K, V, O, kv_in, 0, kv_out, static_cast<float*>(ws), B * H, N, D, Bk,
+                             static_cast<int32_t>(H), dtype == LA_BF16, p, lam, s, "fwd");
+}
+
+int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const float* lambda, int64_t B,
+           int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype, const float* kv_in, void* dQ,
+           void* dK, void* dV, void* ws, size_t ws_bytes, void* hip_stream) {
+    int64_t elems;
+    int rc = check_shape(B, H, N, D, Bk, dtype, &elems);
+    if (rc) return rc;
+    if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return LA_EINVAL;
+    LamArgs lam;
+    if ((rc = load_lambda(lambda, H, &lam))) return rc;
+    for (const void* p : {Q, K, V, dO, static_cast<const void*>(kv_in), static_cast<const void*>(dQ),
+                          static_cast<const void*>(dK), static_cast<const void*>(dV),
+                          static_cast<const void*>(ws)})
+        if (p && !aligned16(p)) return LA_EALIGN;
+    const size_t tb = static_cast<size_t>(elems) * (dtype == LA_BF16 ? 2 : 4);
+    const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
+    const Plan p = make_plan(B, H, N, D, Bk, dtype);
+    const size_t one = slot_bytes(B * H, p, D);
+    const size_t need = one ? 2 * round_up(one) : 0;
+    if (need && (!ws || ws_bytes < need)) return LA_EWORKSPACE;
+    const Range ins[] = {{Q, tb}, {K, tb}, {V, tb}, {dO, tb}, {kv_in, kv_in ? sb : 0}};
+    const Range outs[] = {{dQ, tb}, {dK, tb}, {dV, tb}, {ws, need}};
+    for (const Range& o : outs)
+        for (const Range& i : ins)
+            if (overlap(o, i)) return LA_EINVAL;
+    for (int a = 0; a < 4; ++a)
+        for (int b = a + 1; b < 4; ++b)
+            if (overlap(outs[a], outs[b])) return LA_EINVAL;
+
+    int dev_count = 0;
+    if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count == 0) return LA_ENODEV;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    float* slots_q = static_cast<float*>(ws);
+    float* slots_kv = one ? reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(one)) : nullptr;
+    const int bf16 = dtype == LA_BF16;
+    const int64_t pairs = B * H;
+    const int32_t Hi = static_cast<int32_t>(H);
+
+    // dQ: the forward sweep with (q, k, v) = (dO, V, K) and the transposed initial state.
+    rc = run_forward_sweep(dO, V, K, dQ, kv_in, 1, nullptr, slots_q, pairs, N, D, Bk, Hi, bf16, p, lam, s, "dq");
+    if (rc) return rc;
+
+    // dK, dV: reverse sweep carrying dS, with a chunked suffix over blocks.
+    if (p.chunks > 1) {
+        la::ChunkStateArgs cs{Q, dO, slots_kv, N, p.L, static_cast<int>(D), Bk, Hi, p.chunks, pairs, 1};
+        if (p.mfma)
+            rc = launch("chunk_state_rev_mfma", s, [&] { la::launch_chunk_state_mfma(cs, lam, s); });
+        else
+            rc = launch("chunk_state_rev_generic", s, [&] { la::launch_chunk_state_generic(cs, lam, bf16, s); });
+        if (rc) return rc;
+        la::ScanArgs sc{slots_kv, nullptr, 0, p.L, static_cast<int>(D), Hi, p.chunks, pairs, 1};
+        rc = launch("state_scan_rev", s, [&] { la::launch_scan(sc, lam, s); });
+        if (rc) return rc;
+    }
+    la::SweepArgs a{};
+    a.a = Q;
+    a.b = K;
+    a.c = V;
+    a.g = dO;
+    a.out0 = dK;
+    a.out1 = dV;
+    a.slots = slots_kv;
+    a.N = N;
+    a.L = p.L;
+    a.D = static_cast<int>(D);
+    a.Bk = Bk;
+    a.H = Hi;
+    a.chunks = p.chunks;
+    a.pairs = pairs;
+    if (p.mfma) return launch("dkdv_mfma", s, [&] { la::launch_rev_mfma(a, lam, s); });
+    return launch("dkdv_generic", s, [&] { la::launch_rev_generic(a, lam, bf16, s); });
+}
+
+int la_decode_step(float* state, const void* q, const void* k, const void* v, const float* lambda,
+                   int64_t Bs, int64_t H, int64_t D, int32_t dtype, void* o, void* hip_stream) {
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_EINVAL;
+    if (Bs <= 0 || H <= 0 || D <= 0) return LA_EINVAL;
+    if (!supported_D(D) || H > la::kMaxHeads) return LA_EUNSUPPORTED;
+    if (!state || !q || !k || !v || !o) return LA_EINVAL;
+    LamArgs lam;
+    int rc = load_lambda(lambda, H, &lam);
+    if (rc) return rc;
+    for (const void* p : {static_cast<const void*>(state), q, k, v, static_cast<const void*>(o)})
+        if (!aligned16(p)) return LA_EALIGN;
+    int64_t pairs;
+    if (!mul_ok(Bs, H, &pairs) || pairs > (int64_t(1) << 31)) return LA_EINVAL;
+    const size_t vb = static_cast<size_t>(pairs * D) * (dtype == LA_BF16 ? 2 : 4);
+    const size_t sb = static_cast<size_t>(pairs * D * D) * sizeof(float);
+    const Range rs{state, sb}, ro{o, vb};
+    for (const Range& r : {Range{q, vb}, Range{k, vb}, Range{v, vb}})
+        if (overlap(rs, r) || overlap(ro, r)) return LA_EINVAL;
+    if (overlap(rs, ro)) return LA_EINVAL;
+
+    int dev_count = 0;
+    if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count == 0) return LA_ENODEV;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    la::DecodeArgs a{state, q, k, v, o, static_cast<int>(D), static_cast<int>(H), pairs};
+    return launch("decode", s, [&] { la::launch_decode(a, lam, dtype == LA_BF16, s); });
+}
+
+int la_prof_enable(int on) {
+    g_prof_on.store(on ? 1 : 0);
+    return LA_OK;
+}
+
+int la_prof_collect(la_prof_entry* out, int max_entries) {
+    std::vector<ProfRec> recs;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        recs.swap(g_prof);
+    }
+    std::vector<la_prof_entry> acc;
+    int rc = LA_OK;
+    for (const ProfRec& r : recs) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+        if (e != hipSuccess) rc = hip_fail(e, "la_prof_collect");
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+        auto it = std::find_if(acc.begin(), acc.end(),
+                               [&](const la_prof_entry& x) { return std::strcmp(x.name, r.name) == 0; });
+        if (it == acc.end()) {
+            la_prof_entry x{};
+            std::snprintf(x.name, sizeof(x.name), "%s", r.name);
+            acc.push_back(x);
+            it = acc.end() - 1;
+        }
+        it->launches += 1;
+        it->total_ms += ms;
+    }
+    if (rc) return -rc;
+    const int n = std::min<int>(max_entries, static_cast<int>(acc.size()));
+    for (int i = 0; i < n; ++i) out[i] = acc[i];
+    return n;
+}
+
+}  // extern "C"

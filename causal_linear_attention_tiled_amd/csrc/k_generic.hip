@@ -1,0 +1,322 @@
+// Generic kernels: every shape the library accepts (D <= 128, Bk <= 128,
+// float32 or bfloat16 storage), plain float32 arithmetic, no matrix cores.
+// They follow the block decomposition of Lightning Attention-2 (Tiling
+// paragraph: intra-block part as ordinary masked attention, inter-block part
+// through the carried key-value state) and serve as the path for shapes the
+// MFMA kernels do not cover, and for float32 storage.
+//
+// One workgroup handles one (sequence, chunk).  The D x D float32 state and
+// one Bk x Bk score tile live in LDS; operands are read from global memory
+// (through the caches) as they are needed.
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+constexpr int kMaxD = 128;
+constexpr int kMaxBk = 128;
+
+struct Tile {
+    float state[kMaxD * kMaxD];  // running state, [D][D]
+    float score[kMaxBk * kMaxBk];  // masked, decayed scores of one block, [Bk][Bk]
+    float pw[kMaxBk + 1];        // lam^e, e = 0..Bk
+};
+
+__device__ __forceinline__ void fill_powers(float* pw, float lam, int Bk) {
+    for (int e = threadIdx.x; e <= Bk; e += kThreads) pw[e] = lam_pow(lam, e);
+}
+
+// Forward sweep over one chunk:
+//   O_b = diag(lam^(s+1)) Q_b S + (Q_b K_b^T o M) V_b,  S <- lam^m S + (diag(lam^(m-1-s)) K_b)^T V_b
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs lam) {
+    __shared__ Tile sh;
+    const int64_t pair = blockIdx.x / a.chunks;
+    const int c = blockIdx.x % a.chunks;
+    const int D = a.D, Bk = a.Bk, tid = threadIdx.x;
+    const float lv = lam.lam[pair % a.H];
+    const int64_t t_begin = static_cast<int64_t>(c) * a.L;
+    const int64_t t_end = min(a.N, t_begin + a.L);
+    const int64_t base = pair * a.N * D;
+    fill_powers(sh.pw, lv, Bk);
+
+    const float* init = nullptr;
+    bool transposed = false;
+    if (c == 0) {
+        if (a.kv_in) {
+            init = a.kv_in + pair * D * D;
+            transposed = a.kv_in_transposed != 0;
+        }
+    } else {
+        init = a.slots + (pair * (a.chunks - 1) + (c - 1)) * D * D;
+    }
+    for (int i = tid; i < D * D; i += kThreads) {
+        float x = 0.f;
+        if (init) x = transposed ? init[(i % D) * D + i / D] : init[i];
+        sh.state[i] = x;
+    }
+    __syncthreads();
+
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += Bk) {
+        const int m = static_cast<int>(min(static_cast<int64_t>(Bk), t_end - t0));
+        const int64_t r0 = base + t0 * D;
+        for (int i = tid; i < m * m; i += kThreads) {
+            const int s = i / m, s2 = i % m;
+            float x = 0.f;
+            if (s2 <= s) {
+                for (int f = 0; f < D; ++f) x += ld<BF16>(a.a, r0 + s * D + f) * ld<BF16>(a.b, r0 + s2 * D + f);
+                x *= sh.pw[s - s2];
+            }
+            sh.score[s * kMaxBk + s2] = x;
+        }
+        __syncthreads();
+        for (int i = tid; i < m * D; i += kThreads) {
+            const int s = i / D, col = i % D;
+            float inter = 0.f, intra = 0.f;
+            for (int f = 0; f < D; ++f) inter += ld<BF16>(a.a, r0 + s * D + f) * sh.state[f * D + col];
+            for (int s2 = 0; s2 <= s; ++s2) intra += sh.score[s * kMaxBk + s2] * ld<BF16>(a.c, r0 + s2 * D + col);
+            st<BF16>(a.out0, r0 + s * D + col, sh.pw[s + 1] * inter + intra);
+        }
+        __syncthreads();
+        for (int i = tid; i < D * D; i += kThreads) {
+            const int f = i / D, col = i % D;
+            float acc = 0.f;
+            for (int s = 0; s < m; ++s)
+                acc += sh.pw[m - 1 - s] * ld<BF16>(a.b, r0 + s * D + f) * ld<BF16>(a.c, r0 + s * D + col);
+            sh.state[i] = sh.pw[m] * sh.state[i] + acc;
+        }
+        __syncthreads();
+    }
+    if (a.kv_out && c == a.chunks - 1) {
+        float* dst = a.kv_out + pair * D * D;
+        for (int i = tid; i < D * D; i += kThreads) dst[i] = sh.state[i];
+    }
+}
+
+// Reverse sweep over one chunk (blocks from last to first), carrying
+// dS = sum_{i >= end of block} lam^(i - end) q_i dO_i^T:
+//   dK_b = (G o M)^T Q_b + diag(lam^(m-s)) V_b dS^T,   G = dO_b V_b^T
+//   dV_b = (P o M)^T dO_b + diag(lam^(m-s)) K_b dS,    P = Q_b K_b^T
+//   dS  <- lam^m dS + (diag(lam^s) Q_b)^T dO_b
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs lam) {
+    __shared__ Tile sh;
+    const int64_t pair = blockIdx.x / a.chunks;
+    const int c = blockIdx.x % a.chunks;
+    const int D = a.D, Bk = a.Bk, tid = threadIdx.x;
+    const float lv = lam.lam[pair % a.H];
+    const int64_t t_begin = static_cast<int64_t>(c) * a.L;
+    const int64_t t_end = min(a.N, t_begin + a.L);
+    const int64_t base = pair * a.N * D;
+    fill_powers(sh.pw, lv, Bk);
+    const float* init = (c < a.chunks - 1) ? a.slots + (pair * (a.chunks - 1) + c) * D * D : nullptr;
+    for (int i = tid; i < D * D; i += kThreads) sh.state[i] = init ? init[i] : 0.f;
+    __syncthreads();
+
+    const int64_t nblk = (t_end - t_begin + Bk - 1) / Bk;
+    for (int64_t bi = nblk - 1; bi >= 0; --bi) {
+        const int64_t t0 = t_begin + bi * Bk;
+        const int m = static_cast<int>(min(static_cast<int64_t>(Bk), t_end - t0));
+        const int64_t r0 = base + t0 * D;
+        // G[i][j] = lam^(i-j) dO_i . v_j for i >= j
+        for (int idx = tid; idx < m * m; idx += kThreads) {
+            const int i = idx / m, j = idx % m;
+            float x = 0.f;
+            if (j <= i) {
+                for (int f = 0; f < D; ++f) x += ld<BF16>(a.g, r0 + i * D + f) * ld<BF16>(a.c, r0 + j * D + f);
+                x *= sh.pw[i - j];
+            }
+            sh.score[i * kMaxBk + j] = x;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < m * D; idx += kThreads) {
+            const int j = idx / D, f = idx % D;
+            float intra = 0.f, inter = 0.f;
+            for (int i = j; i < m; ++i) intra += sh.score[i * kMaxBk + j] * ld<BF16>(a.a, r0 + i * D + f);
+            for (int col = 0; col < D; ++col) inter += sh.state[f * D + col] * ld<BF16>(a.c, r0 + j * D + col);
+            st<BF16>(a.out0, r0 + j * D + f, intra + sh.pw[m - j] * inter);
+        }
+        __syncthreads();
+        // P[i][j] = lam^(i-j) q_i . k_j for i >= j
+        for (int idx = tid; idx < m * m; idx += kThreads) {
+            const int i = idx / m, j = idx % m;
+            float x = 0.f;
+            if (j <= i) {
+                for (int f = 0; f < D; ++f) x += ld<BF16>(a.a, r0 + i * D + f) * ld<BF16>(a.b, r0 + j * D + f);
+                x *= sh.pw[i - j];
+            }
+            sh.score[i * kMaxBk + j] = x;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < m * D; idx += kThreads) {
+            const int j = idx / D, col = idx % D;
+            float intra = 0.f, inter = 0.f;
+            for (int i = j; i < m; ++i) intra += sh.score[i * kMaxBk + j] * ld<BF16>(a.g, r0 + i * D + col);
+            for (int f = 0; f < D; ++f) inter += ld<BF16>(a.b, r0 + j * D + f) * sh.state[f * D + col];
+            st<BF16>(a.out1, r0 + j * D + col, intra + sh.pw[m - j] * inter);
+        }
+        __syncthreads();
+        for (int idx = tid; idx < D * D; idx += kThreads) {
+            const int f = idx / D, col = idx % D;
+            float acc = 0.f;
+            for (int s = 0; s < m; ++s)
+                acc += sh.pw[s] * ld<BF16>(a.a, r0 + s * D + f) * ld<BF16>(a.g, r0 + s * D + col);
+            sh.state[idx] = sh.pw[m] * sh.state[idx] + acc;
+        }
+        __syncthreads();
+    }
+}
+
+// Aggregate state of one chunk, started from zero (see ChunkStateArgs).
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_chunk_state_generic(ChunkStateArgs a, LamArgs lam) {
+    __shared__ float state[kMaxD * kMaxD];
+    __shared__ float pw[kMaxBk + 1];
+    const int per = a.chunks - 1;
+    const int64_t pair = blockIdx.x / per;
+    const int slot = blockIdx.x % per;
+    const int c = a.reverse ? slot + 1 : slot;
+    const int D = a.D, Bk = a.Bk, tid = threadIdx.x;
+    fill_powers(pw, lam.lam[pair % a.H], Bk);
+    for (int i = tid; i < D * D; i += kThreads) state[i] = 0.f;
+    __syncthreads();
+    const int64_t t_begin = static_cast<int64_t>(c) * a.L;
+    const int64_t t_end = min(a.N, t_begin + a.L);
+    const int64_t base = pair * a.N * D;
+    const int64_t nblk = (t_end - t_begin + Bk - 1) / Bk;
+    for (int64_t n = 0; n < nblk; ++n) {
+        const int64_t bi = a.reverse ? nblk - 1 - n : n;
+        const int64_t t0 = t_begin + bi * Bk;
+        const int m = static_cast<int>(min(static_cast<int64_t>(Bk), t_end - t0));
+        const int64_t r0 = base + t0 * D;
+        for (int i = tid; i < D * D; i += kThreads) {
+            const int f = i / D, col = i % D;
+            float acc = 0.f;
+            for (int s = 0; s < m; ++s) {
+                const float w = a.reverse ? pw[s] : pw[m - 1 - s];
+                acc += w * ld<BF16>(a.x, r0 + s * D + f) * ld<BF16>(a.y, r0 + s * D + col);
+            }
+            state[i] = pw[m] * state[i] + acc;
+        }
+        __syncthreads();
+    }
+    float* dst = a.slots + (pair * per + slot) * D * D;
+    for (int i = tid; i < D * D; i += kThreads) dst[i] = state[i];
+}
+
+__global__ __launch_bounds__(kThreads) void k_scan(ScanArgs a, LamArgs lam) {
+    const int DD = a.D * a.D;
+    const int per_pair = (DD + kThreads - 1) / kThreads;
+    const int64_t pair = blockIdx.x / per_pair;
+    const int e = (blockIdx.x % per_pair) * kThreads + threadIdx.x;
+    if (e >= DD) return;
+    const float lamL = lam_pow(lam.lam[pair % a.H], a.L);
+    float* sl = a.slots + pair * (a.chunks - 1) * DD + e;
+    if (!a.reverse) {
+        float S = 0.f;
+        if (a.kv_in) {
+            const float* src = a.kv_in + pair * DD;
+            S = a.kv_in_transposed ? src[(e % a.D) * a.D + e / a.D] : src[e];
+        }
+        for (int c = 0; c < a.chunks - 1; ++c) {
+            S = lamL * S + sl[static_cast<int64_t>(c) * DD];
+            sl[static_cast<int64_t>(c) * DD] = S;
+        }
+    } else {
+        float R = 0.f;
+        for (int c = a.chunks - 2; c >= 0; --c) {
+            R = sl[static_cast<int64_t>(c) * DD] + lamL * R;
+            sl[static_cast<int64_t>(c) * DD] = R;
+        }
+    }
+}
+
+// One recurrent step per (sequence, head): S <- lam S + k v^T, o = q S.
+// Thread t owns the 4 columns 4 * (t % (D/4)) .. +3 of rows t / (D/4) + r * (1024/D).
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a, LamArgs lam) {
+    __shared__ float qs[kMaxD], ks[kMaxD], vs[kMaxD];
+    __shared__ float red[kThreads * 4];
+    const int64_t pair = blockIdx.x;
+    const int D = a.D, tid = threadIdx.x;
+    const float lv = lam.lam[pair % a.H];
+    for (int i = tid; i < D; i += kThreads) {
+        qs[i] = ld<BF16>(a.q, pair * D + i);
+        ks[i] = ld<BF16>(a.k, pair * D + i);
+        vs[i] = ld<BF16>(a.v, pair * D + i);
+    }
+    __syncthreads();
+    const int cols4 = D / 4;
+    const int cg = tid % cols4;
+    const int rstep = kThreads / cols4;
+    float4* S = reinterpret_cast<float4*>(a.state + pair * D * D);
+    const float4 vv = make_float4(vs[4 * cg], vs[4 * cg + 1], vs[4 * cg + 2], vs[4 * cg + 3]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r = tid / cols4; r < D; r += rstep) {
+        float4 x = S[r * cols4 + cg];
+        const float kr = ks[r], qr = qs[r];
+        x.x = lv * x.x + kr * vv.x;
+        x.y = lv * x.y + kr * vv.y;
+        x.z = lv * x.z + kr * vv.z;
+        x.w = lv * x.w + kr * vv.w;
+        S[r * cols4 + cg] = x;
+        acc.x += qr * x.x;
+        acc.y += qr * x.y;
+        acc.z += qr * x.z;
+        acc.w += qr * x.w;
+    }
+    red[tid * 4 + 0] = acc.x;
+    red[tid * 4 + 1] = acc.y;
+    red[tid * 4 + 2] = acc.z;
+    red[tid * 4 + 3] = acc.w;
+    __syncthreads();
+    if (tid < D) {
+        const int g = (tid / 4), comp = tid % 4;
+        float o = 0.f;
+        for (int rg = 0; rg < rstep; ++rg) o += red[(rg * cols4 + g) * 4 + comp];
+        st<BF16>(a.o, pair * D + tid, o);
+    }
+}
+
+}  // namespace
+
+void launch_fwd_generic(const SweepArgs& a, const LamArgs& lam, int bf16, hipStream_t s) {
+    dim3 grid(static_cast<unsigned>(a.pairs * a.chunks));
+    if (bf16)
+        hipLaunchKernelGGL(k_fwd_generic<true>, grid, dim3(kThreads), 0, s, a, lam);
+    else
+        hipLaunchKernelGGL(k_fwd_generic<false>, grid, dim3(kThreads), 0, s, a, lam);
+}
+
+void launch_rev_generic(const SweepArgs& a, const LamArgs& lam, int bf16, hipStream_t s) {
+    dim3 grid(static_cast<unsigned>(a.pairs * a.chunks));
+    if (bf16)
+        hipLaunchKernelGGL(k_rev_generic<true>, grid, dim3(kThreads), 0, s, a, lam);
+    else
+        hipLaunchKernelGGL(k_rev_generic<false>, grid, dim3(kThreads), 0, s, a, lam);
+}
+
+void launch_chunk_state_generic(const ChunkStateArgs& a, const LamArgs& lam, int bf16, hipStream_t s) {
+    dim3 grid(static_cast<unsigned>(a.pairs * (a.chunks - 1)));
+    if (bf16)
+        hipLaunchKernelGGL(k_chunk_state_generic<true>, grid, dim3(kThreads), 0, s, a, lam);
+    else
+        hipLaunchKernelGGL(k_chunk_state_generic<false>, grid, dim3(kThreads), 0, s, a, lam);
+}
+
+void launch_scan(const ScanArgs& a, const LamArgs& lam, hipStream_t s) {
+    const int per_pair = (a.D * a.D + kThreads - 1) / kThreads;
+    dim3 grid(static_cast<unsigned>(a.pairs * per_pair));
+    hipLaunchKernelGGL(k_scan, grid, dim3(kThreads), 0, s, a, lam);
+}
+
+void launch_decode(const DecodeArgs& a, const LamArgs& lam, int bf16, hipStream_t s) {
+    dim3 grid(static_cast<unsigned>(a.pairs));
+    if (bf16)
+        hipLaunchKernelGGL(k_decode<true>, grid, dim3(kThreads), 0, s, a, lam);
+    else
+        hipLaunchKernelGGL(k_decode<false>, grid, dim3(kThreads), 0, s, a, lam);
+}
+
+}  // namespace la

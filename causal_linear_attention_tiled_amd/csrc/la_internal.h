@@ -1,0 +1,89 @@
+// Internal declarations shared by the host API (api.cpp) and the HIP kernels.
+// Not part of the public ABI (include/liblinattn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+constexpr int kMaxHeads = 256;  // per-head decay values travel in the kernel arguments
+constexpr int kThreads = 256;   // threads per workgroup of every kernel here
+
+// Per-head decay, passed by value as a kernel argument (1 KiB).
+struct LamArgs {
+    float lam[kMaxHeads];
+};
+
+// One sweep over every (sequence, chunk) of a [P][N][D] problem.
+// Sequence p = b * H + h uses decay lam[h].  Chunk c covers tokens
+// [c * L, min(N, (c + 1) * L)); L is a multiple of Bk.
+struct SweepArgs {
+    const void* a;  // forward: Q      reverse: Q
+    const void* b;  // forward: K      reverse: K
+    const void* c;  // forward: V      reverse: V
+    const void* g;  // reverse only: dO
+    void* out0;     // forward: O (or dQ)   reverse: dK
+    void* out1;     // reverse: dV
+    const float* slots;   // [P][chunks-1][D][D] carried state entering chunk c (c >= 1 fwd,
+                          // c <= chunks-2 reverse), or nullptr when chunks == 1
+    const float* kv_in;   // [P][D][D] initial state of chunk 0 (forward only) or nullptr
+    int kv_in_transposed; // read kv_in as its transpose (dQ sweep)
+    float* kv_out;        // [P][D][D] final state (forward only) or nullptr
+    int64_t N;
+    int64_t L;            // chunk length in tokens
+    int D, Bk, H, chunks;
+    int64_t pairs;
+};
+
+// Chunk aggregate states: for the forward direction chunk c (0..chunks-2)
+//   slot[c] = sum_{t in c} lam^(end_c - 1 - t) x_t y_t^T
+// and for the reverse direction chunk c (1..chunks-1)
+//   slot[c-1] = sum_{t in c} lam^(t - start_c) x_t y_t^T.
+struct ChunkStateArgs {
+    const void* x;  // [P][N][D]
+    const void* y;  // [P][N][D]
+    float* slots;   // [P][chunks-1][D][D]
+    int64_t N, L;
+    int D, Bk, H, chunks;
+    int64_t pairs;
+    int reverse;
+};
+
+// In-place scan of the slots of every sequence.
+//   forward: S = kv_in (or 0); for c = 0..chunks-2: S = lam^L S + slot[c]; slot[c] = S
+//   reverse: R = 0;           for c = chunks-2..0: R = slot[c] + lam^L R; slot[c] = R
+struct ScanArgs {
+    float* slots;
+    const float* kv_in;
+    int kv_in_transposed;
+    int64_t L;
+    int D, H, chunks;
+    int64_t pairs;
+    int reverse;
+};
+
+struct DecodeArgs {
+    float* state;  // [P][D][D]
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    int D, H;
+    int64_t pairs;
+};
+
+// Launchers (each enqueues exactly one kernel on `s`; errors are read by the caller).
+void launch_fwd_generic(const SweepArgs& a, const LamArgs& lam, int bf16, hipStream_t s);
+void launch_rev_generic(const SweepArgs& a, const LamArgs& lam, int bf16, hipStream_t s);
+void launch_chunk_state_generic(const ChunkStateArgs& a, const LamArgs& lam, int bf16, hipStream_t s);
+void launch_scan(const ScanArgs& a, const LamArgs& lam, hipStream_t s);
+void launch_decode(const DecodeArgs& a, const LamArgs& lam, int bf16, hipStream_t s);
+
+// MFMA kernels (bf16 storage, D = 128, Bk in {64, 128}).
+bool mfma_supported(int D, int Bk);
+void launch_fwd_mfma(const SweepArgs& a, const LamArgs& lam, hipStream_t s);
+void launch_rev_mfma(const SweepArgs& a, const LamArgs& lam, hipStream_t s);
+void launch_chunk_state_mfma(const ChunkStateArgs& a, const LamArgs& lam, hipStream_t s);
+
+}  // namespace la

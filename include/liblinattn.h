@@ -1,0 +1,150 @@
+/*
+ * liblinattn -- tiled causal linear attention with per-head decay on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (Lightning Attention-2, "Tiling" paragraph and the record's
+ * mechanism field: causal linear attention split into an intra-block part done
+ * like ordinary attention and an inter-block part carried by a fixed-size
+ * key-value state, in the forward and the backward pass; the glossary page
+ * "Lightning Attention", features list: parallel form for training, recurrent
+ * form with a constant-size state for inference).  For every sequence
+ * (batch b, head h) of N tokens with head dim D and decay lam = lambda[h]:
+ *
+ *     O_t = sum_{j <= t} lam^(t-j) (q_t . k_j) v_j  +  lam^(t+1) q_t S0
+ *
+ * where S0 is an optional initial D x D state (kv_in).  The final state is
+ *     S_N = lam^N S0 + sum_j lam^(N-1-j) k_j v_j^T     (kv_out).
+ * There is no feature map (identity) and no normaliser; lam^0 = 1, so
+ * lam = 0 keeps only the j = t term.
+ *
+ * Conventions shared by every call
+ *  - Layouts are contiguous row-major: Q, K, V, O, dO, dQ, dK, dV are
+ *    [B][H][N][D]; states are [B][H][D][D] float32 with the key index as the
+ *    row and the value index as the column.  Decode tensors are [Bs][H][D].
+ *  - dtype LA_F32: tensors hold float32; LA_BF16: tensors hold bfloat16.
+ *    Arithmetic accumulates in float32 either way; outputs are rounded to
+ *    the tensor dtype (round to nearest even); states are always float32.
+ *  - lambda is a HOST array of H float32 values in [0, 1], read during the
+ *    call only.  Every other pointer is DEVICE memory owned by the caller;
+ *    the library keeps no pointer after a call returns and never allocates
+ *    device memory.  Device pointers must be 16-byte aligned.
+ *  - Every call validates all arguments before it enqueues anything.  On an
+ *    error nothing is enqueued and the code says why (la_strerror).  No call
+ *    aborts or throws.  NaN and Inf inside tensors are not checked; they
+ *    propagate.
+ *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL is the null
+ *    stream) and the call returns without waiting.  Results are valid once
+ *    the stream has reached that point.  Calls are thread-safe and keep no
+ *    state between calls, except the optional profiling below.
+ *  - Supported: D in {16, 32, 64, 128}, block size Bk in {16, 32, 64, 128},
+ *    1 <= H <= 256, any N >= 1 (the last block may be partial).  The block
+ *    size never changes the result beyond float rounding.
+ *  - The environment variable LA_CHUNKS (a positive integer) overrides the
+ *    number of chunks a sequence is split into for the chunked prefix over
+ *    blocks; LA_KERNEL=generic forces the generic (non-MFMA) kernels.  Both
+ *    exist for tests and tuning; a query of the workspace size must be made
+ *    under the same setting as the call it sizes.
+ */
+#ifndef LIBLINATTN_H
+#define LIBLINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+enum {
+    LA_OK = 0,
+    LA_EINVAL = 1,       /* null required pointer, non-positive size, lambda outside [0,1] or NaN,
+                            unknown dtype, outputs overlapping inputs or each other */
+    LA_EUNSUPPORTED = 2, /* D, Bk or H outside the supported set */
+    LA_EALIGN = 3,       /* a device pointer not 16-byte aligned */
+    LA_EWORKSPACE = 4,   /* workspace missing or smaller than the size query returns */
+    LA_EHIP = 5,         /* the HIP runtime reported an error (launch, device query) */
+    LA_ENODEV = 6        /* no HIP device is available */
+};
+
+/* Forward pass (the tiled forward of Lightning Attention-2: per block an
+ * intra-block masked, decayed Q K^T product with V, plus the inter-block
+ * product of Q with the running state, which is then decayed and updated
+ * with K^T V; the state is carried across blocks by a chunked prefix).
+ *   Q, K, V : [B][H][N][D] dtype, device, read only.
+ *   lambda  : host float32[H].
+ *   kv_in   : [B][H][D][D] float32 device initial state S0, or NULL for zero.
+ *   O       : [B][H][N][D] dtype, device, written.
+ *   kv_out  : [B][H][D][D] float32 device, receives S_N; NULL skips it.
+ *             Must not overlap kv_in.
+ *   ws      : device workspace of at least la_fwd_workspace_bytes(...) bytes
+ *             (may be NULL when that size is 0).  Its contents on entry do
+ *             not matter; calls sharing a workspace must be stream-ordered. */
+int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int64_t B, int64_t H,
+           int64_t N, int64_t D, int32_t Bk, int32_t dtype, const float* kv_in, void* O,
+           float* kv_out, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Workspace bytes la_fwd needs for this shape (0 when the sequence is not
+ * split into chunks).  Returns 0 as well for invalid shapes. */
+size_t la_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype);
+
+/* Backward pass of L = <dO, O> for the forward above, with kv_in held
+ * constant and no gradient arriving through kv_out (the same tiling run in
+ * the backward direction: a forward-order sweep for dQ that carries the key-
+ * value state, and a reverse-order sweep for dK and dV that carries the
+ * state's gradient dS = sum_{i >= t} lam^(i-t) q_i dO_i^T):
+ *   dQ_t = sum_{j<=t} lam^(t-j) (dO_t . v_j) k_j + lam^(t+1) S0 dO_t
+ *   dK_j = sum_{i>=j} lam^(i-j) (dO_i . v_j) q_i
+ *   dV_j = sum_{i>=j} lam^(i-j) (q_i . k_j) dO_i
+ * It is stateless: Q, K, V and kv_in are passed again.
+ *   dO      : [B][H][N][D] dtype, device.
+ *   dQ,dK,dV: [B][H][N][D] dtype, device, written; none may overlap an input
+ *             or each other.
+ *   other arguments as for la_fwd. */
+int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const float* lambda,
+           int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype,
+           const float* kv_in, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
+           void* hip_stream);
+
+size_t la_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype);
+
+/* One recurrent decode step for Bs sequences and H heads (the recurrent
+ * inference form with a fixed-size state, glossary page "Lightning
+ * Attention", features list; constant decode memory, Lightning Attention-2
+ * record, mechanism field).  Per (sequence, head), update then read, so the
+ * new token sees itself:
+ *     S <- lam S + k v^T,   o = q S
+ *   state : [Bs][H][D][D] float32 device, updated in place.
+ *   q,k,v : [Bs][H][D] dtype device.   o : [Bs][H][D] dtype device, written.
+ * The state after n steps from S = 0 equals the kv_out of la_fwd over those
+ * n tokens, and o equals that forward's output row. */
+int la_decode_step(float* state, const void* q, const void* k, const void* v, const float* lambda,
+                   int64_t Bs, int64_t H, int64_t D, int32_t dtype, void* o, void* hip_stream);
+
+/* Static text for a status code.  For LA_EHIP the text of the last HIP error
+ * seen by the calling thread is appended (thread-local buffer). */
+const char* la_strerror(int code);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int la_version(void);
+
+/* Optional profiling, used by the benchmark.  While enabled, every kernel the
+ * library launches is bracketed by two HIP events recorded on the launch's
+ * stream.  la_prof_collect waits for the recorded events, sums the elapsed
+ * time per kernel name into `out` (at most `max_entries` entries), clears the
+ * record and returns the number of entries written (or -LA_EHIP). */
+typedef struct {
+    char name[48];
+    int64_t launches;
+    double total_ms;
+} la_prof_entry;
+
+int la_prof_enable(int on);
+int la_prof_collect(la_prof_entry* out, int max_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBLINATTN_H */

@@ -1,0 +1,64 @@
+"""Shared helpers for the GPU parity tests (input staging and comparison only)."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import synth
+
+BF16_BAR = 2e-2
+F32_BAR = 1e-5
+
+
+def torch_dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+def to_dev(a: np.ndarray, dtype: str):
+    """Host array from synth (float32 or bf16 bit patterns) -> device tensor of that dtype."""
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(torch_dev())
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch_dev())
+
+
+def host_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact value of a synth array as float64."""
+    if dtype == "bf16":
+        return synth.bf16_bits_to_f64(a)
+    return np.asarray(a, dtype=np.float64)
+
+
+def got(t) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def lam_pairs(lam: np.ndarray, B: int) -> np.ndarray:
+    """Per-sequence decay for [B, H] sequences (sequence p = b*H + h uses lam[h])."""
+    return np.tile(np.asarray(lam, dtype=np.float32).astype(np.float64), B)
+
+
+def bar(dtype: str) -> float:
+    return BF16_BAR if dtype == "bf16" else F32_BAR
+
+
+def inputs(seed, B, H, N, D, dtype, with_do=False):
+    arrs = synth.qkv(seed, B, H, N, D, dtype, with_do=with_do)
+    return arrs, [to_dev(a, dtype) for a in arrs], [host_f64(a, dtype) for a in arrs]
+
+
+def state_input(seed, B, H, D):
+    """A seeded float32 initial state [B, H, D, D] (entries N(0,1)/sqrt(D))."""
+    return synth.normal(seed, synth.ID_STATE, (B, H, D, D), 1.0 / math.sqrt(D), "f32")
+
+
+def rel_per_pair(y: np.ndarray, ref: np.ndarray) -> float:
+    """Worst rel-L2 over the leading (sequence) index of [P, ...] arrays."""
+    worst = 0.0
+    for i in range(y.shape[0]):
+        den = np.linalg.norm(ref[i].ravel())
+        num = np.linalg.norm((y[i] - ref[i]).ravel())
+        worst = max(worst, num / den if den > 0 else (0.0 if num == 0 else math.inf))
+    return worst

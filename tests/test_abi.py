@@ -1,0 +1,147 @@
+"""The C-ABI library: it loads, exports every declared symbol, and rejects bad arguments.
+
+No test here computes anything on a GPU: every call below fails validation, which
+runs before the library touches the HIP runtime.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import causal_linear_attention_tiled_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "liblinattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert {"la_fwd", "la_bwd", "la_decode_step", "la_fwd_workspace_bytes", "la_bwd_workspace_bytes",
+            "la_strerror"} <= set(names)
+    handle = ctypes.CDLL(la.LIB_PATH)
+    for n in names:
+        assert hasattr(handle, n), f"{n} declared in liblinattn.h but not exported"
+    assert set(names) == set(la.EXPORTS)
+
+
+def test_version_and_strerror():
+    assert la.la_version() >= 10000
+    for code in range(7):
+        assert isinstance(la.la_strerror(code), str) and la.la_strerror(code)
+    assert "unknown" in la.la_strerror(99)
+
+
+# Fake, 256-byte aligned addresses far apart; validation never dereferences them.
+A = 1 << 40
+Q_, K_, V_, O_, S_, W_ = (A * (i + 1) for i in range(6))
+LAM = (ctypes.c_float * 4)(0.5, 0.9, 1.0, 0.0)
+
+
+def fwd(**kw):
+    args = dict(Q=Q_, K=K_, V=V_, lam=LAM, B=2, H=4, N=1000, D=128, Bk=64, dt=la.LA_BF16, kv_in=None,
+                O=O_, kv_out=None, ws=W_, ws_bytes=1 << 40, stream=None)
+    args.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return la.lib.la_fwd(v(args["Q"]), v(args["K"]), v(args["V"]), args["lam"], args["B"], args["H"],
+                         args["N"], args["D"], args["Bk"], args["dt"], v(args["kv_in"]), v(args["O"]),
+                         v(args["kv_out"]), v(args["ws"]), args["ws_bytes"], v(args["stream"]))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), la.LA_EINVAL),
+    (dict(O=None), la.LA_EINVAL),
+    (dict(lam=None), la.LA_EINVAL),
+    (dict(B=0), la.LA_EINVAL),
+    (dict(N=-5), la.LA_EINVAL),
+    (dict(dt=7), la.LA_EINVAL),
+    (dict(D=48), la.LA_EUNSUPPORTED),
+    (dict(D=256), la.LA_EUNSUPPORTED),
+    (dict(Bk=48), la.LA_EUNSUPPORTED),
+    (dict(Bk=256), la.LA_EUNSUPPORTED),
+    (dict(H=300, lam=(ctypes.c_float * 300)(*([0.5] * 300))), la.LA_EUNSUPPORTED),
+    (dict(Q=Q_ + 8), la.LA_EALIGN),
+    (dict(kv_out=S_ + 4), la.LA_EALIGN),
+    (dict(O=Q_), la.LA_EINVAL),                      # output aliases an input
+    (dict(O=K_ + 1024), la.LA_EINVAL),               # output overlaps an input
+    (dict(kv_in=S_, kv_out=S_), la.LA_EINVAL),       # kv_out aliases kv_in
+    (dict(lam=(ctypes.c_float * 4)(0.5, float("nan"), 1.0, 0.0)), la.LA_EINVAL),
+    (dict(lam=(ctypes.c_float * 4)(0.5, 1.5, 1.0, 0.0)), la.LA_EINVAL),
+    (dict(lam=(ctypes.c_float * 4)(0.5, -0.1, 1.0, 0.0)), la.LA_EINVAL),
+])
+def test_fwd_rejects(kw, code):
+    assert fwd(**kw) == code
+
+
+def test_fwd_workspace_checked():
+    # one long sequence is split into chunks, so it needs a workspace
+    need = la.la_fwd_workspace_bytes(1, 1, 4096, 128, 64, la.LA_BF16)
+    assert need > 0
+    lam1 = (ctypes.c_float * 1)(0.9)
+    assert fwd(B=1, H=1, N=4096, lam=lam1, ws=None, ws_bytes=0) == la.LA_EWORKSPACE
+    assert fwd(B=1, H=1, N=4096, lam=lam1, ws_bytes=need - 1) == la.LA_EWORKSPACE
+    assert fwd(B=1, H=1, N=4096, lam=lam1, ws=Q_) == la.LA_EINVAL  # workspace aliases Q
+
+
+def test_workspace_sizes():
+    # enough sequences to fill the chip: no chunks, no workspace
+    assert la.la_fwd_workspace_bytes(128, 16, 1024, 128, 64, la.LA_BF16) == 0
+    assert la.la_bwd_workspace_bytes(128, 16, 1024, 128, 64, la.LA_BF16) == 0
+    # few long sequences: chunked, workspace holds (chunks-1) D x D float32 states per sequence
+    n = la.la_fwd_workspace_bytes(2, 16, 65536, 128, 64, la.LA_BF16)
+    assert n > 0 and n % (128 * 128 * 4 * 32) == 0
+    assert la.la_bwd_workspace_bytes(2, 16, 65536, 128, 64, la.LA_BF16) >= 2 * n
+    # invalid shapes report 0
+    assert la.la_fwd_workspace_bytes(0, 16, 1024, 128, 64, la.LA_BF16) == 0
+    assert la.la_fwd_workspace_bytes(1, 16, 1024, 100, 64, la.LA_BF16) == 0
+
+
+def test_bwd_rejects():
+    v = ctypes.c_void_p
+    lam = (ctypes.c_float * 2)(0.5, 0.5)
+    G_ = A * 10
+    call = lambda dq, dk, dv, g=G_: la.lib.la_bwd(v(Q_), v(K_), v(V_), v(g), lam, 1, 2, 128, 64, 64,
+                                                  la.LA_BF16, None, v(dq) if dq else None, v(dk), v(dv),
+                                                  None, 0, None)
+    assert call(None, S_, W_) == la.LA_EINVAL          # dQ missing
+    assert call(O_, O_, W_) == la.LA_EINVAL            # dQ and dK alias
+    assert call(O_, S_, V_) == la.LA_EINVAL            # dV aliases V
+    assert call(O_ + 2, S_, W_) == la.LA_EALIGN
+    assert call(O_, S_, W_, g=None) == la.LA_EINVAL    # dO missing
+
+
+def test_decode_rejects():
+    v = ctypes.c_void_p
+    lam = (ctypes.c_float * 2)(0.5, 0.5)
+    call = lambda st, o, D=128, dt=la.LA_BF16, lm=lam: la.lib.la_decode_step(
+        v(st) if st else None, v(Q_), v(K_), v(V_), lm, 4, 2, D, dt, v(o) if o else None, None)
+    assert call(None, O_) == la.LA_EINVAL
+    assert call(S_, None) == la.LA_EINVAL
+    assert call(S_, O_, D=100) == la.LA_EUNSUPPORTED
+    assert call(S_, O_, dt=3) == la.LA_EINVAL
+    assert call(S_ + 4, O_) == la.LA_EALIGN
+    assert call(Q_, O_) == la.LA_EINVAL                # state aliases q
+    assert call(S_, O_, lm=(ctypes.c_float * 2)(0.5, 2.0)) == la.LA_EINVAL
+
+
+def test_no_device_reported_without_gpu():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: a valid call would run kernels on the fake pointers")
+    lam1 = (ctypes.c_float * 1)(0.9)
+    assert fwd(B=1, H=1, N=64, lam=lam1, ws=None, ws_bytes=0) == la.LA_ENODEV
+
+
+def test_python_binding_checks_shapes():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 2, 8, 16)
+    with pytest.raises(ValueError):
+        la.la_fwd(q, q, q[..., :8].contiguous(), [0.5, 0.5])
+    with pytest.raises(ValueError):
+        la.la_fwd(q, q, q, [0.5])

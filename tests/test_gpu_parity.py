@@ -1,0 +1,230 @@
+"""GPU parity of la_fwd / la_bwd / la_decode_step against the fp64 oracle (through the C ABI).
+
+Bars (relative L2 over each whole output tensor): 1e-5 for float32 storage,
+2e-2 for bfloat16 storage, against the unrounded fp64 oracle on the same
+seeded inputs.  Probe inputs whose exact results are representable must match
+bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import bar, got, host_f64, inputs, lam_pairs, state_input, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import causal_linear_attention_tiled_amd as la  # noqa: E402
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+@pytest.fixture
+def chunks(monkeypatch):
+    def set_(c):
+        if c is None:
+            monkeypatch.delenv("LA_CHUNKS", raising=False)
+        else:
+            monkeypatch.setenv("LA_CHUNKS", str(c))
+    return set_
+
+
+@pytest.fixture
+def kernel(monkeypatch):
+    def set_(k):
+        if k == "generic":
+            monkeypatch.setenv("LA_KERNEL", "generic")
+        else:
+            monkeypatch.delenv("LA_KERNEL", raising=False)
+    return set_
+
+
+def check_fwd(B, H, N, D, Bk, dtype, lam, seed=0, with_state=False, label=""):
+    print(f"[fwd] {label} B={B} H={H} N={N} D={D} Bk={Bk} {dtype} kv_in={with_state}", flush=True)
+    _, (q, k, v), (qh, kh, vh) = inputs(seed, B, H, N, D, dtype)
+    s0 = state_input(seed, B, H, D) if with_state else None
+    kv_in = torch.from_numpy(s0).cuda() if with_state else None
+    o, s = la.la_fwd(q, k, v, lam, Bk=Bk, kv_in=kv_in)
+    _sync()
+    lp = lam_pairs(lam, B)
+    o_ref, s_ref = oracle.fwd_recurrent(qh, kh, vh, lp, None if s0 is None else s0.astype(np.float64))
+    e_o, e_s = oracle.rel_l2(got(o), o_ref), oracle.rel_l2(got(s), s_ref)
+    print(f"    rel-L2 O={e_o:.3e} kv_out={e_s:.3e}", flush=True)
+    assert e_o <= bar(dtype) and e_s <= bar(dtype)
+    return o, s
+
+
+def check_bwd(B, H, N, D, Bk, dtype, lam, seed=0, with_state=False, label=""):
+    print(f"[bwd] {label} B={B} H={H} N={N} D={D} Bk={Bk} {dtype} kv_in={with_state}", flush=True)
+    _, (q, k, v, g), (qh, kh, vh, gh) = inputs(seed, B, H, N, D, dtype, with_do=True)
+    s0 = state_input(seed, B, H, D) if with_state else None
+    kv_in = torch.from_numpy(s0).cuda() if with_state else None
+    dq, dk, dv = la.la_bwd(q, k, v, g, lam, Bk=Bk, kv_in=kv_in)
+    _sync()
+    refs = oracle.bwd_recurrent(qh, kh, vh, gh, lam_pairs(lam, B), None if s0 is None else s0.astype(np.float64))
+    errs = [oracle.rel_l2(got(x), r) for x, r in zip((dq, dk, dv), refs)]
+    print(f"    rel-L2 dQ={errs[0]:.3e} dK={errs[1]:.3e} dV={errs[2]:.3e}", flush=True)
+    assert max(errs) <= bar(dtype)
+
+
+# ------------------------------------------------------------------ the small float32 workload
+def test_fp32_no_decay_small():
+    """float32, B=1 H=2 N=256 D=16 Bk=64, lam=1 (no decay): forward at the 1e-5 bar."""
+    check_fwd(1, 2, 256, 16, 64, "f32", np.ones(2, np.float32), label="fp32 small")
+
+
+def test_fp32_small_backward():
+    check_bwd(1, 2, 256, 16, 64, "f32", np.ones(2, np.float32), label="fp32 small")
+
+
+# ------------------------------------------------------------------ many tiles and ragged tails
+@pytest.mark.parametrize("kern", ["generic", "default"])
+@pytest.mark.parametrize("D,Bk", [(16, 16), (32, 32), (64, 64), (128, 64), (128, 128), (64, 128)])
+def test_fwd_ragged_bf16(kern, D, Bk, kernel):
+    kernel(kern)
+    H = 3
+    lam = np.array([0.0, 0.9, 1.0], np.float32)
+    check_fwd(2, H, 1000, D, Bk, "bf16", lam, seed=D + Bk, label=kern)
+
+
+@pytest.mark.parametrize("kern", ["generic", "default"])
+@pytest.mark.parametrize("D,Bk", [(32, 16), (128, 64), (128, 128)])
+def test_bwd_ragged_bf16(kern, D, Bk, kernel):
+    kernel(kern)
+    lam = synth.decay_schedule(4)
+    check_bwd(1, 4, 777, D, Bk, "bf16", lam, seed=3, label=kern)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_initial_state(dtype):
+    lam = synth.decay_schedule(4)
+    check_fwd(2, 4, 300, 64, 64, dtype, lam, seed=5, with_state=True)
+    check_bwd(2, 4, 300, 64, 64, dtype, lam, seed=5, with_state=True)
+
+
+@pytest.mark.parametrize("c", [1, 2, 7, 16])
+@pytest.mark.parametrize("kern", ["generic", "default"])
+def test_forced_chunk_counts(c, kern, chunks, kernel):
+    chunks(c)
+    kernel(kern)
+    lam = synth.decay_schedule(2)
+    check_fwd(1, 2, 64 * 16 + 17, 128, 64, "bf16", lam, seed=c, with_state=True, label=f"chunks={c}")
+    check_bwd(1, 2, 64 * 16 + 17, 128, 64, "bf16", lam, seed=c, with_state=True, label=f"chunks={c}")
+
+
+# ------------------------------------------------------------------ bit-exact probes
+def impulse_inputs(N, D, j0, c, dtype):
+    q = np.zeros((1, 1, N, D), np.float32)
+    q[..., 0] = 1.0
+    k = np.zeros_like(q)
+    k[0, 0, j0, 0] = 1.0
+    v = np.zeros_like(q)
+    v[0, 0, j0, c] = 1.0
+    if dtype == "bf16":
+        q, k, v = (synth.f32_to_bf16_bits(x) for x in (q, k, v))
+    return q, k, v
+
+
+@pytest.mark.parametrize("kern", ["generic", "default"])
+@pytest.mark.parametrize("lam_val", [1.0, 0.5])
+@pytest.mark.parametrize("Bk,cks", [(64, 1), (64, 4), (128, 3)])
+def test_impulse_probe_bit_exact(kern, lam_val, Bk, cks, chunks, kernel):
+    """q_t = e0, a single key e0 at j0 with value e_c: O_t = lam^(t-j0) e_c exactly for t >= j0.
+
+    j0 sits on block and chunk boundaries and their neighbours; lam = 1/2 keeps every
+    intermediate an exact power of two while t - j0 <= 100."""
+    kernel(kern)
+    chunks(cks)
+    N, D, c = 700, 128, 5
+    nb = -(-N // Bk)
+    L = -(-nb // cks) * Bk
+    t = np.arange(N)
+    for j0 in [j for j in sorted({0, Bk - 1, Bk, Bk + 1, L - 1, L, L + 1, N - 1}) if j < N]:
+        print(f"[impulse] kern={kern} lam={lam_val} Bk={Bk} chunks={cks} j0={j0}", flush=True)
+        qa, ka, va = impulse_inputs(N, D, j0, c, "bf16")
+        o, s = la.la_fwd(to_dev(qa, "bf16"), to_dev(ka, "bf16"), to_dev(va, "bf16"), [lam_val], Bk=Bk)
+        _sync()
+        rel = t - j0
+        keep = rel <= 100 if lam_val < 1 else np.ones(N, bool)
+        expect = np.zeros((N, D))
+        expect[rel >= 0, c] = np.float64(lam_val) ** rel[rel >= 0]
+        np.testing.assert_array_equal(got(o)[0, 0][keep], expect[keep], err_msg=f"j0={j0}")
+        if lam_val == 1 or N - 1 - j0 <= 100:
+            s_exp = np.zeros((D, D))
+            s_exp[0, c] = np.float64(lam_val) ** (N - 1 - j0)
+            np.testing.assert_array_equal(got(s)[0, 0], s_exp, err_msg=f"state j0={j0}")
+
+
+@pytest.mark.parametrize("kern", ["generic", "default"])
+@pytest.mark.parametrize("N,D,Bk", [(2, 128, 64), (2, 128, 128), (16, 16, 16), (16, 16, 64)])
+def test_all_ones_probe_bit_exact(kern, N, D, Bk, kernel):
+    """lam = 1 and all-ones bf16 inputs: O_t = (t+1) d and S = N * 1 1^T exactly.
+
+    (t+1) d <= 256 keeps every value an integer that bf16 represents exactly."""
+    kernel(kern)
+    ones = synth.f32_to_bf16_bits(np.ones((1, 1, N, D), np.float32))
+    o, s = la.la_fwd(to_dev(ones, "bf16"), to_dev(ones, "bf16"), to_dev(ones, "bf16"), [1.0], Bk=Bk)
+    _sync()
+    np.testing.assert_array_equal(got(o)[0, 0], (np.arange(1, N + 1) * D)[:, None] * np.ones((N, D)))
+    np.testing.assert_array_equal(got(s)[0, 0], N * np.ones((D, D)))
+
+
+def test_run_to_run_bit_identical():
+    lam = synth.decay_schedule(8)
+    _, (q, k, v, g), _ = inputs(11, 2, 8, 3000, 128, "bf16", with_do=True)
+    o1, s1 = la.la_fwd(q, k, v, lam)
+    o2, s2 = la.la_fwd(q, k, v, lam)
+    b1 = la.la_bwd(q, k, v, g, lam)
+    b2 = la.la_bwd(q, k, v, g, lam)
+    _sync()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    for x, y in zip(b1, b2):
+        assert torch.equal(x, y)
+
+
+# ------------------------------------------------------------------ continuation and decode
+@pytest.mark.parametrize("m", [64, 100])
+def test_split_and_continue(m):
+    """fwd over [0, m) -> kv_out -> fwd over [m, N) with kv_in equals one pass (within the bar)."""
+    B, H, N, D = 1, 4, 500, 128
+    lam = synth.decay_schedule(H)
+    _, (q, k, v), (qh, kh, vh) = inputs(13, B, H, N, D, "bf16")
+    oa, sa = la.la_fwd(q[:, :, :m].contiguous(), k[:, :, :m].contiguous(), v[:, :, :m].contiguous(), lam)
+    ob, sb = la.la_fwd(q[:, :, m:].contiguous(), k[:, :, m:].contiguous(), v[:, :, m:].contiguous(), lam,
+                       kv_in=sa)
+    _sync()
+    o_ref, s_ref = oracle.fwd_recurrent(qh, kh, vh, lam_pairs(lam, B))
+    o_cat = np.concatenate([got(oa), got(ob)], axis=2)
+    assert oracle.rel_l2(o_cat, o_ref) <= 2e-2
+    assert oracle.rel_l2(got(sb), s_ref) <= 2e-2
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_matches_oracle_and_forward(dtype):
+    Bs, H, D, steps = 3, 4, 128, 40
+    lam = synth.decay_schedule(H)
+    lp = lam_pairs(lam, Bs)
+    state = torch.zeros((Bs, H, D, D), dtype=torch.float32, device="cuda")
+    S_ref = np.zeros((Bs * H, D, D))
+    qs, ks, vs, outs = [], [], [], []
+    for t in range(steps):
+        arrs = [synth.normal(0, i, (Bs, H, D), 1.0 / math.sqrt(D), dtype) for i in synth.decode_ids(t)]
+        o = la.la_decode_step(state, *(to_dev(a, dtype) for a in arrs), lam)
+        _sync()
+        hq, hk, hv = (host_f64(a, dtype).reshape(Bs * H, D) for a in arrs)
+        o_ref, S_ref = oracle.decode_step(S_ref, hq, hk, hv, lp)
+        assert oracle.rel_l2(got(o).reshape(Bs * H, D), o_ref) <= bar(dtype)
+        qs.append(arrs[0]); ks.append(arrs[1]); vs.append(arrs[2]); outs.append(got(o))
+    assert oracle.rel_l2(got(state).reshape(Bs * H, D, D), S_ref) <= bar(dtype)
+    # the same tokens through la_fwd give the same outputs and final state
+    stack = lambda xs: np.ascontiguousarray(np.stack(xs, axis=2))
+    of, sf = la.la_fwd(to_dev(stack(qs), dtype), to_dev(stack(ks), dtype), to_dev(stack(vs), dtype), lam)
+    _sync()
+    o_dec = np.stack(outs, axis=2)
+    assert oracle.rel_l2(o_dec, got(of)) <= bar(dtype)
+    assert oracle.rel_l2(got(state), got(sf)) <= bar(dtype)
