@@ -328,7 +328,8 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     a.H = Hi;
     a.chunks = p.chunks;
     a.pairs = pairs;
-    if (p.mfma) return launch("dkdv_mfma", s, [&] { la::launch_rev_mfma(a, lam, s); });
+    if (p.mfma && la::mfma_rev_supported(static_cast<int>(D), Bk))
+        return launch("dkdv_mfma", s, [&] { la::launch_rev_mfma(a, lam, s); });
     return launch("dkdv_generic", s, [&] { la::launch_rev_generic(a, lam, bf16, s); });
 }
 

@@ -1,9 +1,7 @@
-// MFMA kernels (placeholder until the matrix-core path lands).
+// Reverse (dK, dV) sweep on matrix cores: not built yet, the generic kernel runs instead.
 #include "la_internal.h"
 
 namespace la {
-bool mfma_supported(int, int) { return false; }
-void launch_fwd_mfma(const SweepArgs&, const LamArgs&, hipStream_t) {}
+bool mfma_rev_supported(int, int) { return false; }
 void launch_rev_mfma(const SweepArgs&, const LamArgs&, hipStream_t) {}
-void launch_chunk_state_mfma(const ChunkStateArgs&, const LamArgs&, hipStream_t) {}
 }  // namespace la

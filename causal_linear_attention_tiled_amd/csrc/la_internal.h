@@ -82,6 +82,7 @@ void launch_decode(const DecodeArgs& a, const LamArgs& lam, int bf16, hipStream_
 
 // MFMA kernels (bf16 storage, D = 128, Bk in {64, 128}).
 bool mfma_supported(int D, int Bk);
+bool mfma_rev_supported(int D, int Bk);
 void launch_fwd_mfma(const SweepArgs& a, const LamArgs& lam, hipStream_t s);
 void launch_rev_mfma(const SweepArgs& a, const LamArgs& lam, hipStream_t s);
 void launch_chunk_state_mfma(const ChunkStateArgs& a, const LamArgs& lam, hipStream_t s);

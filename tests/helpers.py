@@ -62,3 +62,31 @@ def rel_per_pair(y: np.ndarray, ref: np.ndarray) -> float:
         num = np.linalg.norm((y[i] - ref[i]).ravel())
         worst = max(worst, num / den if den > 0 else (0.0 if num == 0 else math.inf))
     return worst
+
+
+def device_stream(seed, sid, shape, dtype, group_elems=1 << 27):
+    """A [..] tensor of stream (seed, sid) generated slice by slice straight into device memory.
+
+    Values are N(0,1)/sqrt(shape[-1]); host memory stays bounded by ``group_elems``."""
+    import torch
+    D = shape[-1]
+    total = int(np.prod(shape))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = torch.empty(total, dtype=tdt, device=torch_dev())
+    flat = out.view(torch.int16) if dtype == "bf16" else out
+    step = max(D, (group_elems // D) * D)
+    for s0 in range(0, total, step):
+        n = min(step, total - s0)
+        host = synth.normal(seed, sid, (n,), 1.0 / math.sqrt(D), dtype, start=s0)
+        if dtype == "bf16":
+            flat[s0:s0 + n].copy_(torch.from_numpy(host.view(np.int16)))
+        else:
+            flat[s0:s0 + n].copy_(torch.from_numpy(host))
+    return out.view(*shape)
+
+
+def sample_pairs(B, H, count):
+    """A fixed, spread-out sample of (b, h) sequence indices (first and last always included)."""
+    P = B * H
+    idx = sorted({0, P - 1} | {int(round(i * (P - 1) / max(1, count - 1))) for i in range(count)})
+    return [(p // H, p % H) for p in idx]
