@@ -1,0 +1,375 @@
+#!/usr/bin/env python3
+"""Benchmark of tiled causal linear attention (forward + backward) on one MI355X.
+
+Workload: the sequence-length sweep at a fixed 131072 tokens per head,
+n in {1024, 4096, 16384, 65536} with batch 131072 / n, 16 heads, head dim 128,
+block 64, per-head decay lambda_h = exp(-2^(-8(h+1)/16)), bf16 storage, inputs
+N(0,1)/sqrt(128) from the seeded generator, resident in HBM.  One step runs, for
+each of the four shapes, la_fwd (output and final state) then la_bwd (dQ, dK,
+dV) through the C ABI.  ``value`` is forward+backward tokens per second over
+the whole step (4 x 131072 tokens).
+
+The JSON line also carries, per sequence length, forward-only and backward-only
+tokens/s with algorithmic TFLOP/s (% of the 2.5 PFLOP/s bf16 dense peak) and
+GB/s; the recurrent decode step at 256 sequences x 64 heads (GB/s against
+8 TB/s); the roofline of the kernel that takes the most time (its average
+launch duration measured with HIP events on its own stream during a second
+pass over the same steps); and the fp64 oracle timed on a bounded sample on the
+host cores.
+
+Subcommand ``summarize`` turns rocprofv3 outputs into the text summaries kept
+under profiles/ (see --help).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+D, BK, H = 128, 64, 16
+SWEEP_N = (1024, 4096, 16384, 65536)
+TOKENS_PER_POINT = 131072
+HBM_PEAK_GBS = 8000.0      # MI355X published HBM3E bandwidth
+BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA rate
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {         # library kernel name -> source file its code lives in
+    "fwd_mfma": "k_fwd_mfma.hip", "dq_mfma": "k_fwd_mfma.hip", "chunk_state_mfma": "k_fwd_mfma.hip",
+    "chunk_state_rev_mfma": "k_fwd_mfma.hip", "dkdv_mfma": "k_bwd_mfma.hip",
+    "dkdv_generic": "k_generic.hip", "state_scan": "k_generic.hip", "state_scan_rev": "k_generic.hip",
+    "decode": "k_generic.hip",
+}
+
+
+# ----------------------------------------------------------------------------- algorithmic counts
+def fwd_flops_per_token_head(d=D, bk=BK):
+    # intra: causal Q K^T and A V over (Bk+1)/2 keys on average; inter: Q S and the state update
+    return 2 * d * (bk + 1) + 4 * d * d
+
+
+def bwd_flops_per_token_head(d=D, bk=BK):
+    # intra: G = dO V^T, P = Q K^T, dQ, dK, dV products; inter: dO S^T, state rebuild,
+    # V dS^T, K dS and the dS update
+    return 5 * d * (bk + 1) + 10 * d * d
+
+
+def kernel_bytes(name, B, Hh, N, d, chunks, with_state=True):
+    """Algorithmic HBM bytes one launch of library kernel `name` must move (bf16 tensors)."""
+    th = B * Hh * N                    # token-heads
+    t = 2 * d * th                     # one bf16 [B, H, N, D] tensor
+    st = B * Hh * d * d * 4            # one float32 state per sequence
+    frac = (chunks - 1) / chunks if chunks > 1 else 0.0
+    return {
+        "fwd_mfma": 4 * t + (st if with_state else 0),
+        "dq_mfma": 4 * t,
+        "dkdv_mfma": 6 * t, "dkdv_generic": 6 * t,
+        "chunk_state_mfma": 2 * t * frac,
+        "chunk_state_rev_mfma": 2 * t * frac,
+        "state_scan": 2 * st * (chunks - 1), "state_scan_rev": 2 * st * (chunks - 1),
+    }.get(name)
+
+
+def source_digest(kernel):
+    src = KERNEL_SOURCES.get(kernel)
+    if not src:
+        return None
+    p = os.path.join(ROOT, "causal_linear_attention_tiled_amd", "csrc", src)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16] if os.path.exists(p) else None
+
+
+def read_traffic(kernel):
+    """Measured HBM bytes per launch of `kernel` from profiles/, or None when absent or stale."""
+    path = os.path.join(PROFILES, f"{kernel}_sweep_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != source_digest(kernel):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------------------- inputs
+def device_normal(torch, sid, shape, seed=0):
+    import numpy as np
+    import synth
+    total = int(np.prod(shape))
+    out = torch.empty(total, dtype=torch.bfloat16, device="cuda")
+    flat = out.view(torch.int16)
+    step = 1 << 27
+    for s0 in range(0, total, step):
+        n = min(step, total - s0)
+        host = synth.normal(seed, sid, (n,), 1.0 / math.sqrt(shape[-1]), "bf16", start=s0)
+        flat[s0:s0 + n].copy_(torch.from_numpy(host.view(np.int16)))
+    return out.view(*shape)
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(seconds_target):
+    """The fp64 oracle (recurrent form, fwd + bwd) on a bounded sample of the sweep workload."""
+    import numpy as np
+    import oracle
+    import synth
+    n = 4096
+    B = TOKENS_PER_POINT // n
+    lam = synth.decay_schedule(H).astype(np.float64)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+
+    def run(pairs):
+        qs, ks, vs, gs, ls = [], [], [], [], []
+        for p in range(pairs):
+            b, h = p // H, p % H
+            q, k, v, g = (synth.bf16_bits_to_f64(synth.pair_slice(0, i, B, H, n, D, b, h, "bf16"))
+                          for i in (1, 2, 3, 4))
+            qs.append(q); ks.append(k); vs.append(v); gs.append(g); ls.append(lam[h])
+        q, k, v, g = (np.stack(x) for x in (qs, ks, vs, gs))
+        t0 = time.perf_counter()
+        oracle.fwd_recurrent(q, k, v, np.array(ls))
+        oracle.bwd_recurrent(q, k, v, g, np.array(ls))
+        return time.perf_counter() - t0
+
+    pairs = threads
+    dt = run(pairs)
+    if dt < seconds_target / 4:
+        pairs = int(min(B * H, max(pairs, pairs * seconds_target / max(dt, 1e-3))))
+        pairs = max(threads, (pairs // threads) * threads)
+        dt = run(pairs)
+    tokens = pairs * n / H          # tokens of the metric carry all H heads
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{pairs} of the {B * H} (batch, head) sequences of the n={n} sweep point "
+                      f"(d={D}, per-head decay), fwd+bwd, recurrent form in fp64, {dt:.1f} s"}
+
+
+# ----------------------------------------------------------------------------- main bench
+def bench(args):
+    import numpy as np
+    import torch
+
+    so = os.path.join(ROOT, "causal_linear_attention_tiled_amd", "liblinattn.so")
+    if not os.path.exists(so):
+        import __graft_entry__
+        __graft_entry__.build()
+    import causal_linear_attention_tiled_amd as la
+    import synth
+
+    torch.cuda.init()
+    lam = synth.decay_schedule(H)
+    shapes = []
+    for n in SWEEP_N:
+        B = TOKENS_PER_POINT // n
+        q, k, v, g = (device_normal(torch, sid, (B, H, n, D)) for sid in (1, 2, 3, 4))
+        o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+        s = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+        wf = la.la_fwd_workspace_bytes(B, H, n, D, BK, la.LA_BF16)
+        wb = la.la_bwd_workspace_bytes(B, H, n, D, BK, la.LA_BF16)
+        ws_f = torch.empty(max(wf, 1), dtype=torch.uint8, device="cuda")
+        ws_b = torch.empty(max(wb, 1), dtype=torch.uint8, device="cuda")
+        chunks = wf // (B * H * D * D * 4) + 1 if wf else 1
+        shapes.append(dict(n=n, B=B, q=q, k=k, v=v, g=g, o=o, s=s, dq=dq, dk=dk, dv=dv, ws_f=ws_f,
+                           ws_b=ws_b, chunks=chunks))
+    torch.cuda.synchronize()
+
+    def fwd(sh):
+        la.la_fwd(sh["q"], sh["k"], sh["v"], lam, BK, out=sh["o"], kv_out=sh["s"], ws=sh["ws_f"])
+
+    def bwd(sh):
+        la.la_bwd(sh["q"], sh["k"], sh["v"], sh["g"], lam, BK, dq=sh["dq"], dk=sh["dk"], dv=sh["dv"],
+                  ws=sh["ws_b"])
+
+    def step():
+        for sh in shapes:
+            fwd(sh)
+            bwd(sh)
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_per_step = timed(step, args.steps)
+    wall = time.perf_counter() - t0
+    tokens_per_step = TOKENS_PER_POINT * len(SWEEP_N)
+    value = tokens_per_step / (ms_per_step * 1e-3)
+
+    # second pass over the same steps with per-kernel HIP events (on the launch stream)
+    la.la_prof_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = la.la_prof_collect()
+    la.la_prof_enable(False)
+
+    # algorithmic bytes per launch for every kernel (same launches, same order every step)
+    bytes_by_kernel = {}
+    for sh in shapes:
+        names = ["fwd_mfma", "dq_mfma", "dkdv_mfma", "dkdv_generic"]
+        if sh["chunks"] > 1:
+            names += ["chunk_state_mfma", "chunk_state_rev_mfma", "state_scan", "state_scan_rev"]
+        for nm in names:
+            b = kernel_bytes(nm, sh["B"], H, sh["n"], D, sh["chunks"])
+            if nm in ("chunk_state_mfma", "state_scan"):
+                b = b * 2  # launched by the forward and by the dQ sweep of the backward
+            bytes_by_kernel.setdefault(nm, []).append(b)
+    kernels = {}
+    for nm, (launches, total_ms) in prof.items():
+        avg_ms = total_ms / launches
+        per_step_bytes = sum(bytes_by_kernel.get(nm, [])) or None
+        launches_per_step = launches / args.steps
+        avg_bytes = per_step_bytes / launches_per_step if per_step_bytes else None
+        kernels[nm] = {"launches_per_step": launches_per_step, "avg_ms": round(avg_ms, 5),
+                       "share": None, "alg_bytes_per_launch": avg_bytes,
+                       "gbs": (avg_bytes / (avg_ms * 1e-3) / 1e9) if avg_bytes else None}
+    total_prof = sum(v[1] for v in prof.values())
+    for nm in kernels:
+        kernels[nm]["share"] = round(prof[nm][1] / total_prof, 4)
+    dom = max(kernels, key=lambda k_: prof[k_][1])
+    dk_ = kernels[dom]
+    achieved = dk_["gbs"]
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1) if achieved else None,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+                "traffic": read_traffic(dom), "avg_launch_ms": dk_["avg_ms"],
+                "alg_bytes_per_launch": dk_["alg_bytes_per_launch"]}
+
+    # per sequence length breakdown
+    sweep = []
+    for sh in shapes:
+        reps = max(3, args.steps)
+        f_ms = timed(lambda: fwd(sh), reps)
+        b_ms = timed(lambda: bwd(sh), reps)
+        th = sh["B"] * H * sh["n"]
+        ff, bf = fwd_flops_per_token_head() * th, bwd_flops_per_token_head() * th
+        fbytes = 8 * D * th + sh["B"] * H * D * D * 4
+        bbytes = 14 * D * th
+        sweep.append({
+            "n": sh["n"], "batch": sh["B"], "chunks": sh["chunks"],
+            "fwd_ms": round(f_ms, 4), "fwd_tokens_per_s": round(TOKENS_PER_POINT / (f_ms * 1e-3)),
+            "fwd_tflops": round(ff / (f_ms * 1e-3) / 1e12, 1),
+            "fwd_pct_bf16_peak": round(100 * ff / (f_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
+            "fwd_gbs": round(fbytes / (f_ms * 1e-3) / 1e9, 1),
+            "bwd_ms": round(b_ms, 4), "bwd_tokens_per_s": round(TOKENS_PER_POINT / (b_ms * 1e-3)),
+            "bwd_tflops": round(bf / (b_ms * 1e-3) / 1e12, 1),
+            "bwd_gbs": round(bbytes / (b_ms * 1e-3) / 1e9, 1),
+            "fwd_bwd_tokens_per_s": round(TOKENS_PER_POINT / ((f_ms + b_ms) * 1e-3)),
+        })
+    fwd_tps = [x["fwd_tokens_per_s"] for x in sweep]
+
+    # recurrent decode step: 256 sequences x 64 heads, float32 state 1 GiB
+    Bs, Hd = 256, 64
+    lam_d = synth.decay_schedule(Hd)
+    state = torch.zeros((Bs, Hd, D, D), dtype=torch.float32, device="cuda")
+    dq_, dk2, dv2 = (device_normal(torch, 16 + i, (Bs, Hd, D)) for i in range(3))
+    od = torch.empty_like(dq_)
+    dec = lambda: la.la_decode_step(state, dq_, dk2, dv2, lam_d, out=od)
+    for _ in range(3):
+        dec()
+    dec_ms = timed(dec, 50)
+    dec_bytes = Bs * Hd * (8 * D * D + 8 * D)
+    decode = {"workload": "recurrent decode step, 256 sequences x 64 heads, d=128, float32 state",
+              "ms": round(dec_ms, 4), "gbs": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
+              "frac_of_8tbs": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+              "tokens_per_s": round(Bs / (dec_ms * 1e-3))}
+
+    tflops_step = sum((fwd_flops_per_token_head() + bwd_flops_per_token_head()) * TOKENS_PER_POINT * H
+                      for _ in SWEEP_N) / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": "fwd+bwd tokens/s over the 1K-64K sequence-length sweep (131072 tokens per point), 1 GPU",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1)/sqrt(d) inputs, resident in HBM",
+        "config": {"workload": "causal linear attention fwd+bwd, seq-length sweep n in {1024,4096,16384,65536}, "
+                               "batch 131072/n, heads 16, d 128, block 64, per-head decay",
+                   "tokens_per_step": tokens_per_step, "heads": H, "head_dim": D, "block": BK},
+        "tflops_alg": round(tflops_step, 1),
+        "pct_bf16_peak": round(100 * tflops_step / BF16_PEAK_TFLOPS, 2),
+        "roofline": roofline,
+        "sweep": sweep,
+        "fwd_flatness": round(max(fwd_tps) / min(fwd_tps), 3),
+        "kernels": kernels,
+        "decode": decode,
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+# ----------------------------------------------------------------------------- rocprofv3 summaries
+def summarize(args):
+    """Summarize rocprofv3 output: kernel stats (--stats) or counters (--pmc FETCH_SIZE / WRITE_SIZE).
+
+    Writes profiles/<kernel>_sweep_*.txt with the figures the benchmark uses."""
+    lines = [f"# command: {args.command}", f"# source: {args.dir}"]
+    if args.kind == "stats":
+        files = glob.glob(os.path.join(args.dir, "**", "*kernel_stats.csv"), recursive=True)
+        rows = list(csv.DictReader(open(files[0])))
+        lines.append("kernel | calls | avg_us | total_ms | pct")
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+            lines.append(f"{r['Name'][:110]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f}")
+        out = os.path.join(PROFILES, f"kernels_{args.tag}_stats.txt")
+    else:
+        files = glob.glob(os.path.join(args.dir, "**", "*counter_collection.csv"), recursive=True)
+        rows = list(csv.DictReader(open(files[0])))
+        by_kernel = {}
+        for r in rows:
+            by_kernel.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+        lines.append("kernel | counter | dispatches | mean_per_dispatch")
+        for (kn, cn), vals in sorted(by_kernel.items()):
+            lines.append(f"{kn[:110]} | {cn} | {len(vals)} | {sum(vals) / len(vals):.1f}")
+        out = os.path.join(PROFILES, f"counters_{args.tag}_{args.kind}.txt")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote", out)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("summarize", nargs="?", help=argparse.SUPPRESS)
+    ap.add_argument("--kind", choices=["stats", "fetch", "write"], default="stats")
+    ap.add_argument("--dir", default="")
+    ap.add_argument("--tag", default="sweep")
+    ap.add_argument("--command", default="")
+    args = ap.parse_args()
+    if args.summarize == "summarize":
+        return summarize(args)
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the library has no multi-GPU "
+                                   "path (sequences would shard by batch and head, or by sequence "
+                                   "segments with one D x D state exchange)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    bench(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -121,17 +121,16 @@ __global__ __launch_bounds__(kThreads, (BK == 64) ? 2 : 1) void k_fwd_mfma(Sweep
     auto load_tile = [&](int64_t t0, int m) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
+            // rows past the end of a partial block read the last valid row and are zeroed
             const int row = r0 + i;
-            if (row < m) {
-                const int64_t off = (t0 + row) * D + 8 * fg;
-                gq[i] = *reinterpret_cast<const u32x4*>(Qg + off);
-                gk[i] = *reinterpret_cast<const u32x4*>(Kg + off);
-                gv[i] = *reinterpret_cast<const u32x4*>(Vg + off);
-            } else {
-                gq[i] = u32x4{0, 0, 0, 0};
-                gk[i] = gq[i];
-                gv[i] = gq[i];
-            }
+            const int64_t off = (t0 + min(row, m - 1)) * D + 8 * fg;
+            const u32x4 z{0, 0, 0, 0};
+            const u32x4 xq = *reinterpret_cast<const u32x4*>(Qg + off);
+            const u32x4 xk = *reinterpret_cast<const u32x4*>(Kg + off);
+            const u32x4 xv = *reinterpret_cast<const u32x4*>(Vg + off);
+            gq[i] = row < m ? xq : z;
+            gk[i] = row < m ? xk : z;
+            gv[i] = row < m ? xv : z;
         }
     };
     load_tile(t_begin, static_cast<int>(min(static_cast<int64_t>(BK), t_end - t_begin)));
@@ -313,14 +312,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_state_mfma(ChunkStateArgs
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             const int row = r0 + i;
-            if (row < m) {
-                const int64_t off = (t0 + row) * D + 8 * fg;
-                gx[i] = *reinterpret_cast<const u32x4*>(Xg + off);
-                gy[i] = *reinterpret_cast<const u32x4*>(Yg + off);
-            } else {
-                gx[i] = u32x4{0, 0, 0, 0};
-                gy[i] = gx[i];
-            }
+            const int64_t off = (t0 + min(row, m - 1)) * D + 8 * fg;
+            const u32x4 z{0, 0, 0, 0};
+            const u32x4 xx = *reinterpret_cast<const u32x4*>(Xg + off);
+            const u32x4 xy = *reinterpret_cast<const u32x4*>(Yg + off);
+            gx[i] = row < m ? xx : z;
+            gy[i] = row < m ? xy : z;
         }
     };
     load_tile(0);
