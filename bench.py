@@ -42,8 +42,8 @@ HBM_PEAK_GBS = 8000.0      # MI355X published HBM3E bandwidth
 BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA rate
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {         # library kernel name -> source file its code lives in
-    "fwd_mfma": "k_fwd_mfma.hip", "dq_mfma": "k_fwd_mfma.hip", "chunk_state_mfma": "k_fwd_mfma.hip",
-    "chunk_state_rev_mfma": "k_fwd_mfma.hip", "dkdv_mfma": "k_bwd_mfma.hip",
+    "fwd_mfma": "k_fwd_mfma.hip", "dq_mfma": "k_fwd_mfma.hip", "fwd_dma": "k_fwd_dma.hip", "dq_dma": "k_fwd_dma.hip", "chunk_state_mfma": "k_fwd_mfma.hip",
+    "chunk_state_rev_mfma": "k_fwd_mfma.hip", "dkdv_mfma": "k_bwd_mfma.hip", "dkdv_dma": "k_bwd_dma.hip",
     "dkdv_generic": "k_generic.hip", "state_scan": "k_generic.hip", "state_scan_rev": "k_generic.hip",
     "decode": "k_generic.hip",
 }
@@ -68,9 +68,9 @@ def kernel_bytes(name, B, Hh, N, d, chunks, with_state=True):
     st = B * Hh * d * d * 4            # one float32 state per sequence
     frac = (chunks - 1) / chunks if chunks > 1 else 0.0
     return {
-        "fwd_mfma": 4 * t + (st if with_state else 0),
-        "dq_mfma": 4 * t,
-        "dkdv_mfma": 6 * t, "dkdv_generic": 6 * t,
+        "fwd_mfma": 4 * t + (st if with_state else 0), "fwd_dma": 4 * t + (st if with_state else 0),
+        "dq_mfma": 4 * t, "dq_dma": 4 * t,
+        "dkdv_mfma": 6 * t, "dkdv_generic": 6 * t, "dkdv_dma": 6 * t,
         "chunk_state_mfma": 2 * t * frac,
         "chunk_state_rev_mfma": 2 * t * frac,
         "state_scan": 2 * st * (chunks - 1), "state_scan_rev": 2 * st * (chunks - 1),
@@ -225,7 +225,7 @@ def bench(args):
     # algorithmic bytes per launch for every kernel (same launches, same order every step)
     bytes_by_kernel = {}
     for sh in shapes:
-        names = ["fwd_mfma", "dq_mfma", "dkdv_mfma", "dkdv_generic"]
+        names = ["fwd_mfma", "dq_mfma", "fwd_dma", "dq_dma", "dkdv_mfma", "dkdv_generic", "dkdv_dma"]
         if sh["chunks"] > 1:
             names += ["chunk_state_mfma", "chunk_state_rev_mfma", "state_scan", "state_scan_rev"]
         for nm in names:

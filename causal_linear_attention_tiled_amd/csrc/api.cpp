@@ -119,6 +119,11 @@ struct Plan {
     bool mfma;
 };
 
+bool env_is(const char* name, const char* value) {
+    const char* e = std::getenv(name);
+    return e && std::strcmp(e, value) == 0;
+}
+
 bool force_generic() {
     const char* e = std::getenv("LA_KERNEL");
     return e && std::strcmp(e, "generic") == 0;
@@ -187,6 +192,10 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
     a.H = H;
     a.chunks = p.chunks;
     a.pairs = pairs;
+    if (p.mfma && la::fwd_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_FWD", "v1")) {
+        const int waves = env_is("LA_FWD_WAVES", "8") ? 8 : 4;
+        return launch(tag[0] == 'd' ? "dq_dma" : "fwd_dma", s, [&] { la::launch_fwd_dma(a, lam, waves, s); });
+    }
     if (p.mfma) return launch(tag[0] == 'd' ? "dq_mfma" : "fwd_mfma", s, [&] { la::launch_fwd_mfma(a, lam, s); });
     return launch(tag[0] == 'd' ? "dq_generic" : "fwd_generic", s, [&] { la::launch_fwd_generic(a, lam, bf16, s); });
 }
@@ -328,6 +337,8 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     a.H = Hi;
     a.chunks = p.chunks;
     a.pairs = pairs;
+    if (p.mfma && la::rev_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_REV", "v1"))
+        return launch("dkdv_dma", s, [&] { la::launch_rev_dma(a, lam, s); });
     if (p.mfma && la::mfma_rev_supported(static_cast<int>(D), Bk))
         return launch("dkdv_mfma", s, [&] { la::launch_rev_mfma(a, lam, s); });
     return launch("dkdv_generic", s, [&] { la::launch_rev_generic(a, lam, bf16, s); });

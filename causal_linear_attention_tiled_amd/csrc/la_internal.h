@@ -87,4 +87,12 @@ void launch_fwd_mfma(const SweepArgs& a, const LamArgs& lam, hipStream_t s);
 void launch_rev_mfma(const SweepArgs& a, const LamArgs& lam, hipStream_t s);
 void launch_chunk_state_mfma(const ChunkStateArgs& a, const LamArgs& lam, hipStream_t s);
 
+// Forward sweep with direct-to-LDS loads (bf16, D = 128, Bk = 64); `waves` compute waves (4 or 8).
+bool fwd_dma_supported(int D, int Bk, int64_t N);
+void launch_fwd_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream_t s);
+
+// Reverse (dK, dV) sweep with direct-to-LDS loads (bf16, D = 128, Bk = 64).
+bool rev_dma_supported(int D, int Bk, int64_t N);
+void launch_rev_dma(const SweepArgs& a, const LamArgs& lam, hipStream_t s);
+
 }  // namespace la

@@ -228,3 +228,38 @@ def test_decode_matches_oracle_and_forward(dtype):
     o_dec = np.stack(outs, axis=2)
     assert oracle.rel_l2(o_dec, got(of)) <= bar(dtype)
     assert oracle.rel_l2(got(state), got(sf)) <= bar(dtype)
+
+
+# ------------------------------------------------------------------ every forward kernel variant
+@pytest.fixture
+def fwd_variant(monkeypatch):
+    def set_(v):
+        monkeypatch.delenv("LA_FWD", raising=False)
+        monkeypatch.delenv("LA_FWD_WAVES", raising=False)
+        monkeypatch.delenv("LA_REV", raising=False)
+        if v == "v1":
+            monkeypatch.setenv("LA_FWD", "v1")
+            monkeypatch.setenv("LA_REV", "v1")
+        elif v == "dma8":
+            monkeypatch.setenv("LA_FWD_WAVES", "8")
+    return set_
+
+
+@pytest.mark.parametrize("variant", ["v1", "dma4", "dma8"])
+@pytest.mark.parametrize("N,cks,with_state", [(64, 1, False), (1000, 1, True), (64 * 13 + 5, 3, True),
+                                             (64 * 40, 6, False)])
+def test_forward_variants(variant, N, cks, with_state, fwd_variant, chunks):
+    """The register-staged and the direct-to-LDS kernels (forward with 4 or 8 compute
+    waves, reverse dK/dV) meet the bar on ragged, chunked and continued sequences."""
+    fwd_variant(variant)
+    chunks(cks)
+    lam = synth.decay_schedule(3)
+    check_fwd(2, 3, N, 128, 64, "bf16", lam, seed=N + cks, with_state=with_state, label=variant)
+    check_bwd(1, 3, N, 128, 64, "bf16", lam, seed=N + cks, with_state=with_state, label=variant)
+
+
+@pytest.mark.parametrize("variant", ["v1", "dma8"])
+def test_impulse_probe_variants(variant, fwd_variant, chunks, kernel):
+    fwd_variant(variant)
+    test_impulse_probe_bit_exact("default", 0.5, 64, 4, chunks, kernel)
+    test_impulse_probe_bit_exact("default", 1.0, 64, 1, chunks, kernel)
