@@ -44,6 +44,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {         # library kernel name -> source file its code lives in
     "fwd_mfma": "k_fwd_mfma.hip", "dq_mfma": "k_fwd_mfma.hip", "fwd_dma": "k_fwd_dma.hip", "dq_dma": "k_fwd_dma.hip", "chunk_state_mfma": "k_fwd_mfma.hip",
     "chunk_state_rev_mfma": "k_fwd_mfma.hip", "dkdv_mfma": "k_bwd_mfma.hip", "dkdv_dma": "k_bwd_dma.hip",
+    "chunk_state_dma": "k_state_dma.hip", "chunk_state_rev_dma": "k_state_dma.hip",
     "dkdv_generic": "k_generic.hip", "state_scan": "k_generic.hip", "state_scan_rev": "k_generic.hip",
     "decode": "k_generic.hip",
 }
@@ -73,6 +74,7 @@ def kernel_bytes(name, B, Hh, N, d, chunks, with_state=True):
         "dkdv_mfma": 6 * t, "dkdv_generic": 6 * t, "dkdv_dma": 6 * t,
         "chunk_state_mfma": 2 * t * frac,
         "chunk_state_rev_mfma": 2 * t * frac,
+        "chunk_state_dma": 2 * t * frac, "chunk_state_rev_dma": 2 * t * frac,
         "state_scan": 2 * st * (chunks - 1), "state_scan_rev": 2 * st * (chunks - 1),
     }.get(name)
 
@@ -227,10 +229,11 @@ def bench(args):
     for sh in shapes:
         names = ["fwd_mfma", "dq_mfma", "fwd_dma", "dq_dma", "dkdv_mfma", "dkdv_generic", "dkdv_dma"]
         if sh["chunks"] > 1:
-            names += ["chunk_state_mfma", "chunk_state_rev_mfma", "state_scan", "state_scan_rev"]
+            names += ["chunk_state_mfma", "chunk_state_rev_mfma", "chunk_state_dma", "chunk_state_rev_dma",
+                      "state_scan", "state_scan_rev"]
         for nm in names:
             b = kernel_bytes(nm, sh["B"], H, sh["n"], D, sh["chunks"])
-            if nm in ("chunk_state_mfma", "state_scan"):
+            if nm in ("chunk_state_mfma", "chunk_state_dma", "state_scan"):
                 b = b * 2  # launched by the forward and by the dQ sweep of the backward
             bytes_by_kernel.setdefault(nm, []).append(b)
     kernels = {}

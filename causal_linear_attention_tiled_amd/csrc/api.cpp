@@ -167,7 +167,9 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
     int rc;
     if (p.chunks > 1) {
         la::ChunkStateArgs cs{k, v, slots, N, p.L, static_cast<int>(D), Bk, H, p.chunks, pairs, 0};
-        if (p.mfma)
+        if (p.mfma && la::state_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_STATE", "v1"))
+            rc = launch("chunk_state_dma", s, [&] { la::launch_chunk_state_dma(cs, lam, s); });
+        else if (p.mfma)
             rc = launch("chunk_state_mfma", s, [&] { la::launch_chunk_state_mfma(cs, lam, s); });
         else
             rc = launch("chunk_state_generic", s, [&] { la::launch_chunk_state_generic(cs, lam, bf16, s); });
@@ -313,7 +315,9 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     // dK, dV: reverse sweep carrying dS, with a chunked suffix over blocks.
     if (p.chunks > 1) {
         la::ChunkStateArgs cs{Q, dO, slots_kv, N, p.L, static_cast<int>(D), Bk, Hi, p.chunks, pairs, 1};
-        if (p.mfma)
+        if (p.mfma && la::state_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_STATE", "v1"))
+            rc = launch("chunk_state_rev_dma", s, [&] { la::launch_chunk_state_dma(cs, lam, s); });
+        else if (p.mfma)
             rc = launch("chunk_state_rev_mfma", s, [&] { la::launch_chunk_state_mfma(cs, lam, s); });
         else
             rc = launch("chunk_state_rev_generic", s, [&] { la::launch_chunk_state_generic(cs, lam, bf16, s); });

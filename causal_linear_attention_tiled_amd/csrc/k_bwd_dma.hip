@@ -12,7 +12,8 @@
 // current one (each block starts with vmcnt(0), so loads and stores may share
 // the counter in any order); every operand whose contraction runs over
 // tokens (dO^T, Q^T, the decayed Q) is read from the row-major tiles with the
-// transposing LDS read (lds_dma.h).  Wave w keeps dS[:, 32w..32w+32) and
+// transposing LDS read in the kappa k order, and every operand contracted
+// over features is a single 16-byte row read in the natural order (lds_dma.h).  Wave w keeps dS[:, 32w..32w+32) and
 // dS^T[:, 32w..32w+32) in MFMA accumulators, computes dV^T for its value
 // columns and dK^T for its key rows, and the masked score tiles P = Q K^T and
 // G = dO V^T are shared through LDS.
@@ -26,12 +27,13 @@ namespace {
 
 constexpr int D = 128;
 constexpr int BK = 64;
-constexpr int NT = BK / 16;
-constexpr int NKS = BK / 32;
+constexpr int NT = BK / 16;   // 16-token columns j per block
+constexpr int NKB = BK / 32;  // 32-token k blocks per block
 constexpr int NSTAGE = 2;
 constexpr int TILE = BK * D;
-constexpr int NCAUSAL = NT * (NT + 1) / 2;
-constexpr int NW = 4;  // compute waves
+constexpr int NW = 4;
+
+constexpr int NCAUSAL = NT * (NT + 1) / 2;  // score tiles (it, jt) with it >= jt
 
 struct RevDmaTiles {
     uint16_t t[NSTAGE][4][TILE];     // per stage: Q, K, V, dO (row-major, swizzled)
@@ -69,43 +71,45 @@ __global__ __launch_bounds__(64 * NW, 1) void k_rev_dma(SweepArgs a, LamArgs lam
 #pragma unroll
         for (int rg = 0; rg < BK / 4; ++rg) {
             const int r = 4 * rg + sub;
-            const int chunk = p ^ (r & 15);
+            const int chunk = p ^ swz_key(r);
             const int voff = static_cast<int>(((t0 + r) * D + 8 * chunk) * 2);
             dma16(rsrc, &sm.t[stage][wu][4 * rg * D], voff);
         }
     };
     issue(0);
 
-    // ---------------------------------------------------------------- compute waves
     uint16_t* __restrict__ dKg = static_cast<uint16_t*>(a.out0) + base;
     uint16_t* __restrict__ dVg = static_cast<uint16_t*>(a.out1) + base;
-    // dS entering this chunk from the right (0 for the last chunk).
-    //   Sv[t8][h][r] = dS[16 t8 + 4 g + r][32 w + 16 h + li]
-    //   Sk[t8][h][r] = dS^T[16 t8 + 4 g + r][32 w + 16 h + li]
+    // dS entering this chunk from the right (0 for the last chunk), in two tile sets
+    // over the interleaved rows rho (lds_dma.h):
+    //   Sv[at][h][r] = dS  [32 (at/2) + rho(at%2, 4g + r)][32 w + 16 h + li]   (value columns)
+    //   Sk[at][h][r] = dS^T[32 (at/2) + rho(at%2, 4g + r)][32 w + 16 h + li]   (key rows)
     f32x4 Sv[8][2], Sk[8][2];
     {
         const float* init = (c < a.chunks - 1) ? a.slots + (pair * (a.chunks - 1) + c) * D * D : nullptr;
 #pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8)
+        for (int at = 0; at < 8; ++at)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
+                const int row0 = 32 * (at >> 1) + rho(at & 1, 4 * g);
+                const int col = 32 * w + 16 * h + li;
                 f32x4 x = zero4(), y = zero4();
                 if (init) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) x[r] = init[(16 * t8 + 4 * g + r) * D + 32 * w + 16 * h + li];
-                    const float4 t4 = *reinterpret_cast<const float4*>(init + (32 * w + 16 * h + li) * D + 16 * t8 + 4 * g);
+                    for (int r = 0; r < 4; ++r) x[r] = init[(row0 + r) * D + col];
+                    const float4 t4 = *reinterpret_cast<const float4*>(init + col * D + row0);
                     y = f32x4{t4.x, t4.y, t4.z, t4.w};
                 }
-                Sv[t8][h] = x;
-                Sk[t8][h] = y;
+                Sv[at][h] = x;
+                Sk[at][h] = y;
             }
     }
-    // lam^s weights of the dS update, s = 32 ks + kappa(g, e) (rows past m are zero)
-    float wq[NKS][8];
+    // lam^s weights of the dS update for s = 32 kb + kappa(g, e) (rows past m are zero)
+    float wq[NKB][8];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wq[ks][e] = sm.pw[32 * ks + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4)];
+        for (int e = 0; e < 8; ++e) wq[kb][e] = 0.f;
 
     for (int64_t i = 0; i < nblk; ++i) {
         const int64_t n = nblk - 1 - i;
@@ -119,9 +123,18 @@ __global__ __launch_bounds__(64 * NW, 1) void k_rev_dma(SweepArgs a, LamArgs lam
         // Only this block's loads (and earlier stores) are outstanding here.
         wait_vmcnt<0>();
         __syncthreads();  // A(i): stage i % 2 is ready; stage (i+1) % 2 is no longer read
+        // Next block's loads: untracked by the compiler (inline asm), so no later
+        // barrier or LDS read waits for them; the next A waits with vmcnt(0).
+        if (i + 1 < nblk) issue(i + 1);
+        if (i == 0) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) wq[kb][e] = sm.pw[32 * kb + kappa(g, e)];
+        }
 
-        // ---- shared score tiles: P = Q K^T and G = dO V^T, (it, jt) with it >= jt,
-        // element (16 it + 4 g + r, 16 jt + li) kept iff i >= j and scaled by lam^(i - j)
+        // ---- shared score tiles: P = Q K^T and G = dO V^T; tile (it, jt), it >= jt, holds
+        // X[i][j] for i = 16 it + 4 g + r, j = 16 jt + li, kept iff i >= j and scaled by lam^(i - j)
 #pragma unroll
         for (int it = 0; it < NT; ++it)
 #pragma unroll
@@ -145,43 +158,41 @@ __global__ __launch_bounds__(64 * NW, 1) void k_rev_dma(SweepArgs a, LamArgs lam
                     *reinterpret_cast<u32x2*>(&dst[idx * 128 + 2 * lane]) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
                 }
         __syncthreads();  // B(i)
-        // Next block's loads go out after B(i), so that barrier never waits on them.
-        if (i + 1 < nblk) issue(i + 1);
 
         // ---- per 16-token column jt: dV^T (value columns 32w..) and dK^T (key rows 32w..)
-        bf16x8 gtf[2][NKS], qtf[2][NKS];  // dO^T[32w+16h+li][s], Q^T[32w+16h+li][s]
+        bf16x8 gtf[2][NKB], qtf[2][NKB];  // dO[32 kb + kappa(g, e)][32w + 16h + li], Q[...][...]
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                gtf[h][ks] = op_tr(Gs, 32 * ks, 32 * w + 16 * h, g, li);
-                qtf[h][ks] = op_tr(Qs, 32 * ks, 32 * w + 16 * h, g, li);
+            for (int kb = 0; kb < NKB; ++kb) {
+                gtf[h][kb] = op_tr_k(Gs, 32 * kb, 32 * w + 16 * h, 4, g, li);
+                qtf[h][kb] = op_tr_k(Qs, 32 * kb, 32 * w + 16 * h, 4, g, li);
             }
 #pragma unroll
         for (int jt = 0; jt < NT; ++jt) {
             const int j = 16 * jt + li;
             const float lj = (j < m) ? sm.pw[m - j] : 0.f;
-            bf16x8 kb[4], vb[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                kb[ks] = op_row(Ks, j, 32 * ks, g);
-                vb[ks] = op_row(Vs, j, 32 * ks, g);
-            }
             f32x4 dv[2], dk[2];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                f32x4 x = zero4(), y = zero4();
+            for (int h = 0; h < 2; ++h) dv[h] = dk[h] = zero4();
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    x = mfma16(operand_from_acc(Sv[2 * ks][h], Sv[2 * ks + 1][h]), kb[ks], x);
-                    y = mfma16(operand_from_acc(Sk[2 * ks][h], Sk[2 * ks + 1][h]), vb[ks], y);
+            for (int kb = 0; kb < 4; ++kb) {
+                const bf16x8 kr = op_row(Ks, j, 32 * kb, g);
+                const bf16x8 vr = op_row(Vs, j, 32 * kb, g);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    dv[h] = mfma16(operand_from_acc(Sv[2 * kb][h], Sv[2 * kb + 1][h]), kr, dv[h]);
+                    dk[h] = mfma16(operand_from_acc(Sk[2 * kb][h], Sk[2 * kb + 1][h]), vr, dk[h]);
                 }
-                dv[h] = x * lj;
-                dk[h] = y * lj;
             }
 #pragma unroll
-            for (int ks = jt / 2; ks < NKS; ++ks) {
-                const int i0 = 2 * ks, i1 = 2 * ks + 1;
+            for (int h = 0; h < 2; ++h) {
+                dv[h] *= lj;
+                dk[h] *= lj;
+            }
+#pragma unroll
+            for (int kb = jt / 2; kb < NKB; ++kb) {
+                const int i0 = 2 * kb, i1 = 2 * kb + 1;
                 const u32x2 z{0, 0};
                 const u32x2 plo = (i0 >= jt) ? ld_frag(sm.p, i0 * (i0 + 1) / 2 + jt, lane) : z;
                 const u32x2 phi = (i1 >= jt) ? ld_frag(sm.p, i1 * (i1 + 1) / 2 + jt, lane) : z;
@@ -190,10 +201,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_rev_dma(SweepArgs a, LamArgs lam
                 const bf16x8 pb = operand(plo, phi), gb = operand(glo, ghi);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    dv[h] = mfma16(gtf[h][ks], pb, dv[h]);
-                    dk[h] = mfma16(qtf[h][ks], gb, dk[h]);
+                    dv[h] = mfma16(gtf[h][kb], pb, dv[h]);
+                    dk[h] = mfma16(qtf[h][kb], gb, dk[h]);
                 }
             }
+            // dv[h][r] = dV[j][32 w + 16 h + 4 g + r], dk[h][r] = dK[j][32 w + 16 h + 4 g + r]
             if (j < m) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -205,28 +217,33 @@ __global__ __launch_bounds__(64 * NW, 1) void k_rev_dma(SweepArgs a, LamArgs lam
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        // ---- dS <- lam^m dS + (diag(lam^s) Q)^T dO, both copies
+        // ---- dS <- lam^m dS + Q^T diag(lam^s) dO, both copies; the weights go on this wave's
+        // own fragments (dO columns for the value copy, Q columns for the key copy)
         const float lm = sm.pw[m];
-        bf16x8 qs[2][NKS];
+        bf16x8 qs[2][NKB], gs[2][NKB];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) qs[h][ks] = scale8(qtf[h][ks], wq[ks]);
-#pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                Sv[t8][h] *= lm;
-                Sk[t8][h] *= lm;
+            for (int kb = 0; kb < NKB; ++kb) {
+                qs[h][kb] = scale8(qtf[h][kb], wq[kb]);
+                gs[h][kb] = scale8(gtf[h][kb], wq[kb]);
             }
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 qa = scale8(op_tr(Qs, 32 * ks, 16 * t8, g, li), wq[ks]);
-                const bf16x8 ga = op_tr(Gs, 32 * ks, 16 * t8, g, li);
+        for (int at = 0; at < 8; ++at) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                Sv[at][h] *= lm;
+                Sk[at][h] *= lm;
+            }
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                // Q^T / dO^T rows 32 (at/2) + rho(at%2, li), k index s = 32 kb + kappa(g, e)
+                const bf16x8 qa = op_tr_k(Qs, 32 * kb, 32 * (at >> 1) + 4 * (at & 1), 8, g, li);
+                const bf16x8 ga = op_tr_k(Gs, 32 * kb, 32 * (at >> 1) + 4 * (at & 1), 8, g, li);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    Sv[t8][h] = mfma16(qa, gtf[h][ks], Sv[t8][h]);
-                    Sk[t8][h] = mfma16(ga, qs[h][ks], Sk[t8][h]);
+                    Sv[at][h] = mfma16(qa, gs[h][kb], Sv[at][h]);
+                    Sk[at][h] = mfma16(ga, qs[h][kb], Sk[at][h]);
                 }
             }
         }

@@ -1,41 +1,48 @@
 // Forward sweep, Bk = 64, D = 128, bf16: a three-stage LDS pipeline fed by
 // direct global-to-LDS loads.
 //
-// Same arithmetic as the register-staged forward kernel (Lightning
-// Attention-2, Tiling paragraph: per block the masked, decayed intra-block
-// product plus the inter-block product with the carried state, then the
-// state's decay and update), with a different data path:
+// Lightning Attention-2 (Tiling paragraph; record mechanism field): per
+// block b with local index s and m tokens,
+//     O_b     = diag(lam^(s+1)) Q_b S_b + ((Q_b K_b^T) o M) V_b,
+//     M[s][s'] = lam^(s-s') for s >= s', else 0,
+//     S_{b+1} = lam^m S_b + K_b^T diag(lam^(m-1-s)) V_b.
+//
+// Data path:
 //   - One extra "loader" wave issues buffer_load_dwordx4 ... lds for the raw
 //     row-major Q, K, V tiles of the block two ahead of the one being
 //     computed.  It never stores, so its vmcnt waits are exact, and it
 //     hands each stage to the compute waves through the block's barriers.
 //     Loads past the end of the sequence come back as zero (buffer bounds).
-//   - Tiles stay row-major, with the 16-byte chunks of row r XOR-swizzled by
-//     (r mod 16) so that both read patterns below are free of bank conflicts.
-//   - Operands whose contraction runs over tokens (V^T for V^T A^T and for
-//     the state update, decayed K^T for the state update) come straight from
-//     the row-major tiles through ds_read_b64_tr_b16: within each 16-lane
-//     group, output lane j element e is input lane j/4 + 4e element j%4, so
-//     lanes reading rows kb+4g+i/4 at columns n0+4(i%4) deliver
-//     B[kb + kappa(g, e)][n0 + lane%16].
+//   - Row-major operands are single 16-byte reads; operands contracted over
+//     tokens (V^T, K^T) come from the same tiles through transposing reads
+//     (lds_dma.h).
 // Compute waves: NW; wave w owns 128/NW value columns of the float32 state
-// (MFMA accumulators) and of the output.
+// and of the output, which is computed transposed: O^T = S^T Q^T + V^T A^T,
+// with the masked, decayed scores A^T = (K Q^T) o M^T shared through LDS.
+// Products contracted over features (K Q^T, S^T Q^T) take the natural k
+// order, so their row-major operands are single 16-byte reads; the state
+// accumulators are kept as tile pairs over the interleaved rows rho, which
+// makes them directly the A operand of S^T Q^T.  Products contracted over
+// tokens (V^T A^T and the state update) take the kappa order, whose
+// transposing reads touch 16 consecutive rows; the score accumulators are
+// then directly the B operand of V^T A^T.
 #include "la_device.h"
 #include "la_internal.h"
-#include "mfma_common.h"
 #include "lds_dma.h"
+#include "mfma_common.h"
 
 namespace la {
 namespace {
 
 constexpr int D = 128;
 constexpr int BK = 64;
-constexpr int NT = BK / 16;
-constexpr int NKS = BK / 32;
+constexpr int NT = BK / 16;                // 16-token output columns per block
+constexpr int NKB = BK / 32;               // 32-token k blocks per block
 constexpr int NSTAGE = 3;
-constexpr int TILE = BK * D;                // elements per tile
-constexpr int NCAUSAL = NT * (NT + 1) / 2;
-constexpr int DMA_PER_BLOCK = 3 * BK / 4;   // 1 KiB loads per block (4 rows of 256 B each)
+constexpr int TILE = BK * D;               // elements per tile
+constexpr int DMA_PER_BLOCK = 3 * BK / 4;  // 1 KiB loads per block (4 rows of 256 B each)
+
+constexpr int NCAUSAL = NT * (NT + 1) / 2;   // score tiles (at, st) with at <= st
 
 struct DmaTiles {
     uint16_t t[NSTAGE][3][TILE];     // per stage: Q, K, V (row-major, swizzled)
@@ -75,7 +82,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
 #pragma unroll
                 for (int rg = 0; rg < BK / 4; ++rg) {
                     const int r = 4 * rg + sub;
-                    const int chunk = p ^ (r & 15);
+                    const int chunk = p ^ swz_key(r);
                     const int voff = static_cast<int>(((t0 + r) * D + 8 * chunk) * 2);
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[x], (lds_void*)&sm.t[stage][x][4 * rg * D], 16, voff, 0, 0, 0);
                 }
@@ -99,6 +106,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
 
     // ---------------------------------------------------------------- compute waves
     uint16_t* __restrict__ Og = static_cast<uint16_t*>(a.out0) + base;
+    // S[at][vt][r] = S[32 (at/2) + rho(at%2, 4g + r)][16 (NVT w + vt) + li]
     f32x4 S[8][NVT];
     {
         const float* init = nullptr;
@@ -116,14 +124,15 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt) {
                 const int col = 16 * (NVT * w + vt) + li;
+                const int row0 = 32 * (at >> 1) + rho(at & 1, 4 * g);
                 f32x4 x = zero4();
                 if (init) {
                     if (tr) {
-                        const float4 t4 = *reinterpret_cast<const float4*>(init + col * D + 16 * at + 4 * g);
+                        const float4 t4 = *reinterpret_cast<const float4*>(init + col * D + row0);
                         x = f32x4{t4.x, t4.y, t4.z, t4.w};
                     } else {
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) x[r] = init[(16 * at + 4 * g + r) * D + col];
+                        for (int r = 0; r < 4; ++r) x[r] = init[(row0 + r) * D + col];
                     }
                 }
                 S[at][vt] = x;
@@ -133,18 +142,6 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
     float rs[NT];
 #pragma unroll
     for (int st = 0; st < NT; ++st) rs[st] = sm.pw[16 * st + li + 1];
-    // decay lam^(m-1-s) of the K operand rows s = 32 ks + kappa(g, e) of the state update
-    float wk[NKS][8];
-    auto set_wk = [&](int m) {
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int s = 32 * ks + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
-                wk[ks][e] = s < m ? sm.pw[m - 1 - s] : 0.f;
-            }
-    };
-    set_wk(BK);
 
     for (int64_t n = 0; n < nblk; ++n) {
         const int64_t t0 = t_begin + n * BK;
@@ -153,10 +150,10 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
         const uint16_t* Qs = sm.t[stage][0];
         const uint16_t* Ks = sm.t[stage][1];
         const uint16_t* Vs = sm.t[stage][2];
-        if (m < BK) set_wk(m);
         __syncthreads();  // A(n)
 
-        // ---- score tiles A^T = (K Q^T) o M^T, shared through LDS
+        // ---- score tiles A^T = (K Q^T) o M^T: tile (at, st), at <= st, holds A^T[s'][s] for
+        // s' = 16 at + 4 g + r, s = 16 st + li; kept iff s' <= s, scaled by lam^(s - s').
 #pragma unroll
         for (int st = 0; st < NT; ++st)
 #pragma unroll
@@ -176,42 +173,45 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
             }
         __syncthreads();  // B(n)
 
-        // ---- V^T fragments (A operand of V^T A^T, B operand of the state update)
-        bf16x8 vf[NVT][NKS];
+        // ---- V^T fragments over tokens (kappa order): A operand of V^T A^T; weighted by
+        // lam^(m-1-s), the B operand of the state update
+        bf16x8 vf[NVT][NKB];
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt)
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) vf[vt][ks] = op_tr(Vs, 32 * ks, 16 * (NVT * w + vt), g, li);
-        bf16x8 sb[NVT][4];
-#pragma unroll
-        for (int vt = 0; vt < NVT; ++vt)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) sb[vt][ks] = operand_from_acc(S[2 * ks][vt], S[2 * ks + 1][vt]);
+            for (int kb = 0; kb < NKB; ++kb) vf[vt][kb] = op_tr_k(Vs, 32 * kb, 16 * (NVT * w + vt), 4, g, li);
 
         // ---- per 16-token column: O^T = diag(lam^(s+1)) S^T Q^T + V^T A^T, store
 #pragma unroll
         for (int st = 0; st < NT; ++st) {
+            // the bf16 state operands are rebuilt per column (opaque to the compiler) rather
+            // than held across the loop: 32 fewer live registers for a few converts
+#pragma unroll
+            for (int at = 0; at < 8; ++at)
+#pragma unroll
+                for (int vt = 0; vt < NVT; ++vt) asm volatile("" : "+v"(S[at][vt]));
             bf16x8 qf[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) qf[ks] = op_row(Qs, 16 * st + li, 32 * ks, g);
+            for (int kb = 0; kb < 4; ++kb) qf[kb] = op_row(Qs, 16 * st + li, 32 * kb, g);
             f32x4 o[NVT];
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt) {
                 f32x4 acc = zero4();
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) acc = mfma16(sb[vt][ks], qf[ks], acc);
+                for (int kb = 0; kb < 4; ++kb) acc = mfma16(operand_from_acc(S[2 * kb][vt], S[2 * kb + 1][vt]), qf[kb], acc);
                 o[vt] = acc * rs[st];
             }
 #pragma unroll
-            for (int ks = 0; ks <= st / 2; ++ks) {
-                const int a0 = 2 * ks, a1 = 2 * ks + 1;
+            for (int kb = 0; kb <= st / 2; ++kb) {
+                const int a0 = 2 * kb, a1 = 2 * kb + 1;
                 const u32x2 lo = *reinterpret_cast<const u32x2*>(&sm.at[(st * (st + 1) / 2 + a0) * 128 + 2 * lane]);
                 u32x2 hi = u32x2{0, 0};
                 if (a1 <= st) hi = *reinterpret_cast<const u32x2*>(&sm.at[(st * (st + 1) / 2 + a1) * 128 + 2 * lane]);
                 const bf16x8 b = operand(lo, hi);
 #pragma unroll
-                for (int vt = 0; vt < NVT; ++vt) o[vt] = mfma16(vf[vt][ks], b, o[vt]);
+                for (int vt = 0; vt < NVT; ++vt) o[vt] = mfma16(vf[vt][kb], b, o[vt]);
             }
+            // o[vt][r] = O[16 st + li][16 (NVT w + vt) + 4 g + r]
             const int s = 16 * st + li;
             if (s < m) {
 #pragma unroll
@@ -223,17 +223,30 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        // ---- S <- lam^m S + (diag(lam^(m-1-s)) K)^T V
+        // ---- S <- lam^m S + K^T diag(lam^(m-1-s)) V
         const float lm = sm.pw[m];
+        bf16x8 vw[NVT][NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            float wk[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int s = 32 * kb + kappa(g, e);
+                wk[e] = s < m ? sm.pw[m - 1 - s] : 0.f;
+            }
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt) vw[vt][kb] = scale8(vf[vt][kb], wk);
+        }
 #pragma unroll
         for (int at = 0; at < 8; ++at) {
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt) S[at][vt] *= lm;
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 kf = scale8(op_tr(Ks, 32 * ks, 16 * at, g, li), wk[ks]);
+            for (int kb = 0; kb < NKB; ++kb) {
+                // K^T[32 (at/2) + rho(at%2, li)][32 kb + kappa(g, e)]
+                const bf16x8 kf = op_tr_k(Ks, 32 * kb, 32 * (at >> 1) + 4 * (at & 1), 8, g, li);
 #pragma unroll
-                for (int vt = 0; vt < NVT; ++vt) S[at][vt] = mfma16(kf, vf[vt][ks], S[at][vt]);
+                for (int vt = 0; vt < NVT; ++vt) S[at][vt] = mfma16(kf, vw[vt][kb], S[at][vt]);
             }
         }
     }
@@ -245,7 +258,8 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dst[(16 * at + 4 * g + r) * D + 16 * (NVT * w + vt) + li] = S[at][vt][r];
+                for (int r = 0; r < 4; ++r)
+                    dst[(32 * (at >> 1) + rho(at & 1, 4 * g + r)) * D + 16 * (NVT * w + vt) + li] = S[at][vt][r];
     }
 }
 

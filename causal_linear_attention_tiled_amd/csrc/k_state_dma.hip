@@ -1,0 +1,136 @@
+// Chunk aggregates for the chunked prefix over blocks (bf16, D = 128,
+// Bk = 64), fed by direct global-to-LDS loads.
+//
+// For every chunk c that another chunk depends on, the state update of the
+// sweep (Lightning Attention-2, Tiling paragraph: the inter-block part is
+// carried by the key-value state) run over the chunk's blocks from zero:
+//   forward: acc <- lam^m acc + X_b^T diag(lam^(m-1-s)) Y_b, blocks in order
+//   reverse: acc <- lam^m acc + X_b^T diag(lam^s) Y_b, blocks last to first
+// with (X, Y) = (K, V) for the forward and (Q, dO) for the gradient state.
+// The loop stores nothing, so the four waves share the loads (8 of the 32
+// loads of a block each) with exact partial vmcnt waits over a three-stage
+// ring.  Both operands come from the row-major tiles through transposing LDS
+// reads; wave w accumulates columns [32w, 32w + 32) of the aggregate.
+#include "la_device.h"
+#include "la_internal.h"
+#include "lds_dma.h"
+#include "mfma_common.h"
+
+namespace la {
+namespace {
+
+constexpr int D = 128;
+constexpr int BK = 64;
+constexpr int NKB = BK / 32;
+constexpr int NSTAGE = 3;
+constexpr int TILE = BK * D;
+constexpr int NW = 4;
+constexpr int LOADS_PER_WAVE = 2 * (BK / 4) / NW;  // 1 KiB loads per wave per block
+
+struct StateTiles {
+    uint16_t t[NSTAGE][2][TILE];  // per stage: X, Y (row-major, swizzled)
+    float pw[BK + 1];
+};
+
+__global__ __launch_bounds__(64 * NW, 1) void k_chunk_state_dma(ChunkStateArgs a, LamArgs lam) {
+    __shared__ StateTiles sm;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
+    const int per = a.chunks - 1;
+    const int64_t pair = blockIdx.x / per;
+    const int slot = blockIdx.x % per;
+    const int c = a.reverse ? slot + 1 : slot;
+    const int64_t t_begin = static_cast<int64_t>(c) * a.L;
+    const int64_t t_end = min(a.N, t_begin + a.L);
+    const int64_t nblk = (t_end - t_begin + BK - 1) / BK;
+    const int64_t base = pair * a.N * D;
+    for (int e = tid; e <= BK; e += 64 * NW) sm.pw[e] = lam_pow(lam.lam[pair % a.H], e);
+
+    const uint32_t bytes = static_cast<uint32_t>(a.N * D * 2);
+    const u32x4 rx = buffer_rsrc(static_cast<const uint16_t*>(a.x) + base, bytes);
+    const u32x4 ry = buffer_rsrc(static_cast<const uint16_t*>(a.y) + base, bytes);
+    // The n-th block of the walk (in order, or from the last block backwards) goes to stage n % 3.
+    // Wave w issues, for each tensor, the loads of row groups w, w + 4, w + 8, w + 12 (4 rows each).
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    auto issue = [&](int64_t n) {
+        const int64_t bi = a.reverse ? nblk - 1 - n : n;
+        const int64_t t0 = t_begin + bi * BK;
+        const int stage = static_cast<int>(n % NSTAGE);
+        const int sub = lane >> 4, p = lane & 15;
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int i = 0; i < LOADS_PER_WAVE / 2; ++i) {
+                const int rg = wu + NW * i;
+                const int r = 4 * rg + sub;
+                const int voff = static_cast<int>(((t0 + r) * D + 8 * (p ^ swz_key(r))) * 2);
+                dma16(x == 0 ? rx : ry, &sm.t[stage][x][4 * rg * D], voff);
+            }
+    };
+    issue(0);
+    if (nblk > 1) issue(1);
+
+    // S[at][h][r] = acc[32 (at/2) + rho(at%2, 4g + r)][32 w + 16 h + li]
+    f32x4 S[8][2];
+#pragma unroll
+    for (int at = 0; at < 8; ++at) S[at][0] = S[at][1] = zero4();
+
+    for (int64_t n = 0; n < nblk; ++n) {
+        const int64_t bi = a.reverse ? nblk - 1 - n : n;
+        const int64_t t0 = t_begin + bi * BK;
+        const int m = static_cast<int>(min(static_cast<int64_t>(BK), t_end - t0));
+        const int stage = static_cast<int>(n % NSTAGE);
+        if (n + 1 < nblk)
+            wait_vmcnt<LOADS_PER_WAVE>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();  // stage n % 3 is complete; stage (n + 2) % 3 is no longer read
+        if (n + 2 < nblk) issue(n + 2);
+        const uint16_t* Xs = sm.t[stage][0];
+        const uint16_t* Ys = sm.t[stage][1];
+        // weights of token s = 32 kb + kappa(g, e), on the Y operand (2 fragments per k block, not 8)
+        float wx[NKB][8];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int s = 32 * kb + kappa(g, e);
+                wx[kb][e] = s < m ? (a.reverse ? sm.pw[s] : sm.pw[m - 1 - s]) : 0.f;
+            }
+        bf16x8 yf[2][NKB];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) yf[h][kb] = scale8(op_tr_k(Ys, 32 * kb, 32 * w + 16 * h, 4, g, li), wx[kb]);
+        const float lm = sm.pw[m];
+#pragma unroll
+        for (int at = 0; at < 8; ++at) {
+            S[at][0] *= lm;
+            S[at][1] *= lm;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const bf16x8 xf = op_tr_k(Xs, 32 * kb, 32 * (at >> 1) + 4 * (at & 1), 8, g, li);
+                S[at][0] = mfma16(xf, yf[0][kb], S[at][0]);
+                S[at][1] = mfma16(xf, yf[1][kb], S[at][1]);
+            }
+        }
+    }
+    float* dst = a.slots + (pair * per + slot) * D * D;
+#pragma unroll
+    for (int at = 0; at < 8; ++at)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[(32 * (at >> 1) + rho(at & 1, 4 * g + r)) * D + 32 * w + 16 * h + li] = S[at][h][r];
+}
+
+}  // namespace
+
+bool state_dma_supported(int d, int bk, int64_t n) { return d == 128 && bk == 64 && n * d * 2 < (int64_t(1) << 31); }
+
+void launch_chunk_state_dma(const ChunkStateArgs& a, const LamArgs& lam, hipStream_t s) {
+    dim3 grid(static_cast<unsigned>(a.pairs * (a.chunks - 1)));
+    hipLaunchKernelGGL(k_chunk_state_dma, grid, dim3(64 * NW), 0, s, a, lam);
+}
+
+}  // namespace la

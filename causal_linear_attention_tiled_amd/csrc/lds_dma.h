@@ -2,15 +2,15 @@
 // [rows][128] bf16 tiles, operand reads from them (plain and transposing),
 // and exact vmcnt waits.
 //
-// Tiles are row-major with the 16-byte chunks of row r XOR-swizzled by
-// (r mod 16): a row read by 16 lanes on consecutive rows and the transposing
-// read below both spread over all banks.
+// Operands here use the natural k order (lane group g holds k = 8g .. 8g + 7)
+// for both MFMA operands, so that every row-major operand is one 16-byte
+// read.  Tiles are row-major with 16-byte chunks XOR-swizzled per row.
 //
 // ds_read_b64_tr_b16: within each 16-lane group, output lane j element e is
-// input lane j/4 + 4e element j%4.  Lanes i of group g reading rows
-// kb + 4g + i/4 at columns n0 + 4(i%4) therefore deliver the B operand
-// B[kb + kappa(g, e)][n0 + lane%16] of a row-major tile whose rows are the
-// contraction index (see mfma_common.h for kappa).
+// input lane j/4 + 4e element j%4.  If input lane i reads 4 elements at row
+// R + i/4 and column C + s * (i%4), output lane j holds rows R .. R+3 at
+// column C + s * (j/4) + j%4, i.e. one half of an operand whose contraction
+// index runs over the tile's rows.
 #pragma once
 
 #include "mfma_common.h"
@@ -23,27 +23,56 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Swizzle of row r: chunk c of the row is stored at position c ^ (r mod 16).
+// Sixteen consecutive rows get distinct keys, so a 16-lane row read spreads
+// over all banks; since the key repeats every 16 rows, reads 16 or 32 rows
+// apart share an address register and differ by an immediate offset.
+__device__ __forceinline__ int swz_key(int row) { return row & 15; }
+
 // Element offset of (row, col) in a swizzled [rows][128] tile.
 __device__ __forceinline__ int swz(int row, int col) {
-    return row * kTileCols + ((((col >> 3) ^ (row & 15))) << 3) + (col & 7);
+    return row * kTileCols + (((col >> 3) ^ swz_key(row)) << 3) + (col & 7);
 }
 
-// kappa-ordered operand from row `row`, k columns [k0, k0 + 32) (row-major read).
+// Natural-order operand: the 8 bf16 at row `row`, columns k0 + 8g .. k0 + 8g + 7
+// (one 16-byte read).
 __device__ __forceinline__ bf16x8 op_row(const uint16_t* t, int row, int k0, int g) {
-    const u32x2 lo = *reinterpret_cast<const u32x2*>(t + swz(row, k0 + 4 * g));
-    const u32x2 hi = *reinterpret_cast<const u32x2*>(t + swz(row, k0 + 16 + 4 * g));
-    return operand(lo, hi);
+    return *reinterpret_cast<const bf16x8*>(t + swz(row, k0 + 8 * g));
 }
 
-// Operand B[kb + kappa(g, e)][n0 + li] of a row-major tile (rows = k), by two transposing reads.
-__device__ __forceinline__ bf16x8 op_tr(const uint16_t* t, int kb, int n0, int g, int li) {
-    const int r = kb + 4 * g + (li >> 2), col = n0 + 4 * (li & 3);
+// Operand from a row-major tile X whose rows are the contraction index, by two
+// transposing reads: lane (g, li) gets X[kb + 8g + e][col(li)], e = 0..7, with
+// col(li) = n0 + cstride * (li / 4) + li % 4.  cstride = 4 gives col = n0 + li;
+// cstride = 8 gives the interleaved rows rho_t(li) (n0 = 32b + 4t) of a tile pair.
+__device__ __forceinline__ bf16x8 op_tr(const uint16_t* t, int kb, int n0, int cstride, int g, int li) {
+    const int r = kb + 8 * g + (li >> 2), col = n0 + cstride * (li & 3);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + swz(r, col)));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + swz(r + 4, col)));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 v{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// The same with the k index in the kappa order of mfma_common.h (rows kb + 4g + e
+// for e < 4, kb + 16 + 4g + e - 4 for e >= 4): the 16 rows one read touches are
+// consecutive, so they have distinct swizzle keys.
+__device__ __forceinline__ bf16x8 op_tr_k(const uint16_t* t, int kb, int n0, int cstride, int g, int li) {
+    const int r = kb + 4 * g + (li >> 2), col = n0 + cstride * (li & 3);
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + swz(r, col)));
     const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(t + swz(r + 16, col)));
     typedef short v8i16 __attribute__((ext_vector_type(8)));
     const v8i16 v{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
 }
+
+// kappa(g, e): the token offset inside a 32-token k block held by lane group g, element e.
+__device__ __forceinline__ constexpr int kappa(int g, int e) { return e < 4 ? 4 * g + e : 16 + 4 * g + e - 4; }
+
+// Row of a 32-row block covered by row i of its tile t (0 or 1): the two tiles
+// of a block interleave in runs of four, so that their accumulators stacked
+// (tile 0 for e < 4, tile 1 for e >= 4) are a natural-order operand whose k
+// index runs over the block's 32 rows.
+__device__ __forceinline__ constexpr int rho(int t, int i) { return 8 * (i >> 2) + 4 * t + (i & 3); }
 
 // Multiply the 8 bf16 of an operand by per-element weights, rounding back to bf16.
 __device__ __forceinline__ bf16x8 scale8(const bf16x8& x, const float* wt) {

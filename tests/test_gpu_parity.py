@@ -237,9 +237,11 @@ def fwd_variant(monkeypatch):
         monkeypatch.delenv("LA_FWD", raising=False)
         monkeypatch.delenv("LA_FWD_WAVES", raising=False)
         monkeypatch.delenv("LA_REV", raising=False)
+        monkeypatch.delenv("LA_STATE", raising=False)
         if v == "v1":
             monkeypatch.setenv("LA_FWD", "v1")
             monkeypatch.setenv("LA_REV", "v1")
+            monkeypatch.setenv("LA_STATE", "v1")
         elif v == "dma8":
             monkeypatch.setenv("LA_FWD_WAVES", "8")
     return set_
