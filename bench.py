@@ -41,6 +41,7 @@ TOKENS_PER_POINT = 131072
 HBM_PEAK_GBS = 8000.0      # MI355X published HBM3E bandwidth
 BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA rate
 PROFILES = os.path.join(ROOT, "profiles")
+CALIB_BYTES = 1 << 30      # bytes read and written by the calibration copy
 KERNEL_SOURCES = {         # library kernel name -> source file its code lives in
     "fwd_mfma": "k_fwd_mfma.hip", "dq_mfma": "k_fwd_mfma.hip", "fwd_dma": "k_fwd_dma.hip", "dq_dma": "k_fwd_dma.hip", "chunk_state_mfma": "k_fwd_mfma.hip",
     "chunk_state_rev_mfma": "k_fwd_mfma.hip", "dkdv_mfma": "k_bwd_mfma.hip", "dkdv_dma": "k_bwd_dma.hip",
@@ -131,7 +132,7 @@ def cpu_baseline(seconds_target):
     lam = synth.decay_schedule(H).astype(np.float64)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
 
-    def run(pairs):
+    def run(pairs, reps=1):
         qs, ks, vs, gs, ls = [], [], [], [], []
         for p in range(pairs):
             b, h = p // H, p % H
@@ -140,20 +141,24 @@ def cpu_baseline(seconds_target):
             qs.append(q); ks.append(k); vs.append(v); gs.append(g); ls.append(lam[h])
         q, k, v, g = (np.stack(x) for x in (qs, ks, vs, gs))
         t0 = time.perf_counter()
-        oracle.fwd_recurrent(q, k, v, np.array(ls))
-        oracle.bwd_recurrent(q, k, v, g, np.array(ls))
+        for _ in range(reps):
+            oracle.fwd_recurrent(q, k, v, np.array(ls))
+            oracle.bwd_recurrent(q, k, v, g, np.array(ls))
         return time.perf_counter() - t0
 
-    pairs = threads
+    pairs, reps = threads, 1
     dt = run(pairs)
     if dt < seconds_target / 4:
-        pairs = int(min(B * H, max(pairs, pairs * seconds_target / max(dt, 1e-3))))
-        pairs = max(threads, (pairs // threads) * threads)
-        dt = run(pairs)
-    tokens = pairs * n / H          # tokens of the metric carry all H heads
+        # more sequences (up to all of this sweep point), then repeated passes over them
+        scale = seconds_target / max(dt, 1e-3)
+        pairs = min(B * H, max(threads, int(pairs * scale) // threads * threads))
+        reps = max(1, int(round(scale * threads / pairs)))
+        dt = run(pairs, reps)
+    tokens = reps * pairs * n / H   # tokens of the metric carry all H heads
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{pairs} of the {B * H} (batch, head) sequences of the n={n} sweep point "
-                      f"(d={D}, per-head decay), fwd+bwd, recurrent form in fp64, {dt:.1f} s"}
+                      f"(d={D}, per-head decay), {reps} pass(es), fwd+bwd, recurrent form in fp64, "
+                      f"{dt:.1f} s"}
 
 
 # ----------------------------------------------------------------------------- main bench
@@ -215,6 +220,15 @@ def bench(args):
     wall = time.perf_counter() - t0
     tokens_per_step = TOKENS_PER_POINT * len(SWEEP_N)
     value = tokens_per_step / (ms_per_step * 1e-3)
+    if args.calib_copy:
+        # a plain device copy of known size, for calibrating the HBM byte counters
+        src = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    if args.quick:
+        print(json.dumps({"ms_per_step": round(ms_per_step, 4), "value": round(value, 1)}), flush=True)
+        return
 
     # second pass over the same steps with per-kernel HIP events (on the launch stream)
     la.la_prof_enable(True)
@@ -322,30 +336,77 @@ def bench(args):
 
 
 # ----------------------------------------------------------------------------- rocprofv3 summaries
-def summarize(args):
-    """Summarize rocprofv3 output: kernel stats (--stats) or counters (--pmc FETCH_SIZE / WRITE_SIZE).
+# library kernel name -> substring of the device function name rocprofv3 reports
+KERNEL_SYMBOLS = {"fwd_dma": "k_fwd_dma", "dq_dma": "k_fwd_dma", "dkdv_dma": "k_rev_dma",
+                  "chunk_state_dma": "k_chunk_state_dma", "chunk_state_rev_dma": "k_chunk_state_dma",
+                  "state_scan": "k_scan", "decode": "k_decode", "fwd_mfma": "k_fwd_mfma",
+                  "dkdv_mfma": "k_rev_mfma"}
 
-    Writes profiles/<kernel>_sweep_*.txt with the figures the benchmark uses."""
-    lines = [f"# command: {args.command}", f"# source: {args.dir}"]
+
+def _csv(dirname, suffix):
+    files = glob.glob(os.path.join(dirname, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *{suffix} under {dirname}")
+    return list(csv.DictReader(open(files[0])))
+
+
+def _counter_means(dirname, counter):
+    """{kernel name: (dispatches, mean counter value per dispatch)} from a --pmc run."""
+    by = {}
+    for r in _csv(dirname, "counter_collection.csv"):
+        if r["Counter_Name"] == counter:
+            by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (len(v), sum(v) / len(v)) for k, v in by.items()}
+
+
+def summarize(args):
+    """Summarize rocprofv3 output into short text files (see --help).
+
+    stats:   kernel table from --kernel-trace --stats
+    fetch / write: per-kernel FETCH_SIZE / WRITE_SIZE means from a --pmc run
+    traffic: HBM bytes per launch of --kernel from the FETCH_SIZE and WRITE_SIZE runs,
+             each scaled by what the same counter reads for the 1 GiB calibration copy."""
+    os.makedirs(args.out, exist_ok=True)
+    lines = [f"# command: {args.command}"]
     if args.kind == "stats":
-        files = glob.glob(os.path.join(args.dir, "**", "*kernel_stats.csv"), recursive=True)
-        rows = list(csv.DictReader(open(files[0])))
+        rows = _csv(args.dir, "kernel_stats.csv")
         lines.append("kernel | calls | avg_us | total_ms | pct")
         for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
             lines.append(f"{r['Name'][:110]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f}")
-        out = os.path.join(PROFILES, f"kernels_{args.tag}_stats.txt")
+        out = os.path.join(args.out, f"kernels_{args.tag}_stats.txt")
+    elif args.kind in ("fetch", "write"):
+        counter = "FETCH_SIZE" if args.kind == "fetch" else "WRITE_SIZE"
+        lines.append(f"kernel | dispatches | mean {counter} (KiB per dispatch)")
+        for k, (n, mean) in sorted(_counter_means(args.dir, counter).items()):
+            lines.append(f"{k[:110]} | {n} | {mean:.1f}")
+        out = os.path.join(args.out, f"counters_{args.tag}_{args.kind}.txt")
     else:
-        files = glob.glob(os.path.join(args.dir, "**", "*counter_collection.csv"), recursive=True)
-        rows = list(csv.DictReader(open(files[0])))
-        by_kernel = {}
-        for r in rows:
-            by_kernel.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
-        lines.append("kernel | counter | dispatches | mean_per_dispatch")
-        for (kn, cn), vals in sorted(by_kernel.items()):
-            lines.append(f"{kn[:110]} | {cn} | {len(vals)} | {sum(vals) / len(vals):.1f}")
-        out = os.path.join(PROFILES, f"counters_{args.tag}_{args.kind}.txt")
-    os.makedirs(PROFILES, exist_ok=True)
+        fetch = _counter_means(args.fetch, "FETCH_SIZE")
+        write = _counter_means(args.write, "WRITE_SIZE")
+        sym = KERNEL_SYMBOLS[args.kernel]
+        pick = lambda d, sub: [v for k, v in d.items() if sub in k]
+        copy_f = pick(fetch, "copy") or pick(fetch, "elementwise")
+        copy_w = pick(write, "copy") or pick(write, "elementwise")
+        kf, kw = pick(fetch, sym), pick(write, sym)
+        if not (copy_f and copy_w and kf and kw):
+            raise SystemExit("kernel or calibration copy missing from the counter runs")
+        calib_kib = CALIB_BYTES / 1024
+        f_fetch = calib_kib / max(v[1] for v in copy_f)
+        f_write = calib_kib / max(v[1] for v in copy_w)
+        fetch_b = kf[0][1] * f_fetch * 1024
+        write_b = kw[0][1] * f_write * 1024
+        lines += [f"kernel: {args.kernel}",
+                  f"device_function_contains: {sym}",
+                  f"dispatches: {kf[0][0]}",
+                  f"fetch_kib_per_dispatch_raw: {kf[0][1]:.1f}",
+                  f"write_kib_per_dispatch_raw: {kw[0][1]:.1f}",
+                  f"calibration: 1 GiB device copy; FETCH_SIZE scale {f_fetch:.4f}, WRITE_SIZE scale {f_write:.4f}",
+                  f"hbm_fetch_bytes_per_launch: {fetch_b:.0f}",
+                  f"hbm_write_bytes_per_launch: {write_b:.0f}",
+                  f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
+                  f"source_sha256_16: {source_digest(args.kernel)}"]
+        out = os.path.join(args.out, f"{args.kernel}_{args.tag}_traffic.txt")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("wrote", out)
@@ -358,8 +419,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--quick", action="store_true", help="timed steps only (for profiled runs)")
+    ap.add_argument("--calib-copy", action="store_true", help="also run a 1 GiB device copy")
+    ap.add_argument("--out", default=PROFILES, help="summarize: output directory")
+    ap.add_argument("--fetch", default="", help="summarize --kind traffic: FETCH_SIZE run dir")
+    ap.add_argument("--write", default="", help="summarize --kind traffic: WRITE_SIZE run dir")
+    ap.add_argument("--kernel", default="dkdv_dma", help="summarize --kind traffic: library kernel name")
     ap.add_argument("summarize", nargs="?", help=argparse.SUPPRESS)
-    ap.add_argument("--kind", choices=["stats", "fetch", "write"], default="stats")
+    ap.add_argument("--kind", choices=["stats", "fetch", "write", "traffic"], default="stats")
     ap.add_argument("--dir", default="")
     ap.add_argument("--tag", default="sweep")
     ap.add_argument("--command", default="")
