@@ -342,7 +342,10 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     a.chunks = p.chunks;
     a.pairs = pairs;
     if (p.mfma && la::rev_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_REV", "v1"))
-        return launch("dkdv_dma", s, [&] { la::launch_rev_dma(a, lam, s); });
+    {
+        const int waves = env_is("LA_REV_WAVES", "4") ? 4 : 8;
+        return launch("dkdv_dma", s, [&] { la::launch_rev_dma(a, lam, waves, s); });
+    }
     if (p.mfma && la::mfma_rev_supported(static_cast<int>(D), Bk))
         return launch("dkdv_mfma", s, [&] { la::launch_rev_mfma(a, lam, s); });
     return launch("dkdv_generic", s, [&] { la::launch_rev_generic(a, lam, bf16, s); });

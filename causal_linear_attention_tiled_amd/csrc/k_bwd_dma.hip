@@ -250,13 +250,199 @@ __global__ __launch_bounds__(64 * NW, 1) void k_rev_dma(SweepArgs a, LamArgs lam
     }
 }
 
+
+// Eight-wave form: the value group (waves 0-3) keeps dS[:, 32 q .. 32 q + 32)
+// and produces dV for those value columns, the key group (waves 4-7) keeps
+// dS^T[:, 32 q .. 32 q + 32) and produces dK for those key rows (q = w mod 4).
+// Each wave holds 64 accumulator registers instead of 128, so two waves share
+// every SIMD and one hides the other's LDS and MFMA latency.  The value group
+// builds the P tiles, the key group the G tiles.
+__global__ __launch_bounds__(64 * 8, 1) void k_rev_dma_split(SweepArgs a, LamArgs lam) {
+    __shared__ RevDmaTiles sm;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = w >> 2, q = w & 3;
+    const int64_t pair = blockIdx.x / a.chunks;
+    const int c = blockIdx.x % a.chunks;
+    const float lv = lam.lam[pair % a.H];
+    const int64_t t_begin = static_cast<int64_t>(c) * a.L;
+    const int64_t t_end = min(a.N, t_begin + a.L);
+    const int64_t nblk = (t_end - t_begin + BK - 1) / BK;
+    const int64_t base = pair * a.N * D;
+
+    for (int e = tid; e <= BK; e += 64 * 8) sm.pw[e] = lam_pow(lv, e);
+
+    // DMA: wave w streams rows 32 (w & 1) .. + 32 of tensor w / 2 (Q, K, V, dO)
+    // of the i-th block of the sweep into stage i % 2, 8 loads of 1 KiB.
+    const int ten = w >> 1, half = w & 1;
+    const void* src = ten == 0 ? a.a : ten == 1 ? a.b : ten == 2 ? a.c : a.g;
+    const u32x4 rsrc = buffer_rsrc(static_cast<const uint16_t*>(src) + base, static_cast<uint32_t>(a.N * D * 2));
+    auto issue = [&](int64_t i) {
+        const int stage = static_cast<int>(i % NSTAGE);
+        const int64_t t0 = t_begin + (nblk - 1 - i) * BK;
+        const int sub = lane >> 4, p = lane & 15;
+#pragma unroll
+        for (int rg = 0; rg < BK / 8; ++rg) {
+            const int r = 32 * half + 4 * rg + sub;
+            const int chunk = p ^ swz_key(r);
+            const int voff = static_cast<int>(((t0 + r) * D + 8 * chunk) * 2);
+            dma16(rsrc, &sm.t[stage][ten][(32 * half + 4 * rg) * D], voff);
+        }
+    };
+    issue(0);
+
+    uint16_t* __restrict__ outg = static_cast<uint16_t*>(grp ? a.out0 : a.out1) + base;
+    // The group's copy over the interleaved rows rho (lds_dma.h):
+    //   S[at][h][r] = X[32 (at/2) + rho(at%2, 4g + r)][32 q + 16 h + li],  X = dS (value group)
+    //   or dS^T (key group), entering this chunk from the right (0 for the last chunk).
+    f32x4 S[8][2];
+    {
+        const float* init = (c < a.chunks - 1) ? a.slots + (pair * (a.chunks - 1) + c) * D * D : nullptr;
+#pragma unroll
+        for (int at = 0; at < 8; ++at)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int row0 = 32 * (at >> 1) + rho(at & 1, 4 * g);
+                const int col = 32 * q + 16 * h + li;
+                f32x4 x = zero4();
+                if (init) {
+                    if (grp) {
+                        const float4 t4 = *reinterpret_cast<const float4*>(init + col * D + row0);
+                        x = f32x4{t4.x, t4.y, t4.z, t4.w};
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) x[r] = init[(row0 + r) * D + col];
+                    }
+                }
+                S[at][h] = x;
+            }
+    }
+    float wq[NKB][8];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wq[kb][e] = 0.f;
+
+    for (int64_t i = 0; i < nblk; ++i) {
+        const int64_t n = nblk - 1 - i;
+        const int64_t t0 = t_begin + n * BK;
+        const int m = static_cast<int>(min(static_cast<int64_t>(BK), t_end - t0));
+        const int stage = static_cast<int>(i % NSTAGE);
+        // value group: rows K, tiles P, token-contracted operand dO, update operand Q^T
+        // key group:   rows V, tiles G, token-contracted operand Q,  update operand dO^T
+        const uint16_t* Xs = sm.t[stage][grp ? 3 : 0];  // score tile A rows (Q or dO)
+        const uint16_t* Rs = sm.t[stage][grp ? 2 : 1];  // score tile B rows and inter rows (K or V)
+        const uint16_t* Ts = sm.t[stage][grp ? 0 : 3];  // intra A operand / update B (dO or Q)
+        uint32_t* tiles = grp ? sm.gg : sm.p;
+        wait_vmcnt<0>();
+        __syncthreads();  // A(i)
+        if (i + 1 < nblk) issue(i + 1);
+        if (i == 0) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) wq[kb][e] = sm.pw[32 * kb + kappa(g, e)];
+        }
+
+        // ---- this group's score tiles (it, jt), it >= jt: X[i][j] for i = 16 it + 4 g + r,
+        // j = 16 jt + li, kept iff i >= j and scaled by lam^(i - j)
+#pragma unroll
+        for (int it = 0; it < NT; ++it)
+#pragma unroll
+            for (int jt = 0; jt <= it; ++jt) {
+                const int idx = it * (it + 1) / 2 + jt;
+                if (idx % 4 != q) continue;
+                f32x4 x = zero4();
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    x = mfma16(op_row(Xs, 16 * it + li, 32 * ks, g), op_row(Rs, 16 * jt + li, 32 * ks, g), x);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int d = 16 * (it - jt) + 4 * g + r - li;
+                    x[r] *= d >= 0 ? sm.pw[d] : 0.f;
+                }
+                *reinterpret_cast<u32x2*>(&tiles[idx * 128 + 2 * lane]) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+            }
+
+        // the group's state as operands, and the token-contracted operand of its columns
+        bf16x8 sop[NKB * 2][2], tf[2][NKB];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) sop[kb][h] = operand_from_acc(S[2 * kb][h], S[2 * kb + 1][h]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) tf[h][kb] = op_tr_k(Ts, 32 * kb, 32 * q + 16 * h, 4, g, li);
+        __syncthreads();  // B(i)
+
+#pragma unroll
+        for (int jt = 0; jt < NT; ++jt) {
+            const int j = 16 * jt + li;
+            const float lj = (j < m) ? sm.pw[m - j] : 0.f;
+            f32x4 acc[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) acc[h] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const bf16x8 rr = op_row(Rs, j, 32 * kb, g);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) acc[h] = mfma16(sop[kb][h], rr, acc[h]);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) acc[h] *= lj;
+#pragma unroll
+            for (int kb = jt / 2; kb < NKB; ++kb) {
+                const int i0 = 2 * kb, i1 = 2 * kb + 1;
+                const u32x2 z{0, 0};
+                const u32x2 lo = (i0 >= jt) ? ld_frag(tiles, i0 * (i0 + 1) / 2 + jt, lane) : z;
+                const u32x2 hi = (i1 >= jt) ? ld_frag(tiles, i1 * (i1 + 1) / 2 + jt, lane) : z;
+                const bf16x8 tb = operand(lo, hi);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) acc[h] = mfma16(tf[h][kb], tb, acc[h]);
+            }
+            // acc[h][r] = dV (value group) or dK (key group) [j][32 q + 16 h + 4 g + r]
+            if (j < m) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int64_t off = (t0 + j) * D + 32 * q + 16 * h + 4 * g;
+                    *reinterpret_cast<u32x2*>(outg + off) = u32x2{pack_bf16(acc[h][0], acc[h][1]), pack_bf16(acc[h][2], acc[h][3])};
+                }
+            }
+        }
+
+        // ---- X <- lam^m X + U^T diag(lam^s) T, U = Q (value group) or dO (key group)
+        const float lm = sm.pw[m];
+        bf16x8 ts[2][NKB];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) ts[h][kb] = scale8(tf[h][kb], wq[kb]);
+#pragma unroll
+        for (int at = 0; at < 8; ++at) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) S[at][h] *= lm;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                // U^T rows 32 (at/2) + rho(at%2, li), k index s = 32 kb + kappa(g, e)
+                const bf16x8 ua = op_tr_k(Xs, 32 * kb, 32 * (at >> 1) + 4 * (at & 1), 8, g, li);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) S[at][h] = mfma16(ua, ts[h][kb], S[at][h]);
+            }
+        }
+    }
+}
+
 }  // namespace
 
 bool rev_dma_supported(int d, int bk, int64_t n) { return d == 128 && bk == 64 && n * d * 2 < (int64_t(1) << 31); }
 
-void launch_rev_dma(const SweepArgs& a, const LamArgs& lam, hipStream_t s) {
+void launch_rev_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(a.pairs * a.chunks));
-    hipLaunchKernelGGL(k_rev_dma, grid, dim3(64 * NW), 0, s, a, lam);
+    if (waves == 8)
+        hipLaunchKernelGGL(k_rev_dma_split, grid, dim3(64 * 8), 0, s, a, lam);
+    else
+        hipLaunchKernelGGL(k_rev_dma, grid, dim3(64 * NW), 0, s, a, lam);
 }
 
 }  // namespace la

@@ -93,7 +93,7 @@ void launch_fwd_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream
 
 // Reverse (dK, dV) sweep with direct-to-LDS loads (bf16, D = 128, Bk = 64).
 bool rev_dma_supported(int D, int Bk, int64_t N);
-void launch_rev_dma(const SweepArgs& a, const LamArgs& lam, hipStream_t s);
+void launch_rev_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream_t s);
 
 // Chunk aggregates with direct-to-LDS loads (bf16, D = 128, Bk = 64).
 bool state_dma_supported(int D, int Bk, int64_t N);

@@ -238,12 +238,17 @@ def fwd_variant(monkeypatch):
         monkeypatch.delenv("LA_FWD_WAVES", raising=False)
         monkeypatch.delenv("LA_REV", raising=False)
         monkeypatch.delenv("LA_STATE", raising=False)
+        monkeypatch.delenv("LA_REV_WAVES", raising=False)
         if v == "v1":
             monkeypatch.setenv("LA_FWD", "v1")
             monkeypatch.setenv("LA_REV", "v1")
             monkeypatch.setenv("LA_STATE", "v1")
+        elif v == "dma4":
+            monkeypatch.setenv("LA_FWD_WAVES", "4")
+            monkeypatch.setenv("LA_REV_WAVES", "4")
         elif v == "dma8":
             monkeypatch.setenv("LA_FWD_WAVES", "8")
+            monkeypatch.setenv("LA_REV_WAVES", "8")
     return set_
 
 
@@ -252,7 +257,7 @@ def fwd_variant(monkeypatch):
                                              (64 * 40, 6, False)])
 def test_forward_variants(variant, N, cks, with_state, fwd_variant, chunks):
     """The register-staged and the direct-to-LDS kernels (forward with 4 or 8 compute
-    waves, reverse dK/dV) meet the bar on ragged, chunked and continued sequences."""
+    waves, reverse dK/dV with 4 or 8 waves) meet the bar on ragged, chunked and continued sequences."""
     fwd_variant(variant)
     chunks(cks)
     lam = synth.decay_schedule(3)
@@ -260,7 +265,7 @@ def test_forward_variants(variant, N, cks, with_state, fwd_variant, chunks):
     check_bwd(1, 3, N, 128, 64, "bf16", lam, seed=N + cks, with_state=with_state, label=variant)
 
 
-@pytest.mark.parametrize("variant", ["v1", "dma8"])
+@pytest.mark.parametrize("variant", ["v1", "dma4", "dma8"])
 def test_impulse_probe_variants(variant, fwd_variant, chunks, kernel):
     fwd_variant(variant)
     test_impulse_probe_bit_exact("default", 0.5, 64, 4, chunks, kernel)
