@@ -152,7 +152,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_rev_dma(SweepArgs a, LamArgs lam
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int d = 16 * (it - jt) + 4 * g + r - li;
-                        x[r] *= d >= 0 ? sm.pw[d] : 0.f;
+                        x[r] *= masked_pw(sm.pw, d, d >= 0);
                     }
                     uint32_t* dst = which ? sm.gg : sm.p;
                     *reinterpret_cast<u32x2*>(&dst[idx * 128 + 2 * lane]) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_rev_dma(SweepArgs a, LamArgs lam
 #pragma unroll
         for (int jt = 0; jt < NT; ++jt) {
             const int j = 16 * jt + li;
-            const float lj = (j < m) ? sm.pw[m - j] : 0.f;
+            const float lj = masked_pw(sm.pw, m - j, j < m);
             f32x4 dv[2], dk[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) dv[h] = dk[h] = zero4();
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(64 * 8, 1) void k_rev_dma_split(SweepArgs a, LamArg
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int d = 16 * (it - jt) + 4 * g + r - li;
-                    x[r] *= d >= 0 ? sm.pw[d] : 0.f;
+                    x[r] *= masked_pw(sm.pw, d, d >= 0);
                 }
                 *reinterpret_cast<u32x2*>(&tiles[idx * 128 + 2 * lane]) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
             }
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(64 * 8, 1) void k_rev_dma_split(SweepArgs a, LamArg
 #pragma unroll
         for (int jt = 0; jt < NT; ++jt) {
             const int j = 16 * jt + li;
-            const float lj = (j < m) ? sm.pw[m - j] : 0.f;
+            const float lj = masked_pw(sm.pw, m - j, j < m);
             f32x4 acc[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) acc[h] = zero4();

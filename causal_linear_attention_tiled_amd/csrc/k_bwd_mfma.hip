@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_rev_mfma(SweepArgs a, LamArgs l
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int d = 16 * (it - jt) + 4 * g + r - li;
-                        x[r] *= d >= 0 ? sm.pw[d] : 0.f;
+                        x[r] *= masked_pw(sm.pw, d, d >= 0);
                     }
                     uint32_t* dst = which ? sm.gg : sm.p;
                     *reinterpret_cast<u32x2*>(&dst[idx * 128 + 2 * lane]) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_rev_mfma(SweepArgs a, LamArgs l
 #pragma unroll
         for (int jt = 0; jt < NT; ++jt) {
             const int j = 16 * jt + li;
-            const float lj = (j < m) ? sm.pw[m - j] : 0.f;
+            const float lj = masked_pw(sm.pw, m - j, j < m);
             bf16x8 kb[4], vb[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {

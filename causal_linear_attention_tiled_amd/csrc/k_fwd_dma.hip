@@ -167,7 +167,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int d = 16 * (st - at) + li - 4 * g - r;
-                    p[r] *= d >= 0 ? sm.pw[d] : 0.f;
+                    p[r] *= masked_pw(sm.pw, d, d >= 0);
                 }
                 *reinterpret_cast<u32x2*>(&sm.at[idx * 128 + 2 * lane]) = u32x2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
             }
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int s = 32 * kb + kappa(g, e);
-                wk[e] = s < m ? sm.pw[m - 1 - s] : 0.f;
+                wk[e] = masked_pw(sm.pw, m - 1 - s, s < m);
             }
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt) vw[vt][kb] = scale8(vf[vt][kb], wk);

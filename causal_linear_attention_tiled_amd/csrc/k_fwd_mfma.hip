@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kThreads, (BK == 64) ? 2 : 1) void k_fwd_mfma(Sweep
         {
             float wk[RPT];
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) wk[i] = (r0 + i < m) ? sm.pw[m - 1 - (r0 + i)] : 0.f;
+            for (int i = 0; i < RPT; ++i) wk[i] = masked_pw(sm.pw, m - 1 - (r0 + i), r0 + i < m);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 uint32_t kw[RPT / 2], vw[RPT / 2];
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kThreads, (BK == 64) ? 2 : 1) void k_fwd_mfma(Sweep
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int d = 16 * (st - at) + li - 4 * g - r;
-                    p[r] *= d >= 0 ? sm.pw[d] : 0.f;
+                    p[r] *= masked_pw(sm.pw, d, d >= 0);
                 }
                 *reinterpret_cast<u32x2*>(&sm.at[idx * 128 + 2 * lane]) =
                     u32x2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};

@@ -3,14 +3,20 @@
 //
 // For every chunk c that another chunk depends on, the state update of the
 // sweep (Lightning Attention-2, Tiling paragraph: the inter-block part is
-// carried by the key-value state) run over the chunk's blocks from zero:
-//   forward: acc <- lam^m acc + X_b^T diag(lam^(m-1-s)) Y_b, blocks in order
-//   reverse: acc <- lam^m acc + X_b^T diag(lam^s) Y_b, blocks last to first
-// with (X, Y) = (K, V) for the forward and (Q, dO) for the gradient state.
-// The loop stores nothing, so the four waves share the loads (8 of the 32
+// carried by the key-value state) summed over the chunk from zero:
+//   forward: acc = sum_t lam^(E - 1 - t) x_t y_t^T   (E = end of the chunk)
+//   reverse: acc = sum_t lam^(t - B) x_t y_t^T       (B = start of the chunk)
+// with (x, y) = (k, v) for the forward and (q, dO) for the gradient state.
+// The blocks are walked away from the reference token (last to first for the
+// forward, first to last for the reverse), so every token's weight is
+// c * lam^(offset in its block) with c = lam^(tokens already walked), a running
+// product in double: the accumulators are never rescaled.  A weight that
+// underflows stands for a term below float range next to the unit-size ones.
+// The loop stores nothing, so the eight waves share the loads (4 of the 32
 // loads of a block each) with exact partial vmcnt waits over a three-stage
 // ring.  Both operands come from the row-major tiles through transposing LDS
-// reads; wave w accumulates columns [32w, 32w + 32) of the aggregate.
+// reads; wave w accumulates columns [16w, 16w + 16) of the aggregate, two
+// waves per SIMD.
 #include "la_device.h"
 #include "la_internal.h"
 #include "lds_dma.h"
@@ -24,7 +30,7 @@ constexpr int BK = 64;
 constexpr int NKB = BK / 32;
 constexpr int NSTAGE = 3;
 constexpr int TILE = BK * D;
-constexpr int NW = 4;
+constexpr int NW = 8;
 constexpr int LOADS_PER_WAVE = 2 * (BK / 4) / NW;  // 1 KiB loads per wave per block
 
 struct StateTiles {
@@ -34,7 +40,8 @@ struct StateTiles {
 
 __global__ __launch_bounds__(64 * NW, 1) void k_chunk_state_dma(ChunkStateArgs a, LamArgs lam) {
     __shared__ StateTiles sm;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int per = a.chunks - 1;
     const int64_t pair = blockIdx.x / per;
     const int slot = blockIdx.x % per;
@@ -43,24 +50,25 @@ __global__ __launch_bounds__(64 * NW, 1) void k_chunk_state_dma(ChunkStateArgs a
     const int64_t t_end = min(a.N, t_begin + a.L);
     const int64_t nblk = (t_end - t_begin + BK - 1) / BK;
     const int64_t base = pair * a.N * D;
-    for (int e = tid; e <= BK; e += 64 * NW) sm.pw[e] = lam_pow(lam.lam[pair % a.H], e);
+    const float lv = lam.lam[pair % a.H];
+    for (int e = tid; e <= BK; e += 64 * NW) sm.pw[e] = lam_pow(lv, e);
+    const double lam_bk = lam_pow64(lv, BK);
 
     const uint32_t bytes = static_cast<uint32_t>(a.N * D * 2);
     const u32x4 rx = buffer_rsrc(static_cast<const uint16_t*>(a.x) + base, bytes);
     const u32x4 ry = buffer_rsrc(static_cast<const uint16_t*>(a.y) + base, bytes);
-    // The n-th block of the walk (in order, or from the last block backwards) goes to stage n % 3.
-    // Wave w issues, for each tensor, the loads of row groups w, w + 4, w + 8, w + 12 (4 rows each).
-    const int wu = __builtin_amdgcn_readfirstlane(w);
+    // The n-th block of the walk goes to stage n % 3; wave w issues, for each
+    // tensor, the loads of row groups w and w + 8 (4 rows each).
+    auto block_of = [&](int64_t n) { return a.reverse ? n : nblk - 1 - n; };
     auto issue = [&](int64_t n) {
-        const int64_t bi = a.reverse ? nblk - 1 - n : n;
-        const int64_t t0 = t_begin + bi * BK;
+        const int64_t t0 = t_begin + block_of(n) * BK;
         const int stage = static_cast<int>(n % NSTAGE);
         const int sub = lane >> 4, p = lane & 15;
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
             for (int i = 0; i < LOADS_PER_WAVE / 2; ++i) {
-                const int rg = wu + NW * i;
+                const int rg = w + NW * i;
                 const int r = 4 * rg + sub;
                 const int voff = static_cast<int>(((t0 + r) * D + 8 * (p ^ swz_key(r))) * 2);
                 dma16(x == 0 ? rx : ry, &sm.t[stage][x][4 * rg * D], voff);
@@ -69,14 +77,14 @@ __global__ __launch_bounds__(64 * NW, 1) void k_chunk_state_dma(ChunkStateArgs a
     issue(0);
     if (nblk > 1) issue(1);
 
-    // S[at][h][r] = acc[32 (at/2) + rho(at%2, 4g + r)][32 w + 16 h + li]
-    f32x4 S[8][2];
+    // S[at][r] = acc[16 at + 4 g + r][16 w + li]
+    f32x4 S[8];
 #pragma unroll
-    for (int at = 0; at < 8; ++at) S[at][0] = S[at][1] = zero4();
+    for (int at = 0; at < 8; ++at) S[at] = zero4();
+    double cw = 1.0;  // lam^(tokens walked so far)
 
     for (int64_t n = 0; n < nblk; ++n) {
-        const int64_t bi = a.reverse ? nblk - 1 - n : n;
-        const int64_t t0 = t_begin + bi * BK;
+        const int64_t t0 = t_begin + block_of(n) * BK;
         const int m = static_cast<int>(min(static_cast<int64_t>(BK), t_end - t0));
         const int stage = static_cast<int>(n % NSTAGE);
         if (n + 1 < nblk)
@@ -87,41 +95,30 @@ __global__ __launch_bounds__(64 * NW, 1) void k_chunk_state_dma(ChunkStateArgs a
         if (n + 2 < nblk) issue(n + 2);
         const uint16_t* Xs = sm.t[stage][0];
         const uint16_t* Ys = sm.t[stage][1];
-        // weights of token s = 32 kb + kappa(g, e), on the Y operand (2 fragments per k block, not 8)
+        // weights of token s = 32 kb + kappa(g, e), on the Y operand
+        const float cf = static_cast<float>(cw);
         float wx[NKB][8];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int s = 32 * kb + kappa(g, e);
-                wx[kb][e] = s < m ? (a.reverse ? sm.pw[s] : sm.pw[m - 1 - s]) : 0.f;
+                wx[kb][e] = cf * masked_pw(sm.pw, a.reverse ? s : m - 1 - s, s < m);
             }
-        bf16x8 yf[2][NKB];
+        bf16x8 yf[NKB];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int kb = 0; kb < NKB; ++kb) yf[kb] = scale8(op_tr_k(Ys, 32 * kb, 16 * w, 4, g, li), wx[kb]);
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) yf[h][kb] = scale8(op_tr_k(Ys, 32 * kb, 32 * w + 16 * h, 4, g, li), wx[kb]);
-        const float lm = sm.pw[m];
+        for (int at = 0; at < 8; ++at)
 #pragma unroll
-        for (int at = 0; at < 8; ++at) {
-            S[at][0] *= lm;
-            S[at][1] *= lm;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const bf16x8 xf = op_tr_k(Xs, 32 * kb, 32 * (at >> 1) + 4 * (at & 1), 8, g, li);
-                S[at][0] = mfma16(xf, yf[0][kb], S[at][0]);
-                S[at][1] = mfma16(xf, yf[1][kb], S[at][1]);
-            }
-        }
+            for (int kb = 0; kb < NKB; ++kb) S[at] = mfma16(op_tr_k(Xs, 32 * kb, 16 * at, 4, g, li), yf[kb], S[at]);
+        cw *= (m == BK) ? lam_bk : lam_pow64(lv, m);
     }
     float* dst = a.slots + (pair * per + slot) * D * D;
 #pragma unroll
     for (int at = 0; at < 8; ++at)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dst[(32 * (at >> 1) + rho(at & 1, 4 * g + r)) * D + 32 * w + 16 * h + li] = S[at][h][r];
+        for (int r = 0; r < 4; ++r) dst[(16 * at + 4 * g + r) * D + 16 * w + li] = S[at][r];
 }
 
 }  // namespace

@@ -35,16 +35,26 @@ __device__ __forceinline__ void st(void* p, int64_t i, float x) {
         static_cast<float*>(p)[i] = x;
 }
 
-// lam^e for e >= 0, by binary powering in double, rounded once to float.
-// lam^0 = 1 exactly, also for lam = 0.
-__device__ __forceinline__ float lam_pow(float lam, int64_t e) {
+// lam^e for e >= 0, by binary powering in double.  lam^0 = 1 exactly, also for lam = 0.
+__device__ __forceinline__ double lam_pow64(float lam, int64_t e) {
     double base = static_cast<double>(lam), r = 1.0;
     while (e > 0) {
         if (e & 1) r *= base;
         base *= base;
         e >>= 1;
     }
-    return static_cast<float>(r);
+    return r;
+}
+
+// The same rounded once to float.
+__device__ __forceinline__ float lam_pow(float lam, int64_t e) { return static_cast<float>(lam_pow64(lam, e)); }
+
+// keep ? pw[e] : 0 for a decay table pw in LDS.  The read is unconditional (the
+// index is clamped to the table), so several of them issue back to back rather
+// than as one masked branch and LDS round trip each.
+__device__ __forceinline__ float masked_pw(const float* pw, int e, bool keep) {
+    const float v = pw[e > 0 ? e : 0];
+    return keep ? v : 0.f;
 }
 
 }  // namespace la
