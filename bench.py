@@ -194,8 +194,9 @@ def bench(args):
         la.la_fwd(sh["q"], sh["k"], sh["v"], lam, BK, out=sh["o"], kv_out=sh["s"], ws=sh["ws_f"])
 
     def bwd(sh):
+        # the forward of the same step left its chunk states in ws_f
         la.la_bwd(sh["q"], sh["k"], sh["v"], sh["g"], lam, BK, dq=sh["dq"], dk=sh["dk"], dv=sh["dv"],
-                  ws=sh["ws_b"])
+                  ws=sh["ws_b"], fwd_ws=sh["ws_f"] if sh["chunks"] > 1 else None)
 
     def step():
         for sh in shapes:
@@ -247,8 +248,6 @@ def bench(args):
                       "state_scan", "state_scan_rev"]
         for nm in names:
             b = kernel_bytes(nm, sh["B"], H, sh["n"], D, sh["chunks"])
-            if nm in ("chunk_state_mfma", "chunk_state_dma", "state_scan"):
-                b = b * 2  # launched by the forward and by the dQ sweep of the backward
             bytes_by_kernel.setdefault(nm, []).append(b)
     kernels = {}
     for nm, (launches, total_ms) in prof.items():

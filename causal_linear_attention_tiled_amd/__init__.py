@@ -44,7 +44,7 @@ def _load():
     lib.la_fwd.restype = ctypes.c_int
     lib.la_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
     lib.la_fwd_workspace_bytes.restype = sz
-    lib.la_bwd.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.la_bwd.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.la_bwd.restype = ctypes.c_int
     lib.la_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
     lib.la_bwd_workspace_bytes.restype = sz
@@ -154,8 +154,12 @@ def la_fwd(q, k, v, lam, Bk: int = 64, kv_in=None, out=None, kv_out=None, want_s
     return out, kv_out
 
 
-def la_bwd(q, k, v, dout, lam, Bk: int = 64, kv_in=None, dq=None, dk=None, dv=None, ws=None):
-    """dQ, dK, dV of L = <dO, O> for la_fwd (kv_in held constant)."""
+def la_bwd(q, k, v, dout, lam, Bk: int = 64, kv_in=None, dq=None, dk=None, dv=None, ws=None,
+           fwd_ws=None):
+    """dQ, dK, dV of L = <dO, O> for la_fwd (kv_in held constant).
+
+    ``fwd_ws``: the tensor passed as ``ws`` to the la_fwd call over the same inputs, unchanged
+    since; the dQ sweep then takes the chunk states from it instead of recomputing them."""
     for name, t in (("Q", q), ("K", k), ("V", v), ("dO", dout)):
         _check_seq(name, t, q)
     B, H, N, D = q.shape
@@ -168,9 +172,13 @@ def la_bwd(q, k, v, dout, lam, Bk: int = 64, kv_in=None, dq=None, dk=None, dv=No
     code = _dtype_code(q)
     nbytes = la_bwd_workspace_bytes(B, H, N, D, Bk, code)
     ws = _workspace(nbytes, q.device, ws)
+    if fwd_ws is not None:
+        need = la_fwd_workspace_bytes(B, H, N, D, Bk, code)
+        if fwd_ws.device != q.device or fwd_ws.numel() * fwd_ws.element_size() < need:
+            raise ValueError(f"fwd_ws must hold the {need}-byte workspace of la_fwd on {q.device}")
     rc = lib.la_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _lam_array(lam, H), B, H, N, D, Bk, code,
-                    _ptr(kv_in), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), nbytes if ws is not None else 0,
-                    _stream(q.device))
+                    _ptr(kv_in), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(fwd_ws), _ptr(ws),
+                    nbytes if ws is not None else 0, _stream(q.device))
     if rc != LA_OK:
         raise LaError(rc, "la_bwd")
     return dq, dk, dv

@@ -160,12 +160,15 @@ size_t round_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // ------------------------------------------------------------------ sweeps
 // Forward-direction sweep (O of la_fwd, or dQ of la_bwd with operands
 // (dO, V, K) and the transposed initial state).
+// With `given` non-null the chunk states are not computed: the sweep reads
+// them, transposed, from `given` (the chunk states a forward pass left in its
+// workspace, which are the transposes of the dQ sweep's states).
 int run_forward_sweep(const void* q, const void* k, const void* v, void* out, const float* kv_in,
-                      int kv_in_t, float* kv_out, float* slots, int64_t pairs, int64_t N, int64_t D,
-                      int32_t Bk, int32_t H, int bf16, const Plan& p, const LamArgs& lam, hipStream_t s,
-                      const char* tag) {
+                      int kv_in_t, float* kv_out, float* slots, const float* given, int64_t pairs,
+                      int64_t N, int64_t D, int32_t Bk, int32_t H, int bf16, const Plan& p,
+                      const LamArgs& lam, hipStream_t s, const char* tag) {
     int rc;
-    if (p.chunks > 1) {
+    if (p.chunks > 1 && !given) {
         la::ChunkStateArgs cs{k, v, slots, N, p.L, static_cast<int>(D), Bk, H, p.chunks, pairs, 0};
         if (p.mfma && la::state_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_STATE", "v1"))
             rc = launch("chunk_state_dma", s, [&] { la::launch_chunk_state_dma(cs, lam, s); });
@@ -183,7 +186,8 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
     a.b = k;
     a.c = v;
     a.out0 = out;
-    a.slots = slots;
+    a.slots = given ? given : slots;
+    a.slots_transposed = given ? 1 : 0;
     a.kv_in = kv_in;
     a.kv_in_transposed = kv_in_t;
     a.kv_out = kv_out;
@@ -267,13 +271,13 @@ int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int
     int dev_count = 0;
     if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count == 0) return LA_ENODEV;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    return run_forward_sweep(Q, K, V, O, kv_in, 0, kv_out, static_cast<float*>(ws), B * H, N, D, Bk,
-                             static_cast<int32_t>(H), dtype == LA_BF16, p, lam, s, "fwd");
+    return run_forward_sweep(Q, K, V, O, kv_in, 0, kv_out, static_cast<float*>(ws), nullptr, B * H, N, D,
+                             Bk, static_cast<int32_t>(H), dtype == LA_BF16, p, lam, s, "fwd");
 }
 
 int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const float* lambda, int64_t B,
            int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype, const float* kv_in, void* dQ,
-           void* dK, void* dV, void* ws, size_t ws_bytes, void* hip_stream) {
+           void* dK, void* dV, const void* fwd_ws, void* ws, size_t ws_bytes, void* hip_stream) {
     int64_t elems;
     int rc = check_shape(B, H, N, D, Bk, dtype, &elems);
     if (rc) return rc;
@@ -281,7 +285,7 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     LamArgs lam;
     if ((rc = load_lambda(lambda, H, &lam))) return rc;
     for (const void* p : {Q, K, V, dO, static_cast<const void*>(kv_in), static_cast<const void*>(dQ),
-                          static_cast<const void*>(dK), static_cast<const void*>(dV),
+                          static_cast<const void*>(dK), static_cast<const void*>(dV), fwd_ws,
                           static_cast<const void*>(ws)})
         if (p && !aligned16(p)) return LA_EALIGN;
     const size_t tb = static_cast<size_t>(elems) * (dtype == LA_BF16 ? 2 : 4);
@@ -290,7 +294,8 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     const size_t one = slot_bytes(B * H, p, D);
     const size_t need = one ? 2 * round_up(one) : 0;
     if (need && (!ws || ws_bytes < need)) return LA_EWORKSPACE;
-    const Range ins[] = {{Q, tb}, {K, tb}, {V, tb}, {dO, tb}, {kv_in, kv_in ? sb : 0}};
+    const Range ins[] = {{Q, tb}, {K, tb}, {V, tb}, {dO, tb}, {kv_in, kv_in ? sb : 0},
+                         {fwd_ws, fwd_ws ? one : 0}};
     const Range outs[] = {{dQ, tb}, {dK, tb}, {dV, tb}, {ws, need}};
     for (const Range& o : outs)
         for (const Range& i : ins)
@@ -309,7 +314,8 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     const int32_t Hi = static_cast<int32_t>(H);
 
     // dQ: the forward sweep with (q, k, v) = (dO, V, K) and the transposed initial state.
-    rc = run_forward_sweep(dO, V, K, dQ, kv_in, 1, nullptr, slots_q, pairs, N, D, Bk, Hi, bf16, p, lam, s, "dq");
+    rc = run_forward_sweep(dO, V, K, dQ, kv_in, 1, nullptr, slots_q, static_cast<const float*>(fwd_ws), pairs,
+                           N, D, Bk, Hi, bf16, p, lam, s, "dq");
     if (rc) return rc;
 
     // dK, dV: reverse sweep carrying dS, with a chunked suffix over blocks.

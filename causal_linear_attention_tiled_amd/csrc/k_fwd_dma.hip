@@ -118,6 +118,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
             }
         } else {
             init = a.slots + (pair * (a.chunks - 1) + (c - 1)) * D * D;
+            tr = a.slots_transposed != 0;
         }
 #pragma unroll
         for (int at = 0; at < 8; ++at)

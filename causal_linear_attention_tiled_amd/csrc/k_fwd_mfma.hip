@@ -95,6 +95,7 @@ __global__ __launch_bounds__(kThreads, (BK == 64) ? 2 : 1) void k_fwd_mfma(Sweep
             }
         } else {
             init = a.slots + (pair * (a.chunks - 1) + (c - 1)) * D * D;
+            tr = a.slots_transposed != 0;
         }
 #pragma unroll
         for (int at = 0; at < 8; ++at)

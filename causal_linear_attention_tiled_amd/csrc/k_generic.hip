@@ -50,6 +50,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs l
         }
     } else {
         init = a.slots + (pair * (a.chunks - 1) + (c - 1)) * D * D;
+        transposed = a.slots_transposed != 0;
     }
     for (int i = tid; i < D * D; i += kThreads) {
         float x = 0.f;

@@ -29,6 +29,8 @@ struct SweepArgs {
                           // c <= chunks-2 reverse), or nullptr when chunks == 1
     const float* kv_in;   // [P][D][D] initial state of chunk 0 (forward only) or nullptr
     int kv_in_transposed; // read kv_in as its transpose (dQ sweep)
+    int slots_transposed; // read the slots as their transposes (dQ sweep fed by the
+                          // forward pass's chunk states)
     float* kv_out;        // [P][D][D] final state (forward only) or nullptr
     int64_t N;
     int64_t L;            // chunk length in tokens

@@ -80,7 +80,10 @@ enum {
  *             Must not overlap kv_in.
  *   ws      : device workspace of at least la_fwd_workspace_bytes(...) bytes
  *             (may be NULL when that size is 0).  Its contents on entry do
- *             not matter; calls sharing a workspace must be stream-ordered. */
+ *             not matter; calls sharing a workspace must be stream-ordered.
+ *             On return it holds the key-value state at the end of every
+ *             chunk but the last (float32), which la_bwd can take as fwd_ws
+ *             instead of computing them again. */
 int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int64_t B, int64_t H,
            int64_t N, int64_t D, int32_t Bk, int32_t dtype, const float* kv_in, void* O,
            float* kv_out, void* ws, size_t ws_bytes, void* hip_stream);
@@ -101,11 +104,19 @@ size_t la_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_
  *   dO      : [B][H][N][D] dtype, device.
  *   dQ,dK,dV: [B][H][N][D] dtype, device, written; none may overlap an input
  *             or each other.
+ *   fwd_ws  : NULL, or the workspace of an la_fwd call with the same Q, K, V,
+ *             lambda, shape, Bk, dtype and kv_in, unchanged since that call
+ *             (device, read only; same LA_CHUNKS setting).  The dQ sweep then
+ *             reads the chunk states from it rather than making one more
+ *             pass over K and V.  Its contents are not checked: a workspace
+ *             from any other call gives wrong dQ.
+ *   ws      : la_bwd_workspace_bytes(...) bytes, as for la_fwd; must not
+ *             overlap fwd_ws.
  *   other arguments as for la_fwd. */
 int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const float* lambda,
            int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype,
-           const float* kv_in, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
-           void* hip_stream);
+           const float* kv_in, void* dQ, void* dK, void* dV, const void* fwd_ws, void* ws,
+           size_t ws_bytes, void* hip_stream);
 
 size_t la_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype);
 

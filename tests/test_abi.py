@@ -108,12 +108,27 @@ def test_bwd_rejects():
     G_ = A * 10
     call = lambda dq, dk, dv, g=G_: la.lib.la_bwd(v(Q_), v(K_), v(V_), v(g), lam, 1, 2, 128, 64, 64,
                                                   la.LA_BF16, None, v(dq) if dq else None, v(dk), v(dv),
-                                                  None, 0, None)
+                                                  None, None, 0, None)
     assert call(None, S_, W_) == la.LA_EINVAL          # dQ missing
     assert call(O_, O_, W_) == la.LA_EINVAL            # dQ and dK alias
     assert call(O_, S_, V_) == la.LA_EINVAL            # dV aliases V
     assert call(O_ + 2, S_, W_) == la.LA_EALIGN
     assert call(O_, S_, W_, g=None) == la.LA_EINVAL    # dO missing
+
+
+def test_bwd_forward_workspace_checked():
+    """fwd_ws (the forward pass's chunk states) is an input: aligned, and disjoint from every output."""
+    v = ctypes.c_void_p
+    lam1 = (ctypes.c_float * 1)(0.9)
+    G_, X_, Y_, WB_ = A * 10, A * 11, A * 12, A * 13
+    N = 4096  # one long sequence: split into chunks
+    assert la.la_fwd_workspace_bytes(1, 1, N, 128, 64, la.LA_BF16) > 0
+    call = lambda fws, ws=WB_: la.lib.la_bwd(v(Q_), v(K_), v(V_), v(G_), lam1, 1, 1, N, 128, 64, la.LA_BF16,
+                                             None, v(O_), v(X_), v(Y_), v(fws) if fws else None, v(ws),
+                                             1 << 40, None)
+    assert call(WB_ + 8) == la.LA_EALIGN
+    assert call(WB_ + 4096) == la.LA_EINVAL            # inside the backward's own workspace
+    assert call(X_) == la.LA_EINVAL                    # aliases dK
 
 
 def test_decode_rejects():

@@ -59,12 +59,19 @@ def check_fwd(B, H, N, D, Bk, dtype, lam, seed=0, with_state=False, label=""):
     return o, s
 
 
-def check_bwd(B, H, N, D, Bk, dtype, lam, seed=0, with_state=False, label=""):
-    print(f"[bwd] {label} B={B} H={H} N={N} D={D} Bk={Bk} {dtype} kv_in={with_state}", flush=True)
+def check_bwd(B, H, N, D, Bk, dtype, lam, seed=0, with_state=False, label="", fwd_ws=False):
+    print(f"[bwd] {label} B={B} H={H} N={N} D={D} Bk={Bk} {dtype} kv_in={with_state} fwd_ws={fwd_ws}",
+          flush=True)
     _, (q, k, v, g), (qh, kh, vh, gh) = inputs(seed, B, H, N, D, dtype, with_do=True)
     s0 = state_input(seed, B, H, D) if with_state else None
     kv_in = torch.from_numpy(s0).cuda() if with_state else None
-    dq, dk, dv = la.la_bwd(q, k, v, g, lam, Bk=Bk, kv_in=kv_in)
+    fws = None
+    if fwd_ws:
+        # the forward pass over the same inputs leaves its chunk states in its workspace
+        nb = la.la_fwd_workspace_bytes(B, H, N, D, Bk, la.LA_BF16 if dtype == "bf16" else la.LA_F32)
+        fws = torch.full((max(nb, 1),), 0xFF, dtype=torch.uint8, device="cuda")
+        la.la_fwd(q, k, v, lam, Bk=Bk, kv_in=kv_in, ws=fws)
+    dq, dk, dv = la.la_bwd(q, k, v, g, lam, Bk=Bk, kv_in=kv_in, fwd_ws=fws)
     _sync()
     refs = oracle.bwd_recurrent(qh, kh, vh, gh, lam_pairs(lam, B), None if s0 is None else s0.astype(np.float64))
     errs = [oracle.rel_l2(got(x), r) for x, r in zip((dq, dk, dv), refs)]
@@ -263,6 +270,18 @@ def test_forward_variants(variant, N, cks, with_state, fwd_variant, chunks):
     lam = synth.decay_schedule(3)
     check_fwd(2, 3, N, 128, 64, "bf16", lam, seed=N + cks, with_state=with_state, label=variant)
     check_bwd(1, 3, N, 128, 64, "bf16", lam, seed=N + cks, with_state=with_state, label=variant)
+
+
+@pytest.mark.parametrize("kern", ["generic", "default"])
+@pytest.mark.parametrize("N,cks,with_state", [(64 * 13 + 5, 3, True), (64 * 40, 6, False), (1000, 2, True),
+                                             (300, 1, True)])
+def test_backward_with_forward_chunk_states(kern, N, cks, with_state, kernel, chunks):
+    """la_bwd fed the forward pass's chunk states (fwd_ws) meets the same bar as when it
+    recomputes them, with and without an initial state, on ragged chunked sequences."""
+    kernel(kern)
+    chunks(cks)
+    lam = synth.decay_schedule(3)
+    check_bwd(1, 3, N, 128, 64, "bf16", lam, seed=N + 7 * cks, with_state=with_state, label=kern, fwd_ws=True)
 
 
 @pytest.mark.parametrize("variant", ["v1", "dma4", "dma8"])

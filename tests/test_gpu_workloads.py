@@ -68,22 +68,45 @@ def test_fwd_sweep_131072_tokens(N):
     check_fwd_sampled(o, s, B, H, N, lam, sample_pairs(B, H, 5))
 
 
+def training_step(B, H, N):
+    """la_fwd then la_bwd as the benchmark runs them: the backward takes the forward's chunk
+    states from the forward's workspace."""
+    lam = synth.decay_schedule(H)
+    q, k, v, g = qkv_dev(B, H, N, with_do=True)
+    nb = la.la_fwd_workspace_bytes(B, H, N, D, 64, la.LA_BF16)
+    ws_f = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda") if nb else None
+    o, s = la.la_fwd(q, k, v, lam, Bk=64, ws=ws_f)
+    dq, dk, dv = la.la_bwd(q, k, v, g, lam, Bk=64, fwd_ws=ws_f)
+    torch.cuda.synchronize()
+    return lam, (o, s), (dq, dk, dv)
+
+
+def check_bwd_sampled(grads, B, H, N, lam, samples):
+    for b, h in samples:
+        qh, kh, vh, gh = pair_inputs(B, H, N, b, h, with_do=True)
+        refs = oracle.bwd_recurrent(qh, kh, vh, gh, float(lam[h]))
+        errs = [oracle.rel_l2(got(x[b, h]), r) for x, r in zip(grads, refs)]
+        print(f"    (b={b}, h={h}) rel-L2 dQ={errs[0]:.3e} dK={errs[1]:.3e} dV={errs[2]:.3e}", flush=True)
+        assert max(errs) <= BF16_BAR
+
+
 def test_fwd_bwd_b2_h32_n8192():
     """bf16 training step, B=2 H=32 N=8192 D=128 Bk=64: O, dQ, dK, dV on sampled sequences."""
     B, H, N = 2, 32, 8192
     print(f"[workload] fwd+bwd B={B} H={H} N={N} Bk=64", flush=True)
-    lam = synth.decay_schedule(H)
-    q, k, v, g = qkv_dev(B, H, N, with_do=True)
-    o, s = la.la_fwd(q, k, v, lam, Bk=64)
-    dq, dk, dv = la.la_bwd(q, k, v, g, lam, Bk=64)
-    torch.cuda.synchronize()
+    lam, (o, s), grads = training_step(B, H, N)
     check_fwd_sampled(o, s, B, H, N, lam, sample_pairs(B, H, 4))
-    for b, h in sample_pairs(B, H, 4):
-        qh, kh, vh, gh = pair_inputs(B, H, N, b, h, with_do=True)
-        refs = oracle.bwd_recurrent(qh, kh, vh, gh, float(lam[h]))
-        errs = [oracle.rel_l2(got(x[b, h]), r) for x, r in zip((dq, dk, dv), refs)]
-        print(f"    (b={b}, h={h}) rel-L2 dQ={errs[0]:.3e} dK={errs[1]:.3e} dV={errs[2]:.3e}", flush=True)
-        assert max(errs) <= BF16_BAR
+    check_bwd_sampled(grads, B, H, N, lam, sample_pairs(B, H, 4))
+
+
+@pytest.mark.parametrize("N", [1024, 4096, 16384, 65536])
+def test_fwd_bwd_sweep_131072_tokens(N):
+    """bf16 training step of the sweep at 131072 tokens per head (B = 131072 / N, H=16, D=128,
+    Bk=64), launched as the benchmark launches it: dQ, dK, dV on sampled sequences."""
+    B, H = 131072 // N, 16
+    print(f"[workload] fwd+bwd sweep B={B} H={H} N={N} Bk=64", flush=True)
+    lam, _, grads = training_step(B, H, N)
+    check_bwd_sampled(grads, B, H, N, lam, sample_pairs(B, H, 3))
 
 
 def test_long_prefill_then_decode():
