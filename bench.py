@@ -42,12 +42,20 @@ HBM_PEAK_GBS = 8000.0      # MI355X published HBM3E bandwidth
 BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA rate
 PROFILES = os.path.join(ROOT, "profiles")
 CALIB_BYTES = 1 << 30      # bytes read and written by the calibration copy
-KERNEL_SOURCES = {         # library kernel name -> source file its code lives in
-    "fwd_mfma": "k_fwd_mfma.hip", "dq_mfma": "k_fwd_mfma.hip", "fwd_dma": "k_fwd_dma.hip", "dq_dma": "k_fwd_dma.hip", "chunk_state_mfma": "k_fwd_mfma.hip",
-    "chunk_state_rev_mfma": "k_fwd_mfma.hip", "dkdv_mfma": "k_bwd_mfma.hip", "dkdv_dma": "k_bwd_dma.hip",
-    "chunk_state_dma": "k_state_dma.hip", "chunk_state_rev_dma": "k_state_dma.hip",
-    "dkdv_generic": "k_generic.hip", "state_scan": "k_generic.hip", "state_scan_rev": "k_generic.hip",
-    "decode": "k_generic.hip",
+# library kernel name (as the library's profiler reports it) -> the device function it
+# launches; several library names can share one device function (the forward sweep
+# serves both la_fwd and the dQ pass of la_bwd)
+DEVICE_FN = {
+    "fwd_dma": "k_fwd_dma", "dq_dma": "k_fwd_dma", "fwd_mfma": "k_fwd_mfma", "dq_mfma": "k_fwd_mfma",
+    "dkdv_dma": "k_rev_dma", "dkdv_mfma": "k_rev_mfma", "dkdv_generic": "k_rev_generic",
+    "chunk_state_dma": "k_chunk_state_dma", "chunk_state_rev_dma": "k_chunk_state_dma",
+    "chunk_state_mfma": "k_chunk_state_mfma", "chunk_state_rev_mfma": "k_chunk_state_mfma",
+    "state_scan": "k_scan", "state_scan_rev": "k_scan", "decode": "k_decode",
+}
+KERNEL_SOURCES = {         # device function -> source file its code lives in
+    "k_fwd_dma": "k_fwd_dma.hip", "k_fwd_mfma": "k_fwd_mfma.hip", "k_rev_dma": "k_bwd_dma.hip",
+    "k_rev_mfma": "k_bwd_mfma.hip", "k_rev_generic": "k_generic.hip", "k_chunk_state_dma": "k_state_dma.hip",
+    "k_chunk_state_mfma": "k_fwd_mfma.hip", "k_scan": "k_generic.hip", "k_decode": "k_generic.hip",
 }
 
 
@@ -81,11 +89,18 @@ def kernel_bytes(name, B, Hh, N, d, chunks, with_state=True):
 
 
 def source_digest(kernel):
+    """Digest of the source of a device function: its .hip file and every csrc header."""
     src = KERNEL_SOURCES.get(kernel)
     if not src:
         return None
-    p = os.path.join(ROOT, "causal_linear_attention_tiled_amd", "csrc", src)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16] if os.path.exists(p) else None
+    csrc = os.path.join(ROOT, "causal_linear_attention_tiled_amd", "csrc")
+    p = os.path.join(csrc, src)
+    if not os.path.exists(p):
+        return None
+    h = hashlib.sha256(open(p, "rb").read())
+    for hdr in sorted(glob.glob(os.path.join(csrc, "*.h"))):
+        h.update(open(hdr, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(kernel):
@@ -255,20 +270,36 @@ def bench(args):
         per_step_bytes = sum(bytes_by_kernel.get(nm, [])) or None
         launches_per_step = launches / args.steps
         avg_bytes = per_step_bytes / launches_per_step if per_step_bytes else None
-        kernels[nm] = {"launches_per_step": launches_per_step, "avg_ms": round(avg_ms, 5),
-                       "share": None, "alg_bytes_per_launch": avg_bytes,
+        kernels[nm] = {"device_function": DEVICE_FN.get(nm, nm), "launches_per_step": launches_per_step,
+                       "avg_ms": round(avg_ms, 5), "share": None, "alg_bytes_per_launch": avg_bytes,
                        "gbs": (avg_bytes / (avg_ms * 1e-3) / 1e9) if avg_bytes else None}
     total_prof = sum(v[1] for v in prof.values())
     for nm in kernels:
         kernels[nm]["share"] = round(prof[nm][1] / total_prof, 4)
-    dom = max(kernels, key=lambda k_: prof[k_][1])
-    dk_ = kernels[dom]
-    achieved = dk_["gbs"]
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1) if achieved else None,
+    # the same per device function: the dominant kernel is the device function that takes
+    # the most time (launches of one function by several library calls pooled)
+    by_fn = {}
+    for nm, (launches, total_ms) in prof.items():
+        f = by_fn.setdefault(DEVICE_FN.get(nm, nm), {"launches": 0, "total_ms": 0.0, "bytes": 0.0,
+                                                     "calls": [], "known": True})
+        f["launches"] += launches
+        f["total_ms"] += total_ms
+        f["calls"].append(nm)
+        b = sum(bytes_by_kernel.get(nm, [])) * args.steps
+        f["bytes"] += b
+        f["known"] &= b > 0
+    dom = max(by_fn, key=lambda k_: by_fn[k_]["total_ms"])
+    df = by_fn[dom]
+    avg_ms = df["total_ms"] / df["launches"]
+    avg_bytes = df["bytes"] / df["launches"] if df["known"] else None
+    achieved = avg_bytes / (avg_ms * 1e-3) / 1e9 if avg_bytes else None
+    roofline = {"bound": "hbm", "kernel": dom, "library_calls": df["calls"],
+                "achieved": round(achieved, 1) if achieved else None,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-                "traffic": read_traffic(dom), "avg_launch_ms": dk_["avg_ms"],
-                "alg_bytes_per_launch": dk_["alg_bytes_per_launch"]}
+                "traffic": read_traffic(dom), "avg_launch_ms": round(avg_ms, 5),
+                "launches_per_step": df["launches"] / args.steps, "alg_bytes_per_launch": avg_bytes,
+                "share": round(df["total_ms"] / total_prof, 4)}
 
     # per sequence length breakdown
     sweep = []
@@ -335,11 +366,6 @@ def bench(args):
 
 
 # ----------------------------------------------------------------------------- rocprofv3 summaries
-# library kernel name -> substring of the device function name rocprofv3 reports
-KERNEL_SYMBOLS = {"fwd_dma": "k_fwd_dma", "dq_dma": "k_fwd_dma", "dkdv_dma": "k_rev_dma",
-                  "chunk_state_dma": "k_chunk_state_dma", "chunk_state_rev_dma": "k_chunk_state_dma",
-                  "state_scan": "k_scan", "decode": "k_decode", "fwd_mfma": "k_fwd_mfma",
-                  "dkdv_mfma": "k_rev_mfma"}
 
 
 def _csv(dirname, suffix):
@@ -383,7 +409,7 @@ def summarize(args):
     else:
         fetch = _counter_means(args.fetch, "FETCH_SIZE")
         write = _counter_means(args.write, "WRITE_SIZE")
-        sym = KERNEL_SYMBOLS[args.kernel]
+        sym = args.kernel
         pick = lambda d, sub: [v for k, v in d.items() if sub in k]
         copy_f = pick(fetch, "copy") or pick(fetch, "elementwise")
         copy_w = pick(write, "copy") or pick(write, "elementwise")
@@ -395,8 +421,7 @@ def summarize(args):
         f_write = calib_kib / max(v[1] for v in copy_w)
         fetch_b = kf[0][1] * f_fetch * 1024
         write_b = kw[0][1] * f_write * 1024
-        lines += [f"kernel: {args.kernel}",
-                  f"device_function_contains: {sym}",
+        lines += [f"kernel: {args.kernel} (every dispatch whose device function name contains it)",
                   f"dispatches: {kf[0][0]}",
                   f"fetch_kib_per_dispatch_raw: {kf[0][1]:.1f}",
                   f"write_kib_per_dispatch_raw: {kw[0][1]:.1f}",
@@ -423,7 +448,7 @@ def main():
     ap.add_argument("--out", default=PROFILES, help="summarize: output directory")
     ap.add_argument("--fetch", default="", help="summarize --kind traffic: FETCH_SIZE run dir")
     ap.add_argument("--write", default="", help="summarize --kind traffic: WRITE_SIZE run dir")
-    ap.add_argument("--kernel", default="dkdv_dma", help="summarize --kind traffic: library kernel name")
+    ap.add_argument("--kernel", default="k_fwd_dma", help="summarize --kind traffic: device function")
     ap.add_argument("summarize", nargs="?", help=argparse.SUPPRESS)
     ap.add_argument("--kind", choices=["stats", "fetch", "write", "traffic"], default="stats")
     ap.add_argument("--dir", default="")
