@@ -17,7 +17,9 @@ the formula and the decay lam come from the workload definition, the feature
 map is the identity, there is no normaliser, position t attends to itself,
 lam is a float32 value promoted to double with lam^0 = 1 (so lam = 0 keeps only
 the diagonal), an optional initial state S0 adds lam^(t+1) q_t S0, and the
-backward is that of L = <dO, O> with S0 held constant.
+backward is that of L = <dO, O> + <G, S_N> for an optional gradient G arriving
+at the final state, giving dQ, dK, dV and the gradient of S0 (no gradient of
+lam).
 """
 from __future__ import annotations
 
@@ -52,7 +54,7 @@ def _lib():
         lib = ctypes.CDLL(_SO)
         vp, i64 = ctypes.c_void_p, ctypes.c_int64
         lib.oracle_fwd_recurrent.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, i64]
-        lib.oracle_bwd_recurrent.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp]
+        lib.oracle_bwd_recurrent.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         lib.oracle_decode_step.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp]
         _lib_handle = lib
     return _lib_handle
@@ -99,18 +101,28 @@ def fwd_recurrent(q, k, v, lam, s_init=None, want_state=True, block=0):
     return tuple(out)
 
 
-def bwd_recurrent(q, k, v, dout, lam, s_init=None, want=("dq", "dk", "dv")):
-    """F2 backward of L = <dO, O>; returns (dQ, dK, dV) (None for those not wanted)."""
+def bwd_recurrent(q, k, v, dout, lam, s_init=None, want=("dq", "dk", "dv"), g_final=None,
+                  want_ds_init=False):
+    """F2 backward of L = <dO, O> + <G, S_N> (G = ``g_final``, the gradient arriving at the
+    final state; zero when None).
+
+    Returns (dQ, dK, dV) (None for those not wanted), followed by dS0, the gradient of the
+    initial state, when ``want_ds_init``."""
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     *lead, n, d = q.shape
     pairs = int(np.prod(lead)) if lead else 1
     lam_arr = _lams(lam, pairs)
     s0 = None if s_init is None else _f64(s_init).reshape(pairs, d, d)
+    gf = None if g_final is None else _f64(g_final).reshape(pairs, d, d)
     dq = np.empty_like(q) if "dq" in want else None
     dk = np.empty_like(q) if "dk" in want else None
     dv = np.empty_like(q) if "dv" in want else None
+    ds0 = np.empty((pairs, d, d)) if want_ds_init else None
     _lib().oracle_bwd_recurrent(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data, pairs,
-                                n, d, lam_arr.ctypes.data, _ptr(s0), _ptr(dq), _ptr(dk), _ptr(dv))
+                                n, d, lam_arr.ctypes.data, _ptr(s0), _ptr(gf), _ptr(dq), _ptr(dk),
+                                _ptr(dv), _ptr(ds0))
+    if want_ds_init:
+        return dq, dk, dv, ds0.reshape(*lead, d, d)
     return dq, dk, dv
 
 

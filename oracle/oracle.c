@@ -66,8 +66,16 @@ static void fwd_one(const double* q, const double* k, const double* v, int64_t n
 }
 
 /* One sequence, backward of L = <dO, O>.  Any of dq, dk, dv may be NULL. */
+/* Backward of L = <dO, O> + <G, S_N> for one sequence (G = dkv_out, may be NULL
+ * for zero).  The forward-order sweep gives dQ (S includes token t); the
+ * reverse sweep carries the adjoint of the state after token t,
+ *     A_t = q_t dO_t^T + lam A_{t+1},   A_{n-1} = q_{n-1} dO_{n-1}^T + G,
+ * (the recurrence S_t = lam S_{t-1} + k_t v_t^T, o_t = q_t S_t run backwards),
+ * so dk_t = A_t v_t, dv_t = A_t^T k_t, and the gradient of the initial state
+ * S_{-1} = S0 is lam A_0 (ds_init, may be NULL). */
 static void bwd_one(const double* q, const double* k, const double* v, const double* dout, int64_t n,
-                    int64_t d, double lam, const double* s_init, double* dq, double* dk, double* dv) {
+                    int64_t d, double lam, const double* s_init, const double* g_final, double* dq,
+                    double* dk, double* dv, double* ds_init) {
     double* S = (double*)calloc((size_t)(d * d), sizeof(double));
     if (dq) {
         if (s_init) memcpy(S, s_init, sizeof(double) * (size_t)(d * d));
@@ -87,17 +95,21 @@ static void bwd_one(const double* q, const double* k, const double* v, const dou
             }
         }
     }
-    if (dk || dv) {
-        memset(S, 0, sizeof(double) * (size_t)(d * d));
+    if (dk || dv || ds_init) {
+        if (g_final)
+            memcpy(S, g_final, sizeof(double) * (size_t)(d * d));
+        else
+            memset(S, 0, sizeof(double) * (size_t)(d * d));
         for (int64_t t = n - 1; t >= 0; --t) {
             const double* qt = q + t * d;
             const double* gt = dout + t * d;
             const double* kt = k + t * d;
             const double* vt = v + t * d;
+            const double dec = (t == n - 1) ? 1.0 : lam;  /* A_{t+1} carries lam; G enters undecayed */
             for (int64_t a = 0; a < d; ++a) {
                 double* row = S + a * d;
                 double qa = qt[a];
-                for (int64_t c = 0; c < d; ++c) row[c] = lam * row[c] + qa * gt[c];
+                for (int64_t c = 0; c < d; ++c) row[c] = dec * row[c] + qa * gt[c];
             }
             if (dk) {
                 double* out = dk + t * d;
@@ -117,6 +129,12 @@ static void bwd_one(const double* q, const double* k, const double* v, const dou
                     for (int64_t c = 0; c < d; ++c) out[c] += ka * row[c];
                 }
             }
+        }
+        if (ds_init) {
+            if (n > 0)
+                for (int64_t e = 0; e < d * d; ++e) ds_init[e] = lam * S[e];
+            else
+                for (int64_t e = 0; e < d * d; ++e) ds_init[e] = g_final ? g_final[e] : 0.0;
         }
     }
     free(S);
@@ -139,12 +157,13 @@ void oracle_fwd_recurrent(const double* q, const double* k, const double* v, int
 
 void oracle_bwd_recurrent(const double* q, const double* k, const double* v, const double* dout,
                           int64_t pairs, int64_t n, int64_t d, const double* lam, const double* s_init,
-                          double* dq, double* dk, double* dv) {
+                          const double* g_final, double* dq, double* dk, double* dv, double* ds_init) {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t p = 0; p < pairs; ++p) {
-        int64_t off = p * n * d;
-        bwd_one(q + off, k + off, v + off, dout + off, n, d, lam[p], s_init ? s_init + p * d * d : NULL,
-                dq ? dq + off : NULL, dk ? dk + off : NULL, dv ? dv + off : NULL);
+        int64_t off = p * n * d, so = p * d * d;
+        bwd_one(q + off, k + off, v + off, dout + off, n, d, lam[p], s_init ? s_init + so : NULL,
+                g_final ? g_final + so : NULL, dq ? dq + off : NULL, dk ? dk + off : NULL,
+                dv ? dv + off : NULL, ds_init ? ds_init + so : NULL);
     }
 }
 

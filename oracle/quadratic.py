@@ -7,8 +7,10 @@ Attention", features list, parallel form for training):
     D[i, j] = lam^(i-j) if i >= j else 0
     P = (Q K^T) * D,  O = P V  [+ diag(lam^(t+1)) Q S0]
     S_final = lam^n S0 + sum_j lam^(n-1-j) k_j v_j^T
-Backward of L = <dO, O> with S0 constant:
-    G = (dO V^T) * D,  dQ = G K [+ diag(lam^(t+1)) dO S0^T],  dK = G^T Q,  dV = P^T dO.
+Backward of L = <dO, O> + <F, S_final> (F: gradient arriving at the final state):
+    G = (dO V^T) * D,  dQ = G K [+ diag(lam^(t+1)) dO S0^T],
+    dK = G^T Q + diag(lam^(n-1-j)) V F^T,  dV = P^T dO + diag(lam^(n-1-j)) K F,
+    dS0 = Q^T diag(lam^(t+1)) dO + lam^n F.
 The n x n matrices make this form usable for n up to a few thousand only.
 """
 from __future__ import annotations
@@ -47,13 +49,14 @@ def fwd_quadratic(q, k, v, lam, s_init=None):
     return o, s_final
 
 
-def bwd_quadratic(q, k, v, dout, lam, s_init=None):
-    """One sequence: returns (dQ, dK, dV) of L = <dO, O>."""
+def bwd_quadratic(q, k, v, dout, lam, s_init=None, g_final=None):
+    """One sequence: returns (dQ, dK, dV, dS0) of L = <dO, O> + <F, S_final>, F = g_final
+    (zero when None)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     g = np.asarray(dout, dtype=np.float64)
-    n = q.shape[0]
+    n, d = q.shape
     lam = float(np.float64(lam))
     D = decay_matrix(n, lam)
     G = (g @ v.T) * D
@@ -64,4 +67,11 @@ def bwd_quadratic(q, k, v, dout, lam, s_init=None):
         dq = dq + _powers(lam, np.arange(1, n + 1))[:, None] * (g @ s0.T)
     dk = G.T @ q
     dv = P.T @ g
-    return dq, dk, dv
+    ds0 = q.T @ (_powers(lam, np.arange(1, n + 1))[:, None] * g)
+    if g_final is not None:
+        f = np.asarray(g_final, dtype=np.float64)
+        w = _powers(lam, np.arange(n - 1, -1, -1))[:, None]  # lam^(n-1-j)
+        dk = dk + w * (v @ f.T)
+        dv = dv + w * (k @ f)
+        ds0 = ds0 + (lam ** n) * f
+    return dq, dk, dv, ds0

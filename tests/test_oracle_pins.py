@@ -55,31 +55,41 @@ def exact_forward(q, k, v, lam, s0=None):
     return O, S
 
 
-def exact_loss(q, k, v, g, lam, s0=None):
-    O, _ = exact_forward(q, k, v, lam, s0)
-    return sum(O[t][c] * Fraction(g[t][c]) for t in range(len(O)) for c in range(len(O[0])))
+def exact_loss(q, k, v, g, lam, s0=None, gf=None):
+    """L = <dO, O> + <G, S_final> from the exact forward (G = gf, the gradient arriving at
+    the final state; absent when None)."""
+    O, S = exact_forward(q, k, v, lam, s0)
+    L = sum(O[t][c] * Fraction(g[t][c]) for t in range(len(O)) for c in range(len(O[0])))
+    if gf is not None:
+        L += sum(S[a][c] * Fraction(gf[a][c]) for a in range(len(S)) for c in range(len(S)))
+    return L
 
 
-def exact_grads(q, k, v, g, lam, s0=None):
-    """Exact dL/dQ, dL/dK, dL/dV of L = <dO, O>.
+def exact_grads(q, k, v, g, lam, s0=None, gf=None, want_ds0=False):
+    """Exact dL/dQ, dL/dK, dL/dV (and dL/dS0) of L = <dO, O> + <G, S_final>.
 
-    L is affine in each of Q, K, V separately, so each partial derivative is an
+    L is affine in each of Q, K, V and S0 separately, so each partial derivative is an
     exact difference of two loss evaluations of the forward definition."""
     n, d = len(q), len(q[0])
     zero = [[0] * d for _ in range(n)]
 
-    def unit(t, a):
-        m = [[0] * d for _ in range(n)]
+    def unit(t, a, rows=n):
+        m = [[0] * d for _ in range(rows)]
         m[t][a] = 1
         return m
 
-    base_q = exact_loss(zero, k, v, g, lam, s0)
-    base_k = exact_loss(q, zero, v, g, lam, s0)
-    base_v = exact_loss(q, k, zero, g, lam, s0)
-    dq = [[exact_loss(unit(t, a), k, v, g, lam, s0) - base_q for a in range(d)] for t in range(n)]
-    dk = [[exact_loss(q, unit(t, a), v, g, lam, s0) - base_k for a in range(d)] for t in range(n)]
-    dv = [[exact_loss(q, k, unit(t, a), g, lam, s0) - base_v for a in range(d)] for t in range(n)]
-    return dq, dk, dv
+    base_q = exact_loss(zero, k, v, g, lam, s0, gf)
+    base_k = exact_loss(q, zero, v, g, lam, s0, gf)
+    base_v = exact_loss(q, k, zero, g, lam, s0, gf)
+    dq = [[exact_loss(unit(t, a), k, v, g, lam, s0, gf) - base_q for a in range(d)] for t in range(n)]
+    dk = [[exact_loss(q, unit(t, a), v, g, lam, s0, gf) - base_k for a in range(d)] for t in range(n)]
+    dv = [[exact_loss(q, k, unit(t, a), g, lam, s0, gf) - base_v for a in range(d)] for t in range(n)]
+    if not want_ds0:
+        return dq, dk, dv
+    zs = [[0] * d for _ in range(d)]
+    base_s = exact_loss(q, k, v, g, lam, zs, gf)
+    ds0 = [[exact_loss(q, k, v, g, lam, unit(a, c, d), gf) - base_s for c in range(d)] for a in range(d)]
+    return dq, dk, dv, ds0
 
 
 def as_f64(m):
@@ -122,9 +132,32 @@ def test_backward_matches_exact_gradients(lam, n, d, seed, with_s0):
     assert np.array_equal(dq, dq_ex)
     assert np.array_equal(dk, dk_ex)
     assert np.array_equal(dv, dv_ex)
-    dq1, dk1, dv1 = oracle.bwd_quadratic(q, k, v, g, lamf, s0)
+    dq1, dk1, dv1, _ = oracle.bwd_quadratic(q, k, v, g, lamf, s0)
     for a, b in ((dq1, dq_ex), (dk1, dk_ex), (dv1, dv_ex)):
         np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("lam", LAMS)
+@pytest.mark.parametrize("n,d,seed,with_s0", [(1, 2, 30, True), (5, 2, 31, False), (8, 3, 32, True)])
+def test_state_gradients_match_exact(lam, n, d, seed, with_s0):
+    """With a gradient G arriving at the final state: dK, dV and the initial-state gradient
+    dS0 equal the exact partial derivatives of L = <dO, O> + <G, S_final>; G is not
+    symmetric, so a transposed G fails."""
+    rng = np.random.default_rng(seed)
+    q, k, v, g = (rng.integers(-3, 4, size=(n, d)).tolist() for _ in range(4))
+    gf = rng.integers(-3, 4, size=(d, d)).tolist()
+    gf[0][d - 1] = 5 if gf[d - 1][0] != 5 else 4
+    s0 = rng.integers(-3, 4, size=(d, d)).tolist() if with_s0 else None
+    ex = [as_f64(m) for m in exact_grads(q, k, v, g, lam, s0, gf, want_ds0=True)]
+    lamf = float(lam)
+    s0a = None if s0 is None else np.array(s0, float)
+    got = oracle.bwd_recurrent(np.array(q, float), np.array(k, float), np.array(v, float),
+                               np.array(g, float), lamf, s0a, g_final=np.array(gf, float), want_ds_init=True)
+    for a, b, name in zip(got, ex, ("dQ", "dK", "dV", "dS0")):
+        np.testing.assert_array_equal(a, b, err_msg=name)
+    got1 = oracle.bwd_quadratic(q, k, v, g, lamf, s0, g_final=gf)
+    for a, b, name in zip(got1, ex, ("dQ", "dK", "dV", "dS0")):
+        np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-13, err_msg=name)
 
 
 @pytest.mark.parametrize("lam", LAMS)
@@ -189,11 +222,23 @@ def test_closed_forms_all_ones(lam):
         np.testing.assert_allclose(s, s_exp, rtol=1e-12)
     dq_exp = d * geo_t[:, None] * ones
     dkv_exp = d * geo_rev[:, None] * ones
-    for dq, dk, dv in (oracle.bwd_recurrent(ones, ones, ones, ones, lam),
-                       oracle.bwd_quadratic(ones, ones, ones, ones, lam)):
+    for grads in (oracle.bwd_recurrent(ones, ones, ones, ones, lam),
+                  oracle.bwd_quadratic(ones, ones, ones, ones, lam)):
+        dq, dk, dv = grads[:3]
         np.testing.assert_allclose(dq, dq_exp, rtol=1e-12)
         np.testing.assert_allclose(dk, dkv_exp, rtol=1e-12)
         np.testing.assert_allclose(dv, dkv_exp, rtol=1e-12)
+    # with G = 1 1^T arriving at the final state: dK_j, dV_j gain lam^(n-1-j) d, and
+    # dS0 = (sum_t lam^(t+1)) 1 1^T + lam^n G
+    ones_dd = np.ones((d, d))
+    tail = lam ** (n - 1 - t) if lam != 0.0 else (t == n - 1).astype(np.float64)
+    head = lam * geo_n
+    ds0_exp = (head + lam ** n) * ones_dd
+    for grads in (oracle.bwd_recurrent(ones, ones, ones, ones, lam, g_final=ones_dd, want_ds_init=True),
+                  oracle.bwd_quadratic(ones, ones, ones, ones, lam, g_final=ones_dd)):
+        np.testing.assert_allclose(grads[1], (dkv_exp + d * tail[:, None]), rtol=1e-12)
+        np.testing.assert_allclose(grads[2], (dkv_exp + d * tail[:, None]), rtol=1e-12)
+        np.testing.assert_allclose(grads[3], ds0_exp, rtol=1e-12)
 
 
 def test_no_decay_is_one_based_i_d_v():
@@ -290,6 +335,25 @@ def test_linear_in_v_and_q():
     np.testing.assert_allclose(o_ac, o_a + o_c, rtol=1e-11, atol=1e-11)
 
 
+def test_state_gradient_adjoint_identity():
+    """L = <dO, O> + <G, S_final> is affine in S0 and in K: L(X + dX) - L(X) = <dL/dX, dX>
+    with L evaluated by the forward form only."""
+    rng = np.random.default_rng(14)
+    n, d, lam = 70, 5, 0.9
+    q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+    s0, gf, dS, = (rng.standard_normal((d, d)) for _ in range(3))
+    dX = rng.standard_normal((n, d))
+
+    def loss(kk, ss):
+        o, sf = oracle.fwd_recurrent(q, kk, v, lam, ss)
+        return np.sum(g * o) + np.sum(gf * sf)
+    dq, dk, dv, ds0 = oracle.bwd_recurrent(q, k, v, g, lam, s0, g_final=gf, want_ds_init=True)
+    base = loss(k, s0)
+    lhs_s, lhs_k = loss(k, s0 + dS) - base, loss(k + dX, s0) - base
+    assert abs(lhs_s - np.sum(ds0 * dS)) < 1e-10 * (1 + abs(lhs_s))
+    assert abs(lhs_k - np.sum(dk * dX)) < 1e-10 * (1 + abs(lhs_k))
+
+
 def test_adjoint_identity_random():
     """<dO, J dX> == <J^T dO, dX> for the exact linear maps X -> O (each of Q, K, V)."""
     rng = np.random.default_rng(13)
@@ -348,3 +412,23 @@ def test_planted_mistakes_are_caught(monkeypatch):
         D = orig(len(q), lam)
         return ((k @ q.T) * D) @ v, None
     assert _brute_force_fails(swapped)
+
+
+def test_planted_state_gradient_mistakes_are_caught():
+    """Plausible slips in the final-state gradient terms fail the exact pin."""
+    rng = np.random.default_rng(33)
+    n, d, lam = 6, 3, Fraction(1, 2)
+    q, k, v, g = (rng.integers(-3, 4, size=(n, d)).tolist() for _ in range(4))
+    gf = rng.integers(-3, 4, size=(d, d)).tolist()
+    gf[0][2], gf[2][0] = 3, -2
+    s0 = rng.integers(-3, 4, size=(d, d)).tolist()
+    _, dk_ex, _, ds0_ex = (as_f64(m) for m in exact_grads(q, k, v, g, lam, s0, gf, want_ds0=True))
+    qa, ka, va, ga, fa, sa = (np.array(x, float) for x in (q, k, v, g, gf, s0))
+    _, dk0, _, ds00 = oracle.bwd_quadratic(qa, ka, va, ga, 0.5, sa)   # no G term
+    w_ok = 0.5 ** np.arange(n - 1, -1, -1)[:, None]
+    assert np.allclose(dk0 + w_ok * (va @ fa.T), dk_ex, rtol=1e-13, atol=1e-13)
+    assert not np.allclose(dk0 + 0.5 * w_ok * (va @ fa.T), dk_ex)       # exponent n - j
+    assert not np.allclose(dk0 + w_ok * (va @ fa), dk_ex)               # G not transposed
+    assert np.allclose(ds00 + 0.5 ** n * fa, ds0_ex, rtol=1e-13, atol=1e-13)
+    assert not np.allclose(ds00 + fa, ds0_ex)                           # G without lam^n
+    assert not np.allclose(ds00, ds0_ex)                                # G dropped
