@@ -44,7 +44,7 @@ def _load():
     lib.la_fwd.restype = ctypes.c_int
     lib.la_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
     lib.la_fwd_workspace_bytes.restype = sz
-    lib.la_bwd.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.la_bwd.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.la_bwd.restype = ctypes.c_int
     lib.la_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
     lib.la_bwd_workspace_bytes.restype = sz
@@ -155,9 +155,12 @@ def la_fwd(q, k, v, lam, Bk: int = 64, kv_in=None, out=None, kv_out=None, want_s
 
 
 def la_bwd(q, k, v, dout, lam, Bk: int = 64, kv_in=None, dq=None, dk=None, dv=None, ws=None,
-           fwd_ws=None):
-    """dQ, dK, dV of L = <dO, O> for la_fwd (kv_in held constant).
+           fwd_ws=None, dkv_out=None, dkv_in=None, want_dkv_in: bool = False):
+    """dQ, dK, dV of L = <dO, O> + <dkv_out, S_N> for la_fwd.
 
+    ``dkv_out``: float32 [B, H, D, D] gradient arriving at the final state (None for zero).
+    ``dkv_in`` / ``want_dkv_in``: receive the gradient of the initial state; returned as a
+    fourth value when either is given.
     ``fwd_ws``: the tensor passed as ``ws`` to the la_fwd call over the same inputs, unchanged
     since; the dQ sweep then takes the chunk states from it instead of recomputing them."""
     for name, t in (("Q", q), ("K", k), ("V", v), ("dO", dout)):
@@ -169,6 +172,10 @@ def la_bwd(q, k, v, dout, lam, Bk: int = 64, kv_in=None, dq=None, dk=None, dv=No
     for name, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
         _check_seq(name, t, q)
     _check_state("kv_in", kv_in, B, H, D, q.device)
+    _check_state("dkv_out", dkv_out, B, H, D, q.device)
+    if dkv_in is None and want_dkv_in:
+        dkv_in = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    _check_state("dkv_in", dkv_in, B, H, D, q.device)
     code = _dtype_code(q)
     nbytes = la_bwd_workspace_bytes(B, H, N, D, Bk, code)
     ws = _workspace(nbytes, q.device, ws)
@@ -177,10 +184,12 @@ def la_bwd(q, k, v, dout, lam, Bk: int = 64, kv_in=None, dq=None, dk=None, dv=No
         if fwd_ws.device != q.device or fwd_ws.numel() * fwd_ws.element_size() < need:
             raise ValueError(f"fwd_ws must hold the {need}-byte workspace of la_fwd on {q.device}")
     rc = lib.la_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _lam_array(lam, H), B, H, N, D, Bk, code,
-                    _ptr(kv_in), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(fwd_ws), _ptr(ws),
-                    nbytes if ws is not None else 0, _stream(q.device))
+                    _ptr(kv_in), _ptr(dkv_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkv_in), _ptr(fwd_ws),
+                    _ptr(ws), nbytes if ws is not None else 0, _stream(q.device))
     if rc != LA_OK:
         raise LaError(rc, "la_bwd")
+    if dkv_in is not None:
+        return dq, dk, dv, dkv_in
     return dq, dk, dv
 
 

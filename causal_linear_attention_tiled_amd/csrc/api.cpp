@@ -177,7 +177,7 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
         else
             rc = launch("chunk_state_generic", s, [&] { la::launch_chunk_state_generic(cs, lam, bf16, s); });
         if (rc) return rc;
-        la::ScanArgs sc{slots, kv_in, kv_in_t, p.L, static_cast<int>(D), H, p.chunks, pairs, 0};
+        la::ScanArgs sc{slots, kv_in, kv_in_t, nullptr, N, p.L, static_cast<int>(D), H, p.chunks, pairs, 0};
         rc = launch("state_scan", s, [&] { la::launch_scan(sc, lam, s); });
         if (rc) return rc;
     }
@@ -276,17 +276,18 @@ int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int
 }
 
 int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const float* lambda, int64_t B,
-           int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype, const float* kv_in, void* dQ,
-           void* dK, void* dV, const void* fwd_ws, void* ws, size_t ws_bytes, void* hip_stream) {
+           int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype, const float* kv_in,
+           const float* dkv_out, void* dQ, void* dK, void* dV, float* dkv_in, const void* fwd_ws, void* ws,
+           size_t ws_bytes, void* hip_stream) {
     int64_t elems;
     int rc = check_shape(B, H, N, D, Bk, dtype, &elems);
     if (rc) return rc;
     if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return LA_EINVAL;
     LamArgs lam;
     if ((rc = load_lambda(lambda, H, &lam))) return rc;
-    for (const void* p : {Q, K, V, dO, static_cast<const void*>(kv_in), static_cast<const void*>(dQ),
-                          static_cast<const void*>(dK), static_cast<const void*>(dV), fwd_ws,
-                          static_cast<const void*>(ws)})
+    for (const void* p : {Q, K, V, dO, static_cast<const void*>(kv_in), static_cast<const void*>(dkv_out),
+                          static_cast<const void*>(dQ), static_cast<const void*>(dK), static_cast<const void*>(dV),
+                          static_cast<const void*>(dkv_in), fwd_ws, static_cast<const void*>(ws)})
         if (p && !aligned16(p)) return LA_EALIGN;
     const size_t tb = static_cast<size_t>(elems) * (dtype == LA_BF16 ? 2 : 4);
     const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
@@ -295,13 +296,14 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     const size_t need = one ? 2 * round_up(one) : 0;
     if (need && (!ws || ws_bytes < need)) return LA_EWORKSPACE;
     const Range ins[] = {{Q, tb}, {K, tb}, {V, tb}, {dO, tb}, {kv_in, kv_in ? sb : 0},
-                         {fwd_ws, fwd_ws ? one : 0}};
-    const Range outs[] = {{dQ, tb}, {dK, tb}, {dV, tb}, {ws, need}};
+                         {dkv_out, dkv_out ? sb : 0}, {fwd_ws, fwd_ws ? one : 0}};
+    const Range outs[] = {{dQ, tb}, {dK, tb}, {dV, tb}, {dkv_in, dkv_in ? sb : 0}, {ws, need}};
+    constexpr int kOuts = sizeof(outs) / sizeof(outs[0]);
     for (const Range& o : outs)
         for (const Range& i : ins)
             if (overlap(o, i)) return LA_EINVAL;
-    for (int a = 0; a < 4; ++a)
-        for (int b = a + 1; b < 4; ++b)
+    for (int a = 0; a < kOuts; ++a)
+        for (int b = a + 1; b < kOuts; ++b)
             if (overlap(outs[a], outs[b])) return LA_EINVAL;
 
     int dev_count = 0;
@@ -328,7 +330,7 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
         else
             rc = launch("chunk_state_rev_generic", s, [&] { la::launch_chunk_state_generic(cs, lam, bf16, s); });
         if (rc) return rc;
-        la::ScanArgs sc{slots_kv, nullptr, 0, p.L, static_cast<int>(D), Hi, p.chunks, pairs, 1};
+        la::ScanArgs sc{slots_kv, nullptr, 0, dkv_out, N, p.L, static_cast<int>(D), Hi, p.chunks, pairs, 1};
         rc = launch("state_scan_rev", s, [&] { la::launch_scan(sc, lam, s); });
         if (rc) return rc;
     }
@@ -340,6 +342,8 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     a.out0 = dK;
     a.out1 = dV;
     a.slots = slots_kv;
+    a.g_final = dkv_out;
+    a.ds_out = dkv_in;
     a.N = N;
     a.L = p.L;
     a.D = static_cast<int>(D);

@@ -7,6 +7,9 @@
 //     dK_b = ((dO_b V_b^T) o M)^T Q_b + diag(lam^(m-s)) V_b dS^T
 //     dV_b = ((Q_b K_b^T) o M)^T dO_b + diag(lam^(m-s)) K_b dS
 //     dS  <- lam^m dS + (diag(lam^s) Q_b)^T dO_b.
+// A gradient F arriving at the final state is the last chunk's starting dS, with the
+// exponents of the sequence's last block lowered by one (it reaches token j as
+// lam^(N-1-j) F); chunk 0 ends with lam dS, the gradient of the initial state.
 // The four waves stream the raw row-major Q, K, V, dO tiles of the next block
 // (in sweep order) into the second of two LDS stages while they compute the
 // current one (each block starts with vmcnt(0), so loads and stores may share
@@ -86,7 +89,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_rev_dma(SweepArgs a, LamArgs lam
     //   Sk[at][h][r] = dS^T[32 (at/2) + rho(at%2, 4g + r)][32 w + 16 h + li]   (key rows)
     f32x4 Sv[8][2], Sk[8][2];
     {
-        const float* init = (c < a.chunks - 1) ? a.slots + (pair * (a.chunks - 1) + c) * D * D : nullptr;
+        const float* init = (c < a.chunks - 1) ? a.slots + (pair * (a.chunks - 1) + c) * D * D
+                                               : (a.g_final ? a.g_final + pair * D * D : nullptr);
 #pragma unroll
         for (int at = 0; at < 8; ++at)
 #pragma unroll
@@ -116,6 +120,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_rev_dma(SweepArgs a, LamArgs lam
         const int64_t t0 = t_begin + n * BK;
         const int m = static_cast<int>(min(static_cast<int64_t>(BK), t_end - t0));
         const int stage = static_cast<int>(i % NSTAGE);
+        // the final-state gradient reaches the sequence's last block one power less decayed
+        const int shift = (c == a.chunks - 1 && a.g_final && i == 0) ? 1 : 0;
         const uint16_t* Qs = sm.t[stage][0];
         const uint16_t* Ks = sm.t[stage][1];
         const uint16_t* Vs = sm.t[stage][2];
@@ -171,7 +177,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_rev_dma(SweepArgs a, LamArgs lam
 #pragma unroll
         for (int jt = 0; jt < NT; ++jt) {
             const int j = 16 * jt + li;
-            const float lj = masked_pw(sm.pw, m - j, j < m);
+            const float lj = masked_pw(sm.pw, m - shift - j, j < m);
             f32x4 dv[2], dk[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) dv[h] = dk[h] = zero4();
@@ -219,7 +225,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_rev_dma(SweepArgs a, LamArgs lam
 
         // ---- dS <- lam^m dS + Q^T diag(lam^s) dO, both copies; the weights go on this wave's
         // own fragments (dO columns for the value copy, Q columns for the key copy)
-        const float lm = sm.pw[m];
+        const float lm = sm.pw[m - shift];
         bf16x8 qs[2][NKB], gs[2][NKB];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -247,6 +253,17 @@ __global__ __launch_bounds__(64 * NW, 1) void k_rev_dma(SweepArgs a, LamArgs lam
                 }
             }
         }
+    }
+    if (c == 0 && a.ds_out) {
+        // gradient of the initial state: lam dS, from the value-column copy
+        float* dst = a.ds_out + pair * D * D;
+#pragma unroll
+        for (int at = 0; at < 8; ++at)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dst[(32 * (at >> 1) + rho(at & 1, 4 * g + r)) * D + 32 * w + 16 * h + li] = lv * Sv[at][h][r];
     }
 }
 
@@ -297,7 +314,8 @@ __global__ __launch_bounds__(64 * 8, 1) void k_rev_dma_split(SweepArgs a, LamArg
     //   or dS^T (key group), entering this chunk from the right (0 for the last chunk).
     f32x4 S[8][2];
     {
-        const float* init = (c < a.chunks - 1) ? a.slots + (pair * (a.chunks - 1) + c) * D * D : nullptr;
+        const float* init = (c < a.chunks - 1) ? a.slots + (pair * (a.chunks - 1) + c) * D * D
+                                               : (a.g_final ? a.g_final + pair * D * D : nullptr);
 #pragma unroll
         for (int at = 0; at < 8; ++at)
 #pragma unroll
@@ -328,6 +346,8 @@ __global__ __launch_bounds__(64 * 8, 1) void k_rev_dma_split(SweepArgs a, LamArg
         const int64_t t0 = t_begin + n * BK;
         const int m = static_cast<int>(min(static_cast<int64_t>(BK), t_end - t0));
         const int stage = static_cast<int>(i % NSTAGE);
+        // the final-state gradient reaches the sequence's last block one power less decayed
+        const int shift = (c == a.chunks - 1 && a.g_final && i == 0) ? 1 : 0;
         // value group: rows K, tiles P, token-contracted operand dO, update operand Q^T
         // key group:   rows V, tiles G, token-contracted operand Q,  update operand dO^T
         const uint16_t* Xs = sm.t[stage][grp ? 3 : 0];  // score tile A rows (Q or dO)
@@ -379,7 +399,7 @@ __global__ __launch_bounds__(64 * 8, 1) void k_rev_dma_split(SweepArgs a, LamArg
 #pragma unroll
         for (int jt = 0; jt < NT; ++jt) {
             const int j = 16 * jt + li;
-            const float lj = masked_pw(sm.pw, m - j, j < m);
+            const float lj = masked_pw(sm.pw, m - shift - j, j < m);
             f32x4 acc[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) acc[h] = zero4();
@@ -412,7 +432,7 @@ __global__ __launch_bounds__(64 * 8, 1) void k_rev_dma_split(SweepArgs a, LamArg
         }
 
         // ---- X <- lam^m X + U^T diag(lam^s) T, U = Q (value group) or dO (key group)
-        const float lm = sm.pw[m];
+        const float lm = sm.pw[m - shift];
         bf16x8 ts[2][NKB];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -430,6 +450,17 @@ __global__ __launch_bounds__(64 * 8, 1) void k_rev_dma_split(SweepArgs a, LamArg
                 for (int h = 0; h < 2; ++h) S[at][h] = mfma16(ua, ts[h][kb], S[at][h]);
             }
         }
+    }
+    if (c == 0 && a.ds_out && grp == 0) {
+        // gradient of the initial state: lam dS, from the value group's copy
+        float* dst = a.ds_out + pair * D * D;
+#pragma unroll
+        for (int at = 0; at < 8; ++at)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dst[(32 * (at >> 1) + rho(at & 1, 4 * g + r)) * D + 32 * q + 16 * h + li] = lv * S[at][h][r];
     }
 }
 

@@ -89,7 +89,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_rev_mfma(SweepArgs a, LamArgs l
     //   Sk[vt][kt][r] = dS^T[16 vt + 4 g + r][32 w + 16 kt + li] = dS[32 w + 16 kt + li][16 vt + 4 g + r]
     f32x4 Sv[8][2], Sk[8][2];
     {
-        const float* init = (c < a.chunks - 1) ? a.slots + (pair * (a.chunks - 1) + c) * D * D : nullptr;
+        const float* init = (c < a.chunks - 1) ? a.slots + (pair * (a.chunks - 1) + c) * D * D
+                                               : (a.g_final ? a.g_final + pair * D * D : nullptr);
 #pragma unroll
         for (int t8 = 0; t8 < 8; ++t8)
 #pragma unroll
@@ -139,6 +140,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_rev_mfma(SweepArgs a, LamArgs l
         for (int e = 0; e < 8; ++e) wq[ks][e] = sm.pw[32 * ks + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4)];
 
     for (int64_t n = nblk - 1; n >= 0; --n) {
+        // the final-state gradient reaches the sequence's last block one power less decayed
+        const int shift = (c == a.chunks - 1 && a.g_final && n == nblk - 1) ? 1 : 0;
         const int64_t t0 = t_begin + n * BK;
         const int m = static_cast<int>(min(static_cast<int64_t>(BK), t_end - t0));
 
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_rev_mfma(SweepArgs a, LamArgs l
 #pragma unroll
         for (int jt = 0; jt < NT; ++jt) {
             const int j = 16 * jt + li;
-            const float lj = masked_pw(sm.pw, m - j, j < m);
+            const float lj = masked_pw(sm.pw, m - shift - j, j < m);
             bf16x8 kb[4], vb[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_rev_mfma(SweepArgs a, LamArgs l
         }
 
         // ---- 4. dS <- lam^m dS + (diag(lam^s) Q)^T dO, both copies
-        const float lm = sm.pw[m];
+        const float lm = sm.pw[m - shift];
         bf16x8 qs[2][NKS];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -272,6 +275,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_rev_mfma(SweepArgs a, LamArgs l
             }
         }
         __syncthreads();
+    }
+    if (c == 0 && a.ds_out) {
+        // gradient of the initial state: lam dS, from the value-column copy
+        float* dst = a.ds_out + pair * D * D;
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[(16 * t8 + 4 * g + r) * D + 32 * w + 16 * h + li] = lv * Sv[t8][h][r];
     }
 }
 

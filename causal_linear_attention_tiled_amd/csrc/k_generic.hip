@@ -100,6 +100,9 @@ __global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs l
 //   dK_b = (G o M)^T Q_b + diag(lam^(m-s)) V_b dS^T,   G = dO_b V_b^T
 //   dV_b = (P o M)^T dO_b + diag(lam^(m-s)) K_b dS,    P = Q_b K_b^T
 //   dS  <- lam^m dS + (diag(lam^s) Q_b)^T dO_b
+// A gradient F arriving at the final state enters as the last chunk's dS with the
+// exponents of the sequence's last block lowered by one (F reaches token j as
+// lam^(N-1-j) F, not lam^(N-j)); chunk 0 ends with lam dS = the gradient of S0.
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs lam) {
     __shared__ Tile sh;
@@ -111,7 +114,9 @@ __global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs l
     const int64_t t_end = min(a.N, t_begin + a.L);
     const int64_t base = pair * a.N * D;
     fill_powers(sh.pw, lv, Bk);
-    const float* init = (c < a.chunks - 1) ? a.slots + (pair * (a.chunks - 1) + c) * D * D : nullptr;
+    const bool last = c == a.chunks - 1;
+    const float* init = !last ? a.slots + (pair * (a.chunks - 1) + c) * D * D
+                              : (a.g_final ? a.g_final + pair * D * D : nullptr);
     for (int i = tid; i < D * D; i += kThreads) sh.state[i] = init ? init[i] : 0.f;
     __syncthreads();
 
@@ -119,6 +124,7 @@ __global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs l
     for (int64_t bi = nblk - 1; bi >= 0; --bi) {
         const int64_t t0 = t_begin + bi * Bk;
         const int m = static_cast<int>(min(static_cast<int64_t>(Bk), t_end - t0));
+        const int shift = (last && a.g_final && bi == nblk - 1) ? 1 : 0;
         const int64_t r0 = base + t0 * D;
         // G[i][j] = lam^(i-j) dO_i . v_j for i >= j
         for (int idx = tid; idx < m * m; idx += kThreads) {
@@ -136,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs l
             float intra = 0.f, inter = 0.f;
             for (int i = j; i < m; ++i) intra += sh.score[i * kMaxBk + j] * ld<BF16>(a.a, r0 + i * D + f);
             for (int col = 0; col < D; ++col) inter += sh.state[f * D + col] * ld<BF16>(a.c, r0 + j * D + col);
-            st<BF16>(a.out0, r0 + j * D + f, intra + sh.pw[m - j] * inter);
+            st<BF16>(a.out0, r0 + j * D + f, intra + sh.pw[m - shift - j] * inter);
         }
         __syncthreads();
         // P[i][j] = lam^(i-j) q_i . k_j for i >= j
@@ -155,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs l
             float intra = 0.f, inter = 0.f;
             for (int i = j; i < m; ++i) intra += sh.score[i * kMaxBk + j] * ld<BF16>(a.g, r0 + i * D + col);
             for (int f = 0; f < D; ++f) inter += ld<BF16>(a.b, r0 + j * D + f) * sh.state[f * D + col];
-            st<BF16>(a.out1, r0 + j * D + col, intra + sh.pw[m - j] * inter);
+            st<BF16>(a.out1, r0 + j * D + col, intra + sh.pw[m - shift - j] * inter);
         }
         __syncthreads();
         for (int idx = tid; idx < D * D; idx += kThreads) {
@@ -163,10 +169,12 @@ __global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs l
             float acc = 0.f;
             for (int s = 0; s < m; ++s)
                 acc += sh.pw[s] * ld<BF16>(a.a, r0 + s * D + f) * ld<BF16>(a.g, r0 + s * D + col);
-            sh.state[idx] = sh.pw[m] * sh.state[idx] + acc;
+            sh.state[idx] = sh.pw[m - shift] * sh.state[idx] + acc;
         }
         __syncthreads();
     }
+    if (c == 0 && a.ds_out)
+        for (int i = tid; i < D * D; i += kThreads) a.ds_out[pair * D * D + i] = lv * sh.state[i];
 }
 
 // Aggregate state of one chunk, started from zero (see ChunkStateArgs).
@@ -225,9 +233,12 @@ __global__ __launch_bounds__(kThreads) void k_scan(ScanArgs a, LamArgs lam) {
             sl[static_cast<int64_t>(c) * DD] = S;
         }
     } else {
-        float R = 0.f;
+        // the final-state gradient reaches the end of chunk chunks-2 decayed over the last
+        // chunk's length minus one (it enters at the last token undecayed)
+        const int64_t len_last = a.N - static_cast<int64_t>(a.chunks - 1) * a.L;
+        float R = a.g_final ? lam_pow(lam.lam[pair % a.H], len_last - 1) * a.g_final[pair * DD + e] : 0.f;
         for (int c = a.chunks - 2; c >= 0; --c) {
-            R = sl[static_cast<int64_t>(c) * DD] + lamL * R;
+            R = sl[static_cast<int64_t>(c) * DD] + (c == a.chunks - 2 ? R : lamL * R);
             sl[static_cast<int64_t>(c) * DD] = R;
         }
     }

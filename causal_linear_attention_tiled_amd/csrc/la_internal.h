@@ -32,6 +32,10 @@ struct SweepArgs {
     int slots_transposed; // read the slots as their transposes (dQ sweep fed by the
                           // forward pass's chunk states)
     float* kv_out;        // [P][D][D] final state (forward only) or nullptr
+    const float* g_final; // reverse only: [P][D][D] gradient arriving at the final state, the
+                          // dS the last chunk starts from, or nullptr for zero
+    float* ds_out;        // reverse only: [P][D][D] gradient of the initial state, lam times
+                          // the dS chunk 0 ends with, or nullptr
     int64_t N;
     int64_t L;            // chunk length in tokens
     int D, Bk, H, chunks;
@@ -54,11 +58,15 @@ struct ChunkStateArgs {
 
 // In-place scan of the slots of every sequence.
 //   forward: S = kv_in (or 0); for c = 0..chunks-2: S = lam^L S + slot[c]; slot[c] = S
-//   reverse: R = 0;           for c = chunks-2..0: R = slot[c] + lam^L R; slot[c] = R
+//   reverse: R = lam^(len_last - 1) G pulled back to the end of chunk chunks-2, then
+//            for c = chunks-2..0: R = slot[c] + (c == chunks-2 ? R : lam^L R); slot[c] = R
+//            (len_last = N - (chunks-1) L, the last chunk's length; G = g_final or 0)
 struct ScanArgs {
     float* slots;
-    const float* kv_in;
+    const float* kv_in;   // forward: initial state, or nullptr
     int kv_in_transposed;
+    const float* g_final; // reverse: gradient arriving at the final state, or nullptr
+    int64_t N;
     int64_t L;
     int D, H, chunks;
     int64_t pairs;

@@ -92,18 +92,25 @@ int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int
  * split into chunks).  Returns 0 as well for invalid shapes. */
 size_t la_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype);
 
-/* Backward pass of L = <dO, O> for the forward above, with kv_in held
- * constant and no gradient arriving through kv_out (the same tiling run in
+/* Backward pass of L = <dO, O> + <F, S_N> for the forward above, where F is
+ * an optional gradient arriving at the final state (the same tiling run in
  * the backward direction: a forward-order sweep for dQ that carries the key-
  * value state, and a reverse-order sweep for dK and dV that carries the
- * state's gradient dS = sum_{i >= t} lam^(i-t) q_i dO_i^T):
+ * state's gradient A_t = sum_{i >= t} lam^(i-t) q_i dO_i^T + lam^(N-1-t) F):
  *   dQ_t = sum_{j<=t} lam^(t-j) (dO_t . v_j) k_j + lam^(t+1) S0 dO_t
- *   dK_j = sum_{i>=j} lam^(i-j) (dO_i . v_j) q_i
- *   dV_j = sum_{i>=j} lam^(i-j) (q_i . k_j) dO_i
- * It is stateless: Q, K, V and kv_in are passed again.
+ *   dK_j = A_j v_j  = sum_{i>=j} lam^(i-j) (dO_i . v_j) q_i + lam^(N-1-j) F v_j
+ *   dV_j = A_j^T k_j = sum_{i>=j} lam^(i-j) (q_i . k_j) dO_i + lam^(N-1-j) F^T k_j
+ *   dS0  = lam A_0  = sum_t lam^(t+1) q_t dO_t^T + lam^N F
+ * No gradient of lambda is computed.  The call is stateless: Q, K, V and
+ * kv_in are passed again.
  *   dO      : [B][H][N][D] dtype, device.
+ *   dkv_out : [B][H][D][D] float32 device gradient F arriving at kv_out, or
+ *             NULL for zero.
  *   dQ,dK,dV: [B][H][N][D] dtype, device, written; none may overlap an input
  *             or each other.
+ *   dkv_in  : [B][H][D][D] float32 device, receives dS0 (the gradient of
+ *             kv_in, also when kv_in is NULL); NULL skips it.  Must not
+ *             overlap an input or another output.
  *   fwd_ws  : NULL, or the workspace of an la_fwd call with the same Q, K, V,
  *             lambda, shape, Bk, dtype and kv_in, unchanged since that call
  *             (device, read only; same LA_CHUNKS setting).  The dQ sweep then
@@ -115,8 +122,8 @@ size_t la_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_
  *   other arguments as for la_fwd. */
 int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const float* lambda,
            int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype,
-           const float* kv_in, void* dQ, void* dK, void* dV, const void* fwd_ws, void* ws,
-           size_t ws_bytes, void* hip_stream);
+           const float* kv_in, const float* dkv_out, void* dQ, void* dK, void* dV, float* dkv_in,
+           const void* fwd_ws, void* ws, size_t ws_bytes, void* hip_stream);
 
 size_t la_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype);
 

@@ -106,14 +106,20 @@ def test_bwd_rejects():
     v = ctypes.c_void_p
     lam = (ctypes.c_float * 2)(0.5, 0.5)
     G_ = A * 10
-    call = lambda dq, dk, dv, g=G_: la.lib.la_bwd(v(Q_), v(K_), v(V_), v(g), lam, 1, 2, 128, 64, 64,
-                                                  la.LA_BF16, None, v(dq) if dq else None, v(dk), v(dv),
-                                                  None, None, 0, None)
+    call = lambda dq, dk, dv, g=G_, gf=None, ds=None: la.lib.la_bwd(
+        v(Q_), v(K_), v(V_), v(g), lam, 1, 2, 128, 64, 64, la.LA_BF16, None, v(gf) if gf else None,
+        v(dq) if dq else None, v(dk), v(dv), v(ds) if ds else None, None, None, 0, None)
     assert call(None, S_, W_) == la.LA_EINVAL          # dQ missing
     assert call(O_, O_, W_) == la.LA_EINVAL            # dQ and dK alias
     assert call(O_, S_, V_) == la.LA_EINVAL            # dV aliases V
     assert call(O_ + 2, S_, W_) == la.LA_EALIGN
     assert call(O_, S_, W_, g=None) == la.LA_EINVAL    # dO missing
+    X_ = A * 11
+    assert call(O_, S_, W_, gf=X_ + 4) == la.LA_EALIGN  # dkv_out misaligned
+    assert call(O_, S_, W_, ds=X_ + 4) == la.LA_EALIGN  # dkv_in misaligned
+    assert call(O_, S_, W_, ds=Q_) == la.LA_EINVAL      # dkv_in aliases Q
+    assert call(O_, S_, W_, ds=O_ + 1024) == la.LA_EINVAL  # dkv_in inside dQ
+    assert call(O_, S_, W_, gf=X_, ds=X_) == la.LA_EINVAL  # dkv_in aliases dkv_out
 
 
 def test_bwd_forward_workspace_checked():
@@ -124,8 +130,8 @@ def test_bwd_forward_workspace_checked():
     N = 4096  # one long sequence: split into chunks
     assert la.la_fwd_workspace_bytes(1, 1, N, 128, 64, la.LA_BF16) > 0
     call = lambda fws, ws=WB_: la.lib.la_bwd(v(Q_), v(K_), v(V_), v(G_), lam1, 1, 1, N, 128, 64, la.LA_BF16,
-                                             None, v(O_), v(X_), v(Y_), v(fws) if fws else None, v(ws),
-                                             1 << 40, None)
+                                             None, None, v(O_), v(X_), v(Y_), None, v(fws) if fws else None,
+                                             v(ws), 1 << 40, None)
     assert call(WB_ + 8) == la.LA_EALIGN
     assert call(WB_ + 4096) == la.LA_EINVAL            # inside the backward's own workspace
     assert call(X_) == la.LA_EINVAL                    # aliases dK

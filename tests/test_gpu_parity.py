@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import bar, got, host_f64, inputs, lam_pairs, state_input, to_dev
+from helpers import BF16_BAR, bar, got, host_f64, inputs, lam_pairs, state_input, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -282,6 +282,72 @@ def test_backward_with_forward_chunk_states(kern, N, cks, with_state, kernel, ch
     chunks(cks)
     lam = synth.decay_schedule(3)
     check_bwd(1, 3, N, 128, 64, "bf16", lam, seed=N + 7 * cks, with_state=with_state, label=kern, fwd_ws=True)
+
+
+def check_state_grads(B, H, N, Bk, lam, seed, with_state, with_gf, label=""):
+    """dQ, dK, dV and the initial-state gradient against the oracle, with an optional
+    gradient arriving at the final state."""
+    D = 128
+    print(f"[bwd-state] {label} B={B} H={H} N={N} Bk={Bk} kv_in={with_state} dkv_out={with_gf}", flush=True)
+    _, (q, k, v, g), (qh, kh, vh, gh) = inputs(seed, B, H, N, D, "bf16", with_do=True)
+    s0 = state_input(seed, B, H, D) if with_state else None
+    gf = state_input(seed + 1000, B, H, D) if with_gf else None
+    kv_in = torch.from_numpy(s0).cuda() if with_state else None
+    dkv_out = torch.from_numpy(gf).cuda() if with_gf else None
+    dq, dk, dv, ds0 = la.la_bwd(q, k, v, g, lam, Bk=Bk, kv_in=kv_in, dkv_out=dkv_out, want_dkv_in=True)
+    _sync()
+    refs = oracle.bwd_recurrent(qh, kh, vh, gh, lam_pairs(lam, B),
+                                None if s0 is None else s0.astype(np.float64),
+                                g_final=None if gf is None else gf.astype(np.float64), want_ds_init=True)
+    errs = [oracle.rel_l2(got(x), r) for x, r in zip((dq, dk, dv, ds0), refs)]
+    print(f"    rel-L2 dQ={errs[0]:.3e} dK={errs[1]:.3e} dV={errs[2]:.3e} dS0={errs[3]:.3e}", flush=True)
+    assert max(errs) <= BF16_BAR
+
+
+@pytest.mark.parametrize("variant", ["v1", "dma4", "dma8", "generic"])
+@pytest.mark.parametrize("N,cks,with_state,with_gf", [(64 * 13 + 5, 3, True, True), (64 * 7, 1, False, True),
+                                                     (1000, 2, True, False), (300, 7, False, True)])
+def test_backward_state_gradients(variant, N, cks, with_state, with_gf, fwd_variant, kernel, chunks):
+    """The gradient arriving at the final state (dkv_out) and the initial-state gradient
+    (dkv_in) in every reverse kernel, chunked and not, ragged, with and without kv_in."""
+    if variant == "generic":
+        fwd_variant("dma8")
+        kernel("generic")
+    else:
+        fwd_variant(variant)
+        kernel("default")
+    chunks(cks)
+    lam = synth.decay_schedule(3)
+    check_state_grads(1, 3, N, 64, lam, seed=N + 3 * cks, with_state=with_state, with_gf=with_gf, label=variant)
+
+
+@pytest.mark.parametrize("kern", ["generic", "default"])
+@pytest.mark.parametrize("N,cks", [(100, 1), (100, 2), (150, 3), (64, 1)])
+def test_final_state_gradient_probe_bit_exact(kern, N, cks, kernel, chunks):
+    """Only a final-state gradient F = e_0 e_c^T, with k = e_0 and v = e_c at every token and
+    q = dO = 0, lam = 1/2: dK_j = 2^-(N-1-j) e_0 and dV_j = 2^-(N-1-j) e_c exactly (for
+    N-1-j <= 100), and the initial-state gradient is 2^-N F; this pins where F enters and
+    its decay across block and chunk boundaries bit for bit."""
+    kernel(kern)
+    chunks(cks)
+    D, c = 128, 7
+    print(f"[probe dkv_out] kern={kern} N={N} chunks={cks}", flush=True)
+    zero = np.zeros((1, 1, N, D), np.float32)
+    kk = zero.copy(); kk[..., 0] = 1.0
+    vv = zero.copy(); vv[..., c] = 1.0
+    q, k, v, g = (to_dev(synth.f32_to_bf16_bits(x), "bf16") for x in (zero, kk, vv, zero))
+    F = np.zeros((1, 1, D, D), np.float32); F[0, 0, 0, c] = 1.0
+    dq, dk, dv, ds0 = la.la_bwd(q, k, v, g, [0.5], Bk=64, dkv_out=torch.from_numpy(F).cuda(), want_dkv_in=True)
+    _sync()
+    rel = N - 1 - np.arange(N)
+    keep = rel <= 100
+    e_k = np.zeros((N, D)); e_k[:, 0] = 0.5 ** rel
+    e_v = np.zeros((N, D)); e_v[:, c] = 0.5 ** rel
+    np.testing.assert_array_equal(got(dk)[0, 0][keep], e_k[keep])
+    np.testing.assert_array_equal(got(dv)[0, 0][keep], e_v[keep])
+    assert not np.any(got(dq))
+    if N <= 120:
+        np.testing.assert_array_equal(got(ds0)[0, 0], 0.5 ** N * F[0, 0].astype(np.float64))
 
 
 @pytest.mark.parametrize("variant", ["v1", "dma4", "dma8"])
