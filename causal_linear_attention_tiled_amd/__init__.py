@@ -50,6 +50,13 @@ def _load():
     lib.la_bwd_workspace_bytes.restype = sz
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i32, vp, vp]
     lib.la_decode_step.restype = ctypes.c_int
+    ip = ctypes.POINTER(ctypes.c_int64)
+    lib.la_fwd_varlen.argtypes = [vp, vp, vp, fp, ip, i64, i64, i64, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.la_fwd_varlen.restype = ctypes.c_int
+    lib.la_fwd_varlen_workspace_bytes.argtypes = [ip, i64, i64, i64, i32, i32]
+    lib.la_fwd_varlen_workspace_bytes.restype = sz
+    lib.la_decode_step_paged.argtypes = [vp, i64, vp, vp, vp, vp, fp, i64, i64, i64, i32, vp, vp]
+    lib.la_decode_step_paged.restype = ctypes.c_int
     lib.la_strerror.argtypes = [ctypes.c_int]
     lib.la_strerror.restype = ctypes.c_char_p
     lib.la_version.restype = ctypes.c_int
@@ -61,6 +68,7 @@ def _load():
 lib = _load()
 
 EXPORTS = ("la_fwd", "la_fwd_workspace_bytes", "la_bwd", "la_bwd_workspace_bytes", "la_decode_step",
+           "la_fwd_varlen", "la_fwd_varlen_workspace_bytes", "la_decode_step_paged",
            "la_strerror", "la_version", "la_prof_enable", "la_prof_collect")
 
 
@@ -191,6 +199,64 @@ def la_bwd(q, k, v, dout, lam, Bk: int = 64, kv_in=None, dq=None, dk=None, dv=No
     if dkv_in is not None:
         return dq, dk, dv, dkv_in
     return dq, dk, dv
+
+
+def _offsets(seq_offsets):
+    arr = (ctypes.c_int64 * len(seq_offsets))(*[int(x) for x in seq_offsets])
+    return arr, len(seq_offsets) - 1
+
+
+def la_fwd_varlen_workspace_bytes(seq_offsets, H, D, Bk, dtype_code) -> int:
+    arr, B = _offsets(seq_offsets)
+    return int(lib.la_fwd_varlen_workspace_bytes(arr, B, H, D, Bk, dtype_code))
+
+
+def la_fwd_varlen(q, k, v, lam, seq_offsets, Bk: int = 64, kv_in=None, out=None, kv_out=None,
+                  want_state: bool = True, ws=None):
+    """Forward over a ragged batch packed token-major: q, k, v [T, H, D] bf16, sequence b is
+    rows seq_offsets[b] .. seq_offsets[b+1].  Returns (O [T, H, D], kv_out [B, H, D, D])."""
+    for name, t in (("Q", q), ("K", k), ("V", v)):
+        if t.dim() != 3 or not t.is_contiguous() or (t is not q and (t.shape != q.shape or t.dtype != q.dtype)):
+            raise ValueError(f"{name} must be a contiguous [T, H, D] tensor matching Q")
+    T, H, D = q.shape
+    arr, B = _offsets(seq_offsets)
+    if arr[B] != T:
+        raise ValueError("seq_offsets[-1] must equal the packed token count")
+    out = torch.empty_like(q) if out is None else out
+    if kv_out is None and want_state:
+        kv_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    _check_state("kv_in", kv_in, B, H, D, q.device)
+    _check_state("kv_out", kv_out, B, H, D, q.device)
+    code = _dtype_code(q)
+    nbytes = int(lib.la_fwd_varlen_workspace_bytes(arr, B, H, D, Bk, code))
+    ws = _workspace(nbytes, q.device, ws)
+    rc = lib.la_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _lam_array(lam, H), arr, B, H, D, Bk, code, _ptr(kv_in),
+                           _ptr(out), _ptr(kv_out), _ptr(ws), nbytes if ws is not None else 0, _stream(q.device))
+    if rc != LA_OK:
+        raise LaError(rc, "la_fwd_varlen")
+    return out, kv_out
+
+
+def la_decode_step_paged(pool, slot_of, q, k, v, lam, out=None):
+    """One recurrent step for Bs sequences whose float32 states live in ``pool``
+    [P, H, D, D] at slots ``slot_of`` (int32 [Bs], distinct); q, k, v [Bs, H, D].  Returns o."""
+    if pool.dtype != torch.float32 or pool.dim() != 4 or not pool.is_contiguous():
+        raise ValueError("pool must be a contiguous float32 [P, H, D, D] tensor")
+    if slot_of.dtype != torch.int32 or slot_of.dim() != 1 or not slot_of.is_contiguous():
+        raise ValueError("slot_of must be a contiguous int32 [Bs] tensor")
+    P, H, D, _ = pool.shape
+    Bs = q.shape[0]
+    if slot_of.shape[0] != Bs:
+        raise ValueError("slot_of needs one slot per sequence")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if tuple(t.shape) != (Bs, H, D) or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a contiguous [Bs, H, D] tensor")
+    out = torch.empty_like(q) if out is None else out
+    rc = lib.la_decode_step_paged(_ptr(pool), P, _ptr(slot_of), _ptr(q), _ptr(k), _ptr(v), _lam_array(lam, H),
+                                  Bs, H, D, _dtype_code(q), _ptr(out), _stream(q.device))
+    if rc != LA_OK:
+        raise LaError(rc, "la_decode_step_paged")
+    return out
 
 
 def la_decode_step(state, q, k, v, lam, out=None):

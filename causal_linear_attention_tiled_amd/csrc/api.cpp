@@ -206,6 +206,49 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
     return launch(tag[0] == 'd' ? "dq_generic" : "fwd_generic", s, [&] { la::launch_fwd_generic(a, lam, bf16, s); });
 }
 
+// ------------------------------------------------------------------ ragged batches
+struct VarPlan {
+    la::VarlenArgs v;
+    int64_t T;               // tokens in the batch
+    int64_t L;               // chunk length (multiple of Bk), the same for every sequence
+    int64_t slots_per_head;  // sum over sequences of (chunks - 1)
+};
+
+// Validates the host offsets and builds the plan.  One chunk length for the
+// whole batch, chosen so that (chunks over the batch) x H reaches the
+// workgroup target; LA_VARLEN_L (a positive multiple of Bk) forces it.
+int make_varplan(const int64_t* offs, int64_t B, int64_t H, int64_t D, int32_t Bk, VarPlan* p) {
+    if (!offs || B <= 0 || H <= 0 || D <= 0) return LA_EINVAL;
+    if (B > la::kMaxVarlenSeqs || H > la::kMaxHeads) return LA_EUNSUPPORTED;
+    if (offs[0] != 0) return LA_EINVAL;
+    for (int64_t b = 0; b < B; ++b)
+        if (offs[b + 1] < offs[b]) return LA_EINVAL;
+    const int64_t T = offs[B];
+    // 32-bit buffer offsets: every element offset of one (sequence, head) stays below 2^31 bytes
+    if (T >= (int64_t(1) << 31) / (H * D * 2)) return LA_EUNSUPPORTED;
+    int64_t L = std::max<int64_t>(kMinBlocksPerChunk * Bk, (T * H + kTargetWorkgroups - 1) / kTargetWorkgroups);
+    const char* env = std::getenv("LA_VARLEN_L");
+    if (env && std::atoll(env) > 0) L = std::atoll(env);
+    L = (L + Bk - 1) / Bk * Bk;
+    p->T = T;
+    p->L = L;
+    p->v.nseq = static_cast<int>(B);
+    p->v.wp[0] = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t n = offs[b + 1] - offs[b];
+        const int64_t C = std::max<int64_t>(1, (n + L - 1) / L);
+        p->v.cu[b] = static_cast<int>(offs[b]);
+        p->v.wp[b + 1] = p->v.wp[b] + static_cast<int>(C);
+    }
+    p->v.cu[B] = static_cast<int>(T);
+    p->slots_per_head = p->v.wp[B] - B;
+    return LA_OK;
+}
+
+size_t varlen_slot_bytes(const VarPlan& p, int64_t H, int64_t D) {
+    return static_cast<size_t>(p.slots_per_head * H) * static_cast<size_t>(D * D) * sizeof(float);
+}
+
 }  // namespace
 
 // ====================================================================== ABI
@@ -361,6 +404,96 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     return launch("dkdv_generic", s, [&] { la::launch_rev_generic(a, lam, bf16, s); });
 }
 
+size_t la_fwd_varlen_workspace_bytes(const int64_t* seq_offsets, int64_t B, int64_t H, int64_t D, int32_t Bk,
+                                     int32_t dtype) {
+    if (dtype != LA_BF16 || D != 128 || Bk != 64) return 0;
+    VarPlan p;
+    if (make_varplan(seq_offsets, B, H, D, Bk, &p) != LA_OK) return 0;
+    return varlen_slot_bytes(p, H, D);
+}
+
+int la_fwd_varlen(const void* Q, const void* K, const void* V, const float* lambda, const int64_t* seq_offsets,
+                  int64_t B, int64_t H, int64_t D, int32_t Bk, int32_t dtype, const float* kv_in, void* O,
+                  float* kv_out, void* ws, size_t ws_bytes, void* hip_stream) {
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_EINVAL;
+    VarPlan p;
+    int rc = make_varplan(seq_offsets, B, H, D, Bk, &p);
+    if (rc) return rc;
+    if (dtype != LA_BF16 || D != 128 || Bk != 64) return LA_EUNSUPPORTED;
+    if (p.T > 0 && (!Q || !K || !V || !O)) return LA_EINVAL;
+    LamArgs lam;
+    if ((rc = load_lambda(lambda, H, &lam))) return rc;
+    for (const void* ptr : {Q, K, V, static_cast<const void*>(O), static_cast<const void*>(kv_in),
+                            static_cast<const void*>(kv_out), static_cast<const void*>(ws)})
+        if (ptr && !aligned16(ptr)) return LA_EALIGN;
+    const size_t tb = static_cast<size_t>(p.T * H * D) * 2;
+    const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
+    const size_t need = varlen_slot_bytes(p, H, D);
+    if (need && (!ws || ws_bytes < need)) return LA_EWORKSPACE;
+    const Range rq{Q, tb}, rk{K, tb}, rv{V, tb}, ro{O, tb}, rin{kv_in, kv_in ? sb : 0},
+        rout{kv_out, kv_out ? sb : 0}, rws{ws, need};
+    for (const Range& r : {rq, rk, rv, rin})
+        if (overlap(ro, r) || overlap(rout, r) || overlap(rws, r)) return LA_EINVAL;
+    if (overlap(ro, rout) || overlap(ro, rws) || overlap(rout, rws)) return LA_EINVAL;
+
+    int dev_count = 0;
+    if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count == 0) return LA_ENODEV;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const int32_t Hi = static_cast<int32_t>(H);
+    float* slots = static_cast<float*>(ws);
+    if (p.slots_per_head > 0) {
+        la::ChunkStateArgs cs{K, V, slots, 0, p.L, static_cast<int>(D), Bk, Hi, 0, 0, 0};
+        rc = launch("chunk_state_varlen_dma", s, [&] { la::launch_chunk_state_dma_varlen(cs, lam, p.v, s); });
+        if (rc) return rc;
+        la::ScanArgs sc{slots, kv_in, 0, nullptr, 0, p.L, static_cast<int>(D), Hi, 0, 0, 0};
+        rc = launch("state_scan_varlen", s, [&] { la::launch_scan_varlen(sc, lam, p.v, s); });
+        if (rc) return rc;
+    }
+    la::SweepArgs a{};
+    a.a = Q;
+    a.b = K;
+    a.c = V;
+    a.out0 = O;
+    a.slots = slots;
+    a.kv_in = kv_in;
+    a.kv_out = kv_out;
+    a.L = p.L;
+    a.D = static_cast<int>(D);
+    a.Bk = Bk;
+    a.H = Hi;
+    return launch("fwd_varlen_dma", s, [&] { la::launch_fwd_dma_varlen(a, lam, p.v, s); });
+}
+
+int la_decode_step_paged(float* pool, int64_t pool_slots, const int32_t* slot_of, const void* q, const void* k,
+                         const void* v, const float* lambda, int64_t Bs, int64_t H, int64_t D, int32_t dtype,
+                         void* o, void* hip_stream) {
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_EINVAL;
+    if (Bs <= 0 || H <= 0 || D <= 0 || pool_slots <= 0) return LA_EINVAL;
+    if (!supported_D(D) || H > la::kMaxHeads) return LA_EUNSUPPORTED;
+    if (!pool || !slot_of || !q || !k || !v || !o) return LA_EINVAL;
+    LamArgs lam;
+    int rc = load_lambda(lambda, H, &lam);
+    if (rc) return rc;
+    for (const void* ptr : {static_cast<const void*>(pool), static_cast<const void*>(slot_of), q, k, v,
+                            static_cast<const void*>(o)})
+        if (!aligned16(ptr)) return LA_EALIGN;
+    int64_t pairs, pool_pairs;
+    if (!mul_ok(Bs, H, &pairs) || pairs > (int64_t(1) << 31)) return LA_EINVAL;
+    if (!mul_ok(pool_slots, H, &pool_pairs) || pool_pairs > (int64_t(1) << 31)) return LA_EINVAL;
+    const size_t vb = static_cast<size_t>(pairs * D) * (dtype == LA_BF16 ? 2 : 4);
+    const size_t pb = static_cast<size_t>(pool_pairs * D * D) * sizeof(float);
+    const Range rp{pool, pb}, ro{o, vb}, ridx{slot_of, static_cast<size_t>(Bs) * sizeof(int32_t)};
+    for (const Range& r : {Range{q, vb}, Range{k, vb}, Range{v, vb}, ridx})
+        if (overlap(rp, r) || overlap(ro, r)) return LA_EINVAL;
+    if (overlap(rp, ro)) return LA_EINVAL;
+
+    int dev_count = 0;
+    if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count == 0) return LA_ENODEV;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    la::DecodeArgs a{pool, q, k, v, o, static_cast<int>(D), static_cast<int>(H), pairs, slot_of, pool_slots};
+    return launch("decode_paged", s, [&] { la::launch_decode(a, lam, dtype == LA_BF16, s); });
+}
+
 int la_decode_step(float* state, const void* q, const void* k, const void* v, const float* lambda,
                    int64_t Bs, int64_t H, int64_t D, int32_t dtype, void* o, void* hip_stream) {
     if (dtype != LA_F32 && dtype != LA_BF16) return LA_EINVAL;
@@ -384,7 +517,7 @@ int la_decode_step(float* state, const void* q, const void* k, const void* v, co
     int dev_count = 0;
     if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count == 0) return LA_ENODEV;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    la::DecodeArgs a{state, q, k, v, o, static_cast<int>(D), static_cast<int>(H), pairs};
+    la::DecodeArgs a{state, q, k, v, o, static_cast<int>(D), static_cast<int>(H), pairs, nullptr, 0};
     return launch("decode", s, [&] { la::launch_decode(a, lam, dtype == LA_BF16, s); });
 }
 

@@ -50,25 +50,26 @@ struct DmaTiles {
     float pw[BK + 1];
 };
 
-template <int NW>
-__global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamArgs lam) {
+template <int NW, bool VARLEN>
+__device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam, const VarlenArgs* var) {
     constexpr int NVT = 8 / NW;  // 16-column value tiles per compute wave
     __shared__ DmaTiles sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
-    const int64_t pair = blockIdx.x / a.chunks;
-    const int c = blockIdx.x % a.chunks;
-    const float lv = lam.lam[pair % a.H];
-    const int64_t t_begin = static_cast<int64_t>(c) * a.L;
-    const int64_t t_end = min(a.N, t_begin + a.L);
+    const Work wk = work_item<VARLEN>(a, var, blockIdx.x);
+    const int c = wk.c;
+    const float lv = lam.lam[wk.head];
+    const int64_t t_begin = wk.t_begin, t_end = wk.t_end;
     const int64_t nblk = (t_end - t_begin + BK - 1) / BK;
-    const int64_t base = pair * a.N * D;
+    const int64_t base = wk.base;
+    const int64_t ld = VARLEN ? wk.ld : D;  // elements between token rows
 
     for (int e = tid; e <= BK; e += 64 * (NW + 1)) sm.pw[e] = lam_pow(lv, e);
     __syncthreads();  // decay table; every wave passes exactly 1 + 2 * nblk barriers
 
     if (w == NW) {
         // ------------------------------------------------------------ loader wave
-        const int bytes = static_cast<int>(a.N * D * 2);
+        // loads at or past the sequence's last row come back as zero
+        const int bytes = wk.n > 0 ? static_cast<int>(((wk.n - 1) * ld + D) * 2) : 0;
         __amdgpu_buffer_rsrc_t rs[3];
         rs[0] = __builtin_amdgcn_make_buffer_rsrc((void*)(static_cast<const uint16_t*>(a.a) + base), 0, bytes, 0x00020000);
         rs[1] = __builtin_amdgcn_make_buffer_rsrc((void*)(static_cast<const uint16_t*>(a.b) + base), 0, bytes, 0x00020000);
@@ -83,11 +84,11 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
                 for (int rg = 0; rg < BK / 4; ++rg) {
                     const int r = 4 * rg + sub;
                     const int chunk = p ^ swz_key(r);
-                    const int voff = static_cast<int>(((t0 + r) * D + 8 * chunk) * 2);
+                    const int voff = static_cast<int>(((t0 + r) * ld + 8 * chunk) * 2);
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[x], (lds_void*)&sm.t[stage][x][4 * rg * D], 16, voff, 0, 0, 0);
                 }
         };
-        issue(0);
+        if (nblk > 0) issue(0);
         if (nblk > 1) issue(1);
         // The loader's own vmcnt wait makes its LDS writes complete before it
         // reaches A(n); a fenced __syncthreads() here would also wait for the
@@ -113,11 +114,11 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
         bool tr = false;
         if (c == 0) {
             if (a.kv_in) {
-                init = a.kv_in + pair * D * D;
+                init = a.kv_in + wk.state * D * D;
                 tr = a.kv_in_transposed != 0;
             }
         } else {
-            init = a.slots + (pair * (a.chunks - 1) + (c - 1)) * D * D;
+            init = a.slots + (wk.slot0 + static_cast<int64_t>(c - 1) * wk.slot_step) * D * D;
             tr = a.slots_transposed != 0;
         }
 #pragma unroll
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
             if (s < m) {
 #pragma unroll
                 for (int vt = 0; vt < NVT; ++vt) {
-                    uint16_t* dst = Og + (t0 + s) * D + 16 * (NVT * w + vt) + 4 * g;
+                    uint16_t* dst = Og + (t0 + s) * ld + 16 * (NVT * w + vt) + 4 * g;
                     *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16(o[vt][0], o[vt][1]), pack_bf16(o[vt][2], o[vt][3])};
                 }
             }
@@ -252,8 +253,8 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
         }
     }
 
-    if (a.kv_out && c == a.chunks - 1) {
-        float* dst = a.kv_out + pair * D * D;
+    if (a.kv_out && c == wk.chunks - 1) {
+        float* dst = a.kv_out + wk.state * D * D;
 #pragma unroll
         for (int at = 0; at < 8; ++at)
 #pragma unroll
@@ -264,10 +265,24 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
     }
 }
 
+template <int NW>
+__global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamArgs lam) {
+    fwd_body<NW, false>(a, lam, nullptr);
+}
+
+__global__ __launch_bounds__(64 * 5, 1) void k_fwd_dma_varlen(SweepArgs a, LamArgs lam, VarlenArgs v) {
+    fwd_body<4, true>(a, lam, &v);
+}
+
 }  // namespace
 
 bool fwd_dma_supported(int d, int bk, int64_t n) {
     return d == 128 && bk == 64 && n * d * 2 < (int64_t(1) << 31);
+}
+
+void launch_fwd_dma_varlen(const SweepArgs& a, const LamArgs& lam, const VarlenArgs& v, hipStream_t s) {
+    dim3 grid(static_cast<unsigned>(static_cast<int64_t>(v.wp[v.nseq]) * a.H));
+    hipLaunchKernelGGL(k_fwd_dma_varlen, grid, dim3(64 * 5), 0, s, a, lam, v);
 }
 
 void launch_fwd_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream_t s) {

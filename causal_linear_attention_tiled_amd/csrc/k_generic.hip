@@ -244,6 +244,26 @@ __global__ __launch_bounds__(kThreads) void k_scan(ScanArgs a, LamArgs lam) {
     }
 }
 
+// Forward scan over the chunk states of a ragged batch: per (sequence b, head h),
+// S = kv_in[b][h] (or 0); for c = 0 .. chunks_b - 2: S = lam^L S + slot; slot = S,
+// with slot (wp[b] - b + c) * H + h.
+__global__ __launch_bounds__(kThreads) void k_scan_varlen(ScanArgs a, LamArgs lam, VarlenArgs v) {
+    const int DD = a.D * a.D;
+    const int per_pair = (DD + kThreads - 1) / kThreads;
+    const int64_t pair = blockIdx.x / per_pair;  // b * H + h
+    const int e = (blockIdx.x % per_pair) * kThreads + threadIdx.x;
+    if (e >= DD) return;
+    const int b = static_cast<int>(pair / a.H), h = static_cast<int>(pair % a.H);
+    const float lamL = lam_pow(lam.lam[h], a.L);
+    const int n_slots = v.wp[b + 1] - v.wp[b] - 1;
+    float S = a.kv_in ? a.kv_in[pair * DD + e] : 0.f;
+    for (int c = 0; c < n_slots; ++c) {
+        float* sl = a.slots + (static_cast<int64_t>(v.wp[b] - b + c) * a.H + h) * DD + e;
+        S = lamL * S + *sl;
+        *sl = S;
+    }
+}
+
 // One recurrent step per (sequence, head): S <- lam S + k v^T, o = q S.
 // Thread t owns the 4 columns 4 * (t % (D/4)) .. +3 of rows t / (D/4) + r * (1024/D).
 template <bool BF16>
@@ -253,6 +273,16 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a, LamArgs lam) 
     const int64_t pair = blockIdx.x;
     const int D = a.D, tid = threadIdx.x;
     const float lv = lam.lam[pair % a.H];
+    int64_t sp = pair;  // the state this (sequence, head) steps
+    if (a.slot_of) {
+        const int32_t slot = a.slot_of[pair / a.H];
+        if (slot < 0 || slot >= a.pool_slots) {
+            // an index outside the pool: no state is touched and the output row is NaN
+            for (int i = tid; i < D; i += kThreads) st<BF16>(a.o, pair * D + i, __builtin_nanf(""));
+            return;
+        }
+        sp = static_cast<int64_t>(slot) * a.H + pair % a.H;
+    }
     for (int i = tid; i < D; i += kThreads) {
         qs[i] = ld<BF16>(a.q, pair * D + i);
         ks[i] = ld<BF16>(a.k, pair * D + i);
@@ -262,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a, LamArgs lam) 
     const int cols4 = D / 4;
     const int cg = tid % cols4;
     const int rstep = kThreads / cols4;
-    float4* S = reinterpret_cast<float4*>(a.state + pair * D * D);
+    float4* S = reinterpret_cast<float4*>(a.state + sp * D * D);
     const float4 vv = make_float4(vs[4 * cg], vs[4 * cg + 1], vs[4 * cg + 2], vs[4 * cg + 3]);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int r = tid / cols4; r < D; r += rstep) {
@@ -315,6 +345,12 @@ void launch_chunk_state_generic(const ChunkStateArgs& a, const LamArgs& lam, int
         hipLaunchKernelGGL(k_chunk_state_generic<true>, grid, dim3(kThreads), 0, s, a, lam);
     else
         hipLaunchKernelGGL(k_chunk_state_generic<false>, grid, dim3(kThreads), 0, s, a, lam);
+}
+
+void launch_scan_varlen(const ScanArgs& a, const LamArgs& lam, const VarlenArgs& v, hipStream_t s) {
+    const int per_pair = (a.D * a.D + kThreads - 1) / kThreads;
+    dim3 grid(static_cast<unsigned>(static_cast<int64_t>(v.nseq) * a.H * per_pair));
+    hipLaunchKernelGGL(k_scan_varlen, grid, dim3(kThreads), 0, s, a, lam, v);
 }
 
 void launch_scan(const ScanArgs& a, const LamArgs& lam, hipStream_t s) {

@@ -38,23 +38,44 @@ struct StateTiles {
     float pw[BK + 1];
 };
 
-__global__ __launch_bounds__(64 * NW, 1) void k_chunk_state_dma(ChunkStateArgs a, LamArgs lam) {
+template <bool VARLEN>
+__device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArgs& lam, const VarlenArgs* var) {
     __shared__ StateTiles sm;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int per = a.chunks - 1;
-    const int64_t pair = blockIdx.x / per;
-    const int slot = blockIdx.x % per;
-    const int c = a.reverse ? slot + 1 : slot;
+    // this workgroup's chunk: c of (sequence, head), its token range and its slot
+    int64_t base, ld, n_seq, dst_slot;
+    int c, head;
+    if constexpr (!VARLEN) {
+        const int per = a.chunks - 1;
+        const int64_t pair = blockIdx.x / per;
+        const int slot = blockIdx.x % per;
+        c = a.reverse ? slot + 1 : slot;
+        base = pair * a.N * D;
+        ld = D;
+        n_seq = a.N;
+        head = static_cast<int>(pair % a.H);
+        dst_slot = pair * per + slot;
+    } else {
+        // forward only: slot s (per head) of sequence b with wp[b] - b <= s < wp[b+1] - b - 1
+        head = static_cast<int>(blockIdx.x % a.H);
+        const int s = static_cast<int>(blockIdx.x / a.H);
+        const int b = find_last_le(var->nseq, s, [&](int i) { return var->wp[i] - i; });
+        c = s - (var->wp[b] - b);
+        base = (static_cast<int64_t>(var->cu[b]) * a.H + head) * D;
+        ld = static_cast<int64_t>(a.H) * D;
+        n_seq = var->cu[b + 1] - var->cu[b];
+        dst_slot = static_cast<int64_t>(s) * a.H + head;
+    }
     const int64_t t_begin = static_cast<int64_t>(c) * a.L;
-    const int64_t t_end = min(a.N, t_begin + a.L);
+    const int64_t t_end = min(n_seq, t_begin + a.L);
     const int64_t nblk = (t_end - t_begin + BK - 1) / BK;
-    const int64_t base = pair * a.N * D;
-    const float lv = lam.lam[pair % a.H];
+    const float lv = lam.lam[head];
     for (int e = tid; e <= BK; e += 64 * NW) sm.pw[e] = lam_pow(lv, e);
     const double lam_bk = lam_pow64(lv, BK);
 
-    const uint32_t bytes = static_cast<uint32_t>(a.N * D * 2);
+    // loads at or past the sequence's last row come back as zero
+    const uint32_t bytes = static_cast<uint32_t>(((n_seq - 1) * ld + D) * 2);
     const u32x4 rx = buffer_rsrc(static_cast<const uint16_t*>(a.x) + base, bytes);
     const u32x4 ry = buffer_rsrc(static_cast<const uint16_t*>(a.y) + base, bytes);
     // The n-th block of the walk goes to stage n % 3; wave w issues, for each
@@ -70,7 +91,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_chunk_state_dma(ChunkStateArgs a
             for (int i = 0; i < LOADS_PER_WAVE / 2; ++i) {
                 const int rg = w + NW * i;
                 const int r = 4 * rg + sub;
-                const int voff = static_cast<int>(((t0 + r) * D + 8 * (p ^ swz_key(r))) * 2);
+                const int voff = static_cast<int>(((t0 + r) * ld + 8 * (p ^ swz_key(r))) * 2);
                 dma16(x == 0 ? rx : ry, &sm.t[stage][x][4 * rg * D], voff);
             }
     };
@@ -114,11 +135,19 @@ __global__ __launch_bounds__(64 * NW, 1) void k_chunk_state_dma(ChunkStateArgs a
             for (int kb = 0; kb < NKB; ++kb) S[at] = mfma16(op_tr_k(Xs, 32 * kb, 16 * at, 4, g, li), yf[kb], S[at]);
         cw *= (m == BK) ? lam_bk : lam_pow64(lv, m);
     }
-    float* dst = a.slots + (pair * per + slot) * D * D;
+    float* dst = a.slots + dst_slot * D * D;
 #pragma unroll
     for (int at = 0; at < 8; ++at)
 #pragma unroll
         for (int r = 0; r < 4; ++r) dst[(16 * at + 4 * g + r) * D + 16 * w + li] = S[at][r];
+}
+
+__global__ __launch_bounds__(64 * NW, 1) void k_chunk_state_dma(ChunkStateArgs a, LamArgs lam) {
+    state_body<false>(a, lam, nullptr);
+}
+
+__global__ __launch_bounds__(64 * NW, 1) void k_chunk_state_dma_varlen(ChunkStateArgs a, LamArgs lam, VarlenArgs v) {
+    state_body<true>(a, lam, &v);
 }
 
 }  // namespace
@@ -128,6 +157,12 @@ bool state_dma_supported(int d, int bk, int64_t n) { return d == 128 && bk == 64
 void launch_chunk_state_dma(const ChunkStateArgs& a, const LamArgs& lam, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(a.pairs * (a.chunks - 1)));
     hipLaunchKernelGGL(k_chunk_state_dma, grid, dim3(64 * NW), 0, s, a, lam);
+}
+
+void launch_chunk_state_dma_varlen(const ChunkStateArgs& a, const LamArgs& lam, const VarlenArgs& v,
+                                   hipStream_t s) {
+    dim3 grid(static_cast<unsigned>(static_cast<int64_t>(v.wp[v.nseq] - v.nseq) * a.H));
+    hipLaunchKernelGGL(k_chunk_state_dma_varlen, grid, dim3(64 * NW), 0, s, a, lam, v);
 }
 
 }  // namespace la

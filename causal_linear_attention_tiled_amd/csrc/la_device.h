@@ -57,4 +57,64 @@ __device__ __forceinline__ float masked_pw(const float* pw, int e, bool keep) {
     return keep ? v : 0.f;
 }
 
+// Largest b in [0, nseq) with key(b) <= x, for a nondecreasing key (a binary search
+// over kernel-argument values, uniform across the workgroup).
+template <typename Key>
+__device__ __forceinline__ int find_last_le(int nseq, int x, Key key) {
+    int lo = 0, hi = nseq - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (key(mid) <= x)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// What one workgroup of a sweep works on: chunk c of one (sequence, head).
+struct Work {
+    int64_t base;    // element offset of the sequence's token 0
+    int64_t ld;      // elements from one token's row to the next
+    int64_t n;       // tokens in the sequence
+    int64_t t_begin, t_end;
+    int64_t state;   // index of the sequence's D x D initial / final state
+    int64_t slot0;   // slot of the state entering chunk 1; chunk c's is slot0 + (c - 1) * step
+    int c, chunks, slot_step, head;
+};
+
+// Dense [P][N][D] problems (pair = blockIdx / chunks) or a ragged batch (VarlenArgs).
+template <bool VARLEN, typename SA, typename VA>
+__device__ __forceinline__ Work work_item(const SA& a, const VA* v, int64_t blk) {
+    Work w;
+    if constexpr (!VARLEN) {
+        const int64_t pair = blk / a.chunks;
+        w.c = static_cast<int>(blk % a.chunks);
+        w.chunks = a.chunks;
+        w.head = static_cast<int>(pair % a.H);
+        w.n = a.N;
+        w.base = pair * a.N * a.D;
+        w.ld = a.D;
+        w.state = pair;
+        w.slot0 = pair * (a.chunks - 1);
+        w.slot_step = 1;
+    } else {
+        const int h = static_cast<int>(blk % a.H);
+        const int wi = static_cast<int>(blk / a.H);
+        const int b = find_last_le(v->nseq, wi, [&](int i) { return v->wp[i]; });
+        w.c = wi - v->wp[b];
+        w.chunks = v->wp[b + 1] - v->wp[b];
+        w.head = h;
+        w.n = v->cu[b + 1] - v->cu[b];
+        w.base = (static_cast<int64_t>(v->cu[b]) * a.H + h) * a.D;
+        w.ld = static_cast<int64_t>(a.H) * a.D;
+        w.state = static_cast<int64_t>(b) * a.H + h;
+        w.slot0 = static_cast<int64_t>(v->wp[b] - b) * a.H + h;
+        w.slot_step = a.H;
+    }
+    w.t_begin = static_cast<int64_t>(w.c) * a.L;
+    w.t_end = min(w.n, w.t_begin + a.L);
+    return w;
+}
+
 }  // namespace la

@@ -15,6 +15,18 @@ struct LamArgs {
     float lam[kMaxHeads];
 };
 
+// A ragged batch (passed by value as a kernel argument, 2 KiB): sequence b covers
+// tokens [cu[b], cu[b+1]) of token-major [T][H][D] tensors, so the rows of one
+// (sequence, head) are H * D elements apart, and is split into wp[b+1] - wp[b]
+// chunks of L tokens (at least one, also for an empty sequence).  Sequence b's
+// chunk states are slots (wp[b] - b + c) * H + h, c = 0 .. chunks - 2.
+constexpr int kMaxVarlenSeqs = 256;
+struct VarlenArgs {
+    int nseq;
+    int cu[kMaxVarlenSeqs + 1];
+    int wp[kMaxVarlenSeqs + 1];
+};
+
 // One sweep over every (sequence, chunk) of a [P][N][D] problem.
 // Sequence p = b * H + h uses decay lam[h].  Chunk c covers tokens
 // [c * L, min(N, (c + 1) * L)); L is a multiple of Bk.
@@ -74,13 +86,15 @@ struct ScanArgs {
 };
 
 struct DecodeArgs {
-    float* state;  // [P][D][D]
+    float* state;  // [P][D][D], or the slot pool [pool_slots][H][D][D] when slot_of is set
     const void* q;
     const void* k;
     const void* v;
     void* o;
     int D, H;
-    int64_t pairs;
+    int64_t pairs;           // Bs * H
+    const int32_t* slot_of;  // [Bs] pool slot of each sequence, or nullptr (state[p] for pair p)
+    int64_t pool_slots;
 };
 
 // Launchers (each enqueues exactly one kernel on `s`; errors are read by the caller).
@@ -100,6 +114,8 @@ void launch_chunk_state_mfma(const ChunkStateArgs& a, const LamArgs& lam, hipStr
 // Forward sweep with direct-to-LDS loads (bf16, D = 128, Bk = 64); `waves` compute waves (4 or 8).
 bool fwd_dma_supported(int D, int Bk, int64_t N);
 void launch_fwd_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream_t s);
+// The same over a ragged batch: one workgroup per (chunk of a sequence, head), wp[nseq] * H in all.
+void launch_fwd_dma_varlen(const SweepArgs& a, const LamArgs& lam, const VarlenArgs& v, hipStream_t s);
 
 // Reverse (dK, dV) sweep with direct-to-LDS loads (bf16, D = 128, Bk = 64).
 bool rev_dma_supported(int D, int Bk, int64_t N);
@@ -108,5 +124,10 @@ void launch_rev_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream
 // Chunk aggregates with direct-to-LDS loads (bf16, D = 128, Bk = 64).
 bool state_dma_supported(int D, int Bk, int64_t N);
 void launch_chunk_state_dma(const ChunkStateArgs& a, const LamArgs& lam, hipStream_t s);
+// Forward chunk aggregates of a ragged batch: one workgroup per (slot, head).
+void launch_chunk_state_dma_varlen(const ChunkStateArgs& a, const LamArgs& lam, const VarlenArgs& v,
+                                   hipStream_t s);
+// Forward scan of a ragged batch's chunk states (ScanArgs.L is the chunk length).
+void launch_scan_varlen(const ScanArgs& a, const LamArgs& lam, const VarlenArgs& v, hipStream_t s);
 
 }  // namespace la

@@ -140,6 +140,47 @@ size_t la_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_
 int la_decode_step(float* state, const void* q, const void* k, const void* v, const float* lambda,
                    int64_t Bs, int64_t H, int64_t D, int32_t dtype, void* o, void* hip_stream);
 
+/* Forward pass over a ragged batch: B sequences of different lengths packed
+ * token-major in one launch (the serving-side prefill that the constant-size
+ * state makes cheap to continue, Lightning Attention-2 record, mechanism
+ * field; the same tiling and chunked prefix as la_fwd).  Sequence b holds
+ * tokens [seq_offsets[b], seq_offsets[b+1]) of the packed tensors.
+ *   Q, K, V, O  : [T][H][D] bf16 device (token-major, T = seq_offsets[B]);
+ *                 row t of head h is (t * H + h) * D.
+ *   seq_offsets : HOST int64[B + 1], seq_offsets[0] = 0, nondecreasing; read
+ *                 during the call only.  Empty sequences are allowed (their
+ *                 final state is kv_in, or 0).  1 <= B <= 256.
+ *   kv_in       : [B][H][D][D] float32 device, or NULL for zero.
+ *   kv_out      : [B][H][D][D] float32 device, or NULL to skip.
+ *   ws          : la_fwd_varlen_workspace_bytes(...) bytes of device memory.
+ * Supported: bf16, D = 128, Bk = 64, and T * H * D * 2 < 2^31 (otherwise
+ * LA_EUNSUPPORTED).  Each sequence's results equal la_fwd over that sequence
+ * alone, up to float rounding.  LA_VARLEN_L (a positive multiple of Bk)
+ * overrides the chunk length; a size query must see the same setting. */
+int la_fwd_varlen(const void* Q, const void* K, const void* V, const float* lambda,
+                  const int64_t* seq_offsets, int64_t B, int64_t H, int64_t D, int32_t Bk,
+                  int32_t dtype, const float* kv_in, void* O, float* kv_out, void* ws,
+                  size_t ws_bytes, void* hip_stream);
+
+/* Workspace bytes for la_fwd_varlen (0 when no sequence is split into chunks,
+ * or for unsupported or invalid arguments). */
+size_t la_fwd_varlen_workspace_bytes(const int64_t* seq_offsets, int64_t B, int64_t H, int64_t D,
+                                     int32_t Bk, int32_t dtype);
+
+/* One recurrent decode step for Bs sequences whose states live in a pool of
+ * slots (paged decode slots for serving; glossary page "Lightning Attention",
+ * features list: recurrent inference with a constant-size state).
+ *   pool    : [pool_slots][H][D][D] float32 device; sequence i steps the
+ *             states of slot slot_of[i], in place.
+ *   slot_of : [Bs] int32 device.  Entries must be distinct and in
+ *             [0, pool_slots); an entry outside that range leaves the pool
+ *             untouched and writes NaN to the sequence's output row (device
+ *             values cannot be checked before the launch).
+ *   q, k, v, o, lambda, dtype, D: as for la_decode_step ([Bs][H][D]). */
+int la_decode_step_paged(float* pool, int64_t pool_slots, const int32_t* slot_of, const void* q,
+                         const void* k, const void* v, const float* lambda, int64_t Bs, int64_t H,
+                         int64_t D, int32_t dtype, void* o, void* hip_stream);
+
 /* Static text for a status code.  For LA_EHIP the text of the last HIP error
  * seen by the calling thread is appended (thread-local buffer). */
 const char* la_strerror(int code);

@@ -166,3 +166,46 @@ def test_python_binding_checks_shapes():
         la.la_fwd(q, q, q[..., :8].contiguous(), [0.5, 0.5])
     with pytest.raises(ValueError):
         la.la_fwd(q, q, q, [0.5])
+
+
+def _offs(xs):
+    return (ctypes.c_int64 * len(xs))(*xs)
+
+
+def test_fwd_varlen_rejects():
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    lam = (ctypes.c_float * 2)(0.5, 0.9)
+
+    def call(offs, B=None, H=2, D=128, Bk=64, dt=la.LA_BF16, O=O_, ws=W_, ws_bytes=1 << 40, kv_out=None):
+        B = len(offs) - 1 if B is None else B
+        return la.lib.la_fwd_varlen(v(Q_), v(K_), v(V_), lam, _offs(offs), B, H, D, Bk, dt, None, v(O),
+                                    v(kv_out), v(ws), ws_bytes, None)
+    assert call([1, 5, 9]) == la.LA_EINVAL                    # offsets must start at 0
+    assert call([0, 9, 5]) == la.LA_EINVAL                    # and not decrease
+    assert call([0] * 258) == la.LA_EUNSUPPORTED              # more than 256 sequences
+    assert call([0, 64], dt=la.LA_F32) == la.LA_EUNSUPPORTED  # bf16 only
+    assert call([0, 64], D=64) == la.LA_EUNSUPPORTED
+    assert call([0, 64], Bk=128) == la.LA_EUNSUPPORTED
+    assert call([0, 64], O=Q_) == la.LA_EINVAL                # output aliases Q
+    assert call([0, 64], O=O_ + 8) == la.LA_EALIGN
+    assert call([0, 1 << 30]) == la.LA_EUNSUPPORTED           # 32-bit buffer offsets
+    big = [0, 100000]
+    need = la.la_fwd_varlen_workspace_bytes(big, 2, 128, 64, la.LA_BF16)
+    assert need > 0
+    assert call(big, ws=None, ws_bytes=0) == la.LA_EWORKSPACE
+    assert call(big, ws_bytes=need - 1) == la.LA_EWORKSPACE
+    assert la.la_fwd_varlen_workspace_bytes([0, 10, 20], 2, 128, 64, la.LA_BF16) == 0  # one chunk each
+
+
+def test_decode_paged_rejects():
+    v = ctypes.c_void_p
+    lam = (ctypes.c_float * 2)(0.5, 0.5)
+    IDX_ = A * 12
+    call = lambda pool=S_, P=8, idx=IDX_, o=O_, D=128: la.lib.la_decode_step_paged(
+        v(pool), P, v(idx) if idx else None, v(Q_), v(K_), v(V_), lam, 4, 2, D, la.LA_BF16, v(o), None)
+    assert call(P=0) == la.LA_EINVAL
+    assert call(idx=None) == la.LA_EINVAL
+    assert call(idx=IDX_ + 4) == la.LA_EALIGN
+    assert call(D=100) == la.LA_EUNSUPPORTED
+    assert call(o=S_ + 4096) == la.LA_EINVAL                  # output inside the pool
+    assert call(idx=S_ + 1024) == la.LA_EINVAL               # slot table inside the pool
