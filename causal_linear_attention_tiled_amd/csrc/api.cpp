@@ -215,8 +215,11 @@ struct VarPlan {
 };
 
 // Validates the host offsets and builds the plan.  One chunk length for the
-// whole batch, chosen so that (chunks over the batch) x H reaches the
-// workgroup target; LA_VARLEN_L (a positive multiple of Bk) forces it.
+// whole batch.  With the longest pieces of work dispatched first, a sequence up
+// to twice a compute unit's average share (T H / 256 tokens) is best left whole:
+// splitting it would add a chunk-aggregate pass whose few long workgroups cost
+// more than the imbalance.  Longer sequences are cut into chunks of that share.
+// LA_VARLEN_L (a positive multiple of Bk) forces the length.
 int make_varplan(const int64_t* offs, int64_t B, int64_t H, int64_t D, int32_t Bk, VarPlan* p) {
     if (!offs || B <= 0 || H <= 0 || D <= 0) return LA_EINVAL;
     if (B > la::kMaxVarlenSeqs || H > la::kMaxHeads) return LA_EUNSUPPORTED;
@@ -226,7 +229,11 @@ int make_varplan(const int64_t* offs, int64_t B, int64_t H, int64_t D, int32_t B
     const int64_t T = offs[B];
     // 32-bit buffer offsets: every element offset of one (sequence, head) stays below 2^31 bytes
     if (T >= (int64_t(1) << 31) / (H * D * 2)) return LA_EUNSUPPORTED;
-    int64_t L = std::max<int64_t>(kMinBlocksPerChunk * Bk, (T * H + kTargetWorkgroups - 1) / kTargetWorkgroups);
+    constexpr int64_t kComputeUnits = 256;
+    const int64_t share = std::max<int64_t>(kMinBlocksPerChunk * Bk, (T * H + kComputeUnits - 1) / kComputeUnits);
+    int64_t n_max = 0;
+    for (int64_t b = 0; b < B; ++b) n_max = std::max<int64_t>(n_max, offs[b + 1] - offs[b]);
+    int64_t L = n_max <= 2 * share ? std::max<int64_t>(n_max, Bk) : share;
     const char* env = std::getenv("LA_VARLEN_L");
     if (env && std::atoll(env) > 0) L = std::atoll(env);
     L = (L + Bk - 1) / Bk * Bk;
@@ -242,6 +249,14 @@ int make_varplan(const int64_t* offs, int64_t B, int64_t H, int64_t D, int32_t B
     }
     p->v.cu[B] = static_cast<int>(T);
     p->slots_per_head = p->v.wp[B] - B;
+    // last chunks, longest first
+    std::vector<int> ord(static_cast<size_t>(B));
+    for (int b = 0; b < B; ++b) ord[b] = b;
+    auto last_len = [&](int b) {
+        return (offs[b + 1] - offs[b]) - static_cast<int64_t>(p->v.wp[b + 1] - p->v.wp[b] - 1) * L;
+    };
+    std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return last_len(x) > last_len(y); });
+    for (int j = 0; j < B; ++j) p->v.last_order[j] = static_cast<uint8_t>(ord[j]);
     return LA_OK;
 }
 
@@ -446,7 +461,17 @@ int la_fwd_varlen(const void* Q, const void* K, const void* V, const float* lamb
         rc = launch("chunk_state_varlen_dma", s, [&] { la::launch_chunk_state_dma_varlen(cs, lam, p.v, s); });
         if (rc) return rc;
         la::ScanArgs sc{slots, kv_in, 0, nullptr, 0, p.L, static_cast<int>(D), Hi, 0, 0, 0};
-        rc = launch("state_scan_varlen", s, [&] { la::launch_scan_varlen(sc, lam, p.v, s); });
+        la::ScanList list;
+        list.count = 0;
+        for (int b = 0; b < p.v.nseq; ++b) {
+            const int n_slots = p.v.wp[b + 1] - p.v.wp[b] - 1;
+            if (n_slots > 0) {
+                list.seq[list.count] = b | (n_slots << 8);
+                list.sbase[list.count] = p.v.wp[b] - b;
+                ++list.count;
+            }
+        }
+        rc = launch("state_scan_varlen", s, [&] { la::launch_scan_varlen(sc, lam, list, s); });
         if (rc) return rc;
     }
     la::SweepArgs a{};

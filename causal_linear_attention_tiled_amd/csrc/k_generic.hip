@@ -244,21 +244,22 @@ __global__ __launch_bounds__(kThreads) void k_scan(ScanArgs a, LamArgs lam) {
     }
 }
 
-// Forward scan over the chunk states of a ragged batch: per (sequence b, head h),
-// S = kv_in[b][h] (or 0); for c = 0 .. chunks_b - 2: S = lam^L S + slot; slot = S,
-// with slot (wp[b] - b + c) * H + h.
-__global__ __launch_bounds__(kThreads) void k_scan_varlen(ScanArgs a, LamArgs lam, VarlenArgs v) {
+// Forward scan over the chunk states of a ragged batch: per listed (sequence b,
+// head h), S = kv_in[b][h] (or 0); for c = 0 .. n_slots - 1: S = lam^L S + slot;
+// slot = S, with slot (sbase + c) * H + h.  Sequences without chunk states are
+// not listed (nothing to scan).
+__global__ __launch_bounds__(kThreads) void k_scan_varlen(ScanArgs a, LamArgs lam, ScanList list) {
     const int DD = a.D * a.D;
     const int per_pair = (DD + kThreads - 1) / kThreads;
-    const int64_t pair = blockIdx.x / per_pair;  // b * H + h
+    const int64_t pair = blockIdx.x / per_pair;  // i * H + h over the list
     const int e = (blockIdx.x % per_pair) * kThreads + threadIdx.x;
     if (e >= DD) return;
-    const int b = static_cast<int>(pair / a.H), h = static_cast<int>(pair % a.H);
+    const int i = static_cast<int>(pair / a.H), h = static_cast<int>(pair % a.H);
+    const int b = list.seq[i] & 0xFF, n_slots = list.seq[i] >> 8;
     const float lamL = lam_pow(lam.lam[h], a.L);
-    const int n_slots = v.wp[b + 1] - v.wp[b] - 1;
-    float S = a.kv_in ? a.kv_in[pair * DD + e] : 0.f;
+    float S = a.kv_in ? a.kv_in[(static_cast<int64_t>(b) * a.H + h) * DD + e] : 0.f;
     for (int c = 0; c < n_slots; ++c) {
-        float* sl = a.slots + (static_cast<int64_t>(v.wp[b] - b + c) * a.H + h) * DD + e;
+        float* sl = a.slots + (static_cast<int64_t>(list.sbase[i] + c) * a.H + h) * DD + e;
         S = lamL * S + *sl;
         *sl = S;
     }
@@ -347,10 +348,10 @@ void launch_chunk_state_generic(const ChunkStateArgs& a, const LamArgs& lam, int
         hipLaunchKernelGGL(k_chunk_state_generic<false>, grid, dim3(kThreads), 0, s, a, lam);
 }
 
-void launch_scan_varlen(const ScanArgs& a, const LamArgs& lam, const VarlenArgs& v, hipStream_t s) {
+void launch_scan_varlen(const ScanArgs& a, const LamArgs& lam, const ScanList& list, hipStream_t s) {
     const int per_pair = (a.D * a.D + kThreads - 1) / kThreads;
-    dim3 grid(static_cast<unsigned>(static_cast<int64_t>(v.nseq) * a.H * per_pair));
-    hipLaunchKernelGGL(k_scan_varlen, grid, dim3(kThreads), 0, s, a, lam, v);
+    dim3 grid(static_cast<unsigned>(static_cast<int64_t>(list.count) * a.H * per_pair));
+    hipLaunchKernelGGL(k_scan_varlen, grid, dim3(kThreads), 0, s, a, lam, list);
 }
 
 void launch_scan(const ScanArgs& a, const LamArgs& lam, hipStream_t s) {

@@ -99,10 +99,18 @@ __device__ __forceinline__ Work work_item(const SA& a, const VA* v, int64_t blk)
         w.slot0 = pair * (a.chunks - 1);
         w.slot_step = 1;
     } else {
+        // full chunks first (sequence-major), then every sequence's last chunk, longest first
         const int h = static_cast<int>(blk % a.H);
         const int wi = static_cast<int>(blk / a.H);
-        const int b = find_last_le(v->nseq, wi, [&](int i) { return v->wp[i]; });
-        w.c = wi - v->wp[b];
+        const int full = v->wp[v->nseq] - v->nseq;
+        int b;
+        if (wi < full) {
+            b = find_last_le(v->nseq, wi, [&](int i) { return v->wp[i] - i; });
+            w.c = wi - (v->wp[b] - b);
+        } else {
+            b = v->last_order[wi - full];
+            w.c = v->wp[b + 1] - v->wp[b] - 1;
+        }
         w.chunks = v->wp[b + 1] - v->wp[b];
         w.head = h;
         w.n = v->cu[b + 1] - v->cu[b];

@@ -15,16 +15,20 @@ struct LamArgs {
     float lam[kMaxHeads];
 };
 
-// A ragged batch (passed by value as a kernel argument, 2 KiB): sequence b covers
+// A ragged batch (passed by value as a kernel argument, 2.3 KiB): sequence b covers
 // tokens [cu[b], cu[b+1]) of token-major [T][H][D] tensors, so the rows of one
 // (sequence, head) are H * D elements apart, and is split into wp[b+1] - wp[b]
 // chunks of L tokens (at least one, also for an empty sequence).  Sequence b's
 // chunk states are slots (wp[b] - b + c) * H + h, c = 0 .. chunks - 2.
+// The sweep runs the full chunks (every chunk but a sequence's last) first, then
+// the last chunks in the order last_order (longest first), so that the longest
+// pieces of work start earliest.
 constexpr int kMaxVarlenSeqs = 256;
 struct VarlenArgs {
     int nseq;
     int cu[kMaxVarlenSeqs + 1];
     int wp[kMaxVarlenSeqs + 1];
+    uint8_t last_order[kMaxVarlenSeqs];
 };
 
 // One sweep over every (sequence, chunk) of a [P][N][D] problem.
@@ -127,7 +131,15 @@ void launch_chunk_state_dma(const ChunkStateArgs& a, const LamArgs& lam, hipStre
 // Forward chunk aggregates of a ragged batch: one workgroup per (slot, head).
 void launch_chunk_state_dma_varlen(const ChunkStateArgs& a, const LamArgs& lam, const VarlenArgs& v,
                                    hipStream_t s);
-// Forward scan of a ragged batch's chunk states (ScanArgs.L is the chunk length).
-void launch_scan_varlen(const ScanArgs& a, const LamArgs& lam, const VarlenArgs& v, hipStream_t s);
+// The sequences of a ragged batch that have chunk states: entry i names sequence
+// seq[i] & 0xFF with (seq[i] >> 8) slots starting at per-head slot sbase[i].
+struct ScanList {
+    int count;
+    int seq[kMaxVarlenSeqs];
+    int sbase[kMaxVarlenSeqs];
+};
+// Forward scan of a ragged batch's chunk states (ScanArgs.L is the chunk length):
+// one workgroup per (listed sequence, head, 256 state elements).
+void launch_scan_varlen(const ScanArgs& a, const LamArgs& lam, const ScanList& list, hipStream_t s);
 
 }  // namespace la
