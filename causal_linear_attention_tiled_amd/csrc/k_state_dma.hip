@@ -12,11 +12,13 @@
 // c * lam^(offset in its block) with c = lam^(tokens already walked), a running
 // product in double: the accumulators are never rescaled.  A weight that
 // underflows stands for a term below float range next to the unit-size ones.
-// The loop stores nothing, so the eight waves share the loads (4 of the 32
-// loads of a block each) with exact partial vmcnt waits over a three-stage
-// ring.  Both operands come from the row-major tiles through transposing LDS
-// reads; wave w accumulates columns [16w, 16w + 16) of the aggregate, two
-// waves per SIMD.
+// The eight waves share the loads (4 of the 32 loads of a block each) over a
+// two-stage ring: the next block's loads are issued as a block starts and
+// waited for (vmcnt 0; the loop stores nothing) at the next.  The ring takes
+// 64 KiB of LDS, so two workgroups share a compute unit and a launch of a few
+// hundred chunks runs in one round.  Both operands come from the row-major
+// tiles through transposing LDS reads; wave w accumulates columns
+// [16w, 16w + 16) of the aggregate.
 #include "la_device.h"
 #include "la_internal.h"
 #include "lds_dma.h"
@@ -28,7 +30,7 @@ namespace {
 constexpr int D = 128;
 constexpr int BK = 64;
 constexpr int NKB = BK / 32;
-constexpr int NSTAGE = 3;
+constexpr int NSTAGE = 2;
 constexpr int TILE = BK * D;
 constexpr int NW = 8;
 constexpr int LOADS_PER_WAVE = 2 * (BK / 4) / NW;  // 1 KiB loads per wave per block
@@ -78,7 +80,7 @@ __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArg
     const uint32_t bytes = static_cast<uint32_t>(((n_seq - 1) * ld + D) * 2);
     const u32x4 rx = buffer_rsrc(static_cast<const uint16_t*>(a.x) + base, bytes);
     const u32x4 ry = buffer_rsrc(static_cast<const uint16_t*>(a.y) + base, bytes);
-    // The n-th block of the walk goes to stage n % 3; wave w issues, for each
+    // The n-th block of the walk goes to stage n % 2; wave w issues, for each
     // tensor, the loads of row groups w and w + 8 (4 rows each).
     auto block_of = [&](int64_t n) { return a.reverse ? n : nblk - 1 - n; };
     auto issue = [&](int64_t n) {
@@ -95,8 +97,7 @@ __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArg
                 dma16(x == 0 ? rx : ry, &sm.t[stage][x][4 * rg * D], voff);
             }
     };
-    issue(0);
-    if (nblk > 1) issue(1);
+    if (nblk > 0) issue(0);
 
     // S[at][r] = acc[16 at + 4 g + r][16 w + li]
     f32x4 S[8];
@@ -108,12 +109,9 @@ __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArg
         const int64_t t0 = t_begin + block_of(n) * BK;
         const int m = static_cast<int>(min(static_cast<int64_t>(BK), t_end - t0));
         const int stage = static_cast<int>(n % NSTAGE);
-        if (n + 1 < nblk)
-            wait_vmcnt<LOADS_PER_WAVE>();
-        else
-            wait_vmcnt<0>();
-        __syncthreads();  // stage n % 3 is complete; stage (n + 2) % 3 is no longer read
-        if (n + 2 < nblk) issue(n + 2);
+        wait_vmcnt<0>();  // this block's loads (the only ones in flight)
+        __syncthreads();  // stage n % 2 is complete; stage (n + 1) % 2 is no longer read
+        if (n + 1 < nblk) issue(n + 1);
         const uint16_t* Xs = sm.t[stage][0];
         const uint16_t* Ys = sm.t[stage][1];
         // weights of token s = 32 kb + kappa(g, e), on the Y operand
@@ -142,11 +140,11 @@ __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArg
         for (int r = 0; r < 4; ++r) dst[(16 * at + 4 * g + r) * D + 16 * w + li] = S[at][r];
 }
 
-__global__ __launch_bounds__(64 * NW, 1) void k_chunk_state_dma(ChunkStateArgs a, LamArgs lam) {
+__global__ __launch_bounds__(64 * NW, 2) void k_chunk_state_dma(ChunkStateArgs a, LamArgs lam) {
     state_body<false>(a, lam, nullptr);
 }
 
-__global__ __launch_bounds__(64 * NW, 1) void k_chunk_state_dma_varlen(ChunkStateArgs a, LamArgs lam, VarlenArgs v) {
+__global__ __launch_bounds__(64 * NW, 2) void k_chunk_state_dma_varlen(ChunkStateArgs a, LamArgs lam, VarlenArgs v) {
     state_body<true>(a, lam, &v);
 }
 
