@@ -30,6 +30,7 @@ import subprocess
 import numpy as np
 
 from .quadratic import (decay_matrix, fwd_quadratic, bwd_quadratic)  # noqa: F401
+from . import feature  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "liboracle.so")
@@ -76,14 +77,15 @@ def _lams(lam, pairs) -> np.ndarray:
     return np.ascontiguousarray(lam)
 
 
-def fwd_recurrent(q, k, v, lam, s_init=None, want_state=True, block=0):
+def fwd_recurrent(q, k, v, lam, s_init=None, want_state=True, block=0, phi="identity"):
     """F2 forward over sequences shaped [..., n, d].
 
     lam: one value or one per sequence (the product of the leading dims).
+    phi: the feature map applied to q and k (oracle.feature).
     Returns (O, S_final) and, if ``block`` > 0, also the states before every
     block start t = b*block, shaped [..., ceil(n/block), d, d].
     """
-    q, k, v = _f64(q), _f64(k), _f64(v)
+    q, k, v = feature.phi(q, phi), feature.phi(k, phi), _f64(v)
     *lead, n, d = q.shape
     pairs = int(np.prod(lead)) if lead else 1
     lam_arr = _lams(lam, pairs)
@@ -102,13 +104,14 @@ def fwd_recurrent(q, k, v, lam, s_init=None, want_state=True, block=0):
 
 
 def bwd_recurrent(q, k, v, dout, lam, s_init=None, want=("dq", "dk", "dv"), g_final=None,
-                  want_ds_init=False):
+                  want_ds_init=False, phi="identity"):
     """F2 backward of L = <dO, O> + <G, S_N> (G = ``g_final``, the gradient arriving at the
-    final state; zero when None).
+    final state; zero when None), with the feature map ``phi`` on q and k.
 
     Returns (dQ, dK, dV) (None for those not wanted), followed by dS0, the gradient of the
-    initial state, when ``want_ds_init``."""
-    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    initial state, when ``want_ds_init``.  dQ and dK are with respect to the raw q and k."""
+    q_raw, k_raw = _f64(q), _f64(k)
+    q, k, v, dout = feature.phi(q_raw, phi), feature.phi(k_raw, phi), _f64(v), _f64(dout)
     *lead, n, d = q.shape
     pairs = int(np.prod(lead)) if lead else 1
     lam_arr = _lams(lam, pairs)
@@ -121,17 +124,24 @@ def bwd_recurrent(q, k, v, dout, lam, s_init=None, want=("dq", "dk", "dv"), g_fi
     _lib().oracle_bwd_recurrent(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data, pairs,
                                 n, d, lam_arr.ctypes.data, _ptr(s0), _ptr(gf), _ptr(dq), _ptr(dk),
                                 _ptr(dv), _ptr(ds0))
+    if phi != "identity":
+        # chain rule through the elementwise feature map
+        if dq is not None:
+            dq *= feature.dphi(q_raw, phi)
+        if dk is not None:
+            dk *= feature.dphi(k_raw, phi)
     if want_ds_init:
         return dq, dk, dv, ds0.reshape(*lead, d, d)
     return dq, dk, dv
 
 
-def decode_step(state, q, k, v, lam):
-    """One recurrent step for states [..., d, d] (updated copy returned) and q, k, v [..., d].
+def decode_step(state, q, k, v, lam, phi="identity"):
+    """One recurrent step for states [..., d, d] (updated copy returned) and q, k, v [..., d],
+    with the feature map ``phi`` on q and k.
 
     Returns (o, new_state)."""
     state = _f64(state).copy()
-    q, k, v = _f64(q), _f64(k), _f64(v)
+    q, k, v = feature.phi(q, phi), feature.phi(k, phi), _f64(v)
     *lead, d = q.shape
     pairs = int(np.prod(lead)) if lead else 1
     lam_arr = _lams(lam, pairs)

@@ -17,6 +17,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import feature
+
 
 def decay_matrix(n: int, lam: float) -> np.ndarray:
     """D[i, j] = lam^(i-j) for i >= j, 0 above the diagonal (lam^0 = 1, also for lam = 0)."""
@@ -30,10 +32,11 @@ def _powers(lam: float, exps: np.ndarray) -> np.ndarray:
     return np.power(np.float64(lam), exps.astype(np.float64))
 
 
-def fwd_quadratic(q, k, v, lam, s_init=None):
-    """One sequence: q, k, v [n, d]; returns (O [n, d], S_final [d, d])."""
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
+def fwd_quadratic(q, k, v, lam, s_init=None, phi="identity"):
+    """One sequence: q, k, v [n, d]; returns (O [n, d], S_final [d, d]) with the feature map
+    ``phi`` (oracle.feature) on q and k."""
+    q = feature.phi(q, phi)
+    k = feature.phi(k, phi)
     v = np.asarray(v, dtype=np.float64)
     n = q.shape[0]
     lam = float(np.float64(lam))
@@ -49,11 +52,14 @@ def fwd_quadratic(q, k, v, lam, s_init=None):
     return o, s_final
 
 
-def bwd_quadratic(q, k, v, dout, lam, s_init=None, g_final=None):
+def bwd_quadratic(q, k, v, dout, lam, s_init=None, g_final=None, phi="identity"):
     """One sequence: returns (dQ, dK, dV, dS0) of L = <dO, O> + <F, S_final>, F = g_final
-    (zero when None)."""
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
+    (zero when None), with the feature map ``phi`` on q and k (dQ, dK with respect to the
+    raw q and k)."""
+    q_raw = np.asarray(q, dtype=np.float64)
+    k_raw = np.asarray(k, dtype=np.float64)
+    q = feature.phi(q_raw, phi)
+    k = feature.phi(k_raw, phi)
     v = np.asarray(v, dtype=np.float64)
     g = np.asarray(dout, dtype=np.float64)
     n, d = q.shape
@@ -74,4 +80,4 @@ def bwd_quadratic(q, k, v, dout, lam, s_init=None, g_final=None):
         dk = dk + w * (v @ f.T)
         dv = dv + w * (k @ f)
         ds0 = ds0 + (lam ** n) * f
-    return dq, dk, dv, ds0
+    return dq * feature.dphi(q_raw, phi), dk * feature.dphi(k_raw, phi), dv, ds0

@@ -432,3 +432,61 @@ def test_planted_state_gradient_mistakes_are_caught():
     assert np.allclose(ds00 + 0.5 ** n * fa, ds0_ex, rtol=1e-13, atol=1e-13)
     assert not np.allclose(ds00 + fa, ds0_ex)                           # G without lam^n
     assert not np.allclose(ds00, ds0_ex)                                # G dropped
+
+
+# ----------------------------------------------------------------- feature maps
+@pytest.mark.parametrize("kind", ["elu1", "relu"])
+def test_feature_maps_match_library(kind):
+    """phi and phi' against torch's float64 elu / relu and autograd."""
+    torch = pytest.importorskip("torch")
+    from oracle import feature
+    x = np.linspace(-6.0, 6.0, 2001)
+    x = x[np.abs(x) > 1e-9]                                  # relu' is undefined at 0
+    tx = torch.from_numpy(x).requires_grad_(True)
+    ty = torch.nn.functional.elu(tx) + 1.0 if kind == "elu1" else torch.relu(tx)
+    ty.sum().backward()
+    # torch forms elu(x) + 1 as (exp(x) - 1) + 1: equal up to a few ulps of 1
+    np.testing.assert_allclose(feature.phi(x, kind), ty.detach().numpy(), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(feature.dphi(x, kind), tx.grad.numpy(), rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("kind", ["elu1", "relu"])
+def test_feature_map_gradients_finite_differences(kind):
+    """dQ, dK of L = <dO, O> + <G, S_final> through phi, against central differences of the
+    forward (inputs kept away from the kink of relu)."""
+    rng = np.random.default_rng(41)
+    n, d, lam, h = 9, 3, 0.8, 1e-6
+    q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+    for x in (q, k):
+        x[np.abs(x) < 0.1] += 0.3
+    gf = rng.standard_normal((d, d))
+
+    def loss(qq, kk):
+        o, s = oracle.fwd_recurrent(qq, kk, v, lam, phi=kind)
+        return np.sum(g * o) + np.sum(gf * s)
+    dq, dk, _ = oracle.bwd_recurrent(q, k, v, g, lam, g_final=gf, phi=kind)
+    fd_q, fd_k = np.zeros_like(q), np.zeros_like(k)
+    for t in range(n):
+        for a in range(d):
+            e = np.zeros_like(q); e[t, a] = h
+            fd_q[t, a] = (loss(q + e, k) - loss(q - e, k)) / (2 * h)
+            fd_k[t, a] = (loss(q, k + e) - loss(q, k - e)) / (2 * h)
+    np.testing.assert_allclose(dq, fd_q, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(dk, fd_k, rtol=1e-6, atol=1e-7)
+    for a, b in zip(oracle.bwd_recurrent(q, k, v, g, lam, g_final=gf, phi=kind),
+                    oracle.bwd_quadratic(q, k, v, g, lam, g_final=gf, phi=kind)):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+def test_feature_map_closed_forms():
+    """elu1 maps q = k = 0 to all ones (the all-ones closed form); relu maps q = -1 to zero, so
+    O, dQ and dK vanish."""
+    n, d, lam = 200, 8, 0.9
+    zero, ones = np.zeros((n, d)), np.ones((n, d))
+    t = np.arange(n, dtype=np.float64)
+    o, _ = oracle.fwd_recurrent(zero, zero, ones, lam, phi="elu1")
+    np.testing.assert_allclose(o, d * ((1 - lam ** (t + 1)) / (1 - lam))[:, None] * ones, rtol=1e-12)
+    o, _ = oracle.fwd_recurrent(-ones, ones, ones, lam, phi="relu")
+    assert not np.any(o)
+    dq, dk, dv = oracle.bwd_recurrent(-ones, ones, ones, ones, lam, phi="relu")
+    assert not np.any(dq) and not np.any(dk) and not np.any(dv)
