@@ -21,6 +21,16 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 
 LA_F32, LA_BF16 = 0, 1
+LA_PHI_IDENTITY, LA_PHI_ELU1, LA_PHI_RELU = 0, 1, 2
+PHI_CODES = {"identity": LA_PHI_IDENTITY, "elu1": LA_PHI_ELU1, "relu": LA_PHI_RELU}
+
+
+def _phi_code(phi) -> int:
+    if isinstance(phi, str):
+        if phi not in PHI_CODES:
+            raise ValueError(f"unknown feature map {phi!r}; one of {sorted(PHI_CODES)}")
+        return PHI_CODES[phi]
+    return int(phi)
 LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EALIGN, LA_EWORKSPACE, LA_EHIP, LA_ENODEV = range(7)
 
 
@@ -40,22 +50,22 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     fp = ctypes.POINTER(ctypes.c_float)
-    lib.la_fwd.argtypes = [vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.la_fwd.argtypes = [vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.la_fwd.restype = ctypes.c_int
     lib.la_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
     lib.la_fwd_workspace_bytes.restype = sz
-    lib.la_bwd.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.la_bwd.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.la_bwd.restype = ctypes.c_int
     lib.la_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
     lib.la_bwd_workspace_bytes.restype = sz
-    lib.la_decode_step.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i32, vp, vp]
+    lib.la_decode_step.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i32, i32, vp, vp]
     lib.la_decode_step.restype = ctypes.c_int
     ip = ctypes.POINTER(ctypes.c_int64)
-    lib.la_fwd_varlen.argtypes = [vp, vp, vp, fp, ip, i64, i64, i64, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.la_fwd_varlen.argtypes = [vp, vp, vp, fp, ip, i64, i64, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.la_fwd_varlen.restype = ctypes.c_int
     lib.la_fwd_varlen_workspace_bytes.argtypes = [ip, i64, i64, i64, i32, i32]
     lib.la_fwd_varlen_workspace_bytes.restype = sz
-    lib.la_decode_step_paged.argtypes = [vp, i64, vp, vp, vp, vp, fp, i64, i64, i64, i32, vp, vp]
+    lib.la_decode_step_paged.argtypes = [vp, i64, vp, vp, vp, vp, fp, i64, i64, i64, i32, i32, vp, vp]
     lib.la_decode_step_paged.restype = ctypes.c_int
     lib.la_strerror.argtypes = [ctypes.c_int]
     lib.la_strerror.restype = ctypes.c_char_p
@@ -137,7 +147,7 @@ def _workspace(nbytes, device, ws):
 
 
 def la_fwd(q, k, v, lam, Bk: int = 64, kv_in=None, out=None, kv_out=None, want_state: bool = True,
-           ws=None):
+           ws=None, phi="identity"):
     """O (and the final float32 state) of causal linear attention with per-head decay.
 
     Returns (O, kv_out); kv_out is None when ``want_state`` is False and none is given."""
@@ -155,7 +165,7 @@ def la_fwd(q, k, v, lam, Bk: int = 64, kv_in=None, out=None, kv_out=None, want_s
     code = _dtype_code(q)
     nbytes = la_fwd_workspace_bytes(B, H, N, D, Bk, code)
     ws = _workspace(nbytes, q.device, ws)
-    rc = lib.la_fwd(_ptr(q), _ptr(k), _ptr(v), _lam_array(lam, H), B, H, N, D, Bk, code, _ptr(kv_in),
+    rc = lib.la_fwd(_ptr(q), _ptr(k), _ptr(v), _lam_array(lam, H), B, H, N, D, Bk, code, _phi_code(phi), _ptr(kv_in),
                     _ptr(out), _ptr(kv_out), _ptr(ws), nbytes if ws is not None else 0, _stream(q.device))
     if rc != LA_OK:
         raise LaError(rc, "la_fwd")
@@ -163,7 +173,7 @@ def la_fwd(q, k, v, lam, Bk: int = 64, kv_in=None, out=None, kv_out=None, want_s
 
 
 def la_bwd(q, k, v, dout, lam, Bk: int = 64, kv_in=None, dq=None, dk=None, dv=None, ws=None,
-           fwd_ws=None, dkv_out=None, dkv_in=None, want_dkv_in: bool = False):
+           fwd_ws=None, dkv_out=None, dkv_in=None, want_dkv_in: bool = False, phi="identity"):
     """dQ, dK, dV of L = <dO, O> + <dkv_out, S_N> for la_fwd.
 
     ``dkv_out``: float32 [B, H, D, D] gradient arriving at the final state (None for zero).
@@ -192,7 +202,7 @@ def la_bwd(q, k, v, dout, lam, Bk: int = 64, kv_in=None, dq=None, dk=None, dv=No
         if fwd_ws.device != q.device or fwd_ws.numel() * fwd_ws.element_size() < need:
             raise ValueError(f"fwd_ws must hold the {need}-byte workspace of la_fwd on {q.device}")
     rc = lib.la_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _lam_array(lam, H), B, H, N, D, Bk, code,
-                    _ptr(kv_in), _ptr(dkv_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkv_in), _ptr(fwd_ws),
+                    _phi_code(phi), _ptr(kv_in), _ptr(dkv_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkv_in), _ptr(fwd_ws),
                     _ptr(ws), nbytes if ws is not None else 0, _stream(q.device))
     if rc != LA_OK:
         raise LaError(rc, "la_bwd")
@@ -212,7 +222,7 @@ def la_fwd_varlen_workspace_bytes(seq_offsets, H, D, Bk, dtype_code) -> int:
 
 
 def la_fwd_varlen(q, k, v, lam, seq_offsets, Bk: int = 64, kv_in=None, out=None, kv_out=None,
-                  want_state: bool = True, ws=None):
+                  want_state: bool = True, ws=None, phi="identity"):
     """Forward over a ragged batch packed token-major: q, k, v [T, H, D] bf16, sequence b is
     rows seq_offsets[b] .. seq_offsets[b+1].  Returns (O [T, H, D], kv_out [B, H, D, D])."""
     for name, t in (("Q", q), ("K", k), ("V", v)):
@@ -230,14 +240,15 @@ def la_fwd_varlen(q, k, v, lam, seq_offsets, Bk: int = 64, kv_in=None, out=None,
     code = _dtype_code(q)
     nbytes = int(lib.la_fwd_varlen_workspace_bytes(arr, B, H, D, Bk, code))
     ws = _workspace(nbytes, q.device, ws)
-    rc = lib.la_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _lam_array(lam, H), arr, B, H, D, Bk, code, _ptr(kv_in),
+    rc = lib.la_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _lam_array(lam, H), arr, B, H, D, Bk, code,
+                           _phi_code(phi), _ptr(kv_in),
                            _ptr(out), _ptr(kv_out), _ptr(ws), nbytes if ws is not None else 0, _stream(q.device))
     if rc != LA_OK:
         raise LaError(rc, "la_fwd_varlen")
     return out, kv_out
 
 
-def la_decode_step_paged(pool, slot_of, q, k, v, lam, out=None):
+def la_decode_step_paged(pool, slot_of, q, k, v, lam, out=None, phi="identity"):
     """One recurrent step for Bs sequences whose float32 states live in ``pool``
     [P, H, D, D] at slots ``slot_of`` (int32 [Bs], distinct); q, k, v [Bs, H, D].  Returns o."""
     if pool.dtype != torch.float32 or pool.dim() != 4 or not pool.is_contiguous():
@@ -253,13 +264,13 @@ def la_decode_step_paged(pool, slot_of, q, k, v, lam, out=None):
             raise ValueError(f"{name} must be a contiguous [Bs, H, D] tensor")
     out = torch.empty_like(q) if out is None else out
     rc = lib.la_decode_step_paged(_ptr(pool), P, _ptr(slot_of), _ptr(q), _ptr(k), _ptr(v), _lam_array(lam, H),
-                                  Bs, H, D, _dtype_code(q), _ptr(out), _stream(q.device))
+                                  Bs, H, D, _dtype_code(q), _phi_code(phi), _ptr(out), _stream(q.device))
     if rc != LA_OK:
         raise LaError(rc, "la_decode_step_paged")
     return out
 
 
-def la_decode_step(state, q, k, v, lam, out=None):
+def la_decode_step(state, q, k, v, lam, out=None, phi="identity"):
     """One recurrent step S <- lam S + k v^T, o = q S; ``state`` [Bs, H, D, D] float32 is updated in place.
 
     q, k, v are [Bs, H, D]; returns o."""
@@ -273,7 +284,7 @@ def la_decode_step(state, q, k, v, lam, out=None):
         raise ValueError("state must be a contiguous float32 [Bs, H, D, D] tensor")
     out = torch.empty_like(q) if out is None else out
     rc = lib.la_decode_step(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _lam_array(lam, H), Bs, H, D,
-                            _dtype_code(q), _ptr(out), _stream(q.device))
+                            _dtype_code(q), _phi_code(phi), _ptr(out), _stream(q.device))
     if rc != LA_OK:
         raise LaError(rc, "la_decode_step")
     return out

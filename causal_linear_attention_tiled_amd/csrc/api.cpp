@@ -87,6 +87,8 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
     return true;
 }
 
+bool valid_phi(int32_t phi) { return phi == LA_PHI_IDENTITY || phi == LA_PHI_ELU1 || phi == LA_PHI_RELU; }
+
 bool supported_D(int64_t D) { return D == 16 || D == 32 || D == 64 || D == 128; }
 bool supported_Bk(int64_t Bk) { return Bk == 16 || Bk == 32 || Bk == 64 || Bk == 128; }
 
@@ -163,16 +165,27 @@ size_t round_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // With `given` non-null the chunk states are not computed: the sweep reads
 // them, transposed, from `given` (the chunk states a forward pass left in its
 // workspace, which are the transposes of the dQ sweep's states).
+// Where the feature map enters a forward-direction sweep over (q, k, v).
+struct PhiUse {
+    int kind;          // kPhi* (0: identity, the rest unused)
+    int sweep_mask;    // operands of the sweep it maps (bit 0: q, 1: k, 2: v)
+    int state_mask;    // operands of the chunk aggregates over (k, v) it maps (bit 0: k, 1: v)
+    const void* grad;  // raw tensor whose phi' multiplies the sweep's output, or nullptr
+};
+
 int run_forward_sweep(const void* q, const void* k, const void* v, void* out, const float* kv_in,
                       int kv_in_t, float* kv_out, float* slots, const float* given, int64_t pairs,
                       int64_t N, int64_t D, int32_t Bk, int32_t H, int bf16, const Plan& p,
-                      const LamArgs& lam, hipStream_t s, const char* tag) {
+                      const LamArgs& lam, const PhiUse& phi, hipStream_t s, const char* tag) {
     int rc;
+    // the register-staged kernels have no feature map: with one, the generic kernels run
+    const bool v1_ok = phi.kind == 0;
     if (p.chunks > 1 && !given) {
-        la::ChunkStateArgs cs{k, v, slots, N, p.L, static_cast<int>(D), Bk, H, p.chunks, pairs, 0};
+        la::ChunkStateArgs cs{k, v, slots, N, p.L, static_cast<int>(D), Bk, H, p.chunks, pairs, 0,
+                              phi.kind, phi.state_mask};
         if (p.mfma && la::state_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_STATE", "v1"))
             rc = launch("chunk_state_dma", s, [&] { la::launch_chunk_state_dma(cs, lam, s); });
-        else if (p.mfma)
+        else if (p.mfma && v1_ok)
             rc = launch("chunk_state_mfma", s, [&] { la::launch_chunk_state_mfma(cs, lam, s); });
         else
             rc = launch("chunk_state_generic", s, [&] { la::launch_chunk_state_generic(cs, lam, bf16, s); });
@@ -198,11 +211,15 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
     a.H = H;
     a.chunks = p.chunks;
     a.pairs = pairs;
+    a.phi = phi.kind;
+    a.phi_mask = phi.sweep_mask;
+    a.phi_grad = phi.grad;
     if (p.mfma && la::fwd_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_FWD", "v1")) {
         const int waves = env_is("LA_FWD_WAVES", "8") ? 8 : 4;
         return launch(tag[0] == 'd' ? "dq_dma" : "fwd_dma", s, [&] { la::launch_fwd_dma(a, lam, waves, s); });
     }
-    if (p.mfma) return launch(tag[0] == 'd' ? "dq_mfma" : "fwd_mfma", s, [&] { la::launch_fwd_mfma(a, lam, s); });
+    if (p.mfma && v1_ok)
+        return launch(tag[0] == 'd' ? "dq_mfma" : "fwd_mfma", s, [&] { la::launch_fwd_mfma(a, lam, s); });
     return launch(tag[0] == 'd' ? "dq_generic" : "fwd_generic", s, [&] { la::launch_fwd_generic(a, lam, bf16, s); });
 }
 
@@ -304,11 +321,12 @@ size_t la_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_
 }
 
 int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int64_t B, int64_t H,
-           int64_t N, int64_t D, int32_t Bk, int32_t dtype, const float* kv_in, void* O, float* kv_out,
-           void* ws, size_t ws_bytes, void* hip_stream) {
+           int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t phi, const float* kv_in, void* O,
+           float* kv_out, void* ws, size_t ws_bytes, void* hip_stream) {
     int64_t elems;
     int rc = check_shape(B, H, N, D, Bk, dtype, &elems);
     if (rc) return rc;
+    if (!valid_phi(phi)) return LA_EINVAL;
     if (!Q || !K || !V || !O) return LA_EINVAL;
     LamArgs lam;
     if ((rc = load_lambda(lambda, H, &lam))) return rc;
@@ -329,17 +347,19 @@ int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int
     int dev_count = 0;
     if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count == 0) return LA_ENODEV;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const PhiUse pu{phi, 3, 1, nullptr};  // phi(q), phi(k); the aggregates map k
     return run_forward_sweep(Q, K, V, O, kv_in, 0, kv_out, static_cast<float*>(ws), nullptr, B * H, N, D,
-                             Bk, static_cast<int32_t>(H), dtype == LA_BF16, p, lam, s, "fwd");
+                             Bk, static_cast<int32_t>(H), dtype == LA_BF16, p, lam, pu, s, "fwd");
 }
 
 int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const float* lambda, int64_t B,
-           int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype, const float* kv_in,
+           int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t phi, const float* kv_in,
            const float* dkv_out, void* dQ, void* dK, void* dV, float* dkv_in, const void* fwd_ws, void* ws,
            size_t ws_bytes, void* hip_stream) {
     int64_t elems;
     int rc = check_shape(B, H, N, D, Bk, dtype, &elems);
     if (rc) return rc;
+    if (!valid_phi(phi)) return LA_EINVAL;
     if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return LA_EINVAL;
     LamArgs lam;
     if ((rc = load_lambda(lambda, H, &lam))) return rc;
@@ -374,16 +394,20 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     const int32_t Hi = static_cast<int32_t>(H);
 
     // dQ: the forward sweep with (q, k, v) = (dO, V, K) and the transposed initial state.
+    // the dQ sweep: phi(k) in the value slot, its own aggregates over (v, phi(k)), and
+    // phi'(q) on the output
+    const PhiUse pu{phi, 4, 2, phi ? Q : nullptr};
     rc = run_forward_sweep(dO, V, K, dQ, kv_in, 1, nullptr, slots_q, static_cast<const float*>(fwd_ws), pairs,
-                           N, D, Bk, Hi, bf16, p, lam, s, "dq");
+                           N, D, Bk, Hi, bf16, p, lam, pu, s, "dq");
     if (rc) return rc;
 
     // dK, dV: reverse sweep carrying dS, with a chunked suffix over blocks.
     if (p.chunks > 1) {
-        la::ChunkStateArgs cs{Q, dO, slots_kv, N, p.L, static_cast<int>(D), Bk, Hi, p.chunks, pairs, 1};
+        la::ChunkStateArgs cs{Q, dO, slots_kv, N, p.L, static_cast<int>(D), Bk, Hi, p.chunks, pairs, 1,
+                              phi, 1};
         if (p.mfma && la::state_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_STATE", "v1"))
             rc = launch("chunk_state_rev_dma", s, [&] { la::launch_chunk_state_dma(cs, lam, s); });
-        else if (p.mfma)
+        else if (p.mfma && phi == 0)
             rc = launch("chunk_state_rev_mfma", s, [&] { la::launch_chunk_state_mfma(cs, lam, s); });
         else
             rc = launch("chunk_state_rev_generic", s, [&] { la::launch_chunk_state_generic(cs, lam, bf16, s); });
@@ -402,6 +426,8 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     a.slots = slots_kv;
     a.g_final = dkv_out;
     a.ds_out = dkv_in;
+    a.phi = phi;
+    a.phi_mask = 3;
     a.N = N;
     a.L = p.L;
     a.D = static_cast<int>(D);
@@ -411,10 +437,11 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     a.pairs = pairs;
     if (p.mfma && la::rev_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_REV", "v1"))
     {
-        const int waves = env_is("LA_REV_WAVES", "4") ? 4 : 8;
+        // the feature map is in the eight-wave form only
+        const int waves = (env_is("LA_REV_WAVES", "4") && phi == 0) ? 4 : 8;
         return launch("dkdv_dma", s, [&] { la::launch_rev_dma(a, lam, waves, s); });
     }
-    if (p.mfma && la::mfma_rev_supported(static_cast<int>(D), Bk))
+    if (p.mfma && phi == 0 && la::mfma_rev_supported(static_cast<int>(D), Bk))
         return launch("dkdv_mfma", s, [&] { la::launch_rev_mfma(a, lam, s); });
     return launch("dkdv_generic", s, [&] { la::launch_rev_generic(a, lam, bf16, s); });
 }
@@ -428,9 +455,10 @@ size_t la_fwd_varlen_workspace_bytes(const int64_t* seq_offsets, int64_t B, int6
 }
 
 int la_fwd_varlen(const void* Q, const void* K, const void* V, const float* lambda, const int64_t* seq_offsets,
-                  int64_t B, int64_t H, int64_t D, int32_t Bk, int32_t dtype, const float* kv_in, void* O,
-                  float* kv_out, void* ws, size_t ws_bytes, void* hip_stream) {
+                  int64_t B, int64_t H, int64_t D, int32_t Bk, int32_t dtype, int32_t phi, const float* kv_in,
+                  void* O, float* kv_out, void* ws, size_t ws_bytes, void* hip_stream) {
     if (dtype != LA_F32 && dtype != LA_BF16) return LA_EINVAL;
+    if (!valid_phi(phi)) return LA_EINVAL;
     VarPlan p;
     int rc = make_varplan(seq_offsets, B, H, D, Bk, &p);
     if (rc) return rc;
@@ -457,7 +485,7 @@ int la_fwd_varlen(const void* Q, const void* K, const void* V, const float* lamb
     const int32_t Hi = static_cast<int32_t>(H);
     float* slots = static_cast<float*>(ws);
     if (p.slots_per_head > 0) {
-        la::ChunkStateArgs cs{K, V, slots, 0, p.L, static_cast<int>(D), Bk, Hi, 0, 0, 0};
+        la::ChunkStateArgs cs{K, V, slots, 0, p.L, static_cast<int>(D), Bk, Hi, 0, 0, 0, phi, 1};
         rc = launch("chunk_state_varlen_dma", s, [&] { la::launch_chunk_state_dma_varlen(cs, lam, p.v, s); });
         if (rc) return rc;
         la::ScanArgs sc{slots, kv_in, 0, nullptr, 0, p.L, static_cast<int>(D), Hi, 0, 0, 0};
@@ -486,13 +514,16 @@ int la_fwd_varlen(const void* Q, const void* K, const void* V, const float* lamb
     a.D = static_cast<int>(D);
     a.Bk = Bk;
     a.H = Hi;
+    a.phi = phi;
+    a.phi_mask = 3;
     return launch("fwd_varlen_dma", s, [&] { la::launch_fwd_dma_varlen(a, lam, p.v, s); });
 }
 
 int la_decode_step_paged(float* pool, int64_t pool_slots, const int32_t* slot_of, const void* q, const void* k,
                          const void* v, const float* lambda, int64_t Bs, int64_t H, int64_t D, int32_t dtype,
-                         void* o, void* hip_stream) {
+                         int32_t phi, void* o, void* hip_stream) {
     if (dtype != LA_F32 && dtype != LA_BF16) return LA_EINVAL;
+    if (!valid_phi(phi)) return LA_EINVAL;
     if (Bs <= 0 || H <= 0 || D <= 0 || pool_slots <= 0) return LA_EINVAL;
     if (!supported_D(D) || H > la::kMaxHeads) return LA_EUNSUPPORTED;
     if (!pool || !slot_of || !q || !k || !v || !o) return LA_EINVAL;
@@ -515,13 +546,14 @@ int la_decode_step_paged(float* pool, int64_t pool_slots, const int32_t* slot_of
     int dev_count = 0;
     if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count == 0) return LA_ENODEV;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    la::DecodeArgs a{pool, q, k, v, o, static_cast<int>(D), static_cast<int>(H), pairs, slot_of, pool_slots};
+    la::DecodeArgs a{pool, q, k, v, o, static_cast<int>(D), static_cast<int>(H), pairs, slot_of, pool_slots, phi};
     return launch("decode_paged", s, [&] { la::launch_decode(a, lam, dtype == LA_BF16, s); });
 }
 
 int la_decode_step(float* state, const void* q, const void* k, const void* v, const float* lambda,
-                   int64_t Bs, int64_t H, int64_t D, int32_t dtype, void* o, void* hip_stream) {
+                   int64_t Bs, int64_t H, int64_t D, int32_t dtype, int32_t phi, void* o, void* hip_stream) {
     if (dtype != LA_F32 && dtype != LA_BF16) return LA_EINVAL;
+    if (!valid_phi(phi)) return LA_EINVAL;
     if (Bs <= 0 || H <= 0 || D <= 0) return LA_EINVAL;
     if (!supported_D(D) || H > la::kMaxHeads) return LA_EUNSUPPORTED;
     if (!state || !q || !k || !v || !o) return LA_EINVAL;
@@ -542,7 +574,7 @@ int la_decode_step(float* state, const void* q, const void* k, const void* v, co
     int dev_count = 0;
     if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count == 0) return LA_ENODEV;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    la::DecodeArgs a{state, q, k, v, o, static_cast<int>(D), static_cast<int>(H), pairs, nullptr, 0};
+    la::DecodeArgs a{state, q, k, v, o, static_cast<int>(D), static_cast<int>(H), pairs, nullptr, 0, phi};
     return launch("decode", s, [&] { la::launch_decode(a, lam, dtype == LA_BF16, s); });
 }
 

@@ -274,6 +274,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_rev_dma(SweepArgs a, LamArgs lam
 // Each wave holds 64 accumulator registers instead of 128, so two waves share
 // every SIMD and one hides the other's LDS and MFMA latency.  The value group
 // builds the P tiles, the key group the G tiles.
+template <bool PHI>
 __global__ __launch_bounds__(64 * 8, 1) void k_rev_dma_split(SweepArgs a, LamArgs lam) {
     __shared__ RevDmaTiles sm;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
@@ -357,6 +358,12 @@ __global__ __launch_bounds__(64 * 8, 1) void k_rev_dma_split(SweepArgs a, LamArg
         wait_vmcnt<0>();
         __syncthreads();  // A(i)
         if (i + 1 < nblk) issue(i + 1);
+        if constexpr (PHI) {
+            // the feature map on this block's query and key tiles, once, in place
+            phi_tile(sm.t[stage][0], a.phi, tid, 64 * 8);
+            phi_tile(sm.t[stage][1], a.phi, tid, 64 * 8);
+            __syncthreads();  // T(i)
+        }
         if (i == 0) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
@@ -425,7 +432,16 @@ __global__ __launch_bounds__(64 * 8, 1) void k_rev_dma_split(SweepArgs a, LamArg
             if (j < m) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const int64_t off = (t0 + j) * D + 32 * q + 16 * h + 4 * g;
+                    const int col = 32 * q + 16 * h + 4 * g;
+                    if (PHI && grp) {
+                        // dK with respect to the raw keys: phi'(k) from the mapped key tile
+                        const u32x2 kp = *reinterpret_cast<const u32x2*>(sm.t[stage][1] + swz(j, col));
+                        acc[h][0] *= dphi_of_phi(__uint_as_float(kp.x << 16), a.phi);
+                        acc[h][1] *= dphi_of_phi(__uint_as_float(kp.x & 0xFFFF0000u), a.phi);
+                        acc[h][2] *= dphi_of_phi(__uint_as_float(kp.y << 16), a.phi);
+                        acc[h][3] *= dphi_of_phi(__uint_as_float(kp.y & 0xFFFF0000u), a.phi);
+                    }
+                    const int64_t off = (t0 + j) * D + col;
                     *reinterpret_cast<u32x2*>(outg + off) = u32x2{pack_bf16(acc[h][0], acc[h][1]), pack_bf16(acc[h][2], acc[h][3])};
                 }
             }
@@ -470,8 +486,10 @@ bool rev_dma_supported(int d, int bk, int64_t n) { return d == 128 && bk == 64 &
 
 void launch_rev_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(a.pairs * a.chunks));
-    if (waves == 8)
-        hipLaunchKernelGGL(k_rev_dma_split, grid, dim3(64 * 8), 0, s, a, lam);
+    if (waves == 8 && a.phi)
+        hipLaunchKernelGGL(k_rev_dma_split<true>, grid, dim3(64 * 8), 0, s, a, lam);
+    else if (waves == 8)
+        hipLaunchKernelGGL(k_rev_dma_split<false>, grid, dim3(64 * 8), 0, s, a, lam);
     else
         hipLaunchKernelGGL(k_rev_dma, grid, dim3(64 * NW), 0, s, a, lam);
 }

@@ -50,7 +50,7 @@ struct DmaTiles {
     float pw[BK + 1];
 };
 
-template <int NW, bool VARLEN>
+template <int NW, bool VARLEN, bool PHI>
 __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam, const VarlenArgs* var) {
     constexpr int NVT = 8 / NW;  // 16-column value tiles per compute wave
     __shared__ DmaTiles sm;
@@ -64,7 +64,7 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
     const int64_t ld = VARLEN ? wk.ld : D;  // elements between token rows
 
     for (int e = tid; e <= BK; e += 64 * (NW + 1)) sm.pw[e] = lam_pow(lv, e);
-    __syncthreads();  // decay table; every wave passes exactly 1 + 2 * nblk barriers
+    __syncthreads();  // decay table; every wave passes exactly 1 + (2 + [phi]) * nblk barriers
 
     if (w == NW) {
         // ------------------------------------------------------------ loader wave
@@ -100,6 +100,7 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
                 wait_vmcnt<0>();
             __builtin_amdgcn_s_barrier();  // A(n): stage n is ready; stage (n+2) % 3 is free
             if (n + 2 < nblk) issue(n + 2);
+            if constexpr (PHI) __builtin_amdgcn_s_barrier();  // T(n): feature map applied
             __builtin_amdgcn_s_barrier();  // B(n)
         }
         return;
@@ -153,6 +154,14 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
         const uint16_t* Ks = sm.t[stage][1];
         const uint16_t* Vs = sm.t[stage][2];
         __syncthreads();  // A(n)
+        if constexpr (PHI) {
+            // the feature map on this block's query and key tiles (in the dQ sweep: the keys,
+            // which sit in the value slot), once, in place
+#pragma unroll
+            for (int x = 0; x < 3; ++x)
+                if (a.phi_mask & (1 << x)) phi_tile(sm.t[stage][x], a.phi, tid, 64 * NW);
+            __syncthreads();  // T(n)
+        }
 
         // ---- score tiles A^T = (K Q^T) o M^T: tile (at, st), at <= st, holds A^T[s'][s] for
         // s' = 16 at + 4 g + r, s = 16 st + li; kept iff s' <= s, scaled by lam^(s - s').
@@ -182,6 +191,21 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
         for (int vt = 0; vt < NVT; ++vt)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) vf[vt][kb] = op_tr_k(Vs, 32 * kb, 16 * (NVT * w + vt), 4, g, li);
+
+        // raw queries of this block's output rows, for phi'(q) in the dQ sweep: loaded now, used
+        // at the stores (rows past the block's end read its last row and are not stored)
+        u32x2 qraw[PHI ? NT : 1][NVT];
+        if constexpr (PHI) {
+            if (a.phi_grad) {
+#pragma unroll
+                for (int st = 0; st < NT; ++st)
+#pragma unroll
+                    for (int vt = 0; vt < NVT; ++vt) {
+                        const int64_t off = (t0 + min(16 * st + li, m - 1)) * ld + 16 * (NVT * w + vt) + 4 * g;
+                        qraw[st][vt] = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.phi_grad) + base + off);
+                    }
+            }
+        }
 
         // ---- per 16-token column: O^T = diag(lam^(s+1)) S^T Q^T + V^T A^T, store
 #pragma unroll
@@ -218,8 +242,17 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
             if (s < m) {
 #pragma unroll
                 for (int vt = 0; vt < NVT; ++vt) {
-                    uint16_t* dst = Og + (t0 + s) * ld + 16 * (NVT * w + vt) + 4 * g;
-                    *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16(o[vt][0], o[vt][1]), pack_bf16(o[vt][2], o[vt][3])};
+                    const int64_t off = (t0 + s) * ld + 16 * (NVT * w + vt) + 4 * g;
+                    f32x4 ov = o[vt];
+                    if (PHI && a.phi_grad) {
+                        // chain rule through the feature map: phi'(raw q) for the dQ sweep
+                        const u32x2 raw = qraw[PHI ? st : 0][vt];
+                        ov[0] *= dphi_of_x(__uint_as_float(raw.x << 16), a.phi);
+                        ov[1] *= dphi_of_x(__uint_as_float(raw.x & 0xFFFF0000u), a.phi);
+                        ov[2] *= dphi_of_x(__uint_as_float(raw.y << 16), a.phi);
+                        ov[3] *= dphi_of_x(__uint_as_float(raw.y & 0xFFFF0000u), a.phi);
+                    }
+                    *reinterpret_cast<u32x2*>(Og + off) = u32x2{pack_bf16(ov[0], ov[1]), pack_bf16(ov[2], ov[3])};
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -265,13 +298,14 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
     }
 }
 
-template <int NW>
+template <int NW, bool PHI>
 __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamArgs lam) {
-    fwd_body<NW, false>(a, lam, nullptr);
+    fwd_body<NW, false, PHI>(a, lam, nullptr);
 }
 
+template <bool PHI>
 __global__ __launch_bounds__(64 * 5, 1) void k_fwd_dma_varlen(SweepArgs a, LamArgs lam, VarlenArgs v) {
-    fwd_body<4, true>(a, lam, &v);
+    fwd_body<4, true, PHI>(a, lam, &v);
 }
 
 }  // namespace
@@ -282,15 +316,25 @@ bool fwd_dma_supported(int d, int bk, int64_t n) {
 
 void launch_fwd_dma_varlen(const SweepArgs& a, const LamArgs& lam, const VarlenArgs& v, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(static_cast<int64_t>(v.wp[v.nseq]) * a.H));
-    hipLaunchKernelGGL(k_fwd_dma_varlen, grid, dim3(64 * 5), 0, s, a, lam, v);
+    if (a.phi)
+        hipLaunchKernelGGL(k_fwd_dma_varlen<true>, grid, dim3(64 * 5), 0, s, a, lam, v);
+    else
+        hipLaunchKernelGGL(k_fwd_dma_varlen<false>, grid, dim3(64 * 5), 0, s, a, lam, v);
 }
 
 void launch_fwd_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(a.pairs * a.chunks));
-    if (waves == 8)
-        hipLaunchKernelGGL(k_fwd_dma<8>, grid, dim3(64 * 9), 0, s, a, lam);
-    else
-        hipLaunchKernelGGL(k_fwd_dma<4>, grid, dim3(64 * 5), 0, s, a, lam);
+    if (waves == 8) {
+        if (a.phi)
+            hipLaunchKernelGGL((k_fwd_dma<8, true>), grid, dim3(64 * 9), 0, s, a, lam);
+        else
+            hipLaunchKernelGGL((k_fwd_dma<8, false>), grid, dim3(64 * 9), 0, s, a, lam);
+    } else {
+        if (a.phi)
+            hipLaunchKernelGGL((k_fwd_dma<4, true>), grid, dim3(64 * 5), 0, s, a, lam);
+        else
+            hipLaunchKernelGGL((k_fwd_dma<4, false>), grid, dim3(64 * 5), 0, s, a, lam);
+    }
 }
 
 }  // namespace la

@@ -39,6 +39,11 @@ __global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs l
     const int64_t t_begin = static_cast<int64_t>(c) * a.L;
     const int64_t t_end = min(a.N, t_begin + a.L);
     const int64_t base = pair * a.N * D;
+    // operand x of slot bit (0: a, 1: b, 2: c), through the feature map when that slot takes it
+    auto opd = [&](const void* p, int bit, int64_t i) {
+        const float x = ld<BF16>(p, i);
+        return (a.phi && ((a.phi_mask >> bit) & 1)) ? phi_apply(x, a.phi) : x;
+    };
     fill_powers(sh.pw, lv, Bk);
 
     const float* init = nullptr;
@@ -66,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs l
             const int s = i / m, s2 = i % m;
             float x = 0.f;
             if (s2 <= s) {
-                for (int f = 0; f < D; ++f) x += ld<BF16>(a.a, r0 + s * D + f) * ld<BF16>(a.b, r0 + s2 * D + f);
+                for (int f = 0; f < D; ++f) x += opd(a.a, 0, r0 + s * D + f) * opd(a.b, 1, r0 + s2 * D + f);
                 x *= sh.pw[s - s2];
             }
             sh.score[s * kMaxBk + s2] = x;
@@ -75,16 +80,17 @@ __global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs l
         for (int i = tid; i < m * D; i += kThreads) {
             const int s = i / D, col = i % D;
             float inter = 0.f, intra = 0.f;
-            for (int f = 0; f < D; ++f) inter += ld<BF16>(a.a, r0 + s * D + f) * sh.state[f * D + col];
-            for (int s2 = 0; s2 <= s; ++s2) intra += sh.score[s * kMaxBk + s2] * ld<BF16>(a.c, r0 + s2 * D + col);
-            st<BF16>(a.out0, r0 + s * D + col, sh.pw[s + 1] * inter + intra);
+            for (int f = 0; f < D; ++f) inter += opd(a.a, 0, r0 + s * D + f) * sh.state[f * D + col];
+            for (int s2 = 0; s2 <= s; ++s2) intra += sh.score[s * kMaxBk + s2] * opd(a.c, 2, r0 + s2 * D + col);
+            const float gr = a.phi_grad ? dphi_of_x(ld<BF16>(a.phi_grad, r0 + s * D + col), a.phi) : 1.f;
+            st<BF16>(a.out0, r0 + s * D + col, gr * (sh.pw[s + 1] * inter + intra));
         }
         __syncthreads();
         for (int i = tid; i < D * D; i += kThreads) {
             const int f = i / D, col = i % D;
             float acc = 0.f;
             for (int s = 0; s < m; ++s)
-                acc += sh.pw[m - 1 - s] * ld<BF16>(a.b, r0 + s * D + f) * ld<BF16>(a.c, r0 + s * D + col);
+                acc += sh.pw[m - 1 - s] * opd(a.b, 1, r0 + s * D + f) * opd(a.c, 2, r0 + s * D + col);
             sh.state[i] = sh.pw[m] * sh.state[i] + acc;
         }
         __syncthreads();
@@ -113,6 +119,11 @@ __global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs l
     const int64_t t_begin = static_cast<int64_t>(c) * a.L;
     const int64_t t_end = min(a.N, t_begin + a.L);
     const int64_t base = pair * a.N * D;
+    // queries and keys through the feature map
+    auto opd = [&](const void* p, int bit, int64_t i) {
+        const float x = ld<BF16>(p, i);
+        return (a.phi && ((a.phi_mask >> bit) & 1)) ? phi_apply(x, a.phi) : x;
+    };
     fill_powers(sh.pw, lv, Bk);
     const bool last = c == a.chunks - 1;
     const float* init = !last ? a.slots + (pair * (a.chunks - 1) + c) * D * D
@@ -140,9 +151,10 @@ __global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs l
         for (int idx = tid; idx < m * D; idx += kThreads) {
             const int j = idx / D, f = idx % D;
             float intra = 0.f, inter = 0.f;
-            for (int i = j; i < m; ++i) intra += sh.score[i * kMaxBk + j] * ld<BF16>(a.a, r0 + i * D + f);
+            for (int i = j; i < m; ++i) intra += sh.score[i * kMaxBk + j] * opd(a.a, 0, r0 + i * D + f);
             for (int col = 0; col < D; ++col) inter += sh.state[f * D + col] * ld<BF16>(a.c, r0 + j * D + col);
-            st<BF16>(a.out0, r0 + j * D + f, intra + sh.pw[m - shift - j] * inter);
+            const float gr = a.phi ? dphi_of_x(ld<BF16>(a.b, r0 + j * D + f), a.phi) : 1.f;
+            st<BF16>(a.out0, r0 + j * D + f, gr * (intra + sh.pw[m - shift - j] * inter));
         }
         __syncthreads();
         // P[i][j] = lam^(i-j) q_i . k_j for i >= j
@@ -150,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs l
             const int i = idx / m, j = idx % m;
             float x = 0.f;
             if (j <= i) {
-                for (int f = 0; f < D; ++f) x += ld<BF16>(a.a, r0 + i * D + f) * ld<BF16>(a.b, r0 + j * D + f);
+                for (int f = 0; f < D; ++f) x += opd(a.a, 0, r0 + i * D + f) * opd(a.b, 1, r0 + j * D + f);
                 x *= sh.pw[i - j];
             }
             sh.score[i * kMaxBk + j] = x;
@@ -160,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs l
             const int j = idx / D, col = idx % D;
             float intra = 0.f, inter = 0.f;
             for (int i = j; i < m; ++i) intra += sh.score[i * kMaxBk + j] * ld<BF16>(a.g, r0 + i * D + col);
-            for (int f = 0; f < D; ++f) inter += ld<BF16>(a.b, r0 + j * D + f) * sh.state[f * D + col];
+            for (int f = 0; f < D; ++f) inter += opd(a.b, 1, r0 + j * D + f) * sh.state[f * D + col];
             st<BF16>(a.out1, r0 + j * D + col, intra + sh.pw[m - shift - j] * inter);
         }
         __syncthreads();
@@ -168,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs l
             const int f = idx / D, col = idx % D;
             float acc = 0.f;
             for (int s = 0; s < m; ++s)
-                acc += sh.pw[s] * ld<BF16>(a.a, r0 + s * D + f) * ld<BF16>(a.g, r0 + s * D + col);
+                acc += sh.pw[s] * opd(a.a, 0, r0 + s * D + f) * ld<BF16>(a.g, r0 + s * D + col);
             sh.state[idx] = sh.pw[m - shift] * sh.state[idx] + acc;
         }
         __syncthreads();
@@ -204,7 +216,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state_generic(ChunkStateArgs
             float acc = 0.f;
             for (int s = 0; s < m; ++s) {
                 const float w = a.reverse ? pw[s] : pw[m - 1 - s];
-                acc += w * ld<BF16>(a.x, r0 + s * D + f) * ld<BF16>(a.y, r0 + s * D + col);
+                const float x = ld<BF16>(a.x, r0 + s * D + f), y = ld<BF16>(a.y, r0 + s * D + col);
+                acc += w * ((a.phi_mask & 1) ? phi_apply(x, a.phi) : x) * ((a.phi_mask & 2) ? phi_apply(y, a.phi) : y);
             }
             state[i] = pw[m] * state[i] + acc;
         }
@@ -285,8 +298,8 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a, LamArgs lam) 
         sp = static_cast<int64_t>(slot) * a.H + pair % a.H;
     }
     for (int i = tid; i < D; i += kThreads) {
-        qs[i] = ld<BF16>(a.q, pair * D + i);
-        ks[i] = ld<BF16>(a.k, pair * D + i);
+        qs[i] = phi_apply(ld<BF16>(a.q, pair * D + i), a.phi);
+        ks[i] = phi_apply(ld<BF16>(a.k, pair * D + i), a.phi);
         vs[i] = ld<BF16>(a.v, pair * D + i);
     }
     __syncthreads();

@@ -40,7 +40,7 @@ struct StateTiles {
     float pw[BK + 1];
 };
 
-template <bool VARLEN>
+template <bool VARLEN, bool PHI>
 __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArgs& lam, const VarlenArgs* var) {
     __shared__ StateTiles sm;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
@@ -112,6 +112,12 @@ __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArg
         wait_vmcnt<0>();  // this block's loads (the only ones in flight)
         __syncthreads();  // stage n % 2 is complete; stage (n + 1) % 2 is no longer read
         if (n + 1 < nblk) issue(n + 1);
+        if constexpr (PHI) {
+            // the feature map on this block's keys or queries, once, in place
+            if (a.phi_mask & 1) phi_tile(sm.t[stage][0], a.phi, tid, 64 * NW);
+            if (a.phi_mask & 2) phi_tile(sm.t[stage][1], a.phi, tid, 64 * NW);
+            __syncthreads();
+        }
         const uint16_t* Xs = sm.t[stage][0];
         const uint16_t* Ys = sm.t[stage][1];
         // weights of token s = 32 kb + kappa(g, e), on the Y operand
@@ -140,12 +146,14 @@ __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArg
         for (int r = 0; r < 4; ++r) dst[(16 * at + 4 * g + r) * D + 16 * w + li] = S[at][r];
 }
 
+template <bool PHI>
 __global__ __launch_bounds__(64 * NW, 2) void k_chunk_state_dma(ChunkStateArgs a, LamArgs lam) {
-    state_body<false>(a, lam, nullptr);
+    state_body<false, PHI>(a, lam, nullptr);
 }
 
+template <bool PHI>
 __global__ __launch_bounds__(64 * NW, 2) void k_chunk_state_dma_varlen(ChunkStateArgs a, LamArgs lam, VarlenArgs v) {
-    state_body<true>(a, lam, &v);
+    state_body<true, PHI>(a, lam, &v);
 }
 
 }  // namespace
@@ -154,13 +162,19 @@ bool state_dma_supported(int d, int bk, int64_t n) { return d == 128 && bk == 64
 
 void launch_chunk_state_dma(const ChunkStateArgs& a, const LamArgs& lam, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(a.pairs * (a.chunks - 1)));
-    hipLaunchKernelGGL(k_chunk_state_dma, grid, dim3(64 * NW), 0, s, a, lam);
+    if (a.phi)
+        hipLaunchKernelGGL(k_chunk_state_dma<true>, grid, dim3(64 * NW), 0, s, a, lam);
+    else
+        hipLaunchKernelGGL(k_chunk_state_dma<false>, grid, dim3(64 * NW), 0, s, a, lam);
 }
 
 void launch_chunk_state_dma_varlen(const ChunkStateArgs& a, const LamArgs& lam, const VarlenArgs& v,
                                    hipStream_t s) {
     dim3 grid(static_cast<unsigned>(static_cast<int64_t>(v.wp[v.nseq] - v.nseq) * a.H));
-    hipLaunchKernelGGL(k_chunk_state_dma_varlen, grid, dim3(64 * NW), 0, s, a, lam, v);
+    if (a.phi)
+        hipLaunchKernelGGL(k_chunk_state_dma_varlen<true>, grid, dim3(64 * NW), 0, s, a, lam, v);
+    else
+        hipLaunchKernelGGL(k_chunk_state_dma_varlen<false>, grid, dim3(64 * NW), 0, s, a, lam, v);
 }
 
 }  // namespace la

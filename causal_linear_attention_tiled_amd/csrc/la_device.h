@@ -49,6 +49,25 @@ __device__ __forceinline__ double lam_pow64(float lam, int64_t e) {
 // The same rounded once to float.
 __device__ __forceinline__ float lam_pow(float lam, int64_t e) { return static_cast<float>(lam_pow64(lam, e)); }
 
+// Elementwise kernel feature maps on queries and keys (identity, elu(x) + 1,
+// relu); both non-identity maps have a derivative that is a function of phi(x)
+// itself: min(1, phi) for elu + 1, [phi > 0] for relu.
+enum { kPhiIdentity = 0, kPhiElu1 = 1, kPhiRelu = 2 };
+
+__device__ __forceinline__ float phi_apply(float x, int kind) {
+    if (kind == kPhiElu1) return x > 0.f ? x + 1.f : __expf(x);
+    if (kind == kPhiRelu) return x > 0.f ? x : 0.f;
+    return x;
+}
+
+__device__ __forceinline__ float dphi_of_phi(float y, int kind) {
+    if (kind == kPhiElu1) return fminf(y, 1.f);
+    if (kind == kPhiRelu) return y > 0.f ? 1.f : 0.f;
+    return 1.f;
+}
+
+__device__ __forceinline__ float dphi_of_x(float x, int kind) { return dphi_of_phi(phi_apply(x, kind), kind); }
+
 // keep ? pw[e] : 0 for a decay table pw in LDS.  The read is unconditional (the
 // index is clamped to the table), so several of them issue back to back rather
 // than as one masked branch and LDS round trip each.

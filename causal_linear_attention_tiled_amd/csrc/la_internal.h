@@ -56,6 +56,10 @@ struct SweepArgs {
     int64_t L;            // chunk length in tokens
     int D, Bk, H, chunks;
     int64_t pairs;
+    int phi;              // feature map (kPhi*) applied to the operands in phi_mask
+    int phi_mask;         // bit 0: a, bit 1: b, bit 2: c (forward: Q, K; dQ sweep: K in c)
+    const void* phi_grad; // forward-direction sweeps: raw tensor whose phi' multiplies out0
+                          // (the dQ sweep's raw Q), or nullptr
 };
 
 // Chunk aggregate states: for the forward direction chunk c (0..chunks-2)
@@ -70,6 +74,8 @@ struct ChunkStateArgs {
     int D, Bk, H, chunks;
     int64_t pairs;
     int reverse;
+    int phi;        // feature map (kPhi*) ...
+    int phi_mask;   // ... applied to x (bit 0) and / or y (bit 1)
 };
 
 // In-place scan of the slots of every sequence.
@@ -99,6 +105,7 @@ struct DecodeArgs {
     int64_t pairs;           // Bs * H
     const int32_t* slot_of;  // [Bs] pool slot of each sequence, or nullptr (state[p] for pair p)
     int64_t pool_slots;
+    int phi;                 // feature map applied to q and k
 };
 
 // Launchers (each enqueues exactly one kernel on `s`; errors are read by the caller).

@@ -13,6 +13,7 @@
 // index runs over the tile's rows.
 #pragma once
 
+#include "la_device.h"
 #include "mfma_common.h"
 
 namespace la {
@@ -83,6 +84,22 @@ __device__ __forceinline__ bf16x8 scale8(const bf16x8& x, const float* wt) {
     for (int i = 0; i < 4; ++i)
         r[i] = pack_bf16(__uint_as_float(u[i] << 16) * wt[2 * i], __uint_as_float(u[i] & 0xFFFF0000u) * wt[2 * i + 1]);
     return __builtin_bit_cast(bf16x8, r);
+}
+
+// Apply the feature map to every element of a [64][128] bf16 tile in LDS, in
+// place, rounding to bf16; thread t of nthr takes 16-byte pieces t, t + nthr, ...
+// (the swizzle does not matter to an elementwise map).
+__device__ __forceinline__ void phi_tile(uint16_t* tile, int kind, int t, int nthr) {
+    for (int c = t; c < 64 * kTileCols / 8; c += nthr) {
+        u32x4* p = reinterpret_cast<u32x4*>(tile + 8 * c);
+        const u32x4 u = *p;
+        u32x4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r[i] = pack_bf16(phi_apply(__uint_as_float(u[i] << 16), kind),
+                             phi_apply(__uint_as_float(u[i] & 0xFFFF0000u), kind));
+        *p = r;
+    }
 }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).

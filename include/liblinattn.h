@@ -57,6 +57,19 @@ extern "C" {
 
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 
+/* Elementwise kernel feature map phi applied to queries and keys (the glossary
+ * page "Lightning Attention", features list and FAQ Q1: a kernel feature map
+ * replaces the softmax; the pages do not name one), so that
+ *     O_t = sum_{j <= t} lam^(t-j) (phi(q_t) . phi(k_j)) v_j (+ lam^(t+1) phi(q_t) S0).
+ *   LA_PHI_IDENTITY : phi(x) = x
+ *   LA_PHI_ELU1     : phi(x) = elu(x) + 1 (x + 1 for x > 0, e^x otherwise)
+ *   LA_PHI_RELU     : phi(x) = max(x, 0), phi'(0) = 0
+ * The map is applied in float32 and rounded to the tensor dtype before use.
+ * Gradients are with respect to the raw Q and K.  The register-staged kernels
+ * (block size 128, LA_FWD / LA_REV / LA_STATE = v1) have no feature map: with
+ * one, those shapes run the generic kernels. */
+enum { LA_PHI_IDENTITY = 0, LA_PHI_ELU1 = 1, LA_PHI_RELU = 2 };
+
 enum {
     LA_OK = 0,
     LA_EINVAL = 1,       /* null required pointer, non-positive size, lambda outside [0,1] or NaN,
@@ -74,6 +87,7 @@ enum {
  * with K^T V; the state is carried across blocks by a chunked prefix).
  *   Q, K, V : [B][H][N][D] dtype, device, read only.
  *   lambda  : host float32[H].
+ *   phi     : LA_PHI_* feature map on Q and K (LA_EINVAL otherwise).
  *   kv_in   : [B][H][D][D] float32 device initial state S0, or NULL for zero.
  *   O       : [B][H][N][D] dtype, device, written.
  *   kv_out  : [B][H][D][D] float32 device, receives S_N; NULL skips it.
@@ -85,7 +99,7 @@ enum {
  *             chunk but the last (float32), which la_bwd can take as fwd_ws
  *             instead of computing them again. */
 int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int64_t B, int64_t H,
-           int64_t N, int64_t D, int32_t Bk, int32_t dtype, const float* kv_in, void* O,
+           int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t phi, const float* kv_in, void* O,
            float* kv_out, void* ws, size_t ws_bytes, void* hip_stream);
 
 /* Workspace bytes la_fwd needs for this shape (0 when the sequence is not
@@ -119,9 +133,11 @@ size_t la_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_
  *             from any other call gives wrong dQ.
  *   ws      : la_bwd_workspace_bytes(...) bytes, as for la_fwd; must not
  *             overlap fwd_ws.
+ *   phi     : the feature map of the forward; dQ and dK are with respect to
+ *             the raw Q and K (phi'(q), phi'(k) applied elementwise).
  *   other arguments as for la_fwd. */
 int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const float* lambda,
-           int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype,
+           int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t phi,
            const float* kv_in, const float* dkv_out, void* dQ, void* dK, void* dV, float* dkv_in,
            const void* fwd_ws, void* ws, size_t ws_bytes, void* hip_stream);
 
@@ -135,10 +151,12 @@ size_t la_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_
  *     S <- lam S + k v^T,   o = q S
  *   state : [Bs][H][D][D] float32 device, updated in place.
  *   q,k,v : [Bs][H][D] dtype device.   o : [Bs][H][D] dtype device, written.
+ *   phi   : LA_PHI_* feature map on q and k.
  * The state after n steps from S = 0 equals the kv_out of la_fwd over those
  * n tokens, and o equals that forward's output row. */
 int la_decode_step(float* state, const void* q, const void* k, const void* v, const float* lambda,
-                   int64_t Bs, int64_t H, int64_t D, int32_t dtype, void* o, void* hip_stream);
+                   int64_t Bs, int64_t H, int64_t D, int32_t dtype, int32_t phi, void* o,
+                   void* hip_stream);
 
 /* Forward pass over a ragged batch: B sequences of different lengths packed
  * token-major in one launch (the serving-side prefill that the constant-size
@@ -159,7 +177,7 @@ int la_decode_step(float* state, const void* q, const void* k, const void* v, co
  * overrides the chunk length; a size query must see the same setting. */
 int la_fwd_varlen(const void* Q, const void* K, const void* V, const float* lambda,
                   const int64_t* seq_offsets, int64_t B, int64_t H, int64_t D, int32_t Bk,
-                  int32_t dtype, const float* kv_in, void* O, float* kv_out, void* ws,
+                  int32_t dtype, int32_t phi, const float* kv_in, void* O, float* kv_out, void* ws,
                   size_t ws_bytes, void* hip_stream);
 
 /* Workspace bytes for la_fwd_varlen (0 when no sequence is split into chunks,
@@ -176,10 +194,10 @@ size_t la_fwd_varlen_workspace_bytes(const int64_t* seq_offsets, int64_t B, int6
  *             [0, pool_slots); an entry outside that range leaves the pool
  *             untouched and writes NaN to the sequence's output row (device
  *             values cannot be checked before the launch).
- *   q, k, v, o, lambda, dtype, D: as for la_decode_step ([Bs][H][D]). */
+ *   q, k, v, o, lambda, dtype, D, phi: as for la_decode_step ([Bs][H][D]). */
 int la_decode_step_paged(float* pool, int64_t pool_slots, const int32_t* slot_of, const void* q,
                          const void* k, const void* v, const float* lambda, int64_t Bs, int64_t H,
-                         int64_t D, int32_t dtype, void* o, void* hip_stream);
+                         int64_t D, int32_t dtype, int32_t phi, void* o, void* hip_stream);
 
 /* Static text for a status code.  For LA_EHIP the text of the last HIP error
  * seen by the calling thread is appended (thread-local buffer). */

@@ -45,12 +45,12 @@ LAM = (ctypes.c_float * 4)(0.5, 0.9, 1.0, 0.0)
 
 
 def fwd(**kw):
-    args = dict(Q=Q_, K=K_, V=V_, lam=LAM, B=2, H=4, N=1000, D=128, Bk=64, dt=la.LA_BF16, kv_in=None,
+    args = dict(Q=Q_, K=K_, V=V_, lam=LAM, B=2, H=4, N=1000, D=128, Bk=64, dt=la.LA_BF16, phi=0, kv_in=None,
                 O=O_, kv_out=None, ws=W_, ws_bytes=1 << 40, stream=None)
     args.update(kw)
     v = lambda x: None if x is None else ctypes.c_void_p(x)
     return la.lib.la_fwd(v(args["Q"]), v(args["K"]), v(args["V"]), args["lam"], args["B"], args["H"],
-                         args["N"], args["D"], args["Bk"], args["dt"], v(args["kv_in"]), v(args["O"]),
+                         args["N"], args["D"], args["Bk"], args["dt"], args["phi"], v(args["kv_in"]), v(args["O"]),
                          v(args["kv_out"]), v(args["ws"]), args["ws_bytes"], v(args["stream"]))
 
 
@@ -61,6 +61,8 @@ def fwd(**kw):
     (dict(B=0), la.LA_EINVAL),
     (dict(N=-5), la.LA_EINVAL),
     (dict(dt=7), la.LA_EINVAL),
+    (dict(phi=3), la.LA_EINVAL),                     # unknown feature map
+    (dict(phi=-1), la.LA_EINVAL),
     (dict(D=48), la.LA_EUNSUPPORTED),
     (dict(D=256), la.LA_EUNSUPPORTED),
     (dict(Bk=48), la.LA_EUNSUPPORTED),
@@ -107,7 +109,7 @@ def test_bwd_rejects():
     lam = (ctypes.c_float * 2)(0.5, 0.5)
     G_ = A * 10
     call = lambda dq, dk, dv, g=G_, gf=None, ds=None: la.lib.la_bwd(
-        v(Q_), v(K_), v(V_), v(g), lam, 1, 2, 128, 64, 64, la.LA_BF16, None, v(gf) if gf else None,
+        v(Q_), v(K_), v(V_), v(g), lam, 1, 2, 128, 64, 64, la.LA_BF16, 0, None, v(gf) if gf else None,
         v(dq) if dq else None, v(dk), v(dv), v(ds) if ds else None, None, None, 0, None)
     assert call(None, S_, W_) == la.LA_EINVAL          # dQ missing
     assert call(O_, O_, W_) == la.LA_EINVAL            # dQ and dK alias
@@ -129,7 +131,7 @@ def test_bwd_forward_workspace_checked():
     G_, X_, Y_, WB_ = A * 10, A * 11, A * 12, A * 13
     N = 4096  # one long sequence: split into chunks
     assert la.la_fwd_workspace_bytes(1, 1, N, 128, 64, la.LA_BF16) > 0
-    call = lambda fws, ws=WB_: la.lib.la_bwd(v(Q_), v(K_), v(V_), v(G_), lam1, 1, 1, N, 128, 64, la.LA_BF16,
+    call = lambda fws, ws=WB_: la.lib.la_bwd(v(Q_), v(K_), v(V_), v(G_), lam1, 1, 1, N, 128, 64, la.LA_BF16, 0,
                                              None, None, v(O_), v(X_), v(Y_), None, v(fws) if fws else None,
                                              v(ws), 1 << 40, None)
     assert call(WB_ + 8) == la.LA_EALIGN
@@ -140,8 +142,8 @@ def test_bwd_forward_workspace_checked():
 def test_decode_rejects():
     v = ctypes.c_void_p
     lam = (ctypes.c_float * 2)(0.5, 0.5)
-    call = lambda st, o, D=128, dt=la.LA_BF16, lm=lam: la.lib.la_decode_step(
-        v(st) if st else None, v(Q_), v(K_), v(V_), lm, 4, 2, D, dt, v(o) if o else None, None)
+    call = lambda st, o, D=128, dt=la.LA_BF16, lm=lam, phi=0: la.lib.la_decode_step(
+        v(st) if st else None, v(Q_), v(K_), v(V_), lm, 4, 2, D, dt, phi, v(o) if o else None, None)
     assert call(None, O_) == la.LA_EINVAL
     assert call(S_, None) == la.LA_EINVAL
     assert call(S_, O_, D=100) == la.LA_EUNSUPPORTED
@@ -149,6 +151,7 @@ def test_decode_rejects():
     assert call(S_ + 4, O_) == la.LA_EALIGN
     assert call(Q_, O_) == la.LA_EINVAL                # state aliases q
     assert call(S_, O_, lm=(ctypes.c_float * 2)(0.5, 2.0)) == la.LA_EINVAL
+    assert call(S_, O_, phi=9) == la.LA_EINVAL
 
 
 def test_no_device_reported_without_gpu():
@@ -178,7 +181,7 @@ def test_fwd_varlen_rejects():
 
     def call(offs, B=None, H=2, D=128, Bk=64, dt=la.LA_BF16, O=O_, ws=W_, ws_bytes=1 << 40, kv_out=None):
         B = len(offs) - 1 if B is None else B
-        return la.lib.la_fwd_varlen(v(Q_), v(K_), v(V_), lam, _offs(offs), B, H, D, Bk, dt, None, v(O),
+        return la.lib.la_fwd_varlen(v(Q_), v(K_), v(V_), lam, _offs(offs), B, H, D, Bk, dt, 0, None, v(O),
                                     v(kv_out), v(ws), ws_bytes, None)
     assert call([1, 5, 9]) == la.LA_EINVAL                    # offsets must start at 0
     assert call([0, 9, 5]) == la.LA_EINVAL                    # and not decrease
@@ -202,7 +205,7 @@ def test_decode_paged_rejects():
     lam = (ctypes.c_float * 2)(0.5, 0.5)
     IDX_ = A * 12
     call = lambda pool=S_, P=8, idx=IDX_, o=O_, D=128: la.lib.la_decode_step_paged(
-        v(pool), P, v(idx) if idx else None, v(Q_), v(K_), v(V_), lam, 4, 2, D, la.LA_BF16, v(o), None)
+        v(pool), P, v(idx) if idx else None, v(Q_), v(K_), v(V_), lam, 4, 2, D, la.LA_BF16, 0, v(o), None)
     assert call(P=0) == la.LA_EINVAL
     assert call(idx=None) == la.LA_EINVAL
     assert call(idx=IDX_ + 4) == la.LA_EALIGN
