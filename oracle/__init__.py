@@ -12,14 +12,15 @@ paragraph and mechanism field of the phantomic12 record; the glossary page
   O = ((Q K^T) * D) V with D[i, j] = lam^(i-j) for i >= j, else 0.
 * F2, recurrent form, ``oracle.c``: S <- lam S + k_t v_t^T, o_t = q_t S.
 
-Readings where the pages are silent (each also listed in the design doc):
-the formula and the decay lam come from the workload definition, the feature
-map is the identity, there is no normaliser, position t attends to itself,
-lam is a float32 value promoted to double with lam^0 = 1 (so lam = 0 keeps only
-the diagonal), an optional initial state S0 adds lam^(t+1) q_t S0, and the
-backward is that of L = <dO, O> + <G, S_N> for an optional gradient G arriving
-at the final state, giving dQ, dK, dV and the gradient of S0 (no gradient of
-lam).
+Readings where the pages are silent: the formula and the decay lam come from
+the workload definition, the feature map is the identity unless one of the
+elementwise maps in ``feature.py`` is asked for, there is no normaliser,
+position t attends to itself, lam is a float32 value promoted to double with
+lam^0 = 1 (so lam = 0 keeps only the diagonal), an optional initial state S0
+adds lam^(t+1) q_t S0, and the backward is that of L = <dO, O> + <G, S_N> for
+an optional gradient G arriving at the final state, giving dQ, dK, dV, the
+gradient of S0, and the derivative of the same loss with respect to lam
+(``dlam_recurrent``).
 """
 from __future__ import annotations
 
@@ -29,7 +30,7 @@ import subprocess
 
 import numpy as np
 
-from .quadratic import (decay_matrix, fwd_quadratic, bwd_quadratic)  # noqa: F401
+from .quadratic import (decay_matrix, fwd_quadratic, bwd_quadratic, dlam_quadratic)  # noqa: F401
 from . import feature  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -57,6 +58,7 @@ def _lib():
         lib.oracle_fwd_recurrent.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, i64]
         lib.oracle_bwd_recurrent.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         lib.oracle_decode_step.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp]
+        lib.oracle_dlam_recurrent.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp]
         _lib_handle = lib
     return _lib_handle
 
@@ -133,6 +135,23 @@ def bwd_recurrent(q, k, v, dout, lam, s_init=None, want=("dq", "dk", "dv"), g_fi
     if want_ds_init:
         return dq, dk, dv, ds0.reshape(*lead, d, d)
     return dq, dk, dv
+
+
+def dlam_recurrent(q, k, v, dout, lam, s_init=None, g_final=None, phi="identity"):
+    """F2 derivative of L = <dO, O> + <G, S_N> with respect to the decay lam, one value per
+    sequence (shape: the leading dims), by forward-mode differentiation of the recurrence
+    (T = dS/dlam carried next to S; oracle.c).  The feature map ``phi`` on q and k does not
+    depend on lam."""
+    q, k, v, dout = feature.phi(q, phi), feature.phi(k, phi), _f64(v), _f64(dout)
+    *lead, n, d = q.shape
+    pairs = int(np.prod(lead)) if lead else 1
+    lam_arr = _lams(lam, pairs)
+    s0 = None if s_init is None else _f64(s_init).reshape(pairs, d, d)
+    gf = None if g_final is None else _f64(g_final).reshape(pairs, d, d)
+    out = np.empty(pairs)
+    _lib().oracle_dlam_recurrent(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data, pairs,
+                                 n, d, lam_arr.ctypes.data, _ptr(s0), _ptr(gf), out.ctypes.data)
+    return out.reshape(lead) if lead else out[0]
 
 
 def decode_step(state, q, k, v, lam, phi="identity"):

@@ -20,6 +20,8 @@
  * The backward is for the loss L = <dO, O> with S0 held constant:
  *   forward sweep  S <- lam S + k_t v_t^T,  dq_t = S dO_t
  *   reverse sweep  dS <- lam dS + q_t dO_t^T,  dk_t = dS v_t,  dv_t = dS^T k_t.
+ * The derivative of the same loss with respect to lam comes from differentiating
+ * the recurrence forward in lam: T = dS/dlam is carried next to S.
  * Pinned by the CPU tests against exact rational brute force of the definition
  * (including exact gradients obtained from the definition by linearity),
  * closed forms for constant inputs, the quadratic masked form and a library
@@ -140,6 +142,50 @@ static void bwd_one(const double* q, const double* k, const double* v, const dou
     free(S);
 }
 
+/* Derivative of L = <dO, O> + <G, S_N> with respect to lam for one sequence
+ * (G = g_final, may be NULL for zero), by forward-mode differentiation of the
+ * recurrence.  With T_t = dS_t/dlam (S_{-1} = S0 does not depend on lam):
+ *     T_t = S_{t-1} + lam T_{t-1},   T_{-1} = 0,
+ *     S_t = lam S_{t-1} + k_t v_t^T,
+ *     d o_t / dlam = q_t T_t,
+ * so dL/dlam = sum_t <dO_t, q_t T_t> + <G, T_{n-1}>. */
+static double dlam_one(const double* q, const double* k, const double* v, const double* dout,
+                       int64_t n, int64_t d, double lam, const double* s_init, const double* g_final) {
+    double* S = (double*)calloc((size_t)(d * d), sizeof(double));
+    double* T = (double*)calloc((size_t)(d * d), sizeof(double));
+    double* u = (double*)calloc((size_t)d, sizeof(double));
+    if (s_init) memcpy(S, s_init, sizeof(double) * (size_t)(d * d));
+    double total = 0.0;
+    for (int64_t t = 0; t < n; ++t) {
+        const double* kt = k + t * d;
+        const double* vt = v + t * d;
+        const double* qt = q + t * d;
+        const double* gt = dout + t * d;
+        for (int64_t a = 0; a < d; ++a) {
+            double* srow = S + a * d;
+            double* trow = T + a * d;
+            double ka = kt[a];
+            for (int64_t c = 0; c < d; ++c) {
+                trow[c] = srow[c] + lam * trow[c];
+                srow[c] = lam * srow[c] + ka * vt[c];
+            }
+        }
+        for (int64_t c = 0; c < d; ++c) u[c] = 0.0;
+        for (int64_t a = 0; a < d; ++a) {
+            double qa = qt[a];
+            const double* trow = T + a * d;
+            for (int64_t c = 0; c < d; ++c) u[c] += qa * trow[c];
+        }
+        for (int64_t c = 0; c < d; ++c) total += u[c] * gt[c];
+    }
+    if (g_final)
+        for (int64_t e = 0; e < d * d; ++e) total += g_final[e] * T[e];
+    free(S);
+    free(T);
+    free(u);
+    return total;
+}
+
 /* Batched forward over `pairs` sequences laid out back to back ([pairs][n][d]).
  * lam: pairs entries.  s_init: [pairs][d][d] or NULL.  s_final: [pairs][d][d] or NULL.
  * s_bounds: [pairs][ceil(n/bk)][d][d] or NULL. */
@@ -164,6 +210,18 @@ void oracle_bwd_recurrent(const double* q, const double* k, const double* v, con
         bwd_one(q + off, k + off, v + off, dout + off, n, d, lam[p], s_init ? s_init + so : NULL,
                 g_final ? g_final + so : NULL, dq ? dq + off : NULL, dk ? dk + off : NULL,
                 dv ? dv + off : NULL, ds_init ? ds_init + so : NULL);
+    }
+}
+
+/* dL/dlam of every sequence (see dlam_one): out[p] for p < pairs. */
+void oracle_dlam_recurrent(const double* q, const double* k, const double* v, const double* dout,
+                           int64_t pairs, int64_t n, int64_t d, const double* lam, const double* s_init,
+                           const double* g_final, double* out) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t p = 0; p < pairs; ++p) {
+        int64_t off = p * n * d, so = p * d * d;
+        out[p] = dlam_one(q + off, k + off, v + off, dout + off, n, d, lam[p],
+                          s_init ? s_init + so : NULL, g_final ? g_final + so : NULL);
     }
 }
 

@@ -81,3 +81,40 @@ def bwd_quadratic(q, k, v, dout, lam, s_init=None, g_final=None, phi="identity")
         dv = dv + w * (k @ f)
         ds0 = ds0 + (lam ** n) * f
     return dq * feature.dphi(q_raw, phi), dk * feature.dphi(k_raw, phi), dv, ds0
+
+
+def _dpowers(lam: float, exps: np.ndarray) -> np.ndarray:
+    """e lam^(e-1) for each e (0 for e = 0, without forming lam^-1)."""
+    e = exps.astype(np.float64)
+    return np.where(e > 0, e * np.power(np.float64(lam), np.maximum(e - 1, 0)), 0.0)
+
+
+def dlam_quadratic(q, k, v, dout, lam, s_init=None, g_final=None, phi="identity"):
+    """One sequence: dL/dlam of L = <dO, O> + <F, S_final> (F = g_final, zero when None),
+    term by term from the parallel form, where lam enters only through
+        D[i, j] = lam^(i-j)  ->  D'[i, j] = (i-j) lam^(i-j-1)  (i > j; 0 on and above the diagonal),
+        lam^(t+1) q_t S0     ->  (t+1) lam^t q_t S0,
+        S_final = lam^n S0 + sum_j lam^(n-1-j) k_j v_j^T
+                             ->  n lam^(n-1) S0 + sum_j (n-1-j) lam^(n-2-j) k_j v_j^T."""
+    q = feature.phi(q, phi)
+    k = feature.phi(k, phi)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(dout, dtype=np.float64)
+    n = q.shape[0]
+    lam = float(np.float64(lam))
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    dD = np.where(i > j, _dpowers(lam, np.where(i > j, i - j, 0)), 0.0)
+    total = float(np.sum((q @ k.T) * dD * (g @ v.T)))
+    s0 = None if s_init is None else np.asarray(s_init, dtype=np.float64)
+    if s0 is not None:
+        w = _dpowers(lam, np.arange(1, n + 1))  # (t+1) lam^t
+        total += float(np.sum(w[:, None] * (q @ s0) * g))
+    if g_final is not None:
+        f = np.asarray(g_final, dtype=np.float64)
+        w = _dpowers(lam, np.arange(n - 1, -1, -1))  # (n-1-j) lam^(n-2-j)
+        dS = (k * w[:, None]).T @ v
+        if s0 is not None:
+            dS = dS + _dpowers(lam, np.array([n]))[0] * s0
+        total += float(np.sum(f * dS))
+    return total

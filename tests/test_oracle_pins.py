@@ -6,6 +6,9 @@
 * closed forms for constant inputs (forward, final state and backward);
 * a library routine at lam = 1: ((Q K^T).tril()) V in torch float64;
 * invariants: the two forms agree, split-and-continue, decode steps == forward;
+* the derivative with respect to lam against the exact derivative of the loss,
+  a polynomial in lam fixed by exact values at n + 1 points, against central
+  differences and against torch float64 autograd;
 * planted mistakes in a copy of the quadratic form are caught by these pins.
 
 The definition is causal linear attention with per-head decay,
@@ -490,3 +493,172 @@ def test_feature_map_closed_forms():
     assert not np.any(o)
     dq, dk, dv = oracle.bwd_recurrent(-ones, ones, ones, ones, lam, phi="relu")
     assert not np.any(dq) and not np.any(dk) and not np.any(dv)
+
+
+# ----------------------------------------------------------------- derivative with respect to lam
+def exact_dlam(q, k, v, g, lam0, s0=None, gf=None):
+    """Exact dL/dlam at lam0 without any derivative formula: L(lam) is a polynomial of degree
+    at most n in lam, so its values at lam = 0..n (exact rationals from the forward
+    definition) fix it, and the derivative of that interpolating polynomial at lam0 is exact."""
+    n = len(q)
+    xs = [Fraction(i) for i in range(n + 1)]
+    ys = [exact_loss(q, k, v, g, x, s0, gf) for x in xs]
+    x0 = Fraction(lam0)
+    total = Fraction(0)
+    for i, xi in enumerate(xs):
+        # derivative of the Lagrange basis polynomial l_i at x0
+        dli = Fraction(0)
+        for m, xm in enumerate(xs):
+            if m == i:
+                continue
+            term = Fraction(1) / (xi - xm)
+            for l_, xl in enumerate(xs):
+                if l_ != i and l_ != m:
+                    term *= (x0 - xl) / (xi - xl)
+            dli += term
+        total += ys[i] * dli
+    return total
+
+
+@pytest.mark.parametrize("lam", LAMS)
+@pytest.mark.parametrize("n,d,seed,with_s0,with_g", [(1, 2, 40, True, True), (4, 2, 41, False, False),
+                                                      (6, 3, 42, True, False), (7, 2, 43, True, True)])
+def test_dlam_matches_exact_polynomial_derivative(lam, n, d, seed, with_s0, with_g):
+    rng = np.random.default_rng(seed)
+    q, k, v, g = (rng.integers(-3, 4, size=(n, d)).tolist() for _ in range(4))
+    s0 = rng.integers(-3, 4, size=(d, d)).tolist() if with_s0 else None
+    gf = rng.integers(-3, 4, size=(d, d)).tolist() if with_g else None
+    ex = float(exact_dlam(q, k, v, g, lam, s0, gf))
+    arr = lambda m: None if m is None else np.array(m, dtype=np.float64)
+    args = (arr(q), arr(k), arr(v), arr(g), float(lam), arr(s0), arr(gf))
+    for got in (oracle.dlam_recurrent(*args), oracle.dlam_quadratic(*args)):
+        assert got == pytest.approx(ex, rel=1e-12, abs=1e-12)
+
+
+@pytest.mark.parametrize("ex", _golden()["dlam"], ids=lambda e: e["name"])
+def test_hand_worked_dlam(ex):
+    q, k, v, g, s0, gf = (np.array(ex[key], dtype=np.float64) for key in ("q", "k", "v", "dO", "S0", "G"))
+    for got in (oracle.dlam_recurrent(q, k, v, g, ex["lam"], s0, gf),
+                oracle.dlam_quadratic(q, k, v, g, ex["lam"], s0, gf)):
+        assert got == pytest.approx(ex["dL_dlam"], rel=0, abs=1e-14)
+
+
+@pytest.mark.parametrize("lam", [0.3, 0.9, 0.99, 0.999])
+def test_dlam_central_differences(lam):
+    """The derivative against central differences of the quadratic-form loss (fp64)."""
+    rng = np.random.default_rng(44)
+    n, d = 300, 8
+    q, k, v, g = (rng.standard_normal((n, d)) / np.sqrt(d) for _ in range(4))
+    s0, gf = rng.standard_normal((d, d)), rng.standard_normal((d, d))
+
+    def loss(x):
+        o, s = quadratic.fwd_quadratic(q, k, v, x, s0)
+        return float(np.sum(o * g) + np.sum(s * gf))
+
+    h = 1e-5 * (1 - lam)
+    fd = (loss(lam + h) - loss(lam - h)) / (2 * h)
+    got = oracle.dlam_recurrent(q, k, v, g, lam, s0, gf)
+    assert got == pytest.approx(fd, rel=1e-6)
+
+
+def test_dlam_torch_autograd():
+    """The derivative against torch float64 autograd of the parallel-form loss, one value per
+    sequence with per-head decays, with a feature map on q and k."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(45)
+    B, H, n, d = 2, 3, 97, 6
+    q, k, v, g = (rng.standard_normal((B, H, n, d)) for _ in range(4))
+    lams = np.array([0.5, 0.9, 0.995])
+    got = oracle.dlam_recurrent(q, k, v, g, np.tile(lams, B), phi="elu1")
+    lam_t = torch.tensor(lams, dtype=torch.float64, requires_grad=True)
+    qt, kt = (torch.nn.functional.elu(torch.from_numpy(x)) + 1 for x in (q, k))
+    vt, gt = torch.from_numpy(v), torch.from_numpy(g)
+    i = torch.arange(n)[:, None]
+    j = torch.arange(n)[None, :]
+    e = (i - j).clamp(min=0).to(torch.float64)
+    per = []
+    for h in range(H):
+        D = torch.where(i >= j, lam_t[h] ** e, torch.zeros((), dtype=torch.float64))
+        o = ((qt[:, h] @ kt[:, h].transpose(-1, -2).contiguous()) * D) @ vt[:, h]
+        per.append((o * gt[:, h]).sum(dim=(-1, -2)))
+    ref = []
+    for b in range(B):
+        for h in range(H):
+            (gl,) = torch.autograd.grad(per[h][b], lam_t, retain_graph=True)
+            ref.append(gl[h].item())
+    np.testing.assert_allclose(got.reshape(-1), ref, rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 64])
+def test_dlam_closed_form_all_ones(n):
+    """lam = 1, all-ones q, k, v, dO, S0, G (d = 3): every pair (t, j <= t) contributes
+    (t - j) d^2, S0 contributes (t + 1) d^2 per t, and G contributes n d^2 + sum_j (n-1-j) d^2:
+    dL/dlam = d^2 ((n-1) n (n+1) / 6 + n^2 + n)."""
+    d = 3
+    ones = np.ones((n, d))
+    s1 = np.ones((d, d))
+    want = d * d * ((n - 1) * n * (n + 1) / 6 + n * n + n)
+    for got in (oracle.dlam_recurrent(ones, ones, ones, ones, 1.0, s1, s1),
+                oracle.dlam_quadratic(ones, ones, ones, ones, 1.0, s1, s1)):
+        assert got == pytest.approx(want, rel=1e-14)
+
+
+def test_dlam_at_zero_decay_is_the_first_order_term():
+    """At lam = 0 only terms linear in lam survive: each token with its predecessor, the
+    initial state's first step, and the final state's last-but-one token."""
+    rng = np.random.default_rng(46)
+    n, d = 9, 4
+    q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+    s0, gf = rng.standard_normal((d, d)), rng.standard_normal((d, d))
+    want = sum((q[t] @ k[t - 1]) * (g[t] @ v[t - 1]) for t in range(1, n))
+    want += q[0] @ s0 @ g[0] + np.sum(gf * np.outer(k[n - 2], v[n - 2]))
+    assert oracle.dlam_recurrent(q, k, v, g, 0.0, s0, gf) == pytest.approx(want, rel=1e-13)
+
+
+def test_dlam_log_derivative_identity():
+    """lam dL/dlam = sum_t t <dO_t, O_t> - sum_j j <v_j, dV_j> + (n-1) <G, S_n> + <S0, dS0>: the
+    exponent t - j of every term split into its query and key positions (S0 at position -1,
+    G at position n-1), evaluated from the pinned forward and backward."""
+    rng = np.random.default_rng(47)
+    n, d, lam = 200, 5, 0.97
+    q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+    s0, gf = rng.standard_normal((d, d)), rng.standard_normal((d, d))
+    o, sn = oracle.fwd_recurrent(q, k, v, lam, s0)
+    _, _, dv, ds0 = oracle.bwd_recurrent(q, k, v, g, lam, s0, want=("dv",), g_final=gf, want_ds_init=True)
+    t = np.arange(n)[:, None]
+    rhs = np.sum(t * o * g) - np.sum(t * v * dv) + (n - 1) * np.sum(gf * sn) + np.sum(s0 * ds0)
+    assert lam * oracle.dlam_recurrent(q, k, v, g, lam, s0, gf) == pytest.approx(rhs, rel=1e-10)
+
+
+def test_planted_dlam_mistakes_are_caught(monkeypatch):
+    """Plausible slips in the derivative fail the exact pin: the derivative weights of the
+    powers off by one, and the state-derivative recurrence fed the updated state."""
+    rng = np.random.default_rng(48)
+    n, d, lam = 5, 2, Fraction(1, 2)
+    q, k, v, g = (rng.integers(-3, 4, size=(n, d)).tolist() for _ in range(4))
+    s0, gf = (rng.integers(-3, 4, size=(d, d)).tolist() for _ in range(2))
+    ex = float(exact_dlam(q, k, v, g, lam, s0, gf))
+    qa, ka, va, ga, sa, fa = (np.array(x, float) for x in (q, k, v, g, s0, gf))
+    ok = quadratic.dlam_quadratic(qa, ka, va, ga, 0.5, sa, fa)
+    assert ok == pytest.approx(ex, rel=1e-13)
+    orig = quadratic._dpowers
+    for wrong in (lambda l, e: e * np.power(l, e.astype(float)),            # e lam^e
+                  lambda l, e: (e + 1) * np.power(l, e.astype(float)),      # (e+1) lam^e
+                  lambda l, e: orig(l, e + 1)):                             # exponent shifted
+        monkeypatch.setattr(quadratic, "_dpowers", wrong)
+        assert quadratic.dlam_quadratic(qa, ka, va, ga, 0.5, sa, fa) != pytest.approx(ex, rel=1e-6)
+    monkeypatch.setattr(quadratic, "_dpowers", orig)
+
+    def recurrent(use_updated_state=False, drop_g=False, s_for_t=False):
+        S, T, tot = sa.copy(), np.zeros((d, d)), 0.0
+        for t in range(n):
+            S_new = 0.5 * S + np.outer(ka[t], va[t])
+            T = (S_new if use_updated_state else S) + 0.5 * T
+            S = S_new
+            tot += qa[t] @ T @ ga[t]
+        if not drop_g:
+            tot += np.sum(fa * (S if s_for_t else T))
+        return tot
+    assert recurrent() == pytest.approx(ex, rel=1e-13)
+    for kw in ({"use_updated_state": True}, {"drop_g": True}, {"s_for_t": True}):
+        assert recurrent(**kw) != pytest.approx(ex, rel=1e-6), kw
