@@ -58,6 +58,10 @@ def _load():
     lib.la_bwd.restype = ctypes.c_int
     lib.la_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
     lib.la_bwd_workspace_bytes.restype = sz
+    lib.la_dlam.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.la_dlam.restype = ctypes.c_int
+    lib.la_dlam_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
+    lib.la_dlam_workspace_bytes.restype = sz
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i32, i32, vp, vp]
     lib.la_decode_step.restype = ctypes.c_int
     ip = ctypes.POINTER(ctypes.c_int64)
@@ -77,7 +81,8 @@ def _load():
 
 lib = _load()
 
-EXPORTS = ("la_fwd", "la_fwd_workspace_bytes", "la_bwd", "la_bwd_workspace_bytes", "la_decode_step",
+EXPORTS = ("la_fwd", "la_fwd_workspace_bytes", "la_bwd", "la_bwd_workspace_bytes", "la_dlam",
+           "la_dlam_workspace_bytes", "la_decode_step",
            "la_fwd_varlen", "la_fwd_varlen_workspace_bytes", "la_decode_step_paged",
            "la_strerror", "la_version", "la_prof_enable", "la_prof_collect")
 
@@ -209,6 +214,33 @@ def la_bwd(q, k, v, dout, lam, Bk: int = 64, kv_in=None, dq=None, dk=None, dv=No
     if dkv_in is not None:
         return dq, dk, dv, dkv_in
     return dq, dk, dv
+
+
+def la_dlam_workspace_bytes(B, H, N, D, Bk, dtype_code) -> int:
+    return int(lib.la_dlam_workspace_bytes(B, H, N, D, Bk, dtype_code))
+
+
+def la_dlam(q, k, v, dout, lam, Bk: int = 64, kv_in=None, dkv_out=None, out=None, ws=None, phi="identity"):
+    """dL/dlam_h summed over the batch, float32 [H], for L = <dO, O> + <dkv_out, S_N> of la_fwd
+    (same inputs, kv_in and feature map)."""
+    for name, t in (("Q", q), ("K", k), ("V", v), ("dO", dout)):
+        _check_seq(name, t, q)
+    B, H, N, D = q.shape
+    _check_state("kv_in", kv_in, B, H, D, q.device)
+    _check_state("dkv_out", dkv_out, B, H, D, q.device)
+    if out is None:
+        out = torch.empty(H, dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (H,) or not out.is_contiguous() or out.device != q.device:
+        raise ValueError(f"out must be a contiguous float32 [H] tensor on {q.device}")
+    code = _dtype_code(q)
+    nbytes = la_dlam_workspace_bytes(B, H, N, D, Bk, code)
+    ws = _workspace(nbytes, q.device, ws)
+    rc = lib.la_dlam(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _lam_array(lam, H), B, H, N, D, Bk, code,
+                     _phi_code(phi), _ptr(kv_in), _ptr(dkv_out), _ptr(out), _ptr(ws),
+                     nbytes if ws is not None else 0, _stream(q.device))
+    if rc != LA_OK:
+        raise LaError(rc, "la_dlam")
+    return out
 
 
 def _offsets(seq_offsets):

@@ -159,6 +159,11 @@ size_t slot_bytes(int64_t pairs, const Plan& p, int64_t D) {
 
 size_t round_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// la_dlam: the (S, T) chunk slots, then one double per (sequence, chunk).
+size_t dlam_ws_bytes(int64_t pairs, const Plan& p, int64_t D) {
+    return round_up(2 * slot_bytes(pairs, p, D)) + round_up(static_cast<size_t>(pairs * p.chunks) * sizeof(double));
+}
+
 // ------------------------------------------------------------------ sweeps
 // Forward-direction sweep (O of la_fwd, or dQ of la_bwd with operands
 // (dO, V, K) and the transposed initial state).
@@ -444,6 +449,67 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     if (p.mfma && phi == 0 && la::mfma_rev_supported(static_cast<int>(D), Bk))
         return launch("dkdv_mfma", s, [&] { la::launch_rev_mfma(a, lam, s); });
     return launch("dkdv_generic", s, [&] { la::launch_rev_generic(a, lam, bf16, s); });
+}
+
+size_t la_dlam_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype) {
+    int64_t elems;
+    if (check_shape(B, H, N, D, Bk, dtype, &elems) != LA_OK) return 0;
+    return dlam_ws_bytes(B * H, make_plan(B, H, N, D, Bk, dtype), D);
+}
+
+int la_dlam(const void* Q, const void* K, const void* V, const void* dO, const float* lambda, int64_t B,
+            int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t phi, const float* kv_in,
+            const float* dkv_out, float* dlam, void* ws, size_t ws_bytes, void* hip_stream) {
+    int64_t elems;
+    int rc = check_shape(B, H, N, D, Bk, dtype, &elems);
+    if (rc) return rc;
+    if (!valid_phi(phi)) return LA_EINVAL;
+    if (!Q || !K || !V || !dO || !dlam) return LA_EINVAL;
+    LamArgs lam;
+    if ((rc = load_lambda(lambda, H, &lam))) return rc;
+    for (const void* p : {Q, K, V, dO, static_cast<const void*>(kv_in), static_cast<const void*>(dkv_out),
+                          static_cast<const void*>(ws)})
+        if (p && !aligned16(p)) return LA_EALIGN;
+    if ((reinterpret_cast<uintptr_t>(dlam) & 3u) != 0) return LA_EALIGN;
+    const size_t tb = static_cast<size_t>(elems) * (dtype == LA_BF16 ? 2 : 4);
+    const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
+    const Plan p = make_plan(B, H, N, D, Bk, dtype);
+    const size_t need = dlam_ws_bytes(B * H, p, D);
+    if (!ws || ws_bytes < need) return LA_EWORKSPACE;
+    const Range ins[] = {{Q, tb}, {K, tb}, {V, tb}, {dO, tb}, {kv_in, kv_in ? sb : 0}, {dkv_out, dkv_out ? sb : 0}};
+    const Range rout{dlam, static_cast<size_t>(H) * sizeof(float)}, rws{ws, need};
+    for (const Range& i : ins)
+        if (overlap(rout, i) || overlap(rws, i)) return LA_EINVAL;
+    if (overlap(rout, rws)) return LA_EINVAL;
+
+    int dev_count = 0;
+    if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count == 0) return LA_ENODEV;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const int64_t pairs = B * H;
+    const int32_t Hi = static_cast<int32_t>(H);
+    const int bf16 = dtype == LA_BF16;
+    const bool mfma = p.mfma && la::dlam_mfma_supported(static_cast<int>(D), Bk);
+    float* slots = static_cast<float*>(ws);
+    double* partial = reinterpret_cast<double*>(static_cast<char*>(ws) + round_up(2 * slot_bytes(pairs, p, D)));
+    if (p.chunks > 1) {
+        la::ChunkStateArgs cs{K, V, slots, N, p.L, static_cast<int>(D), Bk, Hi, p.chunks, pairs, 0, phi, 1};
+        if (mfma)
+            rc = launch("dlam_state_mfma", s, [&] { la::launch_dlam_state_mfma(cs, lam, s); });
+        else
+            rc = launch("dlam_state_generic", s, [&] { la::launch_dlam_state_generic(cs, lam, bf16, s); });
+        if (rc) return rc;
+        la::ScanArgs sc{slots, kv_in, 0, nullptr, N, p.L, static_cast<int>(D), Hi, p.chunks, pairs, 0};
+        rc = launch("dlam_scan", s, [&] { la::launch_dlam_scan(sc, lam, s); });
+        if (rc) return rc;
+    }
+    la::DlamArgs da{Q, K, V, dO, p.chunks > 1 ? slots : nullptr, kv_in, dkv_out, partial, N, p.L,
+                    static_cast<int>(D), Bk, Hi, p.chunks, pairs, phi};
+    if (mfma)
+        rc = launch("dlam_mfma", s, [&] { la::launch_dlam_mfma(da, lam, s); });
+    else
+        rc = launch("dlam_generic", s, [&] { la::launch_dlam_generic(da, lam, bf16, s); });
+    if (rc) return rc;
+    return launch("dlam_reduce", s, [&] { la::launch_dlam_reduce(partial, B, Hi, p.chunks, dlam, s); });
 }
 
 size_t la_fwd_varlen_workspace_bytes(const int64_t* seq_offsets, int64_t B, int64_t H, int64_t D, int32_t Bk,

@@ -49,6 +49,13 @@ __device__ __forceinline__ double lam_pow64(float lam, int64_t e) {
 // The same rounded once to float.
 __device__ __forceinline__ float lam_pow(float lam, int64_t e) { return static_cast<float>(lam_pow64(lam, e)); }
 
+// d(lam^e)/dlam = e lam^(e-1) in double, 0 for e = 0 (lam^-1 is never formed, so lam = 0
+// gives 1 for e = 1 and 0 beyond).
+__device__ __forceinline__ double lam_dpow64(float lam, int64_t e) {
+    return e > 0 ? static_cast<double>(e) * lam_pow64(lam, e - 1) : 0.0;
+}
+__device__ __forceinline__ float lam_dpow(float lam, int64_t e) { return static_cast<float>(lam_dpow64(lam, e)); }
+
 // Elementwise kernel feature maps on queries and keys (identity, elu(x) + 1,
 // relu); both non-identity maps have a derivative that is a function of phi(x)
 // itself: min(1, phi) for elu + 1, [phi > 0] for relu.

@@ -108,6 +108,31 @@ struct DecodeArgs {
     int phi;                 // feature map applied to q and k
 };
 
+// Derivative of L = <dO, O> + <F, S_N> with respect to lam, forward direction,
+// carrying the state S and its derivative T = dS/dlam:
+//   per block (m tokens, local index s):  the block adds
+//     sum_{s' < s} (s-s') lam^(s-s'-1) (q_s . k_s')(dO_s . v_s')
+//     + sum_s [ (s+1) lam^s q_s S dO_s + lam^(s+1) q_s T dO_s ],
+//   then T <- lam^m T + m lam^(m-1) S + sum_s (m-1-s) lam^(m-2-s) k_s v_s^T,
+//        S <- lam^m S + sum_s lam^(m-1-s) k_s v_s^T;
+//   the sequence's last chunk adds <F, T> at its end.
+// Chunk c starts from (S, T) = (kv_in or 0, 0) for c = 0, else from slot c-1 of
+// a scan over the chunk aggregates (slots [P][chunks-1][2][D][D]: S then T).
+struct DlamArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;          // dO
+    const float* slots;     // scanned (S, T) entering chunks 1 .. chunks-1, or nullptr
+    const float* kv_in;     // [P][D][D] or nullptr
+    const float* g_final;   // [P][D][D] F, or nullptr
+    double* partial;        // [P][chunks] contribution of each (sequence, chunk)
+    int64_t N, L;
+    int D, Bk, H, chunks;
+    int64_t pairs;
+    int phi;                // feature map on q and k
+};
+
 // Launchers (each enqueues exactly one kernel on `s`; errors are read by the caller).
 void launch_fwd_generic(const SweepArgs& a, const LamArgs& lam, int bf16, hipStream_t s);
 void launch_rev_generic(const SweepArgs& a, const LamArgs& lam, int bf16, hipStream_t s);
@@ -148,5 +173,17 @@ struct ScanList {
 // Forward scan of a ragged batch's chunk states (ScanArgs.L is the chunk length):
 // one workgroup per (listed sequence, head, 256 state elements).
 void launch_scan_varlen(const ScanArgs& a, const LamArgs& lam, const ScanList& list, hipStream_t s);
+
+// Decay derivative (k_dlam.hip).  Chunk aggregates of (S, T) over (x, y) = (k, v),
+// forward direction, into slots [P][chunks-1][2][D][D] (ChunkStateArgs.slots; phi on x
+// when phi_mask bit 0 is set); the scan (S, T) <- (lam^L S + dS, lam^L T + L lam^(L-1) S + dT)
+// from (kv_in or 0, 0); the sweep; and the sum over batch and chunks per head.
+void launch_dlam_state_generic(const ChunkStateArgs& a, const LamArgs& lam, int bf16, hipStream_t s);
+void launch_dlam_state_mfma(const ChunkStateArgs& a, const LamArgs& lam, hipStream_t s);
+void launch_dlam_scan(const ScanArgs& a, const LamArgs& lam, hipStream_t s);
+void launch_dlam_generic(const DlamArgs& a, const LamArgs& lam, int bf16, hipStream_t s);
+bool dlam_mfma_supported(int D, int Bk);
+void launch_dlam_mfma(const DlamArgs& a, const LamArgs& lam, hipStream_t s);
+void launch_dlam_reduce(const double* partial, int64_t B, int H, int chunks, float* out, hipStream_t s);
 
 }  // namespace la

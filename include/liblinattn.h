@@ -115,7 +115,7 @@ size_t la_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_
  *   dK_j = A_j v_j  = sum_{i>=j} lam^(i-j) (dO_i . v_j) q_i + lam^(N-1-j) F v_j
  *   dV_j = A_j^T k_j = sum_{i>=j} lam^(i-j) (q_i . k_j) dO_i + lam^(N-1-j) F^T k_j
  *   dS0  = lam A_0  = sum_t lam^(t+1) q_t dO_t^T + lam^N F
- * No gradient of lambda is computed.  The call is stateless: Q, K, V and
+ * The gradient of lambda is la_dlam's.  The call is stateless: Q, K, V and
  * kv_in are passed again.
  *   dO      : [B][H][N][D] dtype, device.
  *   dkv_out : [B][H][D][D] float32 device gradient F arriving at kv_out, or
@@ -142,6 +142,34 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
            const void* fwd_ws, void* ws, size_t ws_bytes, void* hip_stream);
 
 size_t la_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype);
+
+/* Derivative of the same loss L = <dO, O> + <F, S_N> with respect to the
+ * per-head decay, summed over the batch:
+ *     dlam[h] = sum_b dL/dlam_h
+ *             = sum_b [ sum_t sum_{j<t} (t-j) lam^(t-j-1) (q_t . k_j)(dO_t . v_j)
+ *                       + sum_t (t+1) lam^t q_t S0 dO_t
+ *                       + <F, N lam^(N-1) S0 + sum_j (N-1-j) lam^(N-2-j) k_j v_j^T> ].
+ * The decay enters the tiled computation (Lightning Attention-2, Tiling
+ * paragraph) only through powers of lam, so the same block decomposition with
+ * every power replaced by its derivative gives this sum: one forward-order
+ * sweep that carries the state S and its derivative T = dS/dlam, with the
+ * chunked prefix over blocks applied to the pair (S, T).  lam = 0 is allowed
+ * (the derivative there keeps the first-order terms).  Same shapes, inputs
+ * and feature map as la_bwd (phi applied to Q and K; it does not depend on
+ * lam).
+ *   dlam : [H] float32 device, written (4-byte aligned; must not overlap an
+ *          input or the workspace).
+ *   ws   : la_dlam_workspace_bytes(...) bytes of device memory (never 0: it
+ *          holds one partial sum per (sequence, chunk)).
+ * Accuracy: the block products run on bf16 operands with float32
+ * accumulation (float32 storage: float32 throughout); partial sums are
+ * added in double. */
+int la_dlam(const void* Q, const void* K, const void* V, const void* dO, const float* lambda,
+            int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t phi,
+            const float* kv_in, const float* dkv_out, float* dlam, void* ws, size_t ws_bytes,
+            void* hip_stream);
+
+size_t la_dlam_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype);
 
 /* One recurrent decode step for Bs sequences and H heads (the recurrent
  * inference form with a fixed-size state, glossary page "Lightning

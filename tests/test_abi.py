@@ -212,3 +212,29 @@ def test_decode_paged_rejects():
     assert call(D=100) == la.LA_EUNSUPPORTED
     assert call(o=S_ + 4096) == la.LA_EINVAL                  # output inside the pool
     assert call(idx=S_ + 1024) == la.LA_EINVAL               # slot table inside the pool
+
+
+def test_dlam_rejects():
+    """la_dlam validates like la_bwd; its workspace is never empty (one partial per
+    (sequence, chunk)) and its [H] output may sit anywhere 4-byte aligned."""
+    v = ctypes.c_void_p
+    lam = (ctypes.c_float * 2)(0.5, 0.0)
+    G_, X_ = A * 10, A * 11
+    need = la.la_dlam_workspace_bytes(1, 2, 128, 64, 64, la.LA_BF16)
+    assert need >= 2 * 8
+    call = lambda out=O_, ws=W_, nb=1 << 40, g=G_, gf=None, kv=None, lm=lam, phi=0: la.lib.la_dlam(
+        v(Q_), v(K_), v(V_), v(g) if g else None, lm, 1, 2, 128, 64, 64, la.LA_BF16, phi, v(kv) if kv else None,
+        v(gf) if gf else None, v(out) if out else None, v(ws) if ws else None, nb, None)
+    assert call(out=None) == la.LA_EINVAL                 # output missing
+    assert call(g=None) == la.LA_EINVAL                   # dO missing
+    assert call(ws=None, nb=0) == la.LA_EWORKSPACE        # workspace always needed
+    assert call(nb=need - 1) == la.LA_EWORKSPACE
+    assert call(out=O_ + 2) == la.LA_EALIGN               # float output misaligned
+    assert call(out=Q_ + 64) == la.LA_EINVAL              # output inside Q
+    assert call(out=W_ + 64) == la.LA_EINVAL              # output inside the workspace
+    assert call(ws=K_) == la.LA_EINVAL                    # workspace aliases K
+    assert call(gf=X_ + 4) == la.LA_EALIGN
+    assert call(out=X_, gf=X_) == la.LA_EINVAL            # output aliases dkv_out
+    assert call(phi=5) == la.LA_EINVAL
+    assert call(lm=(ctypes.c_float * 2)(0.5, 1.25)) == la.LA_EINVAL
+    assert la.la_dlam_workspace_bytes(1, 2, 128, 100, 64, la.LA_BF16) == 0
