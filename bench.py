@@ -366,6 +366,22 @@ def bench(args):
         })
     fwd_tps = [x["fwd_tokens_per_s"] for x in sweep]
 
+    # derivative with respect to the decay (la_dlam) over the same inputs, per sequence length
+    dlam = []
+    for sh in shapes:
+        wsd = torch.empty(la.la_dlam_workspace_bytes(sh["B"], H, sh["n"], D, BK, la.LA_BF16), dtype=torch.uint8,
+                          device="cuda")
+        outd = torch.empty(H, dtype=torch.float32, device="cuda")
+        run_dlam = lambda: la.la_dlam(sh["q"], sh["k"], sh["v"], sh["g"], lam, BK, out=outd, ws=wsd)
+        run_dlam()
+        d_ms = timed(run_dlam, max(3, args.steps))
+        th = sh["B"] * H * sh["n"]
+        # Q, K, V, dO read by the sweep, and K, V once more by the chunk aggregates
+        dbytes = 8 * D * th + (4 * D * th * (sh["chunks"] - 1) / sh["chunks"] if sh["chunks"] > 1 else 0)
+        dlam.append({"n": sh["n"], "batch": sh["B"], "chunks": sh["chunks"], "ms": round(d_ms, 4),
+                     "tokens_per_s": round(TOKENS_PER_POINT / (d_ms * 1e-3)),
+                     "gbs": round(dbytes / (d_ms * 1e-3) / 1e9, 1)})
+
     # recurrent decode step: 256 sequences x 64 heads, float32 state 1 GiB
     Bs, Hd = 256, 64
     lam_d = synth.decay_schedule(Hd)
@@ -403,6 +419,7 @@ def bench(args):
         "kernels": kernels,
         "decode": decode,
         "serving": serving,
+        "decay_gradient": dlam,
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:
