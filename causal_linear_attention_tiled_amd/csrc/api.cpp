@@ -488,12 +488,15 @@ int la_dlam(const void* Q, const void* K, const void* V, const void* dO, const f
     const int64_t pairs = B * H;
     const int32_t Hi = static_cast<int32_t>(H);
     const int bf16 = dtype == LA_BF16;
+    const bool dma = p.mfma && la::dlam_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_DLAM", "v1");
     const bool mfma = p.mfma && la::dlam_mfma_supported(static_cast<int>(D), Bk);
     float* slots = static_cast<float*>(ws);
     double* partial = reinterpret_cast<double*>(static_cast<char*>(ws) + round_up(2 * slot_bytes(pairs, p, D)));
     if (p.chunks > 1) {
         la::ChunkStateArgs cs{K, V, slots, N, p.L, static_cast<int>(D), Bk, Hi, p.chunks, pairs, 0, phi, 1};
-        if (mfma)
+        if (dma)
+            rc = launch("dlam_state_dma", s, [&] { la::launch_dlam_state_dma(cs, lam, s); });
+        else if (mfma)
             rc = launch("dlam_state_mfma", s, [&] { la::launch_dlam_state_mfma(cs, lam, s); });
         else
             rc = launch("dlam_state_generic", s, [&] { la::launch_dlam_state_generic(cs, lam, bf16, s); });
@@ -504,7 +507,9 @@ int la_dlam(const void* Q, const void* K, const void* V, const void* dO, const f
     }
     la::DlamArgs da{Q, K, V, dO, p.chunks > 1 ? slots : nullptr, kv_in, dkv_out, partial, N, p.L,
                     static_cast<int>(D), Bk, Hi, p.chunks, pairs, phi};
-    if (mfma)
+    if (dma)
+        rc = launch("dlam_dma", s, [&] { la::launch_dlam_dma(da, lam, env_is("LA_DLAM_WAVES", "4") ? 4 : 8, s); });
+    else if (mfma)
         rc = launch("dlam_mfma", s, [&] { la::launch_dlam_mfma(da, lam, s); });
     else
         rc = launch("dlam_generic", s, [&] { la::launch_dlam_generic(da, lam, bf16, s); });

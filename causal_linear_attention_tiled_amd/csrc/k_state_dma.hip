@@ -19,6 +19,13 @@
 // hundred chunks runs in one round.  Both operands come from the row-major
 // tiles through transposing LDS reads; wave w accumulates columns
 // [16w, 16w + 16) of the aggregate.
+//
+// The decay-derivative form (forward only) also sums dT = d(acc)/dlam =
+// sum_t (E - 1 - t) lam^(E - 2 - t) x_t y_t^T: with c = lam^W after W walked
+// tokens and dc = W lam^(W - 1) its derivative (both running products in
+// double), token s of an m-token block weighs c lam^(m-1-s) in acc and
+// dc lam^(m-1-s) + c (m-1-s) lam^(m-2-s) in dT.  The two slots of a chunk are
+// stored back to back (acc, then dT).
 #include "la_device.h"
 #include "la_internal.h"
 #include "lds_dma.h"
@@ -38,9 +45,10 @@ constexpr int LOADS_PER_WAVE = 2 * (BK / 4) / NW;  // 1 KiB loads per wave per b
 struct StateTiles {
     uint16_t t[NSTAGE][2][TILE];  // per stage: X, Y (row-major, swizzled)
     float pw[BK + 1];
+    float dpw[BK + 1];            // d(lam^e)/dlam (decay-derivative form)
 };
 
-template <bool VARLEN, bool PHI>
+template <bool VARLEN, bool PHI, bool DL>
 __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArgs& lam, const VarlenArgs* var) {
     __shared__ StateTiles sm;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
@@ -73,7 +81,10 @@ __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArg
     const int64_t t_end = min(n_seq, t_begin + a.L);
     const int64_t nblk = (t_end - t_begin + BK - 1) / BK;
     const float lv = lam.lam[head];
-    for (int e = tid; e <= BK; e += 64 * NW) sm.pw[e] = lam_pow(lv, e);
+    for (int e = tid; e <= BK; e += 64 * NW) {
+        sm.pw[e] = lam_pow(lv, e);
+        if constexpr (DL) sm.dpw[e] = lam_dpow(lv, e);
+    }
     const double lam_bk = lam_pow64(lv, BK);
 
     // loads at or past the sequence's last row come back as zero
@@ -100,10 +111,15 @@ __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArg
     if (nblk > 0) issue(0);
 
     // S[at][r] = acc[16 at + 4 g + r][16 w + li]
-    f32x4 S[8];
+    f32x4 S[8], T[DL ? 8 : 1];
 #pragma unroll
     for (int at = 0; at < 8; ++at) S[at] = zero4();
-    double cw = 1.0;  // lam^(tokens walked so far)
+    if constexpr (DL) {
+#pragma unroll
+        for (int at = 0; at < 8; ++at) T[at] = zero4();
+    }
+    double cw = 1.0;   // lam^(tokens walked so far)
+    double dcw = 0.0;  // its derivative
 
     for (int64_t n = 0; n < nblk; ++n) {
         const int64_t t0 = t_begin + block_of(n) * BK;
@@ -122,38 +138,73 @@ __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArg
         const uint16_t* Ys = sm.t[stage][1];
         // weights of token s = 32 kb + kappa(g, e), on the Y operand
         const float cf = static_cast<float>(cw);
-        float wx[NKB][8];
+        if constexpr (!DL) {
+            float wx[NKB][8];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int s = 32 * kb + kappa(g, e);
-                wx[kb][e] = cf * masked_pw(sm.pw, a.reverse ? s : m - 1 - s, s < m);
+                for (int e = 0; e < 8; ++e) {
+                    const int s = 32 * kb + kappa(g, e);
+                    wx[kb][e] = cf * masked_pw(sm.pw, a.reverse ? s : m - 1 - s, s < m);
+                }
+            bf16x8 yf[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) yf[kb] = scale8(op_tr_k(Ys, 32 * kb, 16 * w, 4, g, li), wx[kb]);
+#pragma unroll
+            for (int at = 0; at < 8; ++at)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) S[at] = mfma16(op_tr_k(Xs, 32 * kb, 16 * at, 4, g, li), yf[kb], S[at]);
+        } else {
+            // one 32-token k block at a time (fewer live registers); every accumulator still
+            // adds k block 0 before k block 1
+            const float dcf = static_cast<float>(dcw);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                float wx[8], wd[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int s = 32 * kb + kappa(g, e);
+                    const float p = masked_pw(sm.pw, m - 1 - s, s < m);
+                    wx[e] = cf * p;
+                    wd[e] = dcf * p + cf * masked_pw(sm.dpw, m - 1 - s, s < m);
+                }
+                const bf16x8 y = op_tr_k(Ys, 32 * kb, 16 * w, 4, g, li);
+                const bf16x8 yf = scale8(y, wx), yd = scale8(y, wd);
+#pragma unroll
+                for (int at = 0; at < 8; ++at) {
+                    const bf16x8 xf = op_tr_k(Xs, 32 * kb, 16 * at, 4, g, li);
+                    S[at] = mfma16(xf, yf, S[at]);
+                    T[at] = mfma16(xf, yd, T[at]);
+                }
             }
-        bf16x8 yf[NKB];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) yf[kb] = scale8(op_tr_k(Ys, 32 * kb, 16 * w, 4, g, li), wx[kb]);
-#pragma unroll
-        for (int at = 0; at < 8; ++at)
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) S[at] = mfma16(op_tr_k(Xs, 32 * kb, 16 * at, 4, g, li), yf[kb], S[at]);
-        cw *= (m == BK) ? lam_bk : lam_pow64(lv, m);
+        }
+        const double lm = (m == BK) ? lam_bk : lam_pow64(lv, m);
+        if constexpr (DL) dcw = dcw * lm + cw * lam_dpow64(lv, m);
+        cw *= lm;
     }
-    float* dst = a.slots + dst_slot * D * D;
+    float* dst = a.slots + dst_slot * (DL ? 2 : 1) * D * D;
 #pragma unroll
     for (int at = 0; at < 8; ++at)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(16 * at + 4 * g + r) * D + 16 * w + li] = S[at][r];
+        for (int r = 0; r < 4; ++r) {
+            dst[(16 * at + 4 * g + r) * D + 16 * w + li] = S[at][r];
+            if constexpr (DL) dst[D * D + (16 * at + 4 * g + r) * D + 16 * w + li] = T[at][r];
+        }
 }
 
 template <bool PHI>
 __global__ __launch_bounds__(64 * NW, 2) void k_chunk_state_dma(ChunkStateArgs a, LamArgs lam) {
-    state_body<false, PHI>(a, lam, nullptr);
+    state_body<false, PHI, false>(a, lam, nullptr);
 }
 
 template <bool PHI>
 __global__ __launch_bounds__(64 * NW, 2) void k_chunk_state_dma_varlen(ChunkStateArgs a, LamArgs lam, VarlenArgs v) {
-    state_body<true, PHI>(a, lam, &v);
+    state_body<true, PHI, false>(a, lam, &v);
+}
+
+template <bool PHI>
+__global__ __launch_bounds__(64 * NW, 4) void k_dlam_state_dma(ChunkStateArgs a, LamArgs lam) {
+    state_body<false, PHI, true>(a, lam, nullptr);
 }
 
 }  // namespace
@@ -166,6 +217,14 @@ void launch_chunk_state_dma(const ChunkStateArgs& a, const LamArgs& lam, hipStre
         hipLaunchKernelGGL(k_chunk_state_dma<true>, grid, dim3(64 * NW), 0, s, a, lam);
     else
         hipLaunchKernelGGL(k_chunk_state_dma<false>, grid, dim3(64 * NW), 0, s, a, lam);
+}
+
+void launch_dlam_state_dma(const ChunkStateArgs& a, const LamArgs& lam, hipStream_t s) {
+    dim3 grid(static_cast<unsigned>(a.pairs * (a.chunks - 1)));
+    if (a.phi)
+        hipLaunchKernelGGL(k_dlam_state_dma<true>, grid, dim3(64 * NW), 0, s, a, lam);
+    else
+        hipLaunchKernelGGL(k_dlam_state_dma<false>, grid, dim3(64 * NW), 0, s, a, lam);
 }
 
 void launch_chunk_state_dma_varlen(const ChunkStateArgs& a, const LamArgs& lam, const VarlenArgs& v,

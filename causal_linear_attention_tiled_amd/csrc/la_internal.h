@@ -180,10 +180,14 @@ void launch_scan_varlen(const ScanArgs& a, const LamArgs& lam, const ScanList& l
 // from (kv_in or 0, 0); the sweep; and the sum over batch and chunks per head.
 void launch_dlam_state_generic(const ChunkStateArgs& a, const LamArgs& lam, int bf16, hipStream_t s);
 void launch_dlam_state_mfma(const ChunkStateArgs& a, const LamArgs& lam, hipStream_t s);
+void launch_dlam_state_dma(const ChunkStateArgs& a, const LamArgs& lam, hipStream_t s);  // k_state_dma.hip
 void launch_dlam_scan(const ScanArgs& a, const LamArgs& lam, hipStream_t s);
 void launch_dlam_generic(const DlamArgs& a, const LamArgs& lam, int bf16, hipStream_t s);
 bool dlam_mfma_supported(int D, int Bk);
 void launch_dlam_mfma(const DlamArgs& a, const LamArgs& lam, hipStream_t s);
 void launch_dlam_reduce(const double* partial, int64_t B, int H, int chunks, float* out, hipStream_t s);
+// The sweep on direct-to-LDS loads (k_dlam_dma.hip; bf16, D = 128, Bk = 64).
+bool dlam_dma_supported(int D, int Bk, int64_t N);
+void launch_dlam_dma(const DlamArgs& a, const LamArgs& lam, int waves, hipStream_t s);  // waves: 4 or 8
 
 }  // namespace la

@@ -21,7 +21,12 @@ import causal_linear_attention_tiled_amd as la  # noqa: E402
 @pytest.fixture
 def env(monkeypatch):
     def set_(kernel=None, chunks=None):
-        for name, val in (("LA_KERNEL", kernel), ("LA_CHUNKS", chunks)):
+        # kernel: "default" (direct-to-LDS sweep with 8 compute waves and aggregates, for bf16
+        # D=128 Bk=64), "dma4" (the same sweep with 4 compute waves), "v1" (the register-staged
+        # matrix-core kernels), "generic"
+        for name, val in (("LA_KERNEL", "generic" if kernel == "generic" else None),
+                          ("LA_DLAM", "v1" if kernel == "v1" else None),
+                          ("LA_DLAM_WAVES", "4" if kernel == "dma4" else None), ("LA_CHUNKS", chunks)):
             if val is None:
                 monkeypatch.delenv(name, raising=False)
             else:
@@ -58,28 +63,28 @@ def run_case(B, H, N, D, Bk, dtype, lam, seed, with_state, with_gf, phi="identit
     return y, ref
 
 
-@pytest.mark.parametrize("kernel", ["default", "generic"])
+@pytest.mark.parametrize("kernel", ["default", "dma4", "v1", "generic"])
 @pytest.mark.parametrize("N,cks,with_state,with_gf", [(64 * 13 + 5, 3, True, True), (64 * 13 + 5, None, True, True),
                                                       (64 * 13 + 5, 3, False, False), (64 * 8, 4, False, True),
                                                       (37, None, True, True), (64, None, False, True)])
 def test_dlam_bf16_d128(env, kernel, N, cks, with_state, with_gf):
-    env(kernel="generic" if kernel == "generic" else None, chunks=cks)
+    env(kernel=kernel, chunks=cks)
     run_case(2, 4, N, 128, 64, "bf16", synth.decay_schedule(4), 3, with_state, with_gf, label=kernel)
 
 
 @pytest.mark.parametrize("phi", ["elu1", "relu"])
-@pytest.mark.parametrize("kernel", ["default", "generic"])
+@pytest.mark.parametrize("kernel", ["default", "dma4", "v1", "generic"])
 def test_dlam_feature_maps(env, kernel, phi):
-    env(kernel="generic" if kernel == "generic" else None, chunks=3)
+    env(kernel=kernel, chunks=3)
     run_case(2, 4, 64 * 11 + 9, 128, 64, "bf16", synth.decay_schedule(4), 5, True, True, phi=phi, label=kernel)
 
 
-@pytest.mark.parametrize("kernel", ["default", "generic"])
+@pytest.mark.parametrize("kernel", ["default", "dma4", "v1", "generic"])
 @pytest.mark.parametrize("lam", [[0.0, 0.0], [1.0, 1.0], [0.0, 1.0]])
 def test_dlam_degenerate_decays(env, kernel, lam):
     """lam = 0 (only first-order terms survive: each token with its predecessor, S0's first
     step, the final state's last-but-one token) and lam = 1 (no decay: every age counts)."""
-    env(kernel="generic" if kernel == "generic" else None, chunks=3)
+    env(kernel=kernel, chunks=3)
     run_case(1, 2, 64 * 7 + 3, 128, 64, "bf16", lam, 7, True, True, label=kernel)
 
 
