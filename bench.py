@@ -218,6 +218,56 @@ def serving_workload(torch, la, lam, timed):
                     "rate is not an HBM figure"}
 
 
+# ----------------------------------------------------------------------------- other workloads
+def other_workloads(torch, la, timed):
+    """The remaining named workloads, each timed on its own (inputs resident, HIP events):
+    bf16 forward B4 H16 N2048; the training step B2 H32 N8192 (fwd, then bwd with the
+    forward's chunk states); the long-context prefill B1 H64 N262144 at block 128."""
+    import synth
+    out = {}
+
+    def fwd_case(name, B, Hh, N, bk, reps):
+        lam_h = synth.decay_schedule(Hh)
+        q, k, v = (device_normal(torch, sid, (B, Hh, N, D)) for sid in (1, 2, 3))
+        o = torch.empty_like(q)
+        s = torch.empty((B, Hh, D, D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(la.la_fwd_workspace_bytes(B, Hh, N, D, bk, la.LA_BF16), 1), dtype=torch.uint8,
+                         device="cuda")
+        fn = lambda: la.la_fwd(q, k, v, lam_h, bk, out=o, kv_out=s, ws=ws)
+        fn()
+        ms = timed(fn, reps)
+        byts = 8 * D * B * Hh * N + B * Hh * D * D * 4
+        out[name] = {"workload": f"bf16 forward B{B} H{Hh} N{N} d{D} block {bk}, per-head decay, final state",
+                     "ms": round(ms, 4), "tokens_per_s": round(B * N / (ms * 1e-3)),
+                     "gbs": round(byts / (ms * 1e-3) / 1e9, 1)}
+        del q, k, v, o, s, ws
+
+    fwd_case("fwd_b4_h16_n2048", 4, 16, 2048, BK, 50)
+
+    B, Hh, N = 2, 32, 8192
+    lam_h = synth.decay_schedule(Hh)
+    q, k, v, g = (device_normal(torch, sid, (B, Hh, N, D)) for sid in (1, 2, 3, 4))
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    s = torch.empty((B, Hh, D, D), dtype=torch.float32, device="cuda")
+    wf = la.la_fwd_workspace_bytes(B, Hh, N, D, BK, la.LA_BF16)
+    ws_f = torch.empty(max(wf, 1), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(max(la.la_bwd_workspace_bytes(B, Hh, N, D, BK, la.LA_BF16), 1), dtype=torch.uint8,
+                       device="cuda")
+
+    def train():
+        la.la_fwd(q, k, v, lam_h, BK, out=o, kv_out=s, ws=ws_f)
+        la.la_bwd(q, k, v, g, lam_h, BK, dq=dq, dk=dk, dv=dv, ws=ws_b, fwd_ws=ws_f if wf else None)
+    train()
+    ms = timed(train, 20)
+    out["train_b2_h32_n8192"] = {"workload": "bf16 fwd+bwd B2 H32 N8192 d128 block 64, per-head decay",
+                                 "ms": round(ms, 4), "tokens_per_s": round(B * N / (ms * 1e-3)),
+                                 "gbs": round((8 + 14) * D * B * Hh * N / (ms * 1e-3) / 1e9, 1)}
+    del q, k, v, g, o, dq, dk, dv, s, ws_f, ws_b
+
+    fwd_case("prefill_b1_h64_n262144_block128", 1, 64, 262144, 128, 5)
+    return out
+
+
 # ----------------------------------------------------------------------------- main bench
 def bench(args):
     import numpy as np
@@ -399,6 +449,7 @@ def bench(args):
               "tokens_per_s": round(Bs / (dec_ms * 1e-3))}
 
     serving = serving_workload(torch, la, lam, timed)
+    workloads = other_workloads(torch, la, timed)
 
     tflops_step = sum((fwd_flops_per_token_head() + bwd_flops_per_token_head()) * TOKENS_PER_POINT * H
                       for _ in SWEEP_N) / (ms_per_step * 1e-3) / 1e12
@@ -420,6 +471,7 @@ def bench(args):
         "decode": decode,
         "serving": serving,
         "decay_gradient": dlam,
+        "workloads": workloads,
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -20,9 +20,12 @@ namespace {
 
 using la::LamArgs;
 
-// Target workgroup count for the chunk plan: two per compute unit of an
-// MI355X (256 CUs), so that a launch fills the chip with some slack.
-constexpr int64_t kTargetWorkgroups = 512;
+// Target workgroup count for the chunk plan: one per compute unit of an MI355X
+// (256 CUs).  The sweep kernels hold one workgroup per CU (their LDS rings), so
+// 256 workgroups run in one round; measured, two rounds of half-length chunks
+// are slower (B4 H16 N2048 forward 72 us against 55 us; B2 H32 N8192 forward and
+// backward 559 us against 497 us) and the long-sequence points are unchanged.
+constexpr int64_t kTargetWorkgroups = 256;
 // A chunk should span at least this many blocks, so the per-chunk state
 // traffic (a few D x D float32 matrices) stays small next to its tokens.
 constexpr int64_t kMinBlocksPerChunk = 4;

@@ -209,7 +209,11 @@ __global__ __launch_bounds__(64 * NW, 4) void k_dlam_state_dma(ChunkStateArgs a,
 
 }  // namespace
 
-bool state_dma_supported(int d, int bk, int64_t n) { return d == 128 && bk == 64 && n * d * 2 < (int64_t(1) << 31); }
+// The aggregate of a chunk does not depend on the block size of the sweep (the chunk
+// length is a multiple of it), so any block size that divides into 64-token blocks is served.
+bool state_dma_supported(int d, int bk, int64_t n) {
+    return d == 128 && (bk == 64 || bk == 128) && n * d * 2 < (int64_t(1) << 31);
+}
 
 void launch_chunk_state_dma(const ChunkStateArgs& a, const LamArgs& lam, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(a.pairs * (a.chunks - 1)));

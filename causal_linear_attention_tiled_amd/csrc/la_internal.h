@@ -157,7 +157,7 @@ void launch_fwd_dma_varlen(const SweepArgs& a, const LamArgs& lam, const VarlenA
 bool rev_dma_supported(int D, int Bk, int64_t N);
 void launch_rev_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream_t s);
 
-// Chunk aggregates with direct-to-LDS loads (bf16, D = 128, Bk = 64).
+// Chunk aggregates with direct-to-LDS loads (bf16, D = 128; Bk = 64 or 128, walked in 64-token blocks).
 bool state_dma_supported(int D, int Bk, int64_t N);
 void launch_chunk_state_dma(const ChunkStateArgs& a, const LamArgs& lam, hipStream_t s);
 // Forward chunk aggregates of a ragged batch: one workgroup per (slot, head).

@@ -124,6 +124,18 @@ def test_forced_chunk_counts(c, kern, chunks, kernel):
     check_bwd(1, 2, 64 * 16 + 17, 128, 64, "bf16", lam, seed=c, with_state=True, label=f"chunks={c}")
 
 
+@pytest.mark.parametrize("c", [2, 5])
+@pytest.mark.parametrize("kern", ["generic", "default"])
+def test_forced_chunk_counts_block128(c, kern, chunks, kernel):
+    """Block 128 with chunks: the sweeps take 128-token blocks; the chunk aggregates walk the
+    chunk in 64-token blocks (an aggregate does not depend on the block size)."""
+    chunks(c)
+    kernel(kern)
+    lam = synth.decay_schedule(2)
+    check_fwd(1, 2, 128 * 9 + 17, 128, 128, "bf16", lam, seed=30 + c, with_state=True, label=f"chunks={c}")
+    check_bwd(1, 2, 128 * 9 + 17, 128, 128, "bf16", lam, seed=30 + c, with_state=True, label=f"chunks={c}")
+
+
 # ------------------------------------------------------------------ bit-exact probes
 def impulse_inputs(N, D, j0, c, dtype):
     q = np.zeros((1, 1, N, D), np.float32)
