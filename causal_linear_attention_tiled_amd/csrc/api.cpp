@@ -226,6 +226,8 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
         const int waves = env_is("LA_FWD_WAVES", "8") ? 8 : 4;
         return launch(tag[0] == 'd' ? "dq_dma" : "fwd_dma", s, [&] { la::launch_fwd_dma(a, lam, waves, s); });
     }
+    if (p.mfma && la::fwd_dma128_supported(static_cast<int>(D), Bk, N) && !env_is("LA_FWD", "v1"))
+        return launch(tag[0] == 'd' ? "dq_dma128" : "fwd_dma128", s, [&] { la::launch_fwd_dma128(a, lam, s); });
     if (p.mfma && v1_ok)
         return launch(tag[0] == 'd' ? "dq_mfma" : "fwd_mfma", s, [&] { la::launch_fwd_mfma(a, lam, s); });
     return launch(tag[0] == 'd' ? "dq_generic" : "fwd_generic", s, [&] { la::launch_fwd_generic(a, lam, bf16, s); });

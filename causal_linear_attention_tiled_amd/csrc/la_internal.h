@@ -153,6 +153,11 @@ void launch_fwd_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream
 // The same over a ragged batch: one workgroup per (chunk of a sequence, head), wp[nseq] * H in all.
 void launch_fwd_dma_varlen(const SweepArgs& a, const LamArgs& lam, const VarlenArgs& v, hipStream_t s);
 
+// The same with 128-token blocks (k_fwd_dma128.hip; bf16, D = 128, Bk = 128): a ring of
+// 64-token half blocks, each block computed in two phases.
+bool fwd_dma128_supported(int D, int Bk, int64_t N);
+void launch_fwd_dma128(const SweepArgs& a, const LamArgs& lam, hipStream_t s);
+
 // Reverse (dK, dV) sweep with direct-to-LDS loads (bf16, D = 128, Bk = 64).
 bool rev_dma_supported(int D, int Bk, int64_t N);
 void launch_rev_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream_t s);
