@@ -71,8 +71,9 @@ def bwd_flops_per_token_head(d=D, bk=BK):
     return 5 * d * (bk + 1) + 10 * d * d
 
 
-def kernel_bytes(name, B, Hh, N, d, chunks, with_state=True):
-    """Algorithmic HBM bytes one launch of library kernel `name` must move (bf16 tensors)."""
+def kernel_bytes(name, B, Hh, N, d, chunks, agg=1, with_state=True):
+    """Algorithmic HBM bytes one launch of library kernel `name` must move (bf16 tensors);
+    `agg`: parts per chunk of the forward direction's aggregates (its scan runs over them)."""
     th = B * Hh * N                    # token-heads
     t = 2 * d * th                     # one bf16 [B, H, N, D] tensor
     st = B * Hh * d * d * 4            # one float32 state per sequence
@@ -84,7 +85,7 @@ def kernel_bytes(name, B, Hh, N, d, chunks, with_state=True):
         "chunk_state_mfma": 2 * t * frac,
         "chunk_state_rev_mfma": 2 * t * frac,
         "chunk_state_dma": 2 * t * frac, "chunk_state_rev_dma": 2 * t * frac,
-        "state_scan": 2 * st * (chunks - 1), "state_scan_rev": 2 * st * (chunks - 1),
+        "state_scan": 2 * st * (chunks - 1) * agg, "state_scan_rev": 2 * st * (chunks - 1),
     }.get(name)
 
 
@@ -292,9 +293,10 @@ def bench(args):
         wb = la.la_bwd_workspace_bytes(B, H, n, D, BK, la.LA_BF16)
         ws_f = torch.empty(max(wf, 1), dtype=torch.uint8, device="cuda")
         ws_b = torch.empty(max(wb, 1), dtype=torch.uint8, device="cuda")
-        chunks = wf // (B * H * D * D * 4) + 1 if wf else 1
+        plan = la.la_plan(B, H, n, D, BK, la.LA_BF16)
+        chunks, agg = plan["chunks"], plan["agg_parts"]
         shapes.append(dict(n=n, B=B, q=q, k=k, v=v, g=g, o=o, s=s, dq=dq, dk=dk, dv=dv, ws_f=ws_f,
-                           ws_b=ws_b, chunks=chunks))
+                           ws_b=ws_b, chunks=chunks, agg=agg))
     torch.cuda.synchronize()
 
     def fwd(sh):
@@ -354,7 +356,7 @@ def bench(args):
             names += ["chunk_state_mfma", "chunk_state_rev_mfma", "chunk_state_dma", "chunk_state_rev_dma",
                       "state_scan", "state_scan_rev"]
         for nm in names:
-            b = kernel_bytes(nm, sh["B"], H, sh["n"], D, sh["chunks"])
+            b = kernel_bytes(nm, sh["B"], H, sh["n"], D, sh["chunks"], sh["agg"])
             bytes_by_kernel.setdefault(nm, []).append(b)
     kernels = {}
     for nm, (launches, total_ms) in prof.items():
@@ -404,7 +406,7 @@ def bench(args):
         fbytes = 8 * D * th + sh["B"] * H * D * D * 4
         bbytes = 14 * D * th
         sweep.append({
-            "n": sh["n"], "batch": sh["B"], "chunks": sh["chunks"],
+            "n": sh["n"], "batch": sh["B"], "chunks": sh["chunks"], "agg_parts": sh["agg"],
             "fwd_ms": round(f_ms, 4), "fwd_tokens_per_s": round(TOKENS_PER_POINT / (f_ms * 1e-3)),
             "fwd_tflops": round(ff / (f_ms * 1e-3) / 1e12, 1),
             "fwd_pct_bf16_peak": round(100 * ff / (f_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),

@@ -56,6 +56,8 @@ def _load():
     lib.la_fwd_workspace_bytes.restype = sz
     lib.la_bwd.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.la_bwd.restype = ctypes.c_int
+    lib.la_plan.argtypes = [i64, i64, i64, i64, i32, i32, vp, vp, vp]
+    lib.la_plan.restype = ctypes.c_int
     lib.la_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
     lib.la_bwd_workspace_bytes.restype = sz
     lib.la_dlam.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
@@ -81,7 +83,7 @@ def _load():
 
 lib = _load()
 
-EXPORTS = ("la_fwd", "la_fwd_workspace_bytes", "la_bwd", "la_bwd_workspace_bytes", "la_dlam",
+EXPORTS = ("la_fwd", "la_fwd_workspace_bytes", "la_plan", "la_bwd", "la_bwd_workspace_bytes", "la_dlam",
            "la_dlam_workspace_bytes", "la_decode_step",
            "la_fwd_varlen", "la_fwd_varlen_workspace_bytes", "la_decode_step_paged",
            "la_strerror", "la_version", "la_prof_enable", "la_prof_collect")
@@ -135,6 +137,15 @@ def _check_state(name, t, B, H, D, device):
 
 def la_fwd_workspace_bytes(B, H, N, D, Bk, dtype_code) -> int:
     return int(lib.la_fwd_workspace_bytes(B, H, N, D, Bk, dtype_code))
+
+
+def la_plan(B, H, N, D, Bk, dtype_code) -> dict:
+    """The chunk plan of la_fwd / la_bwd for this shape: chunks, chunk_len, agg_parts."""
+    c, n, k = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int32()
+    rc = lib.la_plan(B, H, N, D, Bk, dtype_code, ctypes.byref(c), ctypes.byref(n), ctypes.byref(k))
+    if rc != LA_OK:
+        raise LaError(rc, "la_plan")
+    return {"chunks": c.value, "chunk_len": n.value, "agg_parts": k.value}
 
 
 def la_bwd_workspace_bytes(B, H, N, D, Bk, dtype_code) -> int:

@@ -122,6 +122,7 @@ struct Plan {
     int chunks;
     int64_t L;     // chunk length in tokens (multiple of Bk)
     bool mfma;
+    int agg_k;     // forward direction: aggregates over chunks of L / agg_k tokens
 };
 
 bool env_is(const char* name, const char* value) {
@@ -151,6 +152,24 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t d
     p.L = bpc * Bk;
     p.chunks = static_cast<int>((nb + bpc - 1) / bpc);
     p.mfma = dtype == LA_BF16 && la::mfma_supported(static_cast<int>(D), Bk) && !force_generic();
+    // The forward direction's chunk aggregates (one workgroup each, two per CU) are taken
+    // over agg_k equal parts of every chunk when the chunks alone would leave the pass
+    // below 3/4 of a round of 512 workgroups; the scan then runs over the parts, and
+    // chunk c of the sweep starts from part c * agg_k - 1.  Each part keeps at least
+    // kMinBlocksPerChunk blocks.  LA_AGG_K forces it (a power of two dividing the blocks
+    // per chunk).
+    p.agg_k = 1;
+    if (p.chunks > 1) {
+        const char* ek = std::getenv("LA_AGG_K");
+        if (ek && std::atoll(ek) > 0) {
+            const int64_t k = std::atoll(ek);
+            if (bpc % k == 0) p.agg_k = static_cast<int>(k);
+        } else {
+            while ((p.chunks - 1) * p.agg_k * pairs < 384 && bpc % (2 * p.agg_k) == 0 &&
+                   bpc / (2 * p.agg_k) >= kMinBlocksPerChunk)
+                p.agg_k *= 2;
+        }
+    }
     return p;
 }
 
@@ -158,6 +177,11 @@ size_t slot_bytes(int64_t pairs, const Plan& p, int64_t D) {
     if (p.chunks <= 1) return 0;
     return static_cast<size_t>(pairs) * static_cast<size_t>(p.chunks - 1) * static_cast<size_t>(D * D) *
            sizeof(float);
+}
+
+// The forward direction's slots: agg_k per chunk boundary.
+size_t fwd_slot_bytes(int64_t pairs, const Plan& p, int64_t D) {
+    return slot_bytes(pairs, p, D) * static_cast<size_t>(p.agg_k);
 }
 
 size_t round_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -189,7 +213,10 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
     // the register-staged kernels have no feature map: with one, the generic kernels run
     const bool v1_ok = phi.kind == 0;
     if (p.chunks > 1 && !given) {
-        la::ChunkStateArgs cs{k, v, slots, N, p.L, static_cast<int>(D), Bk, H, p.chunks, pairs, 0,
+        // aggregates and scan over the agg_k parts of every chunk but the last
+        const int64_t Lf = p.L / p.agg_k;
+        const int chunks_f = (p.chunks - 1) * p.agg_k + 1;
+        la::ChunkStateArgs cs{k, v, slots, N, Lf, static_cast<int>(D), Bk, H, chunks_f, pairs, 0,
                               phi.kind, phi.state_mask};
         if (p.mfma && la::state_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_STATE", "v1"))
             rc = launch("chunk_state_dma", s, [&] { la::launch_chunk_state_dma(cs, lam, s); });
@@ -198,7 +225,7 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
         else
             rc = launch("chunk_state_generic", s, [&] { la::launch_chunk_state_generic(cs, lam, bf16, s); });
         if (rc) return rc;
-        la::ScanArgs sc{slots, kv_in, kv_in_t, nullptr, N, p.L, static_cast<int>(D), H, p.chunks, pairs, 0};
+        la::ScanArgs sc{slots, kv_in, kv_in_t, nullptr, N, Lf, static_cast<int>(D), H, chunks_f, pairs, 0};
         rc = launch("state_scan", s, [&] { la::launch_scan(sc, lam, s); });
         if (rc) return rc;
     }
@@ -222,6 +249,7 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
     a.phi = phi.kind;
     a.phi_mask = phi.sweep_mask;
     a.phi_grad = phi.grad;
+    a.slot_k = p.agg_k;
     if (p.mfma && la::fwd_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_FWD", "v1")) {
         const int waves = env_is("LA_FWD_WAVES", "8") ? 8 : 4;
         return launch(tag[0] == 'd' ? "dq_dma" : "fwd_dma", s, [&] { la::launch_fwd_dma(a, lam, waves, s); });
@@ -315,19 +343,30 @@ const char* la_strerror(int code) {
     }
 }
 
+int la_plan(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t* chunks,
+            int64_t* chunk_len, int32_t* agg_parts) {
+    int64_t elems;
+    const int rc = check_shape(B, H, N, D, Bk, dtype, &elems);
+    if (rc) return rc;
+    const Plan p = make_plan(B, H, N, D, Bk, dtype);
+    if (chunks) *chunks = p.chunks;
+    if (chunk_len) *chunk_len = p.L;
+    if (agg_parts) *agg_parts = p.agg_k;
+    return LA_OK;
+}
+
 size_t la_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype) {
     int64_t elems;
     if (check_shape(B, H, N, D, Bk, dtype, &elems) != LA_OK) return 0;
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
-    return slot_bytes(B * H, p, D);
+    return fwd_slot_bytes(B * H, p, D);
 }
 
 size_t la_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype) {
     int64_t elems;
     if (check_shape(B, H, N, D, Bk, dtype, &elems) != LA_OK) return 0;
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
-    const size_t one = slot_bytes(B * H, p, D);
-    return one ? 2 * round_up(one) : 0;
+    return round_up(fwd_slot_bytes(B * H, p, D)) + round_up(slot_bytes(B * H, p, D));
 }
 
 int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int64_t B, int64_t H,
@@ -346,7 +385,7 @@ int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int
     const size_t tb = static_cast<size_t>(elems) * (dtype == LA_BF16 ? 2 : 4);
     const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
-    const size_t need = slot_bytes(B * H, p, D);
+    const size_t need = fwd_slot_bytes(B * H, p, D);
     if (need && (!ws || ws_bytes < need)) return LA_EWORKSPACE;
     const Range rq{Q, tb}, rk{K, tb}, rv{V, tb}, ro{O, tb}, rin{kv_in, kv_in ? sb : 0},
         rout{kv_out, kv_out ? sb : 0}, rws{ws, need};
@@ -380,11 +419,12 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     const size_t tb = static_cast<size_t>(elems) * (dtype == LA_BF16 ? 2 : 4);
     const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
-    const size_t one = slot_bytes(B * H, p, D);
-    const size_t need = one ? 2 * round_up(one) : 0;
+    const size_t fq = fwd_slot_bytes(B * H, p, D);  // the dQ sweep's chunk states (forward direction)
+    const size_t rv = slot_bytes(B * H, p, D);      // the dK, dV sweep's (reverse direction)
+    const size_t need = round_up(fq) + round_up(rv);
     if (need && (!ws || ws_bytes < need)) return LA_EWORKSPACE;
     const Range ins[] = {{Q, tb}, {K, tb}, {V, tb}, {dO, tb}, {kv_in, kv_in ? sb : 0},
-                         {dkv_out, dkv_out ? sb : 0}, {fwd_ws, fwd_ws ? one : 0}};
+                         {dkv_out, dkv_out ? sb : 0}, {fwd_ws, fwd_ws ? fq : 0}};
     const Range outs[] = {{dQ, tb}, {dK, tb}, {dV, tb}, {dkv_in, dkv_in ? sb : 0}, {ws, need}};
     constexpr int kOuts = sizeof(outs) / sizeof(outs[0]);
     for (const Range& o : outs)
@@ -397,8 +437,8 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     int dev_count = 0;
     if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count == 0) return LA_ENODEV;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    float* slots_q = static_cast<float*>(ws);
-    float* slots_kv = one ? reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(one)) : nullptr;
+    float* slots_q = fq ? static_cast<float*>(ws) : nullptr;
+    float* slots_kv = rv ? reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(fq)) : nullptr;
     const int bf16 = dtype == LA_BF16;
     const int64_t pairs = B * H;
     const int32_t Hi = static_cast<int32_t>(H);

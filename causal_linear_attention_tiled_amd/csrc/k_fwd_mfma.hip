@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kThreads, (BK == 64) ? 2 : 1) void k_fwd_mfma(Sweep
                 tr = a.kv_in_transposed != 0;
             }
         } else {
-            init = a.slots + (pair * (a.chunks - 1) + (c - 1)) * D * D;
+            init = a.slots + fwd_slot_index(a, pair, c) * D * D;
             tr = a.slots_transposed != 0;
         }
 #pragma unroll

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs l
             transposed = a.kv_in_transposed != 0;
         }
     } else {
-        init = a.slots + (pair * (a.chunks - 1) + (c - 1)) * D * D;
+        init = a.slots + fwd_slot_index(a, pair, c) * D * D;
         transposed = a.slots_transposed != 0;
     }
     for (int i = tid; i < D * D; i += kThreads) {

@@ -122,8 +122,10 @@ __device__ __forceinline__ Work work_item(const SA& a, const VA* v, int64_t blk)
         w.base = pair * a.N * a.D;
         w.ld = a.D;
         w.state = pair;
-        w.slot0 = pair * (a.chunks - 1);
-        w.slot_step = 1;
+        // chunk c >= 1 starts from slot c * k - 1 of the sequence's (chunks - 1) k slots
+        const int64_t k = a.slot_k > 1 ? a.slot_k : 1;
+        w.slot0 = pair * (a.chunks - 1) * k + k - 1;
+        w.slot_step = static_cast<int>(k);
     } else {
         // full chunks first (sequence-major), then every sequence's last chunk, longest first
         const int h = static_cast<int>(blk % a.H);

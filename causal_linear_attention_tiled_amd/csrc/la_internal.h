@@ -60,7 +60,18 @@ struct SweepArgs {
     int phi_mask;         // bit 0: a, bit 1: b, bit 2: c (forward: Q, K; dQ sweep: K in c)
     const void* phi_grad; // forward-direction sweeps: raw tensor whose phi' multiplies out0
                           // (the dQ sweep's raw Q), or nullptr
+    int slot_k;           // forward-direction sweeps: the chunk aggregates were taken over
+                          // chunks of L / slot_k tokens (0 or 1: over the sweep's chunks), so
+                          // the state entering chunk c is slot c * slot_k - 1 of the
+                          // (chunks - 1) * slot_k slots of its sequence
 };
+
+// Slot holding the state that enters chunk c >= 1 of sequence `pair` in a
+// forward-direction sweep.
+__host__ __device__ inline int64_t fwd_slot_index(const SweepArgs& a, int64_t pair, int c) {
+    const int64_t k = a.slot_k > 1 ? a.slot_k : 1;
+    return pair * (a.chunks - 1) * k + c * k - 1;
+}
 
 // Chunk aggregate states: for the forward direction chunk c (0..chunks-2)
 //   slot[c] = sum_{t in c} lam^(end_c - 1 - t) x_t y_t^T

@@ -106,6 +106,16 @@ int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int
  * split into chunks).  Returns 0 as well for invalid shapes. */
 size_t la_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype);
 
+/* The chunk plan la_fwd and la_bwd use for this shape (host only, no device
+ * work): *chunks sequence chunks of *chunk_len tokens (the last may be
+ * shorter; 1 chunk when the sequences alone fill the chip), and
+ * *agg_parts, the parts of a chunk over which the forward direction takes
+ * its chunk aggregates (the chunked prefix over blocks, Lightning
+ * Attention-2, Tiling paragraph).  Any output pointer may be NULL.
+ * Returns LA_OK, or the status la_fwd would return for the shape. */
+int la_plan(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t* chunks,
+            int64_t* chunk_len, int32_t* agg_parts);
+
 /* Backward pass of L = <dO, O> + <F, S_N> for the forward above, where F is
  * an optional gradient arriving at the final state (the same tiling run in
  * the backward direction: a forward-order sweep for dQ that carries the key-

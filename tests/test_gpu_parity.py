@@ -180,6 +180,45 @@ def test_impulse_probe_bit_exact(kern, lam_val, Bk, cks, chunks, kernel):
 
 
 @pytest.mark.parametrize("kern", ["generic", "default"])
+@pytest.mark.parametrize("lam_val", [1.0, 0.5])
+@pytest.mark.parametrize("agg", [2, 4])
+def test_impulse_probe_fine_aggregates(kern, lam_val, agg, chunks, kernel, monkeypatch):
+    """The impulse probe with the forward aggregates taken over agg parts of each chunk (two
+    chunks of 8 blocks): keys on part, chunk and block boundaries and their neighbours."""
+    kernel(kern)
+    chunks(2)
+    monkeypatch.setenv("LA_AGG_K", str(agg))
+    N, D, c, Bk = 1000, 128, 3, 64
+    part = 8 * Bk // agg
+    t = np.arange(N)
+    for j0 in sorted({0, part - 1, part, part + 1, 2 * part - 1, 2 * part, 8 * Bk - 1, 8 * Bk, 8 * Bk + 1,
+                      N - 1}):
+        print(f"[impulse] kern={kern} lam={lam_val} agg={agg} j0={j0}", flush=True)
+        qa, ka, va = impulse_inputs(N, D, j0, c, "bf16")
+        o, s = la.la_fwd(to_dev(qa, "bf16"), to_dev(ka, "bf16"), to_dev(va, "bf16"), [lam_val], Bk=Bk)
+        _sync()
+        rel = t - j0
+        keep = rel <= 100 if lam_val < 1 else np.ones(N, bool)
+        expect = np.zeros((N, D))
+        expect[rel >= 0, c] = np.float64(lam_val) ** rel[rel >= 0]
+        np.testing.assert_array_equal(got(o)[0, 0][keep], expect[keep], err_msg=f"j0={j0}")
+
+
+@pytest.mark.parametrize("kern", ["generic", "default"])
+@pytest.mark.parametrize("cks,agg", [(2, 2), (2, 4), (3, 2)])
+def test_fine_aggregates_parity(kern, cks, agg, chunks, kernel, monkeypatch):
+    """Forward and backward (the backward also fed the forward's states) with the forward
+    aggregates over agg parts of each chunk, ragged tail, initial state."""
+    kernel(kern)
+    chunks(cks)
+    monkeypatch.setenv("LA_AGG_K", str(agg))
+    lam = synth.decay_schedule(3)
+    N = 64 * 15 + 17
+    check_fwd(2, 3, N, 128, 64, "bf16", lam, seed=40 + agg, with_state=True, label=f"{kern} agg={agg}")
+    check_bwd(2, 3, N, 128, 64, "bf16", lam, seed=40 + agg, with_state=True, label=f"{kern} agg={agg}", fwd_ws=True)
+
+
+@pytest.mark.parametrize("kern", ["generic", "default"])
 @pytest.mark.parametrize("N,D,Bk", [(2, 128, 64), (2, 128, 128), (16, 16, 16), (16, 16, 64)])
 def test_all_ones_probe_bit_exact(kern, N, D, Bk, kernel):
     """lam = 1 and all-ones bf16 inputs: O_t = (t+1) d and S = N * 1 1^T exactly.
