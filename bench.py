@@ -73,7 +73,7 @@ def bwd_flops_per_token_head(d=D, bk=BK):
 
 def kernel_bytes(name, B, Hh, N, d, chunks, agg=1, with_state=True):
     """Algorithmic HBM bytes one launch of library kernel `name` must move (bf16 tensors);
-    `agg`: parts per chunk of the forward direction's aggregates (its scan runs over them)."""
+    `agg`: parts per chunk of the chunk aggregates (the scans run over them)."""
     th = B * Hh * N                    # token-heads
     t = 2 * d * th                     # one bf16 [B, H, N, D] tensor
     st = B * Hh * d * d * 4            # one float32 state per sequence
@@ -85,7 +85,7 @@ def kernel_bytes(name, B, Hh, N, d, chunks, agg=1, with_state=True):
         "chunk_state_mfma": 2 * t * frac,
         "chunk_state_rev_mfma": 2 * t * frac,
         "chunk_state_dma": 2 * t * frac, "chunk_state_rev_dma": 2 * t * frac,
-        "state_scan": 2 * st * (chunks - 1) * agg, "state_scan_rev": 2 * st * (chunks - 1),
+        "state_scan": 2 * st * (chunks - 1) * agg, "state_scan_rev": 2 * st * (chunks - 1) * agg,
     }.get(name)
 
 

@@ -152,12 +152,12 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t d
     p.L = bpc * Bk;
     p.chunks = static_cast<int>((nb + bpc - 1) / bpc);
     p.mfma = dtype == LA_BF16 && la::mfma_supported(static_cast<int>(D), Bk) && !force_generic();
-    // The forward direction's chunk aggregates (one workgroup each, two per CU) are taken
-    // over agg_k equal parts of every chunk when the chunks alone would leave the pass
-    // below 3/4 of a round of 512 workgroups; the scan then runs over the parts, and
-    // chunk c of the sweep starts from part c * agg_k - 1.  Each part keeps at least
-    // kMinBlocksPerChunk blocks.  LA_AGG_K forces it (a power of two dividing the blocks
-    // per chunk).
+    // The chunk aggregates (one workgroup each, two per CU) are taken over agg_k equal
+    // parts of every chunk when the chunks alone would leave the pass below 3/4 of a
+    // round of 512 workgroups; the scans then run over the parts, chunk c of a forward
+    // sweep starts from part c * agg_k - 1 and chunk c of a reverse sweep from the
+    // gradient entering part (c + 1) agg_k.  Each part keeps at least kMinBlocksPerChunk
+    // blocks.  LA_AGG_K forces it (dividing the blocks per chunk).
     p.agg_k = 1;
     if (p.chunks > 1) {
         const char* ek = std::getenv("LA_AGG_K");
@@ -366,7 +366,7 @@ size_t la_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_
     int64_t elems;
     if (check_shape(B, H, N, D, Bk, dtype, &elems) != LA_OK) return 0;
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
-    return round_up(fwd_slot_bytes(B * H, p, D)) + round_up(slot_bytes(B * H, p, D));
+    return 2 * round_up(fwd_slot_bytes(B * H, p, D));
 }
 
 int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int64_t B, int64_t H,
@@ -419,8 +419,9 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     const size_t tb = static_cast<size_t>(elems) * (dtype == LA_BF16 ? 2 : 4);
     const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
-    const size_t fq = fwd_slot_bytes(B * H, p, D);  // the dQ sweep's chunk states (forward direction)
-    const size_t rv = slot_bytes(B * H, p, D);      // the dK, dV sweep's (reverse direction)
+    // chunk states of the dQ sweep (forward direction) and of the dK, dV sweep (reverse
+    // direction), both over agg_k parts per chunk boundary
+    const size_t fq = fwd_slot_bytes(B * H, p, D), rv = fq;
     const size_t need = round_up(fq) + round_up(rv);
     if (need && (!ws || ws_bytes < need)) return LA_EWORKSPACE;
     const Range ins[] = {{Q, tb}, {K, tb}, {V, tb}, {dO, tb}, {kv_in, kv_in ? sb : 0},
@@ -451,10 +452,14 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
                            N, D, Bk, Hi, bf16, p, lam, pu, s, "dq");
     if (rc) return rc;
 
-    // dK, dV: reverse sweep carrying dS, with a chunked suffix over blocks.
+    // dK, dV: reverse sweep carrying dS, with a chunked suffix over blocks; the aggregates
+    // are taken over the agg_k parts of every chunk but the first (a part past the end of
+    // the sequence aggregates nothing)
     if (p.chunks > 1) {
-        la::ChunkStateArgs cs{Q, dO, slots_kv, N, p.L, static_cast<int>(D), Bk, Hi, p.chunks, pairs, 1,
-                              phi, 1};
+        const int64_t Lf = p.L / p.agg_k;
+        const int chunks_f = (p.chunks - 1) * p.agg_k + 1;
+        la::ChunkStateArgs cs{Q, dO, slots_kv, N, Lf, static_cast<int>(D), Bk, Hi, chunks_f, pairs, 1,
+                              phi, 1, p.agg_k - 1};
         if (p.mfma && la::state_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_STATE", "v1"))
             rc = launch("chunk_state_rev_dma", s, [&] { la::launch_chunk_state_dma(cs, lam, s); });
         else if (p.mfma && phi == 0)
@@ -462,7 +467,8 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
         else
             rc = launch("chunk_state_rev_generic", s, [&] { la::launch_chunk_state_generic(cs, lam, bf16, s); });
         if (rc) return rc;
-        la::ScanArgs sc{slots_kv, nullptr, 0, dkv_out, N, p.L, static_cast<int>(D), Hi, p.chunks, pairs, 1};
+        la::ScanArgs sc{slots_kv, nullptr, 0, dkv_out, N, Lf, static_cast<int>(D), Hi, chunks_f, pairs, 1,
+                        p.agg_k - 1};
         rc = launch("state_scan_rev", s, [&] { la::launch_scan(sc, lam, s); });
         if (rc) return rc;
     }
@@ -478,6 +484,7 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     a.ds_out = dkv_in;
     a.phi = phi;
     a.phi_mask = 3;
+    a.slot_k = p.agg_k;
     a.N = N;
     a.L = p.L;
     a.D = static_cast<int>(D);

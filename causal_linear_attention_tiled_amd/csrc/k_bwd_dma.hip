@@ -89,7 +89,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_rev_dma(SweepArgs a, LamArgs lam
     //   Sk[at][h][r] = dS^T[32 (at/2) + rho(at%2, 4g + r)][32 w + 16 h + li]   (key rows)
     f32x4 Sv[8][2], Sk[8][2];
     {
-        const float* init = (c < a.chunks - 1) ? a.slots + (pair * (a.chunks - 1) + c) * D * D
+        const float* init = (c < a.chunks - 1) ? a.slots + rev_slot_index(a, pair, c) * D * D
                                                : (a.g_final ? a.g_final + pair * D * D : nullptr);
 #pragma unroll
         for (int at = 0; at < 8; ++at)
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(64 * 8, 1) void k_rev_dma_split(SweepArgs a, LamArg
     //   or dS^T (key group), entering this chunk from the right (0 for the last chunk).
     f32x4 S[8][2];
     {
-        const float* init = (c < a.chunks - 1) ? a.slots + (pair * (a.chunks - 1) + c) * D * D
+        const float* init = (c < a.chunks - 1) ? a.slots + rev_slot_index(a, pair, c) * D * D
                                                : (a.g_final ? a.g_final + pair * D * D : nullptr);
 #pragma unroll
         for (int at = 0; at < 8; ++at)

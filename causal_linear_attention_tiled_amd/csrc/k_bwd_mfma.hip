@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_rev_mfma(SweepArgs a, LamArgs l
     //   Sk[vt][kt][r] = dS^T[16 vt + 4 g + r][32 w + 16 kt + li] = dS[32 w + 16 kt + li][16 vt + 4 g + r]
     f32x4 Sv[8][2], Sk[8][2];
     {
-        const float* init = (c < a.chunks - 1) ? a.slots + (pair * (a.chunks - 1) + c) * D * D
+        const float* init = (c < a.chunks - 1) ? a.slots + rev_slot_index(a, pair, c) * D * D
                                                : (a.g_final ? a.g_final + pair * D * D : nullptr);
 #pragma unroll
         for (int t8 = 0; t8 < 8; ++t8)

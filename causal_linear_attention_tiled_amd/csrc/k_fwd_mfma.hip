@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_state_mfma(ChunkStateArgs
     const int per = a.chunks - 1;
     const int64_t pair = blockIdx.x / per;
     const int slot = blockIdx.x % per;
-    const int c = a.reverse ? slot + 1 : slot;
+    const int c = a.reverse ? slot + 1 + a.part0 : slot;
     const int64_t t_begin = static_cast<int64_t>(c) * a.L;
     const int64_t t_end = min(a.N, t_begin + a.L);
     const int64_t base = pair * a.N * D;

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs l
     };
     fill_powers(sh.pw, lv, Bk);
     const bool last = c == a.chunks - 1;
-    const float* init = !last ? a.slots + (pair * (a.chunks - 1) + c) * D * D
+    const float* init = !last ? a.slots + rev_slot_index(a, pair, c) * D * D
                               : (a.g_final ? a.g_final + pair * D * D : nullptr);
     for (int i = tid; i < D * D; i += kThreads) sh.state[i] = init ? init[i] : 0.f;
     __syncthreads();
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state_generic(ChunkStateArgs
     const int per = a.chunks - 1;
     const int64_t pair = blockIdx.x / per;
     const int slot = blockIdx.x % per;
-    const int c = a.reverse ? slot + 1 : slot;
+    const int c = a.reverse ? slot + 1 + a.part0 : slot;
     const int D = a.D, Bk = a.Bk, tid = threadIdx.x;
     fill_powers(pw, lam.lam[pair % a.H], Bk);
     for (int i = tid; i < D * D; i += kThreads) state[i] = 0.f;
@@ -246,13 +246,21 @@ __global__ __launch_bounds__(kThreads) void k_scan(ScanArgs a, LamArgs lam) {
             sl[static_cast<int64_t>(c) * DD] = S;
         }
     } else {
-        // the final-state gradient reaches the end of chunk chunks-2 decayed over the last
-        // chunk's length minus one (it enters at the last token undecayed)
-        const int64_t len_last = a.N - static_cast<int64_t>(a.chunks - 1) * a.L;
-        float R = a.g_final ? lam_pow(lam.lam[pair % a.H], len_last - 1) * a.g_final[pair * DD + e] : 0.f;
+        // the final-state gradient enters at the last token undecayed, so it reaches the
+        // start of chunk j decayed over N - 1 - j L tokens
+        const float G = a.g_final ? a.g_final[pair * DD + e] : 0.f;
+        float R = 0.f;
+        bool started = false;
         for (int c = a.chunks - 2; c >= 0; --c) {
-            R = sl[static_cast<int64_t>(c) * DD] + (c == a.chunks - 2 ? R : lamL * R);
-            sl[static_cast<int64_t>(c) * DD] = R;
+            const int64_t start = (static_cast<int64_t>(c) + 1 + a.part0) * a.L;
+            float* p = sl + static_cast<int64_t>(c) * DD;
+            if (start >= a.N) {
+                *p = 0.f;  // a part past the end of the sequence
+                continue;
+            }
+            R = started ? *p + lamL * R : *p + lam_pow(lam.lam[pair % a.H], a.N - 1 - start) * G;
+            started = true;
+            *p = R;
         }
     }
 }

@@ -60,7 +60,7 @@ __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArg
         const int per = a.chunks - 1;
         const int64_t pair = blockIdx.x / per;
         const int slot = blockIdx.x % per;
-        c = a.reverse ? slot + 1 : slot;
+        c = a.reverse ? slot + 1 + a.part0 : slot;
         base = pair * a.N * D;
         ld = D;
         n_seq = a.N;

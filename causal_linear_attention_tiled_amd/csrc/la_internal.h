@@ -60,11 +60,18 @@ struct SweepArgs {
     int phi_mask;         // bit 0: a, bit 1: b, bit 2: c (forward: Q, K; dQ sweep: K in c)
     const void* phi_grad; // forward-direction sweeps: raw tensor whose phi' multiplies out0
                           // (the dQ sweep's raw Q), or nullptr
-    int slot_k;           // forward-direction sweeps: the chunk aggregates were taken over
-                          // chunks of L / slot_k tokens (0 or 1: over the sweep's chunks), so
-                          // the state entering chunk c is slot c * slot_k - 1 of the
-                          // (chunks - 1) * slot_k slots of its sequence
+    int slot_k;           // the chunk aggregates were taken over chunks of L / slot_k tokens
+                          // (0 or 1: over the sweep's chunks); see fwd_slot_index and
+                          // rev_slot_index
 };
+
+// Slot holding the gradient state that enters chunk c <= chunks - 2 of sequence `pair`
+// from the right in a reverse sweep (the reverse aggregates are taken over slot_k parts
+// of every chunk but the first, so it is slot c * slot_k of (chunks - 1) * slot_k).
+__host__ __device__ inline int64_t rev_slot_index(const SweepArgs& a, int64_t pair, int c) {
+    const int64_t k = a.slot_k > 1 ? a.slot_k : 1;
+    return (pair * (a.chunks - 1) + c) * k;
+}
 
 // Slot holding the state that enters chunk c >= 1 of sequence `pair` in a
 // forward-direction sweep.
@@ -87,13 +94,16 @@ struct ChunkStateArgs {
     int reverse;
     int phi;        // feature map (kPhi*) ...
     int phi_mask;   // ... applied to x (bit 0) and / or y (bit 1)
+    int part0;      // reverse: slot s aggregates chunk s + 1 + part0 (chunks of L tokens here
+                    // being the parts of the sweep's chunks)
 };
 
 // In-place scan of the slots of every sequence.
 //   forward: S = kv_in (or 0); for c = 0..chunks-2: S = lam^L S + slot[c]; slot[c] = S
-//   reverse: R = lam^(len_last - 1) G pulled back to the end of chunk chunks-2, then
-//            for c = chunks-2..0: R = slot[c] + (c == chunks-2 ? R : lam^L R); slot[c] = R
-//            (len_last = N - (chunks-1) L, the last chunk's length; G = g_final or 0)
+//   reverse: slot c holds the aggregate of chunk j = c + 1 + part0 (chunks of L tokens,
+//            starting at j L); from the last chunk that starts before N down to c = 0:
+//            R = slot[c] + lam^(N - 1 - j L) G for the first one, R = slot[c] + lam^L R after;
+//            slot[c] = R (0 for chunks past the end; G = g_final or 0)
 struct ScanArgs {
     float* slots;
     const float* kv_in;   // forward: initial state, or nullptr
@@ -104,6 +114,7 @@ struct ScanArgs {
     int D, H, chunks;
     int64_t pairs;
     int reverse;
+    int part0;
 };
 
 struct DecodeArgs {

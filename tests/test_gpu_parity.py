@@ -401,6 +401,46 @@ def test_final_state_gradient_probe_bit_exact(kern, N, cks, kernel, chunks):
         np.testing.assert_array_equal(got(ds0)[0, 0], 0.5 ** N * F[0, 0].astype(np.float64))
 
 
+@pytest.mark.parametrize("kern", ["generic", "default"])
+@pytest.mark.parametrize("N,cks,agg", [(773, 4, 2), (1024, 2, 4)])
+def test_final_state_gradient_probe_parts(kern, N, cks, agg, kernel, chunks, monkeypatch):
+    """The final-state gradient probe with the reverse aggregates over parts of each chunk:
+    at N = 773 with 4 chunks of 4 blocks in 2 parts each, the last chunk holds one block,
+    so its second part lies past the end of the sequence and the gradient enters through
+    the part before it."""
+    kernel(kern)
+    chunks(cks)
+    monkeypatch.setenv("LA_AGG_K", str(agg))
+    D, c = 128, 7
+    print(f"[probe dkv_out] kern={kern} N={N} chunks={cks} parts={agg}", flush=True)
+    zero = np.zeros((1, 1, N, D), np.float32)
+    kk = zero.copy(); kk[..., 0] = 1.0
+    vv = zero.copy(); vv[..., c] = 1.0
+    q, k, v, g = (to_dev(synth.f32_to_bf16_bits(x), "bf16") for x in (zero, kk, vv, zero))
+    F = np.zeros((1, 1, D, D), np.float32); F[0, 0, 0, c] = 1.0
+    dq, dk, dv = la.la_bwd(q, k, v, g, [0.5], Bk=64, dkv_out=torch.from_numpy(F).cuda())
+    _sync()
+    rel = N - 1 - np.arange(N)
+    keep = rel <= 100
+    e_k = np.zeros((N, D)); e_k[:, 0] = 0.5 ** rel
+    e_v = np.zeros((N, D)); e_v[:, c] = 0.5 ** rel
+    np.testing.assert_array_equal(got(dk)[0, 0][keep], e_k[keep])
+    np.testing.assert_array_equal(got(dv)[0, 0][keep], e_v[keep])
+    assert not np.any(got(dq))
+
+
+@pytest.mark.parametrize("kern", ["generic", "default"])
+@pytest.mark.parametrize("N,cks,agg", [(773, 4, 2), (64 * 15 + 17, 2, 4), (64 * 17 + 3, 3, 2)])
+def test_state_gradients_parts(kern, N, cks, agg, kernel, chunks, monkeypatch):
+    """dQ, dK, dV, the final-state gradient's path and dS0 with the aggregates over parts of
+    each chunk (both directions), including a part past the end of the sequence."""
+    kernel(kern)
+    chunks(cks)
+    monkeypatch.setenv("LA_AGG_K", str(agg))
+    lam = synth.decay_schedule(3)
+    check_state_grads(1, 3, N, 64, lam, seed=N + agg, with_state=True, with_gf=True, label=f"{kern} parts={agg}")
+
+
 @pytest.mark.parametrize("variant", ["v1", "dma4", "dma8"])
 def test_impulse_probe_variants(variant, fwd_variant, chunks, kernel):
     fwd_variant(variant)
