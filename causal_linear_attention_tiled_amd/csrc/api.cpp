@@ -188,7 +188,7 @@ size_t round_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // la_dlam: the (S, T) chunk slots, then one double per (sequence, chunk).
 size_t dlam_ws_bytes(int64_t pairs, const Plan& p, int64_t D) {
-    return round_up(2 * slot_bytes(pairs, p, D)) + round_up(static_cast<size_t>(pairs * p.chunks) * sizeof(double));
+    return round_up(2 * fwd_slot_bytes(pairs, p, D)) + round_up(static_cast<size_t>(pairs * p.chunks) * sizeof(double));
 }
 
 // ------------------------------------------------------------------ sweeps
@@ -543,9 +543,12 @@ int la_dlam(const void* Q, const void* K, const void* V, const void* dO, const f
     const bool dma = p.mfma && la::dlam_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_DLAM", "v1");
     const bool mfma = p.mfma && la::dlam_mfma_supported(static_cast<int>(D), Bk);
     float* slots = static_cast<float*>(ws);
-    double* partial = reinterpret_cast<double*>(static_cast<char*>(ws) + round_up(2 * slot_bytes(pairs, p, D)));
+    double* partial = reinterpret_cast<double*>(static_cast<char*>(ws) + round_up(2 * fwd_slot_bytes(pairs, p, D)));
+    // the (S, T) aggregates and their scan run over the agg_k parts of every chunk but the last
+    const int64_t Lf = p.L / p.agg_k;
+    const int chunks_f = (p.chunks - 1) * p.agg_k + 1;
     if (p.chunks > 1) {
-        la::ChunkStateArgs cs{K, V, slots, N, p.L, static_cast<int>(D), Bk, Hi, p.chunks, pairs, 0, phi, 1};
+        la::ChunkStateArgs cs{K, V, slots, N, Lf, static_cast<int>(D), Bk, Hi, chunks_f, pairs, 0, phi, 1};
         if (dma)
             rc = launch("dlam_state_dma", s, [&] { la::launch_dlam_state_dma(cs, lam, s); });
         else if (mfma)
@@ -553,12 +556,12 @@ int la_dlam(const void* Q, const void* K, const void* V, const void* dO, const f
         else
             rc = launch("dlam_state_generic", s, [&] { la::launch_dlam_state_generic(cs, lam, bf16, s); });
         if (rc) return rc;
-        la::ScanArgs sc{slots, kv_in, 0, nullptr, N, p.L, static_cast<int>(D), Hi, p.chunks, pairs, 0};
+        la::ScanArgs sc{slots, kv_in, 0, nullptr, N, Lf, static_cast<int>(D), Hi, chunks_f, pairs, 0};
         rc = launch("dlam_scan", s, [&] { la::launch_dlam_scan(sc, lam, s); });
         if (rc) return rc;
     }
     la::DlamArgs da{Q, K, V, dO, p.chunks > 1 ? slots : nullptr, kv_in, dkv_out, partial, N, p.L,
-                    static_cast<int>(D), Bk, Hi, p.chunks, pairs, phi};
+                    static_cast<int>(D), Bk, Hi, p.chunks, pairs, phi, p.agg_k};
     if (dma)
         rc = launch("dlam_dma", s, [&] { la::launch_dlam_dma(da, lam, env_is("LA_DLAM_WAVES", "4") ? 4 : 8, s); });
     else if (mfma)

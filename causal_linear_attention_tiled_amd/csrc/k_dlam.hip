@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void k_dlam_generic(DlamArgs a, LamArgs l
             T[i] = 0.f;
         }
     } else {
-        const float* src = a.slots + (pair * (a.chunks - 1) + (c - 1)) * 2 * static_cast<int64_t>(DD);
+        const float* src = a.slots + dlam_slot_offset(a, pair, c);
         for (int i = tid; i < DD; i += kThreads) {
             S[i] = src[i];
             T[i] = src[DD + i];
@@ -413,7 +413,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dlam_mfma(DlamArgs a, LamArgs l
         if (c == 0) {
             s_src = a.kv_in ? a.kv_in + pair * D * D : nullptr;
         } else {
-            s_src = a.slots + (pair * (a.chunks - 1) + (c - 1)) * 2 * static_cast<int64_t>(D * D);
+            s_src = a.slots + dlam_slot_offset(a, pair, c);
             t_src = s_src + D * D;
         }
 #pragma unroll

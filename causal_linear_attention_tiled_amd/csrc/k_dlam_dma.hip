@@ -101,7 +101,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_dlam_dma(DlamArgs a, LamAr
             if (c == 0) {
                 s_src = a.kv_in ? a.kv_in + pair * D * D : nullptr;
             } else {
-                s_src = a.slots + (pair * (a.chunks - 1) + (c - 1)) * 2 * static_cast<int64_t>(D * D);
+                s_src = a.slots + dlam_slot_offset(a, pair, c);
                 t_src = s_src + D * D;
             }
 #pragma unroll

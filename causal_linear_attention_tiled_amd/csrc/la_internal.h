@@ -153,7 +153,16 @@ struct DlamArgs {
     int D, Bk, H, chunks;
     int64_t pairs;
     int phi;                // feature map on q and k
+    int slot_k;             // the (S, T) aggregates were taken over chunks of L / slot_k
+                            // tokens (0 or 1: over these chunks): chunk c >= 1 starts from
+                            // slot c * slot_k - 1 of the sequence's (chunks - 1) * slot_k
 };
+
+// First float of the (S, T) slot pair that chunk c >= 1 of sequence `pair` starts from.
+__host__ __device__ inline int64_t dlam_slot_offset(const DlamArgs& a, int64_t pair, int c) {
+    const int64_t k = a.slot_k > 1 ? a.slot_k : 1;
+    return (pair * (a.chunks - 1) * k + c * k - 1) * 2 * static_cast<int64_t>(a.D) * a.D;
+}
 
 // Launchers (each enqueues exactly one kernel on `s`; errors are read by the caller).
 void launch_fwd_generic(const SweepArgs& a, const LamArgs& lam, int bf16, hipStream_t s);

@@ -101,6 +101,16 @@ def test_dlam_bf16_generic_shapes(env, D, Bk):
     run_case(2, 3, 5 * Bk + 7, D, Bk, "bf16", np.array([0.5, 0.97, 1.0]), 11, True, True)
 
 
+@pytest.mark.parametrize("kernel", ["default", "v1", "generic"])
+@pytest.mark.parametrize("cks,agg", [(2, 2), (2, 4), (3, 2)])
+def test_dlam_aggregate_parts(env, kernel, cks, agg, monkeypatch):
+    """The (S, T) chunk aggregates and their scan over agg parts of each chunk."""
+    env(kernel=kernel, chunks=cks)
+    monkeypatch.setenv("LA_AGG_K", str(agg))
+    run_case(2, 3, 64 * 15 + 17, 128, 64, "bf16", synth.decay_schedule(3), 17 + agg, True, True,
+             label=f"{kernel} parts={agg}")
+
+
 def test_dlam_per_head_batch_sum(env):
     """Heads with equal decays but different inputs: the result is the sum over the batch of
     each head's own sequences (not mixed across heads)."""
