@@ -482,7 +482,12 @@ __global__ __launch_bounds__(64 * 8, 1) void k_rev_dma_split(SweepArgs a, LamArg
 
 }  // namespace
 
-bool rev_dma_supported(int d, int bk, int64_t n) { return d == 128 && bk == 64 && n * d * 2 < (int64_t(1) << 31); }
+// Bk = 128 runs its blocks as two 64-token halves (the dK, dV of a 128-token block need its
+// four operand tiles twice over, more than LDS holds): the same function, with the
+// second half's contribution to the first carried through dS instead of a score tile.
+bool rev_dma_supported(int d, int bk, int64_t n) {
+    return d == 128 && (bk == 64 || bk == 128) && n * d * 2 < (int64_t(1) << 31);
+}
 
 void launch_rev_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(a.pairs * a.chunks));

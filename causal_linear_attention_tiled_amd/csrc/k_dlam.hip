@@ -531,7 +531,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_dlam_mfma(DlamArgs a, LamArgs l
             }
 
         // ---- 4. inter: per 16-token column st, X^T = S^T Q^T and Y^T = T^T Q^T for this
-        //         wave's columns col = 32 w + 16 vt + 4 g + r, against dO[s][col]
+        //         wave's columns col = 32 w + 16 vt + 4 g + r, against dO[s][col]; T enters as
+        //         its bf16 operand plus the residual of that rounding
         {
             bf16x8 sb[2][4], tb[2][4];
 #pragma unroll
@@ -555,6 +556,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_dlam_mfma(DlamArgs a, LamArgs l
                     for (int ks = 0; ks < 4; ++ks) {
                         x = mfma16(sb[vt][ks], qf[ks], x);
                         y = mfma16(tb[vt][ks], qf[ks], y);
+                        // T is large next to the result near lam = 1: add its rounding residual
+                        y = mfma16(operand_residual_from_acc(T[2 * ks][vt], T[2 * ks + 1][vt]), qf[ks], y);
                     }
                     const u32x2 d = *reinterpret_cast<const u32x2*>(&sm.g[s * QP + 32 * w + 16 * vt + 4 * g]);
                     const float d0 = lo_bf16(d.x), d1 = hi_bf16(d.x), d2 = lo_bf16(d.y), d3 = hi_bf16(d.y);

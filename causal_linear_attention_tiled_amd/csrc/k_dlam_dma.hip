@@ -9,12 +9,12 @@
 //     current block computes (it never stores, so vmcnt(0) waits exactly for the
 //     block it hands over);
 //   - NW compute waves (4 or 8), wave w owning value columns [128w/NW, 128(w+1)/NW) of S and T
-//     in MFMA accumulators (the forward kernel's interleaved-row layout, so the
-//     accumulators are directly the A operand of S^T Q^T and T^T Q^T);
+//     in MFMA accumulators (the forward kernel's interleaved-row layout);
 //   - per block: the causal 16x16 tiles of P^T = K Q^T and G^T = V dO^T, shared
 //     out over the waves, multiplied elementwise with the derivative mask
-//     (s-s') lam^(s-s'-1) and summed; S^T Q^T and T^T Q^T dotted with dO^T under
-//     the row weights (s+1) lam^s and lam^(s+1); then
+//     (s-s') lam^(s-s'-1) and summed; the inter-block terms as the elementwise
+//     products of S and T with Q^T diag(w) dO under the row weights (s+1) lam^s
+//     and lam^(s+1); then
 //     T <- lam^m T + m lam^(m-1) S + K^T diag((m-1-s) lam^(m-2-s)) V and
 //     S <- lam^m S + K^T diag(lam^(m-1-s)) V.
 // The loader wave takes part in the final reduction, so every wave passes every
@@ -157,35 +157,51 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_dlam_dma(DlamArgs a, LamAr
                     }
                 }
 
-            // ---- inter, in two passes (S then T, so one set of converted operands is live):
-            //      x[r] = (X^T Q^T)[col][s] for X = S (weight (s+1) lam^s) and X = T (lam^(s+1)),
-            //      col = 16 (NVT w + vt) + 4 g + r, dotted with dO[s][col]
+            // ---- inter: the term sum_s w_s q_s X dO_s^T is the elementwise product of X with
+            //      M = Q^T diag(w) dO, for X = S (w_s = (s+1) lam^s) and X = T (lam^(s+1)).  M is
+            //      built on the matrix cores from the bf16 tiles, in the accumulators' own layout
+            //      (Q read as the state update reads K), so the state itself never passes through
+            //      bf16.  T grows like (t+1) S0 and the summed ages of the keys at lam near 1,
+            //      large next to the result, so the weighted dO it meets also carries its
+            //      rounding residual, as a second operand.
+            {
+                bf16x8 gs[NKB][NVT], gt[NKB][NVT], gr[NKB][NVT];
 #pragma unroll
-            for (int pass = 0; pass < 2; ++pass) {
-                bf16x8 xb[NVT][4];
+                for (int kb = 0; kb < NKB; ++kb) {
+                    float ws[8], wt[8];
 #pragma unroll
-                for (int vt = 0; vt < NVT; ++vt)
-#pragma unroll
-                    for (int kb = 0; kb < 4; ++kb)
-                        xb[vt][kb] = pass == 0 ? operand_from_acc(S[2 * kb][vt], S[2 * kb + 1][vt])
-                                               : operand_from_acc(T[2 * kb][vt], T[2 * kb + 1][vt]);
-#pragma unroll
-                for (int st = 0; st < NT; ++st) {
-                    const int s = 16 * st + li;
-                    bf16x8 qf[4];
-#pragma unroll
-                    for (int kb = 0; kb < 4; ++kb) qf[kb] = op_row(Qs, s, 32 * kb, g);
-                    const float wt = pass == 0 ? sm.dpw[s + 1] : sm.pw[s + 1];
+                    for (int e = 0; e < 8; ++e) {
+                        const int s = 32 * kb + kappa(g, e);
+                        ws[e] = masked_pw(sm.dpw, s + 1, s < m);
+                        wt[e] = masked_pw(sm.pw, s + 1, s < m);
+                    }
 #pragma unroll
                     for (int vt = 0; vt < NVT; ++vt) {
-                        f32x4 x = zero4();
-#pragma unroll
-                        for (int kb = 0; kb < 4; ++kb) x = mfma16(xb[vt][kb], qf[kb], x);
-                        const u32x2 d = *reinterpret_cast<const u32x2*>(Gs + swz(s, 16 * (NVT * w + vt) + 4 * g));
-                        part += wt * (__uint_as_float(d.x << 16) * x[0] + __uint_as_float(d.x & 0xFFFF0000u) * x[1] +
-                                      __uint_as_float(d.y << 16) * x[2] + __uint_as_float(d.y & 0xFFFF0000u) * x[3]);
+                        const bf16x8 gf = op_tr_k(Gs, 32 * kb, 16 * (NVT * w + vt), 4, g, li);
+                        gs[kb][vt] = scale8(gf, ws);
+                        scale8_split(gf, wt, gt[kb][vt], gr[kb][vt]);
                     }
-                    // keep the scheduler from hoisting every column's LDS reads (register pressure)
+                }
+#pragma unroll
+                for (int at = 0; at < 8; ++at) {
+                    f32x4 ms[NVT], mt[NVT];
+#pragma unroll
+                    for (int vt = 0; vt < NVT; ++vt) ms[vt] = mt[vt] = zero4();
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) {
+                        const bf16x8 qf = op_tr_k(Qs, 32 * kb, 32 * (at >> 1) + 4 * (at & 1), 8, g, li);
+#pragma unroll
+                        for (int vt = 0; vt < NVT; ++vt) {
+                            ms[vt] = mfma16(qf, gs[kb][vt], ms[vt]);
+                            mt[vt] = mfma16(qf, gt[kb][vt], mt[vt]);
+                            mt[vt] = mfma16(qf, gr[kb][vt], mt[vt]);
+                        }
+                    }
+#pragma unroll
+                    for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) part += S[at][vt][r] * ms[vt][r] + T[at][vt][r] * mt[vt][r];
+                    // keep the scheduler from hoisting every band's LDS reads (register pressure)
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -260,7 +276,10 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_dlam_dma(DlamArgs a, LamAr
 
 }  // namespace
 
-bool dlam_dma_supported(int d, int bk, int64_t n) { return d == D && bk == BK && n * d * 2 < (int64_t(1) << 31); }
+// Bk = 128 runs its blocks as two 64-token halves, as the dK, dV sweep does.
+bool dlam_dma_supported(int d, int bk, int64_t n) {
+    return d == D && (bk == BK || bk == 2 * BK) && n * d * 2 < (int64_t(1) << 31);
+}
 
 void launch_dlam_dma(const DlamArgs& a, const LamArgs& lam, int waves, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(a.pairs * a.chunks));

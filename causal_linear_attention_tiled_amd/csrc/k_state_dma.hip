@@ -21,11 +21,16 @@
 // [16w, 16w + 16) of the aggregate.
 //
 // The decay-derivative form (forward only) also sums dT = d(acc)/dlam =
-// sum_t (E - 1 - t) lam^(E - 2 - t) x_t y_t^T: with c = lam^W after W walked
-// tokens and dc = W lam^(W - 1) its derivative (both running products in
-// double), token s of an m-token block weighs c lam^(m-1-s) in acc and
-// dc lam^(m-1-s) + c (m-1-s) lam^(m-2-s) in dT.  The two slots of a chunk are
-// stored back to back (acc, then dT).
+// sum_t (E - 1 - t) lam^(E - 2 - t) x_t y_t^T.  It walks the blocks first to
+// last and rescales instead: per m-token block, (acc, dT) <- (lam^m acc,
+// lam^m dT + m lam^(m-1) acc) plus the block's own terms, token s weighing
+// lam^(m-1-s) in acc and (m-1-s) lam^(m-2-s) in dT.  Folding a token's whole
+// age into one rounded operand weight would give dT a rounding error of its
+// own, unrelated to acc's; carried this way, dT stays the derivative of the
+// acc that was actually summed, up to the rounding of the small in-block
+// weights, which matters where the loss's decay derivative is a sum that
+// cancels (lam near 1).  The two slots of a chunk are stored back to back
+// (acc, then dT).
 #include "la_device.h"
 #include "la_internal.h"
 #include "lds_dma.h"
@@ -93,7 +98,7 @@ __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArg
     const u32x4 ry = buffer_rsrc(static_cast<const uint16_t*>(a.y) + base, bytes);
     // The n-th block of the walk goes to stage n % 2; wave w issues, for each
     // tensor, the loads of row groups w and w + 8 (4 rows each).
-    auto block_of = [&](int64_t n) { return a.reverse ? n : nblk - 1 - n; };
+    auto block_of = [&](int64_t n) { return (a.reverse || DL) ? n : nblk - 1 - n; };
     auto issue = [&](int64_t n) {
         const int64_t t0 = t_begin + block_of(n) * BK;
         const int stage = static_cast<int>(n % NSTAGE);
@@ -118,8 +123,7 @@ __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArg
 #pragma unroll
         for (int at = 0; at < 8; ++at) T[at] = zero4();
     }
-    double cw = 1.0;   // lam^(tokens walked so far)
-    double dcw = 0.0;  // its derivative
+    double cw = 1.0;  // lam^(tokens walked so far), for the form without rescaling
 
     for (int64_t n = 0; n < nblk; ++n) {
         const int64_t t0 = t_begin + block_of(n) * BK;
@@ -137,8 +141,8 @@ __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArg
         const uint16_t* Xs = sm.t[stage][0];
         const uint16_t* Ys = sm.t[stage][1];
         // weights of token s = 32 kb + kappa(g, e), on the Y operand
-        const float cf = static_cast<float>(cw);
         if constexpr (!DL) {
+            const float cf = static_cast<float>(cw);
             float wx[NKB][8];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
@@ -155,18 +159,25 @@ __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArg
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) S[at] = mfma16(op_tr_k(Xs, 32 * kb, 16 * at, 4, g, li), yf[kb], S[at]);
         } else {
+            // the blocks before this one age by m tokens: T first, from the S it had
+            const float lmf = sm.pw[m], dlmf = sm.dpw[m];
+#pragma unroll
+            for (int at = 0; at < 8; ++at)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    T[at][r] = lmf * T[at][r] + dlmf * S[at][r];
+                    S[at][r] = lmf * S[at][r];
+                }
             // one 32-token k block at a time (fewer live registers); every accumulator still
             // adds k block 0 before k block 1
-            const float dcf = static_cast<float>(dcw);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 float wx[8], wd[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int s = 32 * kb + kappa(g, e);
-                    const float p = masked_pw(sm.pw, m - 1 - s, s < m);
-                    wx[e] = cf * p;
-                    wd[e] = dcf * p + cf * masked_pw(sm.dpw, m - 1 - s, s < m);
+                    wx[e] = masked_pw(sm.pw, m - 1 - s, s < m);
+                    wd[e] = masked_pw(sm.dpw, m - 1 - s, s < m);
                 }
                 const bf16x8 y = op_tr_k(Ys, 32 * kb, 16 * w, 4, g, li);
                 const bf16x8 yf = scale8(y, wx), yd = scale8(y, wd);
@@ -178,9 +189,7 @@ __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArg
                 }
             }
         }
-        const double lm = (m == BK) ? lam_bk : lam_pow64(lv, m);
-        if constexpr (DL) dcw = dcw * lm + cw * lam_dpow64(lv, m);
-        cw *= lm;
+        if constexpr (!DL) cw *= (m == BK) ? lam_bk : lam_pow64(lv, m);
     }
     float* dst = a.slots + dst_slot * (DL ? 2 : 1) * D * D;
 #pragma unroll

@@ -189,7 +189,8 @@ void launch_fwd_dma_varlen(const SweepArgs& a, const LamArgs& lam, const VarlenA
 bool fwd_dma128_supported(int D, int Bk, int64_t N);
 void launch_fwd_dma128(const SweepArgs& a, const LamArgs& lam, hipStream_t s);
 
-// Reverse (dK, dV) sweep with direct-to-LDS loads (bf16, D = 128, Bk = 64).
+// Reverse (dK, dV) sweep with direct-to-LDS loads (bf16, D = 128; 64-token blocks, Bk = 128
+// as two halves).
 bool rev_dma_supported(int D, int Bk, int64_t N);
 void launch_rev_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream_t s);
 
@@ -222,7 +223,8 @@ void launch_dlam_generic(const DlamArgs& a, const LamArgs& lam, int bf16, hipStr
 bool dlam_mfma_supported(int D, int Bk);
 void launch_dlam_mfma(const DlamArgs& a, const LamArgs& lam, hipStream_t s);
 void launch_dlam_reduce(const double* partial, int64_t B, int H, int chunks, float* out, hipStream_t s);
-// The sweep on direct-to-LDS loads (k_dlam_dma.hip; bf16, D = 128, Bk = 64).
+// The sweep on direct-to-LDS loads (k_dlam_dma.hip; bf16, D = 128; 64-token blocks, Bk = 128
+// as two halves).
 bool dlam_dma_supported(int D, int Bk, int64_t N);
 void launch_dlam_dma(const DlamArgs& a, const LamArgs& lam, int waves, hipStream_t s);  // waves: 4 or 8
 

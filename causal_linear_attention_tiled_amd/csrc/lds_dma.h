@@ -86,6 +86,22 @@ __device__ __forceinline__ bf16x8 scale8(const bf16x8& x, const float* wt) {
     return __builtin_bit_cast(bf16x8, r);
 }
 
+// The same products as a pair of operands, hi = bf16(x * wt) and lo = bf16(x * wt - hi):
+// together they carry the weighted operand to about 16 significant bits.
+__device__ __forceinline__ void scale8_split(const bf16x8& x, const float* wt, bf16x8& hi, bf16x8& lo) {
+    const u32x4 u = __builtin_bit_cast(u32x4, x);
+    u32x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = __uint_as_float(u[i] << 16) * wt[2 * i];
+        const float b = __uint_as_float(u[i] & 0xFFFF0000u) * wt[2 * i + 1];
+        h[i] = pack_bf16(a, b);
+        l[i] = pack_bf16(a - __uint_as_float(h[i] << 16), b - __uint_as_float(h[i] & 0xFFFF0000u));
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
 // Apply the feature map to every element of a [64][128] bf16 tile in LDS, in
 // place, rounding to bf16; thread t of nthr takes 16-byte pieces t, t + nthr, ...
 // (the swizzle does not matter to an elementwise map).

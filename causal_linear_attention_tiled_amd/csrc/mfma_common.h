@@ -52,6 +52,21 @@ __device__ __forceinline__ bf16x8 operand_from_acc(const f32x4& top, const f32x4
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// x - bf16(x) for two floats (bf16 as pack_bf16 rounds), rounded to bf16 and packed.
+__device__ __forceinline__ uint32_t pack_bf16_residual(float lo, float hi) {
+    const uint32_t h = pack_bf16(lo, hi);
+    return pack_bf16(lo - __uint_as_float(h << 16), hi - __uint_as_float(h & 0xFFFF0000u));
+}
+
+// The rounding residual of operand_from_acc: the two operands together carry the
+// accumulators to about 16 significant bits, for a product whose operand is large
+// next to the result it feeds.
+__device__ __forceinline__ bf16x8 operand_residual_from_acc(const f32x4& top, const f32x4& bottom) {
+    u32x4 v{pack_bf16_residual(top[0], top[1]), pack_bf16_residual(top[2], top[3]),
+            pack_bf16_residual(bottom[0], bottom[1]), pack_bf16_residual(bottom[2], bottom[3])};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 // Read a kappa-ordered operand fragment from a row-major bf16 tile in LDS:
 // row `row`, k columns [k0, k0 + 32).  `pitch` is the row pitch in elements.
 __device__ __forceinline__ bf16x8 lds_operand(const uint16_t* base, int row, int pitch, int k0, int g) {

@@ -14,8 +14,8 @@
  *
  * where S0 is an optional initial D x D state (kv_in).  The final state is
  *     S_N = lam^N S0 + sum_j lam^(N-1-j) k_j v_j^T     (kv_out).
- * There is no feature map (identity) and no normaliser; lam^0 = 1, so
- * lam = 0 keeps only the j = t term.
+ * The default feature map is the identity (LA_PHI_* below); there is no
+ * normaliser; lam^0 = 1, so lam = 0 keeps only the j = t term.
  *
  * Conventions shared by every call
  *  - Layouts are contiguous row-major: Q, K, V, O, dO, dQ, dK, dV are
@@ -38,12 +38,18 @@
  *    state between calls, except the optional profiling below.
  *  - Supported: D in {16, 32, 64, 128}, block size Bk in {16, 32, 64, 128},
  *    1 <= H <= 256, any N >= 1 (the last block may be partial).  The block
- *    size never changes the result beyond float rounding.
+ *    size never changes the result beyond float rounding.  For bf16 with
+ *    D = 128 the forward-direction sweeps (la_fwd, the dQ sweep of la_bwd)
+ *    take 64- or 128-token blocks as asked; the dK, dV sweep of la_bwd and
+ *    the sweep of la_dlam step a 128-token block as two 64-token halves (the
+ *    same function, with the second half's share of the first half's
+ *    gradients carried through the state instead of a score tile).
  *  - The environment variable LA_CHUNKS (a positive integer) overrides the
  *    number of chunks a sequence is split into for the chunked prefix over
- *    blocks; LA_KERNEL=generic forces the generic (non-MFMA) kernels.  Both
- *    exist for tests and tuning; a query of the workspace size must be made
- *    under the same setting as the call it sizes.
+ *    blocks, LA_AGG_K the number of parts of a chunk the chunk aggregates are
+ *    taken over (la_plan); LA_KERNEL=generic forces the generic (non-MFMA)
+ *    kernels.  They exist for tests and tuning; a query of the workspace size
+ *    must be made under the same setting as the call it sizes.
  */
 #ifndef LIBLINATTN_H
 #define LIBLINATTN_H
@@ -66,8 +72,8 @@ typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
  *   LA_PHI_RELU     : phi(x) = max(x, 0), phi'(0) = 0
  * The map is applied in float32 and rounded to the tensor dtype before use.
  * Gradients are with respect to the raw Q and K.  The register-staged kernels
- * (block size 128, LA_FWD / LA_REV / LA_STATE = v1) have no feature map: with
- * one, those shapes run the generic kernels. */
+ * (selected with LA_FWD / LA_REV / LA_STATE / LA_DLAM = v1) have no feature
+ * map: with one, those paths run the generic kernels. */
 enum { LA_PHI_IDENTITY = 0, LA_PHI_ELU1 = 1, LA_PHI_RELU = 2 };
 
 enum {

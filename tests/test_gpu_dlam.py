@@ -96,7 +96,8 @@ def test_dlam_float32(env, D, Bk, N, cks):
 
 @pytest.mark.parametrize("D,Bk", [(64, 64), (128, 128), (128, 32)])
 def test_dlam_bf16_generic_shapes(env, D, Bk):
-    """bf16 shapes outside the matrix-core kernel (routed to the generic kernels)."""
+    """bf16 shapes outside the 64-token matrix-core sweep: D = 64 and Bk = 32 run the generic
+    kernels, Bk = 128 the direct-to-LDS sweep in 64-token halves."""
     env(chunks=3)
     run_case(2, 3, 5 * Bk + 7, D, Bk, "bf16", np.array([0.5, 0.97, 1.0]), 11, True, True)
 
