@@ -100,12 +100,26 @@ __global__ __launch_bounds__(kThreads) void k_dlam_scan(ScanArgs a, LamArgs lam)
     const float lamL = lam_pow(lv, a.L), dlamL = lam_dpow(lv, a.L);
     float* sl = a.slots + pair * (a.chunks - 1) * 2 * static_cast<int64_t>(DD) + e;
     float S = a.kv_in ? a.kv_in[pair * DD + e] : 0.f, T = 0.f;
-    for (int c = 0; c < a.chunks - 1; ++c) {
-        float* p = sl + static_cast<int64_t>(c) * 2 * DD;
-        T = lamL * T + dlamL * S + p[DD];
-        S = lamL * S + p[0];
-        p[0] = S;
-        p[DD] = T;
+    const int n = a.chunks - 1;
+    // each batch's loads go out before any of its stores (one memory latency per batch)
+    constexpr int kBatch = 8;
+    float xs[kBatch], xt[kBatch];
+    for (int c0 = 0; c0 < n; c0 += kBatch) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const float* p = sl + static_cast<int64_t>(c0 + j) * 2 * DD;
+            xs[j] = c0 + j < n ? p[0] : 0.f;
+            xt[j] = c0 + j < n ? p[DD] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+            if (c0 + j < n) {
+                float* p = sl + static_cast<int64_t>(c0 + j) * 2 * DD;
+                T = lamL * T + dlamL * S + xt[j];
+                S = lamL * S + xs[j];
+                p[0] = S;
+                p[DD] = T;
+            }
     }
 }
 

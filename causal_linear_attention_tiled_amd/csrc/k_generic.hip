@@ -227,40 +227,64 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state_generic(ChunkStateArgs
     for (int i = tid; i < D * D; i += kThreads) dst[i] = state[i];
 }
 
+constexpr int kScanBatch = 8;  // chunk slots whose loads a scan thread keeps in flight
+
 __global__ __launch_bounds__(kThreads) void k_scan(ScanArgs a, LamArgs lam) {
     const int DD = a.D * a.D;
     const int per_pair = (DD + kThreads - 1) / kThreads;
     const int64_t pair = blockIdx.x / per_pair;
     const int e = (blockIdx.x % per_pair) * kThreads + threadIdx.x;
     if (e >= DD) return;
-    const float lamL = lam_pow(lam.lam[pair % a.H], a.L);
-    float* sl = a.slots + pair * (a.chunks - 1) * DD + e;
+    const float lv = lam.lam[pair % a.H];
+    const float lamL = lam_pow(lv, a.L);
+    const int n = a.chunks - 1;
+    float* sl = a.slots + pair * n * DD + e;
+    // Each batch's loads are issued before any of its stores: the slots are distinct,
+    // which the compiler cannot see, and a memory latency per slot would dominate.
+    float x[kScanBatch];
     if (!a.reverse) {
         float S = 0.f;
         if (a.kv_in) {
             const float* src = a.kv_in + pair * DD;
             S = a.kv_in_transposed ? src[(e % a.D) * a.D + e / a.D] : src[e];
         }
-        for (int c = 0; c < a.chunks - 1; ++c) {
-            S = lamL * S + sl[static_cast<int64_t>(c) * DD];
-            sl[static_cast<int64_t>(c) * DD] = S;
+        for (int c0 = 0; c0 < n; c0 += kScanBatch) {
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j) x[j] = c0 + j < n ? sl[static_cast<int64_t>(c0 + j) * DD] : 0.f;
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j)
+                if (c0 + j < n) {
+                    S = lamL * S + x[j];
+                    sl[static_cast<int64_t>(c0 + j) * DD] = S;
+                }
         }
     } else {
         // the final-state gradient enters at the last token undecayed, so it reaches the
         // start of chunk j decayed over N - 1 - j L tokens
         const float G = a.g_final ? a.g_final[pair * DD + e] : 0.f;
+        auto start_of = [&](int c) { return (static_cast<int64_t>(c) + 1 + a.part0) * a.L; };
         float R = 0.f;
         bool started = false;
-        for (int c = a.chunks - 2; c >= 0; --c) {
-            const int64_t start = (static_cast<int64_t>(c) + 1 + a.part0) * a.L;
-            float* p = sl + static_cast<int64_t>(c) * DD;
-            if (start >= a.N) {
-                *p = 0.f;  // a part past the end of the sequence
-                continue;
+        for (int c1 = n - 1; c1 >= 0; c1 -= kScanBatch) {
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j) {
+                const int c = c1 - j;
+                x[j] = (c >= 0 && start_of(c) < a.N) ? sl[static_cast<int64_t>(c) * DD] : 0.f;
             }
-            R = started ? *p + lamL * R : *p + lam_pow(lam.lam[pair % a.H], a.N - 1 - start) * G;
-            started = true;
-            *p = R;
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j) {
+                const int c = c1 - j;
+                if (c < 0) break;
+                float* p = sl + static_cast<int64_t>(c) * DD;
+                const int64_t start = start_of(c);
+                if (start >= a.N) {
+                    *p = 0.f;  // a part past the end of the sequence
+                    continue;
+                }
+                R = started ? x[j] + lamL * R : x[j] + lam_pow(lv, a.N - 1 - start) * G;
+                started = true;
+                *p = R;
+            }
         }
     }
 }
@@ -279,10 +303,18 @@ __global__ __launch_bounds__(kThreads) void k_scan_varlen(ScanArgs a, LamArgs la
     const int b = list.seq[i] & 0xFF, n_slots = list.seq[i] >> 8;
     const float lamL = lam_pow(lam.lam[h], a.L);
     float S = a.kv_in ? a.kv_in[(static_cast<int64_t>(b) * a.H + h) * DD + e] : 0.f;
-    for (int c = 0; c < n_slots; ++c) {
-        float* sl = a.slots + (static_cast<int64_t>(list.sbase[i] + c) * a.H + h) * DD + e;
-        S = lamL * S + *sl;
-        *sl = S;
+    float* sl = a.slots + (static_cast<int64_t>(list.sbase[i]) * a.H + h) * DD + e;
+    const int64_t step = static_cast<int64_t>(a.H) * DD;
+    float x[kScanBatch];
+    for (int c0 = 0; c0 < n_slots; c0 += kScanBatch) {
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) x[j] = c0 + j < n_slots ? sl[(c0 + j) * step] : 0.f;
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j)
+            if (c0 + j < n_slots) {
+                S = lamL * S + x[j];
+                sl[(c0 + j) * step] = S;
+            }
     }
 }
 
