@@ -39,8 +39,18 @@ struct DlamTiles {
     uint16_t t[NSTAGE][4][TILE];  // per stage: Q, K, V, dO (row-major, swizzled)
     float pw[BK + 2];
     float dpw[BK + 2];
+    // token weights by token s of an m-token block, zero for s >= m: (s+1) lam^s,
+    // lam^(s+1), lam^(m-1-s), (m-1-s) lam^(m-2-s); set 0 for full blocks, set 1 for
+    // the workgroup's last block.  A lane reads its 8 as two 16-byte runs.
+    alignas(16) float wtab[2][4][BK];
     double red[kMaxWaves + 1];
 };
+
+// Weights of tokens 32 kb + kappa(g, e) from a table by token: e = 0..3 (half 0) or
+// e = 4..7 (half 1), each a run of four tokens.
+__device__ __forceinline__ f32x4 lane_weights(const float* tab, int kb, int g, int half) {
+    return *reinterpret_cast<const f32x4*>(tab + 32 * kb + 16 * half + 4 * g);
+}
 
 // NW compute waves (4 or 8), each owning 128 / NW value columns.
 template <int NW, bool PHI>
@@ -59,6 +69,15 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_dlam_dma(DlamArgs a, LamAr
     for (int e = tid; e <= BK + 1; e += 64 * (NW + 1)) {
         sm.pw[e] = lam_pow(lv, e);
         sm.dpw[e] = lam_dpow(lv, e);
+    }
+    const int m_last = nblk > 0 ? static_cast<int>(t_end - t_begin - (nblk - 1) * BK) : BK;
+    for (int i = tid; i < 2 * BK; i += 64 * (NW + 1)) {
+        const int set = i / BK, e = i % BK, m = set ? m_last : BK;
+        const bool in = e < m;
+        sm.wtab[set][0][e] = in ? lam_dpow(lv, e + 1) : 0.f;
+        sm.wtab[set][1][e] = in ? lam_pow(lv, e + 1) : 0.f;
+        sm.wtab[set][2][e] = in ? lam_pow(lv, m - 1 - e) : 0.f;
+        sm.wtab[set][3][e] = in ? lam_dpow(lv, m - 1 - e) : 0.f;
     }
     __syncthreads();  // tables; then every wave passes (2 + [phi]) barriers per block and one more
 
@@ -135,6 +154,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_dlam_dma(DlamArgs a, LamAr
             const uint16_t* Ks = sm.t[stage][1];
             const uint16_t* Vs = sm.t[stage][2];
             const uint16_t* Gs = sm.t[stage][3];
+            const float (*wset)[BK] = sm.wtab[n == nblk - 1 ? 1 : 0];
             float part = 0.f;
 
             // ---- intra: tile (at, st) holds [s' = 16 at + 4 g + r][s = 16 st + li] of P^T and G^T
@@ -168,13 +188,10 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_dlam_dma(DlamArgs a, LamAr
                 bf16x8 gs[NKB][NVT], gt[NKB][NVT], gr[NKB][NVT];
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
-                    float ws[8], wt[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int s = 32 * kb + kappa(g, e);
-                        ws[e] = masked_pw(sm.dpw, s + 1, s < m);
-                        wt[e] = masked_pw(sm.pw, s + 1, s < m);
-                    }
+                    const f32x4 ws0 = lane_weights(wset[0], kb, g, 0), ws1 = lane_weights(wset[0], kb, g, 1);
+                    const f32x4 wt0 = lane_weights(wset[1], kb, g, 0), wt1 = lane_weights(wset[1], kb, g, 1);
+                    const float ws[8] = {ws0[0], ws0[1], ws0[2], ws0[3], ws1[0], ws1[1], ws1[2], ws1[3]};
+                    const float wt[8] = {wt0[0], wt0[1], wt0[2], wt0[3], wt1[0], wt1[1], wt1[2], wt1[3]};
 #pragma unroll
                     for (int vt = 0; vt < NVT; ++vt) {
                         const bf16x8 gf = op_tr_k(Gs, 32 * kb, 16 * (NVT * w + vt), 4, g, li);
@@ -201,8 +218,6 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_dlam_dma(DlamArgs a, LamAr
                     for (int vt = 0; vt < NVT; ++vt)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) part += S[at][vt][r] * ms[vt][r] + T[at][vt][r] * mt[vt][r];
-                    // keep the scheduler from hoisting every band's LDS reads (register pressure)
-                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             acc += static_cast<double>(part);
@@ -220,13 +235,10 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_dlam_dma(DlamArgs a, LamAr
                 // one 32-token k block at a time; every accumulator adds k block 0 before 1
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
-                    float wk[8], wd[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int s = 32 * kb + kappa(g, e);
-                        wk[e] = masked_pw(sm.pw, m - 1 - s, s < m);
-                        wd[e] = masked_pw(sm.dpw, m - 1 - s, s < m);
-                    }
+                    const f32x4 wk0 = lane_weights(wset[2], kb, g, 0), wk1 = lane_weights(wset[2], kb, g, 1);
+                    const f32x4 wd0 = lane_weights(wset[3], kb, g, 0), wd1 = lane_weights(wset[3], kb, g, 1);
+                    const float wk[8] = {wk0[0], wk0[1], wk0[2], wk0[3], wk1[0], wk1[1], wk1[2], wk1[3]};
+                    const float wd[8] = {wd0[0], wd0[1], wd0[2], wd0[3], wd1[0], wd1[1], wd1[2], wd1[3]};
                     bf16x8 vw[NVT], vd[NVT];
 #pragma unroll
                     for (int vt = 0; vt < NVT; ++vt) {
