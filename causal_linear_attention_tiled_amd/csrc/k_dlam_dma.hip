@@ -46,12 +46,6 @@ struct DlamTiles {
     double red[kMaxWaves + 1];
 };
 
-// Weights of tokens 32 kb + kappa(g, e) from a table by token: e = 0..3 (half 0) or
-// e = 4..7 (half 1), each a run of four tokens.
-__device__ __forceinline__ f32x4 lane_weights(const float* tab, int kb, int g, int half) {
-    return *reinterpret_cast<const f32x4*>(tab + 32 * kb + 16 * half + 4 * g);
-}
-
 // NW compute waves (4 or 8), each owning 128 / NW value columns.
 template <int NW, bool PHI>
 __global__ __launch_bounds__(64 * (NW + 1), 1) void k_dlam_dma(DlamArgs a, LamArgs lam) {

@@ -48,6 +48,9 @@ struct DmaTiles {
     uint16_t t[NSTAGE][3][TILE];     // per stage: Q, K, V (row-major, swizzled)
     uint32_t at[NCAUSAL * 128];      // masked decayed score tiles, B-operand fragments
     float pw[BK + 1];
+    // state-update weights by token s, lam^(m-1-s) (zero for s >= m): set 0 for full
+    // blocks, set 1 for the workgroup's last block; read as 16-byte runs
+    alignas(16) float wk[2][BK];
 };
 
 template <int NW, bool VARLEN, bool PHI>
@@ -64,6 +67,11 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
     const int64_t ld = VARLEN ? wk.ld : D;  // elements between token rows
 
     for (int e = tid; e <= BK; e += 64 * (NW + 1)) sm.pw[e] = lam_pow(lv, e);
+    const int m_last = nblk > 0 ? static_cast<int>(t_end - t_begin - (nblk - 1) * BK) : BK;
+    for (int i = tid; i < 2 * BK; i += 64 * (NW + 1)) {
+        const int e = i % BK, m = i < BK ? BK : m_last;
+        sm.wk[i / BK][e] = e < m ? lam_pow(lv, m - 1 - e) : 0.f;
+    }
     __syncthreads();  // decay table; every wave passes exactly 1 + (2 + [phi]) * nblk barriers
 
     if (w == NW) {
@@ -208,14 +216,14 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
         }
 
         // ---- per 16-token column: O^T = diag(lam^(s+1)) S^T Q^T + V^T A^T, store
+        // the bf16 state operands, converted once per block
+        bf16x8 sb[NVT][4];
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) sb[vt][kb] = operand_from_acc(S[2 * kb][vt], S[2 * kb + 1][vt]);
 #pragma unroll
         for (int st = 0; st < NT; ++st) {
-            // the bf16 state operands are rebuilt per column (opaque to the compiler) rather
-            // than held across the loop: 32 fewer live registers for a few converts
-#pragma unroll
-            for (int at = 0; at < 8; ++at)
-#pragma unroll
-                for (int vt = 0; vt < NVT; ++vt) asm volatile("" : "+v"(S[at][vt]));
             bf16x8 qf[4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) qf[kb] = op_row(Qs, 16 * st + li, 32 * kb, g);
@@ -224,7 +232,7 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
             for (int vt = 0; vt < NVT; ++vt) {
                 f32x4 acc = zero4();
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) acc = mfma16(operand_from_acc(S[2 * kb][vt], S[2 * kb + 1][vt]), qf[kb], acc);
+                for (int kb = 0; kb < 4; ++kb) acc = mfma16(sb[vt][kb], qf[kb], acc);
                 o[vt] = acc * rs[st];
             }
 #pragma unroll
@@ -261,14 +269,11 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
         // ---- S <- lam^m S + K^T diag(lam^(m-1-s)) V
         const float lm = sm.pw[m];
         bf16x8 vw[NVT][NKB];
+        const float* wtab = sm.wk[n == nblk - 1 ? 1 : 0];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            float wk[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int s = 32 * kb + kappa(g, e);
-                wk[e] = masked_pw(sm.pw, m - 1 - s, s < m);
-            }
+            const f32x4 w0 = lane_weights(wtab, kb, g, 0), w1 = lane_weights(wtab, kb, g, 1);
+            const float wk[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt) vw[vt][kb] = scale8(vf[vt][kb], wk);
         }

@@ -70,6 +70,12 @@ __device__ __forceinline__ bf16x8 op_tr_k(const uint16_t* t, int kb, int n0, int
 // kappa(g, e): the token offset inside a 32-token k block held by lane group g, element e.
 __device__ __forceinline__ constexpr int kappa(int g, int e) { return e < 4 ? 4 * g + e : 16 + 4 * g + e - 4; }
 
+// Weights of tokens 32 kb + kappa(g, e) from a 16-byte aligned table by token:
+// e = 0..3 (half 0) or e = 4..7 (half 1), each a run of four tokens.
+__device__ __forceinline__ f32x4 lane_weights(const float* tab, int kb, int g, int half) {
+    return *reinterpret_cast<const f32x4*>(tab + 32 * kb + 16 * half + 4 * g);
+}
+
 // Row of a 32-row block covered by row i of its tile t (0 or 1): the two tiles
 // of a block interleave in runs of four, so that their accumulators stacked
 // (tile 0 for e < 4, tile 1 for e >= 4) are a natural-order operand whose k
