@@ -93,7 +93,12 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 bool valid_phi(int32_t phi) { return phi == LA_PHI_IDENTITY || phi == LA_PHI_ELU1 || phi == LA_PHI_RELU; }
 
 bool supported_D(int64_t D) { return D == 16 || D == 32 || D == 64 || D == 128; }
-bool supported_Bk(int64_t Bk) { return Bk == 16 || Bk == 32 || Bk == 64 || Bk == 128; }
+bool supported_Bk(int64_t Bk) { return Bk == 16 || Bk == 32 || Bk == 64 || Bk == 128 || Bk == 256; }
+
+// The largest block the kernels step: a 256-token block changes where the chunk
+// boundaries may fall (multiples of 256) and is swept as two 128-token blocks (the
+// same function; 128-token blocks already fill the LDS of the forward kernel).
+constexpr int32_t kMaxKernelBk = 128;
 
 // Shape checks common to la_fwd / la_bwd and their size queries.
 int check_shape(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype, int64_t* elems) {
@@ -121,6 +126,7 @@ int load_lambda(const float* lambda, int64_t H, LamArgs* out) {
 struct Plan {
     int chunks;
     int64_t L;     // chunk length in tokens (multiple of Bk)
+    int32_t bk;    // block size the kernels step (Bk, or 128 for Bk = 256)
     bool mfma;
     int agg_k;     // forward direction: aggregates over chunks of L / agg_k tokens
 };
@@ -151,7 +157,8 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t d
     const int64_t bpc = (nb + C - 1) / C;
     p.L = bpc * Bk;
     p.chunks = static_cast<int>((nb + bpc - 1) / bpc);
-    p.mfma = dtype == LA_BF16 && la::mfma_supported(static_cast<int>(D), Bk) && !force_generic();
+    p.bk = std::min(Bk, kMaxKernelBk);
+    p.mfma = dtype == LA_BF16 && la::mfma_supported(static_cast<int>(D), p.bk) && !force_generic();
     // The chunk aggregates (one workgroup each, two per CU) are taken over agg_k equal
     // parts of every chunk when the chunks alone would leave the pass below 3/4 of a
     // round of 512 workgroups; the scans then run over the parts, chunk c of a forward
@@ -330,7 +337,7 @@ const char* la_strerror(int code) {
     switch (code) {
         case LA_OK: return "ok";
         case LA_EINVAL: return "invalid argument";
-        case LA_EUNSUPPORTED: return "unsupported shape (D in {16,32,64,128}, Bk in {16,32,64,128}, H <= 256)";
+        case LA_EUNSUPPORTED: return "unsupported shape (D in {16,32,64,128}, Bk in {16,32,64,128,256}, H <= 256)";
         case LA_EALIGN: return "device pointer not 16-byte aligned";
         case LA_EWORKSPACE: return "workspace missing or too small";
         case LA_EHIP: {
@@ -385,6 +392,7 @@ int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int
     const size_t tb = static_cast<size_t>(elems) * (dtype == LA_BF16 ? 2 : 4);
     const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
+    Bk = p.bk;  // the block the kernels step
     const size_t need = fwd_slot_bytes(B * H, p, D);
     if (need && (!ws || ws_bytes < need)) return LA_EWORKSPACE;
     const Range rq{Q, tb}, rk{K, tb}, rv{V, tb}, ro{O, tb}, rin{kv_in, kv_in ? sb : 0},
@@ -419,6 +427,7 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     const size_t tb = static_cast<size_t>(elems) * (dtype == LA_BF16 ? 2 : 4);
     const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
+    Bk = p.bk;  // the block the kernels step
     // chunk states of the dQ sweep (forward direction) and of the dK, dV sweep (reverse
     // direction), both over agg_k parts per chunk boundary
     const size_t fq = fwd_slot_bytes(B * H, p, D), rv = fq;
@@ -526,6 +535,7 @@ int la_dlam(const void* Q, const void* K, const void* V, const void* dO, const f
     const size_t tb = static_cast<size_t>(elems) * (dtype == LA_BF16 ? 2 : 4);
     const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
+    Bk = p.bk;  // the block the kernels step
     const size_t need = dlam_ws_bytes(B * H, p, D);
     if (!ws || ws_bytes < need) return LA_EWORKSPACE;
     const Range ins[] = {{Q, tb}, {K, tb}, {V, tb}, {dO, tb}, {kv_in, kv_in ? sb : 0}, {dkv_out, dkv_out ? sb : 0}};

@@ -36,14 +36,16 @@
  *    stream) and the call returns without waiting.  Results are valid once
  *    the stream has reached that point.  Calls are thread-safe and keep no
  *    state between calls, except the optional profiling below.
- *  - Supported: D in {16, 32, 64, 128}, block size Bk in {16, 32, 64, 128},
- *    1 <= H <= 256, any N >= 1 (the last block may be partial).  The block
- *    size never changes the result beyond float rounding.  For bf16 with
- *    D = 128 the forward-direction sweeps (la_fwd, the dQ sweep of la_bwd)
- *    take 64- or 128-token blocks as asked; the dK, dV sweep of la_bwd and
- *    the sweep of la_dlam step a 128-token block as two 64-token halves (the
- *    same function, with the second half's share of the first half's
- *    gradients carried through the state instead of a score tile).
+ *  - Supported: D in {16, 32, 64, 128}, block size Bk in {16, 32, 64, 128,
+ *    256}, 1 <= H <= 256, any N >= 1 (the last block may be partial).  The
+ *    block size never changes the result beyond float rounding.  For bf16
+ *    with D = 128 the forward-direction sweeps (la_fwd, the dQ sweep of
+ *    la_bwd) take 64- or 128-token blocks as asked; the dK, dV sweep of
+ *    la_bwd and the sweep of la_dlam step a 128-token block as two 64-token
+ *    halves (the same function, with the second half's share of the first
+ *    half's gradients carried through the state instead of a score tile).
+ *    Bk = 256 places the chunk boundaries of the chunked prefix on multiples
+ *    of 256 tokens and is stepped as two 128-token blocks by every kernel.
  *  - The environment variable LA_CHUNKS (a positive integer) overrides the
  *    number of chunks a sequence is split into for the chunked prefix over
  *    blocks, LA_AGG_K the number of parts of a chunk the chunk aggregates are

@@ -66,7 +66,8 @@ def fwd(**kw):
     (dict(D=48), la.LA_EUNSUPPORTED),
     (dict(D=256), la.LA_EUNSUPPORTED),
     (dict(Bk=48), la.LA_EUNSUPPORTED),
-    (dict(Bk=256), la.LA_EUNSUPPORTED),
+    (dict(Bk=512), la.LA_EUNSUPPORTED),
+    (dict(Bk=0), la.LA_EINVAL),
     (dict(H=300, lam=(ctypes.c_float * 300)(*([0.5] * 300))), la.LA_EUNSUPPORTED),
     (dict(Q=Q_ + 8), la.LA_EALIGN),
     (dict(kv_out=S_ + 4), la.LA_EALIGN),
@@ -254,3 +255,9 @@ def test_plan():
     assert la.la_fwd_workspace_bytes(2, 16, 65536, 128, 64, la.LA_BF16) == 32 * 7 * 2 * 128 * 128 * 4
     with pytest.raises(la.LaError):
         la.la_plan(1, 16, 1024, 100, 64, la.LA_BF16)
+    # a 256-token block: chunk boundaries on multiples of 256 (the kernels step 128-token blocks)
+    p = la.la_plan(2, 16, 65536, 128, 256, la.LA_BF16)
+    assert p["chunks"] > 1 and p["chunk_len"] % 256 == 0 and (p["chunk_len"] // p["agg_parts"]) % 256 == 0
+    assert la.la_plan(1, 2, 300, 16, 256, la.LA_F32) == {"chunks": 1, "chunk_len": 512, "agg_parts": 1}
+    with pytest.raises(la.LaError):
+        la.la_plan(1, 16, 1024, 128, 512, la.LA_BF16)

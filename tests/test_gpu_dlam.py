@@ -88,16 +88,17 @@ def test_dlam_degenerate_decays(env, kernel, lam):
     run_case(1, 2, 64 * 7 + 3, 128, 64, "bf16", lam, 7, True, True, label=kernel)
 
 
-@pytest.mark.parametrize("D,Bk,N,cks", [(64, 32, 300, 3), (16, 16, 70, None), (128, 128, 300, 2), (32, 64, 1, None)])
+@pytest.mark.parametrize("D,Bk,N,cks", [(64, 32, 300, 3), (16, 16, 70, None), (128, 128, 300, 2), (32, 64, 1, None),
+                                           (16, 256, 600, 2)])
 def test_dlam_float32(env, D, Bk, N, cks):
     env(chunks=cks)
     run_case(2, 3, N, D, Bk, "f32", np.array([0.3, 0.9, 0.999]), 9, True, True)
 
 
-@pytest.mark.parametrize("D,Bk", [(64, 64), (128, 128), (128, 32)])
+@pytest.mark.parametrize("D,Bk", [(64, 64), (128, 128), (128, 32), (128, 256)])
 def test_dlam_bf16_generic_shapes(env, D, Bk):
     """bf16 shapes outside the 64-token matrix-core sweep: D = 64 and Bk = 32 run the generic
-    kernels, Bk = 128 the direct-to-LDS sweep in 64-token halves."""
+    kernels, Bk = 128 and 256 the direct-to-LDS sweep in 64-token steps."""
     env(chunks=3)
     run_case(2, 3, 5 * Bk + 7, D, Bk, "bf16", np.array([0.5, 0.97, 1.0]), 11, True, True)
 

@@ -91,7 +91,7 @@ def test_fp32_small_backward():
 
 # ------------------------------------------------------------------ many tiles and ragged tails
 @pytest.mark.parametrize("kern", ["generic", "default"])
-@pytest.mark.parametrize("D,Bk", [(16, 16), (32, 32), (64, 64), (128, 64), (128, 128), (64, 128)])
+@pytest.mark.parametrize("D,Bk", [(16, 16), (32, 32), (64, 64), (128, 64), (128, 128), (64, 128), (128, 256), (16, 256)])
 def test_fwd_ragged_bf16(kern, D, Bk, kernel):
     kernel(kern)
     H = 3
@@ -100,7 +100,7 @@ def test_fwd_ragged_bf16(kern, D, Bk, kernel):
 
 
 @pytest.mark.parametrize("kern", ["generic", "default"])
-@pytest.mark.parametrize("D,Bk", [(32, 16), (128, 64), (128, 128)])
+@pytest.mark.parametrize("D,Bk", [(32, 16), (128, 64), (128, 128), (128, 256), (32, 256)])
 def test_bwd_ragged_bf16(kern, D, Bk, kernel):
     kernel(kern)
     lam = synth.decay_schedule(4)
@@ -136,6 +136,18 @@ def test_forced_chunk_counts_block128(c, kern, chunks, kernel):
     check_bwd(1, 2, 128 * 9 + 17, 128, 128, "bf16", lam, seed=30 + c, with_state=True, label=f"chunks={c}")
 
 
+@pytest.mark.parametrize("c", [2, 3])
+@pytest.mark.parametrize("kern", ["generic", "default"])
+def test_forced_chunk_counts_block256(c, kern, chunks, kernel):
+    """Block 256: chunk boundaries on multiples of 256 tokens, every kernel stepping 128-token
+    blocks (the same function)."""
+    chunks(c)
+    kernel(kern)
+    lam = synth.decay_schedule(2)
+    check_fwd(1, 2, 256 * 5 + 17, 128, 256, "bf16", lam, seed=40 + c, with_state=True, label=f"chunks={c}")
+    check_bwd(1, 2, 256 * 5 + 17, 128, 256, "bf16", lam, seed=40 + c, with_state=True, label=f"chunks={c}")
+
+
 # ------------------------------------------------------------------ bit-exact probes
 def impulse_inputs(N, D, j0, c, dtype):
     q = np.zeros((1, 1, N, D), np.float32)
@@ -151,7 +163,7 @@ def impulse_inputs(N, D, j0, c, dtype):
 
 @pytest.mark.parametrize("kern", ["generic", "default"])
 @pytest.mark.parametrize("lam_val", [1.0, 0.5])
-@pytest.mark.parametrize("Bk,cks", [(64, 1), (64, 4), (128, 3)])
+@pytest.mark.parametrize("Bk,cks", [(64, 1), (64, 4), (128, 3), (256, 2)])
 def test_impulse_probe_bit_exact(kern, lam_val, Bk, cks, chunks, kernel):
     """q_t = e0, a single key e0 at j0 with value e_c: O_t = lam^(t-j0) e_c exactly for t >= j0.
 
