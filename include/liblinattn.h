@@ -50,8 +50,11 @@
  *    number of chunks a sequence is split into for the chunked prefix over
  *    blocks, LA_AGG_K the number of parts of a chunk the chunk aggregates are
  *    taken over (la_plan); LA_KERNEL=generic forces the generic (non-MFMA)
- *    kernels.  They exist for tests and tuning; a query of the workspace size
- *    must be made under the same setting as the call it sizes.
+ *    kernels; LA_FWD_WAVES=8, LA_REV_WAVES=4 and LA_DLAM_WAVES=4 select the
+ *    other wave counts of the bf16 D = 128 direct-to-LDS sweeps (forward and
+ *    dQ, dK and dV, decay derivative).  They exist for tests and tuning; a
+ *    query of the workspace size must be made under the same setting as the
+ *    call it sizes.
  */
 #ifndef LIBLINATTN_H
 #define LIBLINATTN_H
