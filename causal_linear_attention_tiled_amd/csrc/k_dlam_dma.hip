@@ -233,12 +233,15 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_dlam_dma(DlamArgs a, LamAr
                     const f32x4 wd0 = lane_weights(wset[3], kb, g, 0), wd1 = lane_weights(wset[3], kb, g, 1);
                     const float wk[8] = {wk0[0], wk0[1], wk0[2], wk0[3], wk1[0], wk1[1], wk1[2], wk1[3]};
                     const float wd[8] = {wd0[0], wd0[1], wd0[2], wd0[3], wd1[0], wd1[1], wd1[2], wd1[3]};
-                    bf16x8 vw[NVT], vd[NVT];
+                    // both weighted operands as bf16 pairs (hi + rounding residual): their single
+                    // roundings, carried block after block in S and T, are what is left of the
+                    // error where the result cancels by orders of magnitude
+                    bf16x8 vw[NVT], vwr[NVT], vd[NVT], vdr[NVT];
 #pragma unroll
                     for (int vt = 0; vt < NVT; ++vt) {
                         const bf16x8 vf = op_tr_k(Vs, 32 * kb, 16 * (NVT * w + vt), 4, g, li);
-                        vw[vt] = scale8(vf, wk);
-                        vd[vt] = scale8(vf, wd);
+                        scale8_split(vf, wk, vw[vt], vwr[vt]);
+                        scale8_split(vf, wd, vd[vt], vdr[vt]);
                     }
 #pragma unroll
                     for (int at = 0; at < 8; ++at) {
@@ -247,6 +250,8 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_dlam_dma(DlamArgs a, LamAr
                         for (int vt = 0; vt < NVT; ++vt) {
                             S[at][vt] = mfma16(kf, vw[vt], S[at][vt]);
                             T[at][vt] = mfma16(kf, vd[vt], T[at][vt]);
+                            S[at][vt] = mfma16(kf, vwr[vt], S[at][vt]);
+                            T[at][vt] = mfma16(kf, vdr[vt], T[at][vt]);
                         }
                     }
                 }

@@ -179,13 +179,18 @@ __device__ __forceinline__ void state_body(const ChunkStateArgs& a, const LamArg
                     wx[e] = masked_pw(sm.pw, m - 1 - s, s < m);
                     wd[e] = masked_pw(sm.dpw, m - 1 - s, s < m);
                 }
+                // the weighted operands as bf16 pairs (hi + rounding residual), as in the sweep
                 const bf16x8 y = op_tr_k(Ys, 32 * kb, 16 * w, 4, g, li);
-                const bf16x8 yf = scale8(y, wx), yd = scale8(y, wd);
+                bf16x8 yf, yfr, yd, ydr;
+                scale8_split(y, wx, yf, yfr);
+                scale8_split(y, wd, yd, ydr);
 #pragma unroll
                 for (int at = 0; at < 8; ++at) {
                     const bf16x8 xf = op_tr_k(Xs, 32 * kb, 16 * at, 4, g, li);
                     S[at] = mfma16(xf, yf, S[at]);
                     T[at] = mfma16(xf, yd, T[at]);
+                    S[at] = mfma16(xf, yfr, S[at]);
+                    T[at] = mfma16(xf, ydr, T[at]);
                 }
             }
         }
@@ -211,8 +216,10 @@ __global__ __launch_bounds__(64 * NW, 2) void k_chunk_state_dma_varlen(ChunkStat
     state_body<true, PHI, false>(a, lam, &v);
 }
 
+// The decay-derivative form carries S and T with both weighted operands as bf16 pairs:
+// 184 registers, so one workgroup per compute unit (no spills).
 template <bool PHI>
-__global__ __launch_bounds__(64 * NW, 4) void k_dlam_state_dma(ChunkStateArgs a, LamArgs lam) {
+__global__ __launch_bounds__(64 * NW, 1) void k_dlam_state_dma(ChunkStateArgs a, LamArgs lam) {
     state_body<false, PHI, true>(a, lam, nullptr);
 }
 

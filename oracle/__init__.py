@@ -30,7 +30,7 @@ import subprocess
 
 import numpy as np
 
-from .quadratic import (decay_matrix, fwd_quadratic, bwd_quadratic, dlam_quadratic)  # noqa: F401
+from .quadratic import (decay_matrix, fwd_quadratic, bwd_quadratic, dlam_quadratic, dlam_magnitude)  # noqa: F401
 from . import feature  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

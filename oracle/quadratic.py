@@ -118,3 +118,34 @@ def dlam_quadratic(q, k, v, dout, lam, s_init=None, g_final=None, phi="identity"
             dS = dS + _dpowers(lam, np.array([n]))[0] * s0
         total += float(np.sum(f * dS))
     return total
+
+
+def dlam_magnitude(q, k, v, dout, lam, s_init=None, g_final=None, phi="identity"):
+    """One sequence: the sum of the magnitudes of the terms dlam_quadratic adds up,
+        sum_{i>j} |D'[i, j] (q_i . k_j)(v_j . dO_i)| + sum_t |(t+1) lam^t q_t S0 dO_t^T|
+        + sum_j |(n-1-j) lam^(n-2-j) k_j F v_j^T| + |n lam^(n-1) <F, S0>|.
+    Rounding each term moves the sum by up to this much times the unit roundoff, whatever
+    the size of the sum itself, so it is the scale an approximate dL/dlam is judged
+    against.  With every term of one sign it equals |dL/dlam|."""
+    q = feature.phi(q, phi)
+    k = feature.phi(k, phi)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(dout, dtype=np.float64)
+    n = q.shape[0]
+    lam = float(np.float64(lam))
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    dD = np.where(i > j, _dpowers(lam, np.where(i > j, i - j, 0)), 0.0)
+    total = float(np.sum(np.abs((q @ k.T) * dD * (g @ v.T))))
+    s0 = None if s_init is None else np.asarray(s_init, dtype=np.float64)
+    if s0 is not None:
+        w = _dpowers(lam, np.arange(1, n + 1))  # (t+1) lam^t
+        total += float(np.sum(np.abs(w * np.einsum("td,de,te->t", q, s0, g))))
+    if g_final is not None:
+        f = np.asarray(g_final, dtype=np.float64)
+        w = _dpowers(lam, np.arange(n - 1, -1, -1))  # (n-1-j) lam^(n-2-j)
+        total += float(np.sum(np.abs(w * np.einsum("td,de,te->t", k, f, v))))
+        if s0 is not None:
+            total += abs(float(_dpowers(lam, np.array([n]))[0] * np.sum(f * s0)))
+    return total
+

@@ -5,7 +5,8 @@ per head.  Covered: the matrix-core path (bf16, D=128, Bk=64) and the generic ke
 (S, T)), initial state and final-state gradient, the feature maps, ragged tails, lam = 0
 and lam = 1, and the training-step sizes on sampled heads.  The bar is the relative L2
 error of the [H] result, and also each head's error against the sum of the magnitudes of
-its per-sequence terms."""
+its per-sequence values; each head's cancellation (the magnitude of its terms over its
+value) is printed beside it."""
 import numpy as np
 import pytest
 
@@ -51,12 +52,19 @@ def run_case(B, H, N, D, Bk, dtype, lam, seed, with_state, with_gf, phi="identit
     ref = per.sum(axis=0)
     y = got(out)
     err = oracle.rel_l2(y, ref)
-    # each head against the size of its summands: a batch sum can cancel (elu + 1 features
-    # make every q . k positive and large), so |ref| alone is no scale for it
+    # each head against the size of its per-sequence values: a batch sum can cancel (elu + 1
+    # features make every q . k positive and large), so |ref| alone is no scale for it
     scale = np.abs(per).sum(axis=0)
     head = np.abs(y - ref) / np.maximum(scale, 1e-300)
+    # how far each head's value cancels within its terms (diagnostic: sum of the terms'
+    # magnitudes over the value; random inputs give hundreds to thousands)
+    mag = np.array([[oracle.dlam_magnitude(qh[b, h], kh[b, h], vh[b, h], gh[b, h], float(lam[h]),
+                                           None if s0 is None else s0[b, h].astype(np.float64),
+                                           None if gf is None else gf[b, h].astype(np.float64), phi=phi)
+                     for h in range(H)] for b in range(B)]).sum(axis=0)
     print(f"    rel-L2 {err:.2e}; per head |err| / sum_b |dL/dlam_bh| "
-          f"{np.array2string(head, precision=2, floatmode='unique')}", flush=True)
+          f"{np.array2string(head, precision=2, floatmode='unique')}; cancellation "
+          f"{np.array2string(mag / np.maximum(scale, 1e-300), precision=0)}", flush=True)
     assert np.all(np.isfinite(y))
     assert err <= bar(dtype)
     assert np.all(head <= bar(dtype))

@@ -662,3 +662,21 @@ def test_planted_dlam_mistakes_are_caught(monkeypatch):
     assert recurrent() == pytest.approx(ex, rel=1e-13)
     for kw in ({"use_updated_state": True}, {"drop_g": True}, {"s_for_t": True}):
         assert recurrent(**kw) != pytest.approx(ex, rel=1e-6), kw
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.5, 0.9, 1.0])
+@pytest.mark.parametrize("phi", ["identity", "elu1"])
+def test_dlam_magnitude_is_the_derivative_when_no_term_cancels(lam, phi):
+    """The magnitude scale of dL/dlam (the sum of its terms' absolute values) equals the
+    recurrent oracle's dL/dlam itself when every input is nonnegative, so that no term can
+    cancel another; on signed inputs it bounds |dL/dlam| from above."""
+    rng = np.random.default_rng(49)
+    n, d = 40, 6
+    q, k, v, g = (rng.uniform(0.0, 1.0, (n, d)) for _ in range(4))
+    s0, gf = rng.uniform(0.0, 1.0, (d, d)), rng.uniform(0.0, 1.0, (d, d))
+    for s_init, g_final in ((None, None), (s0, None), (None, gf), (s0, gf)):
+        mag = oracle.dlam_magnitude(q, k, v, g, lam, s_init, g_final, phi=phi)
+        assert mag == pytest.approx(oracle.dlam_recurrent(q, k, v, g, lam, s_init, g_final, phi=phi), rel=1e-12)
+    qs, ks, vs, gs = (rng.standard_normal((n, d)) for _ in range(4))
+    signed = oracle.dlam_recurrent(qs, ks, vs, gs, lam, s0 - 0.5, gf - 0.5, phi=phi)
+    assert abs(signed) <= oracle.dlam_magnitude(qs, ks, vs, gs, lam, s0 - 0.5, gf - 0.5, phi=phi) * (1 + 1e-12)
