@@ -1,4 +1,5 @@
-"""Seeded random configurations over the whole argument space, each against the oracle:
+"""Seeded random configurations over the whole argument space (short sequences, and a set of
+longer ones with more chunks), each against the oracle:
 storage dtype, head dim, block size, sequence length (ragged), batch and heads, decays
 (including 0 and 1), feature map, initial state, final-state gradient, forced chunk
 counts and aggregate parts.  Forward, backward (with and without the forward's chunk
@@ -29,9 +30,34 @@ def draw(seed):
                 with_state=bool(r.random() < 0.5), with_gf=bool(r.random() < 0.5), fwd_ws=bool(r.random() < 0.5))
 
 
+def draw_long(seed):
+    """Longer sequences (1000-6000 tokens) with more chunks and aggregate parts, block sizes up
+    to 256."""
+    r = np.random.default_rng(5000 + seed)
+    dtype = "bf16" if r.random() < 0.85 else "f32"
+    D = int(r.choice([64, 128], p=[0.2, 0.8]))
+    Bk = int(r.choice([64, 128, 256]))
+    N = int(r.integers(1000, 6000))
+    B, H = int(r.integers(1, 3)), int(r.integers(1, 3))
+    lam = r.choice([0.0, 1.0, 0.9, 0.99, 0.999, 0.9999], size=H).astype(np.float32)
+    phi = str(r.choice(["identity", "identity", "elu1", "relu"]))
+    cks = int(r.choice([0, 2, 3, 5, 8, 13]))
+    agg = int(r.choice([0, 2, 3, 4])) if cks else 0
+    return dict(dtype=dtype, D=D, Bk=Bk, N=N, B=B, H=H, lam=lam, phi=phi, cks=cks, agg=agg,
+                with_state=bool(r.random() < 0.5), with_gf=bool(r.random() < 0.5), fwd_ws=bool(r.random() < 0.5))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_long_configuration(seed, monkeypatch):
+    check_configuration(draw_long(seed), seed, monkeypatch)
+
+
 @pytest.mark.parametrize("seed", range(24))
 def test_random_configuration(seed, monkeypatch):
-    c = draw(seed)
+    check_configuration(draw(seed), seed, monkeypatch)
+
+
+def check_configuration(c, seed, monkeypatch):
     monkeypatch.delenv("LA_KERNEL", raising=False)
     monkeypatch.delenv("LA_AGG_K", raising=False)
     if c["cks"]:
