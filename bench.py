@@ -29,6 +29,7 @@ import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -174,7 +175,38 @@ def cpu_baseline(seconds_target):
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{pairs} of the {B * H} (batch, head) sequences of the n={n} sweep point "
                       f"(d={D}, per-head decay), {reps} pass(es), fwd+bwd, recurrent form in fp64, "
-                      f"{dt:.1f} s"}
+                      f"{dt:.1f} s",
+            "cpu_model": cpu_model(), "one_thread": one_thread_oracle(n)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def one_thread_oracle(n):
+    """The oracle on one thread (its OpenMP loop over sequences pinned to one thread, in a
+    child process): fwd+bwd of one (batch, head) sequence of the sweep point."""
+    code = ("import sys, time, numpy as np; sys.path.insert(0, %r); import oracle, synth; "
+            "q, k, v, g = (synth.bf16_bits_to_f64(synth.pair_slice(0, i, %d, %d, %d, %d, 0, 0, 'bf16'))[None] "
+            "for i in (1, 2, 3, 4)); lam = synth.decay_schedule(%d)[:1].astype(np.float64); "
+            "oracle.fwd_recurrent(q[:, :8], k[:, :8], v[:, :8], lam); t0 = time.perf_counter(); "
+            "oracle.fwd_recurrent(q, k, v, lam); oracle.bwd_recurrent(q, k, v, g, lam); "
+            "print(time.perf_counter() - t0)" % (ROOT, TOKENS_PER_POINT // n, H, n, D, H))
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    try:
+        out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                             timeout=120, check=True).stdout.split()
+        dt = float(out[-1])
+    except (subprocess.SubprocessError, ValueError, IndexError):
+        return None
+    return {"value": n / H / dt, "unit": "tokens/s", "seconds": round(dt, 3),
+            "sample": f"one (batch, head) sequence of n={n}, fwd+bwd, 1 thread"}
 
 
 # ----------------------------------------------------------------------------- serving
