@@ -111,8 +111,9 @@ def test_fwd_bwd_sweep_131072_tokens(N):
 
 def test_long_prefill_then_decode():
     """bf16 prefill B=1 H=64 N=262144 D=128 Bk=128, then 256 recurrent decode steps for 256
-    sequences that all start from the prefill's final state; checked against the oracle and
-    against la_fwd continued from that state."""
+    sequences that all start from the prefill's final state; checked against the oracle,
+    against la_fwd continued from that state, and (slot 0) against one la_fwd over all
+    262144 + 256 tokens."""
     B, H, N, Bs, steps = 1, 64, 262144, 256, 256
     print(f"[workload] prefill B={B} H={H} N={N} Bk=128", flush=True)
     lam = synth.decay_schedule(H)
@@ -171,3 +172,18 @@ def test_long_prefill_then_decode():
     e_fs = oracle.rel_l2(st_h, got(sf))
     print(f"    decode vs la_fwd(kv_in) rel-L2 o={e_f:.3e} state={e_fs:.3e}", flush=True)
     assert e_f <= BF16_BAR and e_fs <= BF16_BAR
+    del of, sf, kv_in
+
+    # slot 0 against one la_fwd over all N + 256 tokens (2050 blocks of 128): the prefill's
+    # tokens followed by the slot's decode tokens
+    print(f"[workload] slot 0 against la_fwd over {N + steps} tokens", flush=True)
+    q, k, v = qkv_dev(B, H, N)
+    tail = [stack(x)[0:1] for x in (dec_q, dec_k, dec_v)]
+    q, k, v = (torch.cat([a, b], dim=2).contiguous() for a, b in zip((q, k, v), tail))
+    del tail
+    oa, sa = la.la_fwd(q, k, v, lam, Bk=128)
+    torch.cuda.synchronize()
+    e_all = oracle.rel_l2(o_dec[0:1].astype(np.float64), got(oa[:, :, N:]))
+    e_alls = oracle.rel_l2(st_h[0], got(sa[0]))
+    print(f"    slot 0 decode vs la_fwd over {N + steps} tokens rel-L2 o={e_all:.3e} state={e_alls:.3e}", flush=True)
+    assert e_all <= BF16_BAR and e_alls <= BF16_BAR
