@@ -488,7 +488,9 @@ def bench(args):
     tflops_step = sum((fwd_flops_per_token_head() + bwd_flops_per_token_head()) * TOKENS_PER_POINT * H
                       for _ in SWEEP_N) / (ms_per_step * 1e-3) / 1e12
     out = {
-        "metric": "fwd+bwd tokens/s over the 1K-64K sequence-length sweep (131072 tokens per point), 1 GPU",
+        # value: fwd+bwd tokens/s over the whole sweep (131072 tokens per point); the per-point
+        # tokens/s, TFLOP/s and % of bf16 peak are under "sweep", the step's under "tflops_alg"
+        "metric": "fwd/bwd tokens/s + TFLOP/s (% bf16 MFMA peak) vs seq len 1K\u201364K, 1 GPU",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
