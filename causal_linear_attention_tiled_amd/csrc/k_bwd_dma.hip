@@ -429,21 +429,28 @@ __global__ __launch_bounds__(64 * 8, 1) void k_rev_dma_split(SweepArgs a, LamArg
                 for (int h = 0; h < 2; ++h) acc[h] = mfma16(tf[h][kb], tb, acc[h]);
             }
             // acc[h][r] = dV (value group) or dK (key group) [j][32 q + 16 h + 4 g + r]
-            if (j < m) {
+            u32x2 pk[2];
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int col = 32 * q + 16 * h + 4 * g;
-                    if (PHI && grp) {
-                        // dK with respect to the raw keys: phi'(k) from the mapped key tile
-                        const u32x2 kp = *reinterpret_cast<const u32x2*>(sm.t[stage][1] + swz(j, col));
-                        acc[h][0] *= dphi_of_phi(__uint_as_float(kp.x << 16), a.phi);
-                        acc[h][1] *= dphi_of_phi(__uint_as_float(kp.x & 0xFFFF0000u), a.phi);
-                        acc[h][2] *= dphi_of_phi(__uint_as_float(kp.y << 16), a.phi);
-                        acc[h][3] *= dphi_of_phi(__uint_as_float(kp.y & 0xFFFF0000u), a.phi);
-                    }
-                    const int64_t off = (t0 + j) * D + col;
-                    *reinterpret_cast<u32x2*>(outg + off) = u32x2{pack_bf16(acc[h][0], acc[h][1]), pack_bf16(acc[h][2], acc[h][3])};
+            for (int h = 0; h < 2; ++h) {
+                if (PHI && grp) {
+                    // dK with respect to the raw keys: phi'(k) from the mapped key tile
+                    const u32x2 kp = *reinterpret_cast<const u32x2*>(sm.t[stage][1] + swz(j, 32 * q + 16 * h + 4 * g));
+                    acc[h][0] *= dphi_of_phi(__uint_as_float(kp.x << 16), a.phi);
+                    acc[h][1] *= dphi_of_phi(__uint_as_float(kp.x & 0xFFFF0000u), a.phi);
+                    acc[h][2] *= dphi_of_phi(__uint_as_float(kp.y << 16), a.phi);
+                    acc[h][3] *= dphi_of_phi(__uint_as_float(kp.y & 0xFFFF0000u), a.phi);
                 }
+                pk[h] = u32x2{pack_bf16(acc[h][0], acc[h][1]), pack_bf16(acc[h][2], acc[h][3])};
+            }
+            {
+                // 16-byte stores, as in the forward kernel: after swapping the odd 16-lane rows
+                // of tile 0's words with the even rows of tile 1's, row group g holds the 8
+                // consecutive columns 8 gs .. 8 gs + 7 of the wave's 32, gs = 0, 2, 1, 3
+                const auto x = __builtin_amdgcn_permlane16_swap(pk[0].x, pk[1].x, false, false);
+                const auto y = __builtin_amdgcn_permlane16_swap(pk[0].y, pk[1].y, false, false);
+                const int gs = (g & 1) * 2 + (g >> 1);
+                if (j < m)
+                    *reinterpret_cast<u32x4*>(outg + (t0 + j) * D + 32 * q + 8 * gs) = u32x4{x[0], y[0], x[1], y[1]};
             }
         }
 

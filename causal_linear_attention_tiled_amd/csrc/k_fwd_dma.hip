@@ -247,21 +247,34 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
             }
             // o[vt][r] = O[16 st + li][16 (NVT w + vt) + 4 g + r]
             const int s = 16 * st + li;
-            if (s < m) {
+            u32x2 pk[NVT];
 #pragma unroll
-                for (int vt = 0; vt < NVT; ++vt) {
-                    const int64_t off = (t0 + s) * ld + 16 * (NVT * w + vt) + 4 * g;
-                    f32x4 ov = o[vt];
-                    if (PHI && a.phi_grad) {
-                        // chain rule through the feature map: phi'(raw q) for the dQ sweep
-                        const u32x2 raw = qraw[PHI ? st : 0][vt];
-                        ov[0] *= dphi_of_x(__uint_as_float(raw.x << 16), a.phi);
-                        ov[1] *= dphi_of_x(__uint_as_float(raw.x & 0xFFFF0000u), a.phi);
-                        ov[2] *= dphi_of_x(__uint_as_float(raw.y << 16), a.phi);
-                        ov[3] *= dphi_of_x(__uint_as_float(raw.y & 0xFFFF0000u), a.phi);
-                    }
-                    *reinterpret_cast<u32x2*>(Og + off) = u32x2{pack_bf16(ov[0], ov[1]), pack_bf16(ov[2], ov[3])};
+            for (int vt = 0; vt < NVT; ++vt) {
+                f32x4 ov = o[vt];
+                if (PHI && a.phi_grad) {
+                    // chain rule through the feature map: phi'(raw q) for the dQ sweep
+                    const u32x2 raw = qraw[PHI ? st : 0][vt];
+                    ov[0] *= dphi_of_x(__uint_as_float(raw.x << 16), a.phi);
+                    ov[1] *= dphi_of_x(__uint_as_float(raw.x & 0xFFFF0000u), a.phi);
+                    ov[2] *= dphi_of_x(__uint_as_float(raw.y << 16), a.phi);
+                    ov[3] *= dphi_of_x(__uint_as_float(raw.y & 0xFFFF0000u), a.phi);
                 }
+                pk[vt] = u32x2{pack_bf16(ov[0], ov[1]), pack_bf16(ov[2], ov[3])};
+            }
+            if constexpr (NVT == 2) {
+                // 16-byte stores (8-byte ones write HBM ~20% slower): swap the odd 16-lane rows
+                // of the first tile's words with the even rows of the second's, which leaves
+                // row group g holding 8 consecutive columns 8 gs .. 8 gs + 7 of the wave's 32,
+                // gs = 0, 2, 1, 3 for g = 0..3 (all lanes take part; the store is masked)
+                const auto x = __builtin_amdgcn_permlane16_swap(pk[0].x, pk[1].x, false, false);
+                const auto y = __builtin_amdgcn_permlane16_swap(pk[0].y, pk[1].y, false, false);
+                const int gs = (g & 1) * 2 + (g >> 1);
+                if (s < m)
+                    *reinterpret_cast<u32x4*>(Og + (t0 + s) * ld + 32 * w + 8 * gs) = u32x4{x[0], y[0], x[1], y[1]};
+            } else if (s < m) {
+#pragma unroll
+                for (int vt = 0; vt < NVT; ++vt)
+                    *reinterpret_cast<u32x2*>(Og + (t0 + s) * ld + 16 * (NVT * w + vt) + 4 * g) = pk[vt];
             }
             __builtin_amdgcn_sched_barrier(0);
         }
