@@ -185,20 +185,33 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma128(SweepArgs a, La
     // store one 16-token column of outputs (rows h * 64 + 16 st + li of the block)
     auto store = [&](int64_t t0, int m, int h, int st, const f32x4 (&o)[NVT]) {
         const int s = HB * h + 16 * st + li;
-        if (s >= m) return;
+        u32x2 pk[NVT];
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt) {
-            const int64_t off = (t0 + s) * ld + 16 * (NVT * w + vt) + 4 * g;
             f32x4 ov = o[vt];
             if (PHI && a.phi_grad) {
-                // chain rule through the feature map: phi'(raw q) for the dQ sweep
-                const u32x2 raw = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.phi_grad) + base + off);
+                // chain rule through the feature map: phi'(raw q) for the dQ sweep (rows past
+                // the block's end read its last row and are not stored)
+                const int64_t roff = (t0 + min(s, m - 1)) * ld + 16 * (NVT * w + vt) + 4 * g;
+                const u32x2 raw = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.phi_grad) + base + roff);
                 ov[0] *= dphi_of_x(__uint_as_float(raw.x << 16), a.phi);
                 ov[1] *= dphi_of_x(__uint_as_float(raw.x & 0xFFFF0000u), a.phi);
                 ov[2] *= dphi_of_x(__uint_as_float(raw.y << 16), a.phi);
                 ov[3] *= dphi_of_x(__uint_as_float(raw.y & 0xFFFF0000u), a.phi);
             }
-            *reinterpret_cast<u32x2*>(Og + off) = u32x2{pack_bf16(ov[0], ov[1]), pack_bf16(ov[2], ov[3])};
+            pk[vt] = u32x2{pack_bf16(ov[0], ov[1]), pack_bf16(ov[2], ov[3])};
+        }
+        if constexpr (NVT == 2) {
+            // 16-byte stores: the 16-lane swap of the forward kernel (row group g then holds
+            // columns 8 gs .. 8 gs + 7 of the wave's 32, gs = 0, 2, 1, 3); every lane swaps
+            const auto x = __builtin_amdgcn_permlane16_swap(pk[0].x, pk[1].x, false, false);
+            const auto y = __builtin_amdgcn_permlane16_swap(pk[0].y, pk[1].y, false, false);
+            const int gs = (g & 1) * 2 + (g >> 1);
+            if (s < m) *reinterpret_cast<u32x4*>(Og + (t0 + s) * ld + 32 * w + 8 * gs) = u32x4{x[0], y[0], x[1], y[1]};
+        } else if (s < m) {
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt)
+                *reinterpret_cast<u32x2*>(Og + (t0 + s) * ld + 16 * (NVT * w + vt) + 4 * g) = pk[vt];
         }
     };
     // diag(lam^(off + s + 1)) S^T Q_h^T for the column st of a half
