@@ -273,7 +273,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_rev_dma(SweepArgs a, LamArgs lam
 // dS^T[:, 32 q .. 32 q + 32) and produces dK for those key rows (q = w mod 4).
 // Each wave holds 64 accumulator registers instead of 128, so two waves share
 // every SIMD and one hides the other's LDS and MFMA latency.  The value group
-// builds the P tiles, the key group the G tiles.
+// builds the P tiles, the key group the G tiles.  dK and dV rows leave as
+// 16-byte stores (a 16-lane swap pairs a lane's two 4-column pieces), which
+// also drain sooner before the next block's vmcnt(0).
 template <bool PHI>
 __global__ __launch_bounds__(64 * 8, 1) void k_rev_dma_split(SweepArgs a, LamArgs lam) {
     __shared__ RevDmaTiles sm;

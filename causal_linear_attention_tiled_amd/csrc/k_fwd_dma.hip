@@ -25,7 +25,9 @@
 // makes them directly the A operand of S^T Q^T.  Products contracted over
 // tokens (V^T A^T and the state update) take the kappa order, whose
 // transposing reads touch 16 consecutive rows; the score accumulators are
-// then directly the B operand of V^T A^T.
+// then directly the B operand of V^T A^T.  Outputs leave as 16-byte stores:
+// a lane's two 4-column pieces of a row (one per value tile) are regrouped by
+// a 16-lane swap into 8 consecutive columns (8-byte stores write HBM slower).
 #include "la_device.h"
 #include "la_internal.h"
 #include "lds_dma.h"
