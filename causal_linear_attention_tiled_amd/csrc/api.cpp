@@ -50,19 +50,26 @@ std::vector<ProfRec> g_prof;
 template <typename Fn>
 int launch(const char* name, hipStream_t s, Fn&& fn) {
     hipEvent_t e0 = nullptr, e1 = nullptr;
+    // events created for this launch are destroyed on every failure path
+    auto fail = [&](hipError_t e, const char* where) {
+        if (e0) (void)hipEventDestroy(e0);
+        if (e1) (void)hipEventDestroy(e1);
+        return hip_fail(e, where);
+    };
     const bool prof = g_prof_on.load(std::memory_order_relaxed) != 0;
     if (prof) {
-        if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)
-            return hip_fail(hipGetLastError(), "hipEventCreate");
-        hipError_t er = hipEventRecord(e0, s);
-        if (er != hipSuccess) return hip_fail(er, "hipEventRecord");
+        hipError_t er = hipEventCreate(&e0);
+        if (er == hipSuccess) er = hipEventCreate(&e1);
+        if (er != hipSuccess) return fail(er, "hipEventCreate");
+        er = hipEventRecord(e0, s);
+        if (er != hipSuccess) return fail(er, "hipEventRecord");
     }
     fn();
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, name);
+    if (e != hipSuccess) return fail(e, name);
     if (prof) {
         hipError_t er = hipEventRecord(e1, s);
-        if (er != hipSuccess) return hip_fail(er, "hipEventRecord");
+        if (er != hipSuccess) return fail(er, "hipEventRecord");
         std::lock_guard<std::mutex> lk(g_prof_mu);
         g_prof.push_back({name, e0, e1});
     }
