@@ -458,3 +458,29 @@ def test_impulse_probe_variants(variant, fwd_variant, chunks, kernel):
     fwd_variant(variant)
     test_impulse_probe_bit_exact("default", 0.5, 64, 4, chunks, kernel)
     test_impulse_probe_bit_exact("default", 1.0, 64, 1, chunks, kernel)
+
+
+# ------------------------------------------------------------------ non-finite inputs
+@pytest.mark.parametrize("kern", ["generic", "default"])
+def test_non_finite_inputs_propagate(kern, kernel):
+    """Nothing checks for NaN: a NaN query leaves only its own output row non-finite; a NaN key
+    leaves every row from its position on non-finite and the rows before its block unchanged
+    (the earlier rows of its own block may be reached through the masked score tile)."""
+    kernel(kern)
+    N, D, Bk = 300, 128, 64
+    _, (q, k, v), _ = inputs(21, 1, 1, N, D, "bf16")
+    lam = [0.9]
+    o_ref, _ = la.la_fwd(q, k, v, lam, Bk=Bk)
+    q_nan = q.clone()
+    q_nan[0, 0, 100, 3] = float("nan")
+    o_q, _ = la.la_fwd(q_nan, k, v, lam, Bk=Bk)
+    k_nan = k.clone()
+    k_nan[0, 0, 130, 7] = float("nan")
+    o_k, s_k = la.la_fwd(q, k_nan, v, lam, Bk=Bk)
+    _sync()
+    ref, oq, ok_ = got(o_ref)[0, 0], got(o_q)[0, 0], got(o_k)[0, 0]
+    rows = np.arange(N) != 100
+    assert np.all(np.isnan(oq[100])) and np.array_equal(oq[rows], ref[rows])
+    assert np.array_equal(ok_[:128], ref[:128])
+    assert not np.any(np.isfinite(ok_[130:]).all(axis=1))
+    assert not np.all(np.isfinite(got(s_k)))
