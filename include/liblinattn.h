@@ -45,7 +45,7 @@
  *    halves (the same function, with the second half's share of the first
  *    half's gradients carried through the state instead of a score tile).
  *    Bk = 256 places the chunk boundaries of the chunked prefix on multiples
- *    of 256 tokens and is stepped as two 128-token blocks by every kernel.
+ *    of 256 tokens; the kernels then step it as they step Bk = 128.
  *  - The environment variable LA_CHUNKS (a positive integer) overrides the
  *    number of chunks a sequence is split into for the chunked prefix over
  *    blocks, LA_AGG_K the number of parts of a chunk the chunk aggregates are
