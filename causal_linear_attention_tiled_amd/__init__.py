@@ -120,19 +120,43 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _check_tensor(name, t, shape, dtype, device):
+    """A caller-supplied tensor: a contiguous GPU tensor on ``device`` with exactly this shape
+    and dtype.  The C ABI receives bare pointers and can check none of this itself."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got one on {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_lead(name, t, dims):
+    """The first operand of a call: a contiguous float32 or bfloat16 GPU tensor of ``dims`` dims."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dimensions (got {t.dim()})")
+    _check_tensor(name, t, None, None, None)
+    _dtype_code(t)
+
+
 def _check_seq(name, t, ref=None):
-    if t.dim() != 4 or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous [B, H, N, D] tensor")
-    if ref is not None and (t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device):
-        raise ValueError(f"{name} must match Q in shape, dtype and device")
+    if ref is None:
+        _check_lead(name, t, 4)
+    else:
+        _check_tensor(name, t, ref.shape, ref.dtype, ref.device)
 
 
 def _check_state(name, t, B, H, D, device):
-    if t is None:
-        return
-    if t.dtype != torch.float32 or tuple(t.shape) != (B, H, D, D) or not t.is_contiguous() \
-            or t.device != device:
-        raise ValueError(f"{name} must be a contiguous float32 [B, H, D, D] tensor on {device}")
+    if t is not None:
+        _check_tensor(name, t, (B, H, D, D), torch.float32, device)
 
 
 def la_fwd_workspace_bytes(B, H, N, D, Bk, dtype_code) -> int:
@@ -152,14 +176,20 @@ def la_bwd_workspace_bytes(B, H, N, D, Bk, dtype_code) -> int:
     return int(lib.la_bwd_workspace_bytes(B, H, N, D, Bk, dtype_code))
 
 
+def _check_bytes(name, t, nbytes, device):
+    """A caller's byte buffer: contiguous, on ``device``, at least ``nbytes`` long."""
+    _check_tensor(name, t, None, None, device)
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} needs {nbytes} bytes (got {t.numel() * t.element_size()})")
+
+
 def _workspace(nbytes, device, ws):
-    if nbytes == 0:
+    if ws is not None:
+        _check_bytes("ws", ws, nbytes, device)
         return ws
-    if ws is None:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    if ws.numel() * ws.element_size() < nbytes:
-        raise ValueError(f"workspace needs {nbytes} bytes")
-    return ws
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 def la_fwd(q, k, v, lam, Bk: int = 64, kv_in=None, out=None, kv_out=None, want_state: bool = True,
@@ -214,9 +244,7 @@ def la_bwd(q, k, v, dout, lam, Bk: int = 64, kv_in=None, dq=None, dk=None, dv=No
     nbytes = la_bwd_workspace_bytes(B, H, N, D, Bk, code)
     ws = _workspace(nbytes, q.device, ws)
     if fwd_ws is not None:
-        need = la_fwd_workspace_bytes(B, H, N, D, Bk, code)
-        if fwd_ws.device != q.device or fwd_ws.numel() * fwd_ws.element_size() < need:
-            raise ValueError(f"fwd_ws must hold the {need}-byte workspace of la_fwd on {q.device}")
+        _check_bytes("fwd_ws", fwd_ws, la_fwd_workspace_bytes(B, H, N, D, Bk, code), q.device)
     rc = lib.la_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _lam_array(lam, H), B, H, N, D, Bk, code,
                     _phi_code(phi), _ptr(kv_in), _ptr(dkv_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkv_in), _ptr(fwd_ws),
                     _ptr(ws), nbytes if ws is not None else 0, _stream(q.device))
@@ -241,8 +269,7 @@ def la_dlam(q, k, v, dout, lam, Bk: int = 64, kv_in=None, dkv_out=None, out=None
     _check_state("dkv_out", dkv_out, B, H, D, q.device)
     if out is None:
         out = torch.empty(H, dtype=torch.float32, device=q.device)
-    if out.dtype != torch.float32 or tuple(out.shape) != (H,) or not out.is_contiguous() or out.device != q.device:
-        raise ValueError(f"out must be a contiguous float32 [H] tensor on {q.device}")
+    _check_tensor("out", out, (H,), torch.float32, q.device)
     code = _dtype_code(q)
     nbytes = la_dlam_workspace_bytes(B, H, N, D, Bk, code)
     ws = _workspace(nbytes, q.device, ws)
@@ -268,14 +295,15 @@ def la_fwd_varlen(q, k, v, lam, seq_offsets, Bk: int = 64, kv_in=None, out=None,
                   want_state: bool = True, ws=None, phi="identity"):
     """Forward over a ragged batch packed token-major: q, k, v [T, H, D] bf16, sequence b is
     rows seq_offsets[b] .. seq_offsets[b+1].  Returns (O [T, H, D], kv_out [B, H, D, D])."""
-    for name, t in (("Q", q), ("K", k), ("V", v)):
-        if t.dim() != 3 or not t.is_contiguous() or (t is not q and (t.shape != q.shape or t.dtype != q.dtype)):
-            raise ValueError(f"{name} must be a contiguous [T, H, D] tensor matching Q")
+    _check_lead("Q", q, 3)
+    for name, t in (("K", k), ("V", v)):
+        _check_tensor(name, t, q.shape, q.dtype, q.device)
     T, H, D = q.shape
     arr, B = _offsets(seq_offsets)
     if arr[B] != T:
         raise ValueError("seq_offsets[-1] must equal the packed token count")
     out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out, q.shape, q.dtype, q.device)
     if kv_out is None and want_state:
         kv_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     _check_state("kv_in", kv_in, B, H, D, q.device)
@@ -294,18 +322,18 @@ def la_fwd_varlen(q, k, v, lam, seq_offsets, Bk: int = 64, kv_in=None, out=None,
 def la_decode_step_paged(pool, slot_of, q, k, v, lam, out=None, phi="identity"):
     """One recurrent step for Bs sequences whose float32 states live in ``pool``
     [P, H, D, D] at slots ``slot_of`` (int32 [Bs], distinct); q, k, v [Bs, H, D].  Returns o."""
-    if pool.dtype != torch.float32 or pool.dim() != 4 or not pool.is_contiguous():
-        raise ValueError("pool must be a contiguous float32 [P, H, D, D] tensor")
-    if slot_of.dtype != torch.int32 or slot_of.dim() != 1 or not slot_of.is_contiguous():
-        raise ValueError("slot_of must be a contiguous int32 [Bs] tensor")
+    if not isinstance(pool, torch.Tensor) or pool.dim() != 4:
+        raise ValueError("pool must be a float32 [P, H, D, D] tensor")
     P, H, D, _ = pool.shape
+    _check_tensor("pool", pool, (P, H, D, D), torch.float32, None)
+    _check_lead("q", q, 3)
     Bs = q.shape[0]
-    if slot_of.shape[0] != Bs:
-        raise ValueError("slot_of needs one slot per sequence")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if tuple(t.shape) != (Bs, H, D) or not t.is_contiguous() or t.dtype != q.dtype:
-            raise ValueError(f"{name} must be a contiguous [Bs, H, D] tensor")
+    _check_tensor("q", q, (Bs, H, D), None, pool.device)
+    _check_tensor("slot_of", slot_of, (Bs,), torch.int32, pool.device)
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, q.shape, q.dtype, q.device)
     out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out, q.shape, q.dtype, q.device)
     rc = lib.la_decode_step_paged(_ptr(pool), P, _ptr(slot_of), _ptr(q), _ptr(k), _ptr(v), _lam_array(lam, H),
                                   Bs, H, D, _dtype_code(q), _phi_code(phi), _ptr(out), _stream(q.device))
     if rc != LA_OK:
@@ -317,15 +345,13 @@ def la_decode_step(state, q, k, v, lam, out=None, phi="identity"):
     """One recurrent step S <- lam S + k v^T, o = q S; ``state`` [Bs, H, D, D] float32 is updated in place.
 
     q, k, v are [Bs, H, D]; returns o."""
-    if q.dim() != 3 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous [Bs, H, D] tensor")
+    _check_lead("q", q, 3)
     Bs, H, D = q.shape
     for name, t in (("k", k), ("v", v)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
-            raise ValueError(f"{name} must match q")
-    if state.dtype != torch.float32 or tuple(state.shape) != (Bs, H, D, D) or not state.is_contiguous():
-        raise ValueError("state must be a contiguous float32 [Bs, H, D, D] tensor")
+        _check_tensor(name, t, q.shape, q.dtype, q.device)
+    _check_tensor("state", state, (Bs, H, D, D), torch.float32, q.device)
     out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out, q.shape, q.dtype, q.device)
     rc = lib.la_decode_step(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _lam_array(lam, H), Bs, H, D,
                             _dtype_code(q), _phi_code(phi), _ptr(out), _stream(q.device))
     if rc != LA_OK:

@@ -20,12 +20,37 @@ namespace {
 
 using la::LamArgs;
 
-// Target workgroup count for the chunk plan: one per compute unit of an MI355X
-// (256 CUs).  The sweep kernels hold one workgroup per CU (their LDS rings), so
-// 256 workgroups run in one round; measured, two rounds of half-length chunks
-// are slower (B4 H16 N2048 forward 72 us against 55 us; B2 H32 N8192 forward and
-// backward 559 us against 497 us) and the long-sequence points are unchanged.
-constexpr int64_t kTargetWorkgroups = 256;
+// Target workgroup count for the chunk plan: one per compute unit (256 on an
+// MI355X; queried from the current device, 256 when none answers).  The sweep
+// kernels hold one workgroup per CU (their LDS rings), so that many workgroups run
+// in one round; measured, two rounds of half-length chunks are slower (B4 H16
+// N2048 forward 72 us against 55 us; B2 H32 N8192 forward and backward 559 us
+// against 497 us) and the long-sequence points are unchanged.
+constexpr int64_t kDefaultComputeUnits = 256;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int64_t compute_units() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return kDefaultComputeUnits;
+    }
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            return kDefaultComputeUnits;
+        }
+        g_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// A launch of W workgroups of up to 1024 threads keeps W * 1024 below 2^32, the
+// limit on the threads of one grid dimension; larger calls are rejected before
+// anything is enqueued.
+constexpr int64_t kMaxWorkgroups = ((int64_t(1) << 32) - 1) / 1024;
 // A chunk should span at least this many blocks, so the per-chunk state
 // traffic (a few D x D float32 matrices) stays small next to its tokens.
 constexpr int64_t kMinBlocksPerChunk = 4;
@@ -156,8 +181,9 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t d
     const char* env = std::getenv("LA_CHUNKS");
     if (env && std::atoll(env) > 0) {
         C = std::atoll(env);
-    } else if (pairs < kTargetWorkgroups) {
-        C = (kTargetWorkgroups + pairs - 1) / pairs;
+    } else if (pairs < compute_units()) {
+        const int64_t target = compute_units();
+        C = (target + pairs - 1) / pairs;
         C = std::min<int64_t>(C, std::max<int64_t>(1, nb / kMinBlocksPerChunk));
     }
     C = std::max<int64_t>(1, std::min<int64_t>(C, nb));
@@ -199,6 +225,16 @@ size_t fwd_slot_bytes(int64_t pairs, const Plan& p, int64_t D) {
 }
 
 size_t round_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Largest workgroup count any launch of a chunked call makes: the sweeps (one per
+// sequence and chunk), the aggregates (agg_k per chunk boundary) and the scans
+// (D * D / 256 per sequence).
+bool plan_grid_ok(int64_t pairs, const Plan& p, int64_t D) {
+    const int64_t per = std::max<int64_t>({static_cast<int64_t>(p.chunks),
+                                           static_cast<int64_t>(p.chunks - 1) * p.agg_k,
+                                           p.chunks > 1 ? (D * D + 255) / 256 : 1});
+    return pairs <= kMaxWorkgroups / per;
+}
 
 // la_dlam: the (S, T) chunk slots, then one double per (sequence, chunk).
 size_t dlam_ws_bytes(int64_t pairs, const Plan& p, int64_t D) {
@@ -298,8 +334,8 @@ int make_varplan(const int64_t* offs, int64_t B, int64_t H, int64_t D, int32_t B
     const int64_t T = offs[B];
     // 32-bit buffer offsets: every element offset of one (sequence, head) stays below 2^31 bytes
     if (T >= (int64_t(1) << 31) / (H * D * 2)) return LA_EUNSUPPORTED;
-    constexpr int64_t kComputeUnits = 256;
-    const int64_t share = std::max<int64_t>(kMinBlocksPerChunk * Bk, (T * H + kComputeUnits - 1) / kComputeUnits);
+    const int64_t cus = compute_units();
+    const int64_t share = std::max<int64_t>(kMinBlocksPerChunk * Bk, (T * H + cus - 1) / cus);
     int64_t n_max = 0;
     for (int64_t b = 0; b < B; ++b) n_max = std::max<int64_t>(n_max, offs[b + 1] - offs[b]);
     int64_t L = n_max <= 2 * share ? std::max<int64_t>(n_max, Bk) : share;
@@ -318,6 +354,7 @@ int make_varplan(const int64_t* offs, int64_t B, int64_t H, int64_t D, int32_t B
     }
     p->v.cu[B] = static_cast<int>(T);
     p->slots_per_head = p->v.wp[B] - B;
+    if (static_cast<int64_t>(p->v.wp[B]) * H > kMaxWorkgroups) return LA_EUNSUPPORTED;
     // last chunks, longest first
     std::vector<int> ord(static_cast<size_t>(B));
     for (int b = 0; b < B; ++b) ord[b] = b;
@@ -399,6 +436,7 @@ int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int
     const size_t tb = static_cast<size_t>(elems) * (dtype == LA_BF16 ? 2 : 4);
     const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
+    if (!plan_grid_ok(B * H, p, D)) return LA_EUNSUPPORTED;
     Bk = p.bk;  // the block the kernels step
     const size_t need = fwd_slot_bytes(B * H, p, D);
     if (need && (!ws || ws_bytes < need)) return LA_EWORKSPACE;
@@ -434,6 +472,7 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     const size_t tb = static_cast<size_t>(elems) * (dtype == LA_BF16 ? 2 : 4);
     const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
+    if (!plan_grid_ok(B * H, p, D)) return LA_EUNSUPPORTED;
     Bk = p.bk;  // the block the kernels step
     // chunk states of the dQ sweep (forward direction) and of the dK, dV sweep (reverse
     // direction), both over agg_k parts per chunk boundary
@@ -542,6 +581,7 @@ int la_dlam(const void* Q, const void* K, const void* V, const void* dO, const f
     const size_t tb = static_cast<size_t>(elems) * (dtype == LA_BF16 ? 2 : 4);
     const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
+    if (!plan_grid_ok(B * H, p, D)) return LA_EUNSUPPORTED;
     Bk = p.bk;  // the block the kernels step
     const size_t need = dlam_ws_bytes(B * H, p, D);
     if (!ws || ws_bytes < need) return LA_EWORKSPACE;
@@ -678,6 +718,7 @@ int la_decode_step_paged(float* pool, int64_t pool_slots, const int32_t* slot_of
         if (!aligned16(ptr)) return LA_EALIGN;
     int64_t pairs, pool_pairs;
     if (!mul_ok(Bs, H, &pairs) || pairs > (int64_t(1) << 31)) return LA_EINVAL;
+    if (pairs > kMaxWorkgroups) return LA_EUNSUPPORTED;
     if (!mul_ok(pool_slots, H, &pool_pairs) || pool_pairs > (int64_t(1) << 31)) return LA_EINVAL;
     const size_t vb = static_cast<size_t>(pairs * D) * (dtype == LA_BF16 ? 2 : 4);
     const size_t pb = static_cast<size_t>(pool_pairs * D * D) * sizeof(float);
@@ -707,6 +748,7 @@ int la_decode_step(float* state, const void* q, const void* k, const void* v, co
         if (!aligned16(p)) return LA_EALIGN;
     int64_t pairs;
     if (!mul_ok(Bs, H, &pairs) || pairs > (int64_t(1) << 31)) return LA_EINVAL;
+    if (pairs > kMaxWorkgroups) return LA_EUNSUPPORTED;
     const size_t vb = static_cast<size_t>(pairs * D) * (dtype == LA_BF16 ? 2 : 4);
     const size_t sb = static_cast<size_t>(pairs * D * D) * sizeof(float);
     const Range rs{state, sb}, ro{o, vb};

@@ -39,10 +39,14 @@ _lib_handle = None
 
 
 def build() -> str:
-    """Compile liboracle.so with gcc (always recompiles)."""
+    """Compile liboracle.so with gcc (always recompiles).
+
+    Portable x86-64 code (the library may be built on one host and run on another) and no
+    contraction of a*b + c into fused multiply-adds, so every host rounds the fp64 sums the
+    same way."""
     src = os.path.join(_HERE, "oracle.c")
     tmp = _SO + ".tmp"
-    subprocess.run(["gcc", "-O3", "-march=native", "-fPIC", "-shared", "-fopenmp", "-o", tmp, src],
+    subprocess.run(["gcc", "-O3", "-ffp-contract=off", "-fPIC", "-shared", "-fopenmp", "-o", tmp, src],
                    check=True)
     os.replace(tmp, _SO)
     return _SO
@@ -170,12 +174,26 @@ def decode_step(state, q, k, v, lam, phi="identity"):
     return o, state
 
 
+def _norm2(x: np.ndarray) -> float:
+    """Euclidean norm without underflow or overflow of the squares: scaled by the largest
+    magnitude first (NaN propagates)."""
+    x = np.abs(x.ravel())
+    if x.size == 0:
+        return 0.0
+    m = float(np.max(x))
+    if not np.isfinite(m) or m == 0.0:
+        return m
+    return m * float(np.sqrt(np.sum((x / m) ** 2)))
+
+
 def rel_l2(y, ref) -> float:
-    """||y - ref||_2 / ||ref||_2 in fp64 (0 when both are exactly zero)."""
+    """||y - ref||_2 / ||ref||_2 in fp64 (0 when both are exactly zero; NaN anywhere gives NaN)."""
     y = np.asarray(y, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    den = float(np.linalg.norm(ref.ravel()))
-    num = float(np.linalg.norm((y - ref).ravel()))
+    den = _norm2(ref)
+    num = _norm2(y - ref)
+    if np.isnan(num) or np.isnan(den):
+        return float("nan")
     if den == 0.0:
         return 0.0 if num == 0.0 else float("inf")
     return num / den

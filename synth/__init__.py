@@ -34,7 +34,8 @@ def build() -> str:
     """Compile libsynth.so with gcc (always recompiles)."""
     src = os.path.join(_HERE, "synth.c")
     tmp = _SO + ".tmp"
-    subprocess.run(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-o", tmp, src, "-lm"], check=True)
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-fopenmp", "-o", tmp, src, "-lm"],
+                   check=True)
     os.replace(tmp, _SO)
     return _SO
 

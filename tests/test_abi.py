@@ -261,3 +261,27 @@ def test_plan():
     assert la.la_plan(1, 2, 300, 16, 256, la.LA_F32) == {"chunks": 1, "chunk_len": 512, "agg_parts": 1}
     with pytest.raises(la.LaError):
         la.la_plan(1, 16, 1024, 128, 512, la.LA_BF16)
+
+
+def test_grid_limit_rejected_before_any_enqueue():
+    """A call whose launches would exceed 2^32 threads in one grid dimension (at most
+    4194303 workgroups of up to 1024 threads) fails validation with LA_EUNSUPPORTED,
+    before the library looks for a device or enqueues anything: here 2^20 x 16 sequences
+    of one token each (one workgroup per sequence)."""
+    v = ctypes.c_void_p
+    lam16 = (ctypes.c_float * 16)(*([0.5] * 16))
+    assert fwd(B=1 << 20, H=16, N=1, lam=lam16, ws=None, ws_bytes=0) == la.LA_EUNSUPPORTED
+    assert fwd(B=(1 << 18) - 1, H=16, N=1, lam=lam16, ws=None, ws_bytes=0) != la.LA_EUNSUPPORTED
+    G_ = A * 10
+    rc = la.lib.la_bwd(v(Q_), v(K_), v(V_), v(G_), lam16, 1 << 20, 16, 1, 128, 64, la.LA_BF16, 0, None, None,
+                       v(O_), v(A * 20), v(A * 30), None, None, None, 0, None)
+    assert rc == la.LA_EUNSUPPORTED
+    rc = la.lib.la_dlam(v(Q_), v(K_), v(V_), v(G_), lam16, 1 << 20, 16, 1, 128, 64, la.LA_BF16, 0, None, None,
+                        v(O_), v(W_), 1 << 40, None)
+    assert rc == la.LA_EUNSUPPORTED
+    rc = la.lib.la_decode_step(v(S_), v(Q_), v(K_), v(V_), lam16, 1 << 19, 16, 16, la.LA_BF16, 0, v(O_), None)
+    assert rc == la.LA_EUNSUPPORTED
+    IDX_ = A * 12
+    rc = la.lib.la_decode_step_paged(v(S_), 8, v(IDX_), v(Q_), v(K_), v(V_), lam16, 1 << 19, 16, 16, la.LA_BF16,
+                                     0, v(O_), None)
+    assert rc == la.LA_EUNSUPPORTED

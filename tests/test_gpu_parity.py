@@ -12,7 +12,8 @@ import pytest
 
 import oracle
 import synth
-from helpers import BF16_BAR, bar, got, host_f64, inputs, lam_pairs, state_input, to_dev
+from helpers import (BF16_BAR, bar, got, host_f64, inputs, lam_pairs, rel_per_pair, row_bar, state_input, to_dev,
+                     worst_row)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,9 +54,16 @@ def check_fwd(B, H, N, D, Bk, dtype, lam, seed=0, with_state=False, label=""):
     _sync()
     lp = lam_pairs(lam, B)
     o_ref, s_ref = oracle.fwd_recurrent(qh, kh, vh, lp, None if s0 is None else s0.astype(np.float64))
-    e_o, e_s = oracle.rel_l2(got(o), o_ref), oracle.rel_l2(got(s), s_ref)
-    print(f"    rel-L2 O={e_o:.3e} kv_out={e_s:.3e}", flush=True)
+    P = B * H
+    yo, ys = got(o).reshape(P, N, D), got(s).reshape(P, D, D)
+    o_ref, s_ref = o_ref.reshape(P, N, D), s_ref.reshape(P, D, D)
+    e_o, e_s = oracle.rel_l2(yo, o_ref), oracle.rel_l2(ys, s_ref)
+    p_o, p_s, r_o = rel_per_pair(yo, o_ref), rel_per_pair(ys, s_ref), worst_row(yo, o_ref)
+    print(f"    rel-L2 O={e_o:.3e} kv_out={e_s:.3e}; worst sequence O={p_o:.3e} kv_out={p_s:.3e}; "
+          f"worst row O={r_o:.3e}", flush=True)
     assert e_o <= bar(dtype) and e_s <= bar(dtype)
+    assert p_o <= bar(dtype) and p_s <= bar(dtype)
+    assert r_o <= row_bar(dtype)
     return o, s
 
 
@@ -74,9 +82,17 @@ def check_bwd(B, H, N, D, Bk, dtype, lam, seed=0, with_state=False, label="", fw
     dq, dk, dv = la.la_bwd(q, k, v, g, lam, Bk=Bk, kv_in=kv_in, fwd_ws=fws)
     _sync()
     refs = oracle.bwd_recurrent(qh, kh, vh, gh, lam_pairs(lam, B), None if s0 is None else s0.astype(np.float64))
-    errs = [oracle.rel_l2(got(x), r) for x, r in zip((dq, dk, dv), refs)]
-    print(f"    rel-L2 dQ={errs[0]:.3e} dK={errs[1]:.3e} dV={errs[2]:.3e}", flush=True)
+    P = B * H
+    ys = [got(x).reshape(P, N, D) for x in (dq, dk, dv)]
+    refs = [r.reshape(P, N, D) for r in refs]
+    errs = [oracle.rel_l2(y, r) for y, r in zip(ys, refs)]
+    pair = [rel_per_pair(y, r) for y, r in zip(ys, refs)]
+    rows = [worst_row(y, r) for y, r in zip(ys, refs)]
+    print(f"    rel-L2 dQ={errs[0]:.3e} dK={errs[1]:.3e} dV={errs[2]:.3e}; worst sequence "
+          f"{max(pair):.3e}; worst row dQ={rows[0]:.3e} dK={rows[1]:.3e} dV={rows[2]:.3e}", flush=True)
     assert max(errs) <= bar(dtype)
+    assert max(pair) <= bar(dtype)
+    assert max(rows) <= row_bar(dtype)
 
 
 # ------------------------------------------------------------------ the small float32 workload

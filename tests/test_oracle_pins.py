@@ -680,3 +680,61 @@ def test_dlam_magnitude_is_the_derivative_when_no_term_cancels(lam, phi):
     qs, ks, vs, gs = (rng.standard_normal((n, d)) for _ in range(4))
     signed = oracle.dlam_recurrent(qs, ks, vs, gs, lam, s0 - 0.5, gf - 0.5, phi=phi)
     assert abs(signed) <= oracle.dlam_magnitude(qs, ks, vs, gs, lam, s0 - 0.5, gf - 0.5, phi=phi) * (1 + 1e-12)
+
+
+# ------------------------------------------------------------------ the error measure itself
+def test_rel_l2_known_values():
+    """rel-L2 = ||y - ref|| / ||ref||, with ref in the denominator: values fixed by hand."""
+    assert abs(oracle.rel_l2([1.0, 0.0], [1.0, 1.0]) - 1.0 / np.sqrt(2.0)) < 1e-15
+    x = np.array([3.0, -4.0])
+    assert oracle.rel_l2(2 * x, x) == 1.0          # ||x|| / ||x||
+    assert oracle.rel_l2(x, 2 * x) == 0.5          # ||x|| / ||2x||: the reference is the second argument
+    assert oracle.rel_l2(x, x) == 0.0
+    assert oracle.rel_l2(np.zeros(3), np.zeros(3)) == 0.0
+    assert oracle.rel_l2([1e-300, 0.0], [0.0, 0.0]) == float("inf")
+    assert oracle.rel_l2([[1.0, 2.0], [2.0, 0.0]], [[1.0, 2.0], [2.0, 4.0]]) == 4.0 / 5.0   # all elements
+
+
+def test_rel_l2_sees_a_planted_difference():
+    rng = np.random.default_rng(7)
+    ref = rng.standard_normal((3, 50, 8))
+    y = ref.copy()
+    y[1, 17, 5] += 0.25
+    assert abs(oracle.rel_l2(y, ref) - 0.25 / np.linalg.norm(ref)) < 1e-15
+    assert not oracle.rel_l2(ref * (1 + 3e-2), ref) <= 2e-2   # a 3% scale error fails the bf16 bar
+    y[0, 0, 0] = np.nan
+    assert not oracle.rel_l2(y, ref) <= 2e-2                  # NaN never passes a bar
+
+
+def test_rel_per_pair_is_the_worst_sequence():
+    from helpers import rel_per_pair, worst_row
+    ref = np.ones((3, 4, 2))
+    y = ref.copy()
+    y[2, 1, 0] = 3.0                   # sequence 2: ||diff|| = 2 over ||ref|| = sqrt(8)
+    assert abs(rel_per_pair(y, ref) - 2.0 / np.sqrt(8.0)) < 1e-15
+    assert abs(oracle.rel_l2(y, ref) - 2.0 / np.sqrt(24.0)) < 1e-15
+    # worst row: ||diff of row|| over the sequence's RMS row norm (sqrt(2) here)
+    assert abs(worst_row(y, ref) - 2.0 / np.sqrt(2.0)) < 1e-15
+    assert rel_per_pair(ref, ref) == 0.0 and worst_row(ref, ref) == 0.0
+
+
+def test_dlam_magnitude_signed_hand_example():
+    """n = 2, d = 1, lam = 1/2 with mixed signs.  The terms of dL/dlam, by hand:
+    g1 q1 k0 v0 = 18, g0 q0 s0 = -3, 2 lam g1 q1 s0 = 9, f k0 v0 = -1.5, 2 lam f s0 = -0.75,
+    so dL/dlam = 21.75 and the sum of their magnitudes 32.25 (a dropped abs() or term shows)."""
+    q = np.array([[1.0], [-2.0]])
+    k = np.array([[3.0], [-1.0]])
+    v = np.array([[-1.0], [2.0]])
+    g = np.array([[2.0], [3.0]])
+    s0 = np.array([[-1.5]])
+    f = np.array([[0.5]])
+    assert oracle.dlam_magnitude(q, k, v, g, 0.5, s0, f) == 32.25
+    assert oracle.dlam_quadratic(q, k, v, g, 0.5, s0, f) == 21.75
+    assert float(oracle.dlam_recurrent(q, k, v, g, 0.5, s0, f)) == 21.75
+
+
+def test_rel_l2_has_no_underflow_or_overflow():
+    """Squares of 1e-300 underflow and of 1e300 overflow in fp64; the measure must not."""
+    assert abs(oracle.rel_l2([2e-300, 0.0], [1e-300, 0.0]) - 1.0) < 1e-15
+    assert abs(oracle.rel_l2([2e300, 0.0], [1e300, 0.0]) - 1.0) < 1e-15
+    assert abs(oracle.rel_l2([1e-300, 1.0], [0.0, 1.0]) - 1e-300) < 1e-315
