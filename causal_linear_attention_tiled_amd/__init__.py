@@ -31,7 +31,7 @@ def _phi_code(phi) -> int:
             raise ValueError(f"unknown feature map {phi!r}; one of {sorted(PHI_CODES)}")
         return PHI_CODES[phi]
     return int(phi)
-LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EALIGN, LA_EWORKSPACE, LA_EHIP, LA_ENODEV = range(7)
+LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EALIGN, LA_EWORKSPACE, LA_EHIP, LA_ENODEV, LA_ESCRATCH = range(8)
 
 
 class LaError(RuntimeError):
@@ -52,6 +52,10 @@ def _load():
     fp = ctypes.POINTER(ctypes.c_float)
     lib.la_fwd.argtypes = [vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.la_fwd.restype = ctypes.c_int
+    lib.la_fwd_noalloc.argtypes = [vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, i32, vp, vp, vp, vp]
+    lib.la_fwd_noalloc.restype = ctypes.c_int
+    lib.la_scratch_bytes.argtypes = []
+    lib.la_scratch_bytes.restype = sz
     lib.la_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
     lib.la_fwd_workspace_bytes.restype = sz
     lib.la_bwd.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -83,7 +87,7 @@ def _load():
 
 lib = _load()
 
-EXPORTS = ("la_fwd", "la_fwd_workspace_bytes", "la_plan", "la_bwd", "la_bwd_workspace_bytes", "la_dlam",
+EXPORTS = ("la_fwd", "la_fwd_noalloc", "la_scratch_bytes", "la_fwd_workspace_bytes", "la_plan", "la_bwd", "la_bwd_workspace_bytes", "la_dlam",
            "la_dlam_workspace_bytes", "la_decode_step",
            "la_fwd_varlen", "la_fwd_varlen_workspace_bytes", "la_decode_step_paged",
            "la_strerror", "la_version", "la_prof_enable", "la_prof_collect")
@@ -215,6 +219,29 @@ def la_fwd(q, k, v, lam, Bk: int = 64, kv_in=None, out=None, kv_out=None, want_s
                     _ptr(out), _ptr(kv_out), _ptr(ws), nbytes if ws is not None else 0, _stream(q.device))
     if rc != LA_OK:
         raise LaError(rc, "la_fwd")
+    return out, kv_out
+
+
+def la_scratch_bytes() -> int:
+    return int(lib.la_scratch_bytes())
+
+
+def la_fwd_noalloc(q, k, v, lam, out, Bk: int = 64, kv_in=None, kv_out=None, phi="identity"):
+    """la_fwd without a workspace, for callers that cannot allocate: the chunk states go to
+    the library's static per-device scratch (la_scratch_bytes()).  The caller passes the
+    output O (and kv_out, or None to skip the final state); nothing is allocated here.
+    Calls overlapping in time on one device race (they share the scratch)."""
+    _check_seq("Q", q)
+    _check_seq("K", k, q)
+    _check_seq("V", v, q)
+    _check_seq("O", out, q)
+    B, H, N, D = q.shape
+    _check_state("kv_in", kv_in, B, H, D, q.device)
+    _check_state("kv_out", kv_out, B, H, D, q.device)
+    rc = lib.la_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _lam_array(lam, H), B, H, N, D, Bk, _dtype_code(q),
+                            _phi_code(phi), _ptr(kv_in), _ptr(out), _ptr(kv_out), _stream(q.device))
+    if rc != LA_OK:
+        raise LaError(rc, "la_fwd_noalloc")
     return out, kv_out
 
 

@@ -63,6 +63,15 @@ int hip_fail(hipError_t e, const char* where) {
 }
 
 // ------------------------------------------------------------------ profiling
+// While alive on a thread, launches on that thread record no profiling events
+// (la_fwd_noalloc creates no HIP objects).
+thread_local bool g_no_events = false;
+struct NoEventsGuard {
+    bool prev;
+    explicit NoEventsGuard(bool on) : prev(g_no_events) { g_no_events = g_no_events || on; }
+    ~NoEventsGuard() { g_no_events = prev; }
+};
+
 struct ProfRec {
     const char* name;
     hipEvent_t start, stop;
@@ -81,7 +90,7 @@ int launch(const char* name, hipStream_t s, Fn&& fn) {
         if (e1) (void)hipEventDestroy(e1);
         return hip_fail(e, where);
     };
-    const bool prof = g_prof_on.load(std::memory_order_relaxed) != 0;
+    const bool prof = g_prof_on.load(std::memory_order_relaxed) != 0 && !g_no_events;
     if (prof) {
         hipError_t er = hipEventCreate(&e0);
         if (er == hipSuccess) er = hipEventCreate(&e1);
@@ -98,6 +107,38 @@ int launch(const char* name, hipStream_t s, Fn&& fn) {
         std::lock_guard<std::mutex> lk(g_prof_mu);
         g_prof.push_back({name, e0, e1});
     }
+    return LA_OK;
+}
+
+// ------------------------------------------------------------------ static scratch
+// Device memory for la_fwd_noalloc, the entry point for callers that cannot
+// allocate (HIP graph capture, serving loops, harnesses that forbid hipMalloc):
+// its chunk states go here instead of a caller workspace.  Every device holds its
+// own copy of the array, at its own address, until the process ends; the host
+// name `scratch` is only a stand-in, so host code uses the address
+// hipGetSymbolAddress returns for the current device, fetched once per device.
+// Every call on a device shares the array: calls that overlap in time on one
+// device race.  Nothing in it needs to start at zero (the aggregates and the
+// scan write every chunk state before the sweep reads it).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return LA_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress");
+        if (!p) return hip_fail(hipErrorInvalidSymbol, "hipGetSymbolAddress");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return LA_OK;
 }
 
@@ -370,6 +411,48 @@ size_t varlen_slot_bytes(const VarPlan& p, int64_t H, int64_t D) {
     return static_cast<size_t>(p.slots_per_head * H) * static_cast<size_t>(D * D) * sizeof(float);
 }
 
+// la_fwd and la_fwd_noalloc: the same validation and kernels; with use_scratch
+// the chunk states go to the library's static scratch array instead of `ws`.
+int fwd_entry(const void* Q, const void* K, const void* V, const float* lambda, int64_t B, int64_t H,
+              int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t phi, const float* kv_in, void* O,
+              float* kv_out, void* ws, size_t ws_bytes, bool use_scratch, void* hip_stream) {
+    int64_t elems;
+    int rc = check_shape(B, H, N, D, Bk, dtype, &elems);
+    if (rc) return rc;
+    if (!valid_phi(phi)) return LA_EINVAL;
+    if (!Q || !K || !V || !O) return LA_EINVAL;
+    LamArgs lam;
+    if ((rc = load_lambda(lambda, H, &lam))) return rc;
+    for (const void* p : {Q, K, V, static_cast<const void*>(O), static_cast<const void*>(kv_in),
+                          static_cast<const void*>(kv_out), static_cast<const void*>(ws)})
+        if (p && !aligned16(p)) return LA_EALIGN;
+    const size_t tb = static_cast<size_t>(elems) * (dtype == LA_BF16 ? 2 : 4);
+    const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
+    const Plan p = make_plan(B, H, N, D, Bk, dtype);
+    if (!plan_grid_ok(B * H, p, D)) return LA_EUNSUPPORTED;
+    Bk = p.bk;  // the block the kernels step
+    const size_t need = fwd_slot_bytes(B * H, p, D);
+    if (use_scratch) {
+        if (need > kScratchBytes) return LA_ESCRATCH;
+    } else if (need && (!ws || ws_bytes < need)) {
+        return LA_EWORKSPACE;
+    }
+    const Range rq{Q, tb}, rk{K, tb}, rv{V, tb}, ro{O, tb}, rin{kv_in, kv_in ? sb : 0},
+        rout{kv_out, kv_out ? sb : 0}, rws{ws, need};
+    for (const Range& r : {rq, rk, rv, rin})
+        if (overlap(ro, r) || overlap(rout, r) || overlap(rws, r)) return LA_EINVAL;
+    if (overlap(ro, rout) || overlap(ro, rws) || overlap(rout, rws)) return LA_EINVAL;
+
+    int dev_count = 0;
+    if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count == 0) return LA_ENODEV;
+    if (use_scratch && need && (rc = scratch_address(&ws))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const PhiUse pu{phi, 3, 1, nullptr};  // phi(q), phi(k); the aggregates map k
+    const NoEventsGuard quiet(use_scratch);
+    return run_forward_sweep(Q, K, V, O, kv_in, 0, kv_out, static_cast<float*>(ws), nullptr, B * H, N, D,
+                             Bk, static_cast<int32_t>(H), dtype == LA_BF16, p, lam, pu, s, "fwd");
+}
+
 }  // namespace
 
 // ====================================================================== ABI
@@ -390,6 +473,7 @@ const char* la_strerror(int code) {
             return buf;
         }
         case LA_ENODEV: return "no HIP device";
+        case LA_ESCRATCH: return "chunk states exceed the static scratch of la_fwd_noalloc (la_scratch_bytes)";
         default: return "unknown status";
     }
 }
@@ -423,36 +507,18 @@ size_t la_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_
 int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int64_t B, int64_t H,
            int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t phi, const float* kv_in, void* O,
            float* kv_out, void* ws, size_t ws_bytes, void* hip_stream) {
-    int64_t elems;
-    int rc = check_shape(B, H, N, D, Bk, dtype, &elems);
-    if (rc) return rc;
-    if (!valid_phi(phi)) return LA_EINVAL;
-    if (!Q || !K || !V || !O) return LA_EINVAL;
-    LamArgs lam;
-    if ((rc = load_lambda(lambda, H, &lam))) return rc;
-    for (const void* p : {Q, K, V, static_cast<const void*>(O), static_cast<const void*>(kv_in),
-                          static_cast<const void*>(kv_out), static_cast<const void*>(ws)})
-        if (p && !aligned16(p)) return LA_EALIGN;
-    const size_t tb = static_cast<size_t>(elems) * (dtype == LA_BF16 ? 2 : 4);
-    const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
-    const Plan p = make_plan(B, H, N, D, Bk, dtype);
-    if (!plan_grid_ok(B * H, p, D)) return LA_EUNSUPPORTED;
-    Bk = p.bk;  // the block the kernels step
-    const size_t need = fwd_slot_bytes(B * H, p, D);
-    if (need && (!ws || ws_bytes < need)) return LA_EWORKSPACE;
-    const Range rq{Q, tb}, rk{K, tb}, rv{V, tb}, ro{O, tb}, rin{kv_in, kv_in ? sb : 0},
-        rout{kv_out, kv_out ? sb : 0}, rws{ws, need};
-    for (const Range& r : {rq, rk, rv, rin})
-        if (overlap(ro, r) || overlap(rout, r) || overlap(rws, r)) return LA_EINVAL;
-    if (overlap(ro, rout) || overlap(ro, rws) || overlap(rout, rws)) return LA_EINVAL;
-
-    int dev_count = 0;
-    if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count == 0) return LA_ENODEV;
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    const PhiUse pu{phi, 3, 1, nullptr};  // phi(q), phi(k); the aggregates map k
-    return run_forward_sweep(Q, K, V, O, kv_in, 0, kv_out, static_cast<float*>(ws), nullptr, B * H, N, D,
-                             Bk, static_cast<int32_t>(H), dtype == LA_BF16, p, lam, pu, s, "fwd");
+    return fwd_entry(Q, K, V, lambda, B, H, N, D, Bk, dtype, phi, kv_in, O, kv_out, ws, ws_bytes, false,
+                     hip_stream);
 }
+
+int la_fwd_noalloc(const void* Q, const void* K, const void* V, const float* lambda, int64_t B, int64_t H,
+                   int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t phi, const float* kv_in, void* O,
+                   float* kv_out, void* hip_stream) {
+    return fwd_entry(Q, K, V, lambda, B, H, N, D, Bk, dtype, phi, kv_in, O, kv_out, nullptr, 0, true,
+                     hip_stream);
+}
+
+size_t la_scratch_bytes(void) { return kScratchBytes; }
 
 int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const float* lambda, int64_t B,
            int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t phi, const float* kv_in,

@@ -89,7 +89,8 @@ enum {
     LA_EALIGN = 3,       /* a device pointer not 16-byte aligned */
     LA_EWORKSPACE = 4,   /* workspace missing or smaller than the size query returns */
     LA_EHIP = 5,         /* the HIP runtime reported an error (launch, device query) */
-    LA_ENODEV = 6        /* no HIP device is available */
+    LA_ENODEV = 6,       /* no HIP device is available */
+    LA_ESCRATCH = 7      /* la_fwd_noalloc: the call's chunk states exceed la_scratch_bytes() */
 };
 
 /* Forward pass (the tiled forward of Lightning Attention-2: per block an
@@ -112,6 +113,27 @@ enum {
 int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int64_t B, int64_t H,
            int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t phi, const float* kv_in, void* O,
            float* kv_out, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* la_fwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, kernels and arguments as la_fwd without a workspace.  The chunk
+ * states that la_fwd keeps in `ws` go to a static device array of the library
+ * instead, la_scratch_bytes() = 64 MiB per device (held until the process ends).
+ * The call allocates nothing and creates no HIP object (no profiling events).
+ *   Returns LA_ESCRATCH, with nothing enqueued, when the call needs more than
+ *   la_scratch_bytes() (that is, when la_fwd_workspace_bytes(...) would exceed
+ *   it); otherwise the statuses of la_fwd.
+ *   Every call on a device shares that device's array, which keeps the last
+ *   call's contents: calls that overlap in time on one device (different
+ *   streams, or threads without ordering) race and give wrong results.
+ *   Stream-ordered calls are safe.  The array's contents are not an output
+ *   (pass la_fwd's workspace, not this one, to la_bwd as fwd_ws). */
+int la_fwd_noalloc(const void* Q, const void* K, const void* V, const float* lambda, int64_t B, int64_t H,
+                   int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t phi, const float* kv_in, void* O,
+                   float* kv_out, void* hip_stream);
+
+/* Size of la_fwd_noalloc's static scratch array in bytes (per device). */
+size_t la_scratch_bytes(void);
 
 /* Workspace bytes la_fwd needs for this shape (0 when the sequence is not
  * split into chunks).  Returns 0 as well for invalid shapes. */

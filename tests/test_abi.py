@@ -33,7 +33,7 @@ def test_header_symbols_exported():
 
 def test_version_and_strerror():
     assert la.la_version() >= 10000
-    for code in range(7):
+    for code in range(8):
         assert isinstance(la.la_strerror(code), str) and la.la_strerror(code)
     assert "unknown" in la.la_strerror(99)
 
@@ -285,3 +285,33 @@ def test_grid_limit_rejected_before_any_enqueue():
     rc = la.lib.la_decode_step_paged(v(S_), 8, v(IDX_), v(Q_), v(K_), v(V_), lam16, 1 << 19, 16, 16, la.LA_BF16,
                                      0, v(O_), None)
     assert rc == la.LA_EUNSUPPORTED
+
+
+def test_noalloc_scratch_limit():
+    """la_fwd_noalloc rejects, before touching any device, a call whose chunk states exceed
+    the static scratch (LA_ESCRATCH), and validates like la_fwd otherwise."""
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    limit = la.la_scratch_bytes()
+    assert limit == 64 << 20
+    lam = (ctypes.c_float * 64)(*([0.9] * 64))
+
+    def call(B=1, H=64, N=32 * 4 * 64, Q=Q_, O=O_):
+        return la.lib.la_fwd_noalloc(v(Q), v(K_), v(V_), lam, B, H, N, 128, 64, la.LA_BF16, 0, None, v(O),
+                                     None, None)
+    import os
+    old = os.environ.get("LA_CHUNKS")
+    try:
+        os.environ["LA_CHUNKS"] = "32"          # 64 sequences x 31 chunk states x 64 KiB = 124 MiB
+        assert la.la_fwd_workspace_bytes(1, 64, 32 * 4 * 64, 128, 64, la.LA_BF16) > limit
+        assert call() == la.LA_ESCRATCH
+        assert "scratch" in la.la_strerror(la.LA_ESCRATCH)
+        os.environ["LA_CHUNKS"] = "8"           # 64 x 7 x 64 KiB = 28 MiB: fits (then no device here)
+        assert 0 < la.la_fwd_workspace_bytes(1, 64, 32 * 4 * 64, 128, 64, la.LA_BF16) <= limit
+        assert call(Q=None) == la.LA_EINVAL
+        assert call(O=Q_) == la.LA_EINVAL        # output aliases an input
+        assert call(O=O_ + 8) == la.LA_EALIGN
+    finally:
+        if old is None:
+            os.environ.pop("LA_CHUNKS", None)
+        else:
+            os.environ["LA_CHUNKS"] = old
