@@ -55,8 +55,12 @@ DEVICE_FN = {
 }
 KERNEL_SOURCES = {         # device function -> source file its code lives in
     "k_fwd_dma": "k_fwd_dma.hip", "k_fwd_mfma": "k_fwd_mfma.hip", "k_rev_dma": "k_bwd_dma.hip",
+    "k_rev_dma_split": "k_bwd_dma.hip",
     "k_rev_mfma": "k_bwd_mfma.hip", "k_rev_generic": "k_generic.hip", "k_chunk_state_dma": "k_state_dma.hip",
     "k_chunk_state_mfma": "k_fwd_mfma.hip", "k_scan": "k_generic.hip", "k_decode": "k_generic.hip",
+    "k_fwd_dma128": "k_fwd_dma128.hip", "k_fwd_dma_varlen": "k_fwd_dma.hip", "k_dlam_dma": "k_dlam_dma.hip",
+    "k_dlam_state_dma": "k_state_dma.hip", "k_dlam_scan": "k_dlam.hip", "k_dlam_reduce": "k_dlam.hip",
+    "k_chunk_state_dma_varlen": "k_state_dma.hip", "k_scan_varlen": "k_generic.hip",
 }
 
 
@@ -67,9 +71,15 @@ def fwd_flops_per_token_head(d=D, bk=BK):
 
 
 def bwd_flops_per_token_head(d=D, bk=BK):
-    # intra: G = dO V^T, P = Q K^T, dQ, dK, dV products; inter: dO S^T, state rebuild,
-    # V dS^T, K dS and the dS update
-    return 5 * d * (bk + 1) + 10 * d * d
+    # the algorithmic count of the backward: intra G = dO V^T, P = Q K^T and the dQ, dK, dV
+    # products over (Bk+1)/2 keys on average; inter dO S^T, V dS^T, K dS and the dS update
+    return 5 * d * (bk + 1) + 8 * d * d
+
+
+def bwd_flops_executed_per_token_head(d=D, bk=BK):
+    # as executed: the dQ sweep also carries the state S over its blocks (+2 d^2), since only
+    # chunk-start states are kept from the forward
+    return bwd_flops_per_token_head(d, bk) + 2 * d * d
 
 
 def kernel_bytes(name, B, Hh, N, d, chunks, agg=1, with_state=True):
@@ -136,6 +146,42 @@ def device_normal(torch, sid, shape, seed=0):
         host = synth.normal(seed, sid, (n,), 1.0 / math.sqrt(shape[-1]), "bf16", start=s0)
         flat[s0:s0 + n].copy_(torch.from_numpy(host.view(np.int16)))
     return out.view(*shape)
+
+
+# ----------------------------------------------------------------------------- HBM probe
+def hbm_rates(torch, timed):
+    """What this GPU's HBM delivers to plain streaming kernels (torch's own), in GB/s: a 4 GiB
+    read (row sums of a [2^20, 1024] float32 tensor, the fastest read-only torch kernel measured
+    here: a full reduction or a bf16 sum runs at 1-4 TB/s), a 4 GiB write (fill) and a
+    2 + 2 GiB copy (reads and writes mixed 1:1)."""
+    x = torch.empty(1 << 30, dtype=torch.float32, device="cuda")
+    x.fill_(1.0)
+    nbytes = x.numel() * 4
+    rows = x.view(1 << 20, 1 << 10)
+    r_ms = timed(lambda: rows.sum(dim=1), 10)
+    w_ms = timed(lambda: x.fill_(0.5), 10)
+    half = x.numel() // 2
+    a, b = x[:half], x[half:]
+    c_ms = timed(lambda: b.copy_(a), 10)
+    del x, rows, a, b
+    return {"read_gbs": round(nbytes / (r_ms * 1e-3) / 1e9, 1), "write_gbs": round(nbytes / (w_ms * 1e-3) / 1e9, 1),
+            "copy_gbs": round(2 * half * 4 / (c_ms * 1e-3) / 1e9, 1),
+            "note": "torch row-sum / fill / copy kernels over 4 GiB; context for the roofline, not the peak"}
+
+
+def flatness_floor(sweep, rates):
+    """The sweep's forward flatness if every point ran at the probe's read and write rates:
+    a point reads Q, K, V and writes O (reads and writes do not overlap on this HBM), and a
+    point split into C chunks reads K and V of C - 1 chunks once more for the chunk
+    aggregates.  Returns (floor flatness, per-point floor ms)."""
+    r, w = rates["read_gbs"] * 1e9, rates["write_gbs"] * 1e9
+    ms = []
+    for x in sweep:
+        tensor = 2 * D * x["batch"] * H * x["n"]
+        state = x["batch"] * H * D * D * 4
+        extra = 2 * tensor * (x["chunks"] - 1) / x["chunks"] if x["chunks"] > 1 else 0.0
+        ms.append(1e3 * ((3 * tensor + extra) / r + (tensor + state) / w))
+    return max(ms) / min(ms), ms
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -251,6 +297,49 @@ def serving_workload(torch, la, lam, timed):
                     "rate is not an HBM figure"}
 
 
+# ----------------------------------------------------------------------------- breakdowns
+def kernel_breakdown(torch, la, fn, reps):
+    """Per library kernel of one call of fn: launches and average microseconds, from HIP events
+    the library records around each launch on its stream."""
+    torch.cuda.synchronize()
+    la.la_prof_collect()
+    la.la_prof_enable(True)
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    prof = la.la_prof_collect()
+    la.la_prof_enable(False)
+    out = {nm: {"launches_per_call": launches / reps, "avg_us": round(1e3 * total / launches, 2)}
+           for nm, (launches, total) in prof.items()}
+    out["sum_us_per_call"] = round(sum(1e3 * total / reps for _, total in prof.values()), 2)
+    return out
+
+
+def graph_ms(torch, fn, reps):
+    """fn captured once in a HIP graph (torch.cuda.CUDAGraph) and replayed: milliseconds per
+    replay, which leaves out the host side of every launch."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del g
+    return ms
+
+
 # ----------------------------------------------------------------------------- other workloads
 def other_workloads(torch, la, timed):
     """The remaining named workloads, each timed on its own (inputs resident, HIP events):
@@ -270,9 +359,13 @@ def other_workloads(torch, la, timed):
         fn()
         ms = timed(fn, reps)
         byts = 8 * D * B * Hh * N + B * Hh * D * D * 4
+        plan = la.la_plan(B, Hh, N, D, bk, la.LA_BF16)
         out[name] = {"workload": f"bf16 forward B{B} H{Hh} N{N} d{D} block {bk}, per-head decay, final state",
-                     "ms": round(ms, 4), "tokens_per_s": round(B * N / (ms * 1e-3)),
-                     "gbs": round(byts / (ms * 1e-3) / 1e9, 1)}
+                     "plan": plan, "ms": round(ms, 4), "graph_ms": round(graph_ms(torch, fn, reps), 4),
+                     "tokens_per_s": round(B * N / (ms * 1e-3)),
+                     "gbs": round(byts / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_8tbs": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "kernels": kernel_breakdown(torch, la, fn, max(3, reps // 4))}
         del q, k, v, o, s, ws
 
     fwd_case("fwd_b4_h16_n2048", 4, 16, 2048, BK, 50)
@@ -292,13 +385,107 @@ def other_workloads(torch, la, timed):
         la.la_bwd(q, k, v, g, lam_h, BK, dq=dq, dk=dk, dv=dv, ws=ws_b, fwd_ws=ws_f if wf else None)
     train()
     ms = timed(train, 20)
+    byts = (8 + 14) * D * B * Hh * N
     out["train_b2_h32_n8192"] = {"workload": "bf16 fwd+bwd B2 H32 N8192 d128 block 64, per-head decay",
-                                 "ms": round(ms, 4), "tokens_per_s": round(B * N / (ms * 1e-3)),
-                                 "gbs": round((8 + 14) * D * B * Hh * N / (ms * 1e-3) / 1e9, 1)}
+                                 "plan": la.la_plan(B, Hh, N, D, BK, la.LA_BF16),
+                                 "ms": round(ms, 4), "graph_ms": round(graph_ms(torch, train, 20), 4),
+                                 "tokens_per_s": round(B * N / (ms * 1e-3)),
+                                 "gbs": round(byts / (ms * 1e-3) / 1e9, 1),
+                                 "frac_of_8tbs": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                 "kernels": kernel_breakdown(torch, la, train, 5)}
     del q, k, v, g, o, dq, dk, dv, s, ws_f, ws_b
 
     fwd_case("prefill_b1_h64_n262144_block128", 1, 64, 262144, 128, 5)
     return out
+
+
+# ----------------------------------------------------------------------------- counter runs
+def profile_all(args):
+    """One call of every workload, for rocprofv3 counter runs (no timing loops): the sweep step
+    (la_fwd + la_bwd at every n), la_dlam at every n, the bf16 forward B4 H16 N2048, the
+    training step B2 H32 N8192, the long-context prefill B1 H64 N262144 at block 128, the
+    decode step (256 sequences x 64 heads), the ragged prefill and paged decode, and a 1 GiB
+    device copy (the byte counters' calibration).  Prints one line per workload."""
+    import numpy as np
+    import torch
+    import causal_linear_attention_tiled_amd as la
+    import synth
+
+    def say(msg):
+        print(f"[profile-all] {msg}", flush=True)
+
+    lam = synth.decay_schedule(H)
+    only = set(args.only.split(",")) if args.only else None
+    want = lambda name: only is None or name in only
+    for n in SWEEP_N if (want("sweep") or want("dlam")) else ():
+        B = TOKENS_PER_POINT // n
+        q, k, v, g = (device_normal(torch, sid, (B, H, n, D)) for sid in (1, 2, 3, 4))
+        ws_f = torch.empty(max(la.la_fwd_workspace_bytes(B, H, n, D, BK, la.LA_BF16), 1), dtype=torch.uint8,
+                           device="cuda")
+        if want("sweep"):
+            o, s = la.la_fwd(q, k, v, lam, BK, ws=ws_f)
+            la.la_bwd(q, k, v, g, lam, BK, fwd_ws=ws_f if la.la_fwd_workspace_bytes(B, H, n, D, BK, la.LA_BF16)
+                      else None)
+            torch.cuda.synchronize()
+            say(f"sweep n={n}")
+        if want("dlam"):
+            la.la_dlam(q, k, v, g, lam, BK)
+            torch.cuda.synchronize()
+            say(f"dlam n={n}")
+        del q, k, v, g, ws_f
+    if want("fwd2048"):
+        q, k, v = (device_normal(torch, sid, (4, 16, 2048, D)) for sid in (1, 2, 3))
+        la.la_fwd(q, k, v, lam, BK)
+        torch.cuda.synchronize()
+        say("forward B4 H16 N2048")
+        del q, k, v
+    if want("train"):
+        lam32 = synth.decay_schedule(32)
+        q, k, v, g = (device_normal(torch, sid, (2, 32, 8192, D)) for sid in (1, 2, 3, 4))
+        ws_f = torch.empty(max(la.la_fwd_workspace_bytes(2, 32, 8192, D, BK, la.LA_BF16), 1), dtype=torch.uint8,
+                           device="cuda")
+        la.la_fwd(q, k, v, lam32, BK, ws=ws_f)
+        la.la_bwd(q, k, v, g, lam32, BK, fwd_ws=ws_f)
+        torch.cuda.synchronize()
+        say("training step B2 H32 N8192")
+        del q, k, v, g, ws_f
+    if want("prefill"):
+        lam64 = synth.decay_schedule(64)
+        q, k, v = (device_normal(torch, sid, (1, 64, 262144, D)) for sid in (1, 2, 3))
+        la.la_fwd(q, k, v, lam64, 128)
+        torch.cuda.synchronize()
+        say("long-context prefill B1 H64 N262144 block 128")
+        del q, k, v
+    if want("decode"):
+        lam64 = synth.decay_schedule(64)
+        state = torch.zeros((256, 64, D, D), dtype=torch.float32, device="cuda")
+        dq_, dk_, dv_ = (device_normal(torch, 16 + i, (256, 64, D)) for i in range(3))
+        la.la_decode_step(state, dq_, dk_, dv_, lam64)
+        torch.cuda.synchronize()
+        say("decode step 256 x 64")
+        del state, dq_, dk_, dv_
+    if want("serving"):
+        rng = np.random.default_rng(2024)
+        lens = np.exp(rng.uniform(np.log(128), np.log(8192), 64)).astype(np.int64)
+        offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        T = int(offs[-1])
+        qv, kv_, vv = (device_normal(torch, sid, (T, H, D)) for sid in (1, 2, 3))
+        _, sv = la.la_fwd_varlen(qv, kv_, vv, lam, offs, BK)
+        pool = torch.zeros((256, H, D, D), dtype=torch.float32, device="cuda")
+        slots = rng.permutation(256)[:len(lens)]
+        pool[torch.from_numpy(slots).cuda()] = sv
+        slot_of = torch.from_numpy(slots.astype(np.int32)).cuda()
+        d3 = [device_normal(torch, 16 + i, (len(lens), H, D)) for i in range(3)]
+        la.la_decode_step_paged(pool, slot_of, *d3, lam)
+        torch.cuda.synchronize()
+        say(f"ragged prefill ({T} tokens) and paged decode")
+        del qv, kv_, vv, pool, d3
+    if args.calib_copy:
+        src = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        say("calibration copy 1 GiB")
 
 
 # ----------------------------------------------------------------------------- main bench
@@ -487,6 +674,12 @@ def bench(args):
 
     tflops_step = sum((fwd_flops_per_token_head() + bwd_flops_per_token_head()) * TOKENS_PER_POINT * H
                       for _ in SWEEP_N) / (ms_per_step * 1e-3) / 1e12
+    tflops_exec = sum((fwd_flops_per_token_head() + bwd_flops_executed_per_token_head()) * TOKENS_PER_POINT * H
+                      for _ in SWEEP_N) / (ms_per_step * 1e-3) / 1e12
+    rates = hbm_rates(torch, timed)
+    floor, floor_ms = flatness_floor(sweep, rates)
+    for x, f in zip(sweep, floor_ms):
+        x["fwd_floor_ms"] = round(f, 4)
     out = {
         # value: fwd+bwd tokens/s over the whole sweep (131072 tokens per point); the per-point
         # tokens/s, TFLOP/s and % of bf16 peak are under "sweep", the step's under "tflops_alg"
@@ -500,9 +693,16 @@ def bench(args):
                    "tokens_per_step": tokens_per_step, "heads": H, "head_dim": D, "block": BK},
         "tflops_alg": round(tflops_step, 1),
         "pct_bf16_peak": round(100 * tflops_step / BF16_PEAK_TFLOPS, 2),
+        "tflops_alg_counts": "forward 2d(Bk+1)+4d^2, backward 5d(Bk+1)+8d^2 flop per token-head",
+        "tflops_executed_count": round(tflops_exec, 1),
+        "tflops_executed_note": "backward counted with the dQ sweep's own state carry (+2d^2)",
         "roofline": roofline,
         "sweep": sweep,
         "fwd_flatness": round(max(fwd_tps) / min(fwd_tps), 3),
+        "fwd_flatness_floor": round(floor, 3),
+        "fwd_flatness_floor_note": "the forward's flatness if every sweep point ran at hbm_rates (reads and "
+                                   "writes not overlapping), with the chunk aggregates' extra reads of K, V",
+        "hbm_rates": rates,
         "kernels": kernels,
         "decode": decode,
         "serving": serving,
@@ -534,6 +734,44 @@ def _counter_means(dirname, counter):
     return {k: (len(v), sum(v) / len(v)) for k, v in by.items()}
 
 
+def _fn(kernel_name):
+    """Device function of a demangled kernel name ('k_fwd_dma' from '... ::k_fwd_dma<4, false>(...)'),
+    else the name up to its argument list."""
+    import re
+    m = re.search(r"(k_[A-Za-z0-9_]+)\s*[<(]", kernel_name)
+    return m.group(1) if m else kernel_name.split("(")[0][-60:]
+
+
+def _dispatch_table(dirname):
+    """{dispatch id: {"fn", "name", "grid", counters...}} from a --pmc run (with or without a
+    kernel trace in the same directory; durations in ns when one is there)."""
+    rows = _csv(dirname, "counter_collection.csv")
+    disp = {}
+    for r in rows:
+        did = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        d = disp.setdefault(did, {"fn": _fn(r["Kernel_Name"]), "name": r["Kernel_Name"],
+                                  "grid": int(float(r.get("Grid_Size", 0) or 0))})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+            d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    try:
+        trace = _csv(dirname, "kernel_trace.csv")
+    except SystemExit:
+        trace = []
+    for r in trace:
+        did = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        if did in disp:
+            disp[did]["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    return disp
+
+
+def _groups(disp, key):
+    by = {}
+    for d in disp.values():
+        by.setdefault(key(d), []).append(d)
+    return by
+
+
 def summarize(args):
     """Summarize rocprofv3 output into short text files (see --help).
 
@@ -556,30 +794,70 @@ def summarize(args):
         for k, (n, mean) in sorted(_counter_means(args.dir, counter).items()):
             lines.append(f"{k[:110]} | {n} | {mean:.1f}")
         out = os.path.join(args.out, f"counters_{args.tag}_{args.kind}.txt")
+    elif args.kind == "pmc":
+        # every counter of the run, mean per dispatch, per (device function, grid size)
+        disp = _dispatch_table(args.dir)
+        names = sorted({k for d in disp.values() for k in d if k not in ("fn", "name", "grid", "ns")})
+        lines.append("function | grid | dispatches | " + " | ".join(f"mean {n}" for n in names))
+        for (fn, grid), ds in sorted(_groups(disp, lambda d: (d["fn"], d["grid"])).items()):
+            means = [sum(d.get(n, 0.0) for d in ds) / len(ds) for n in names]
+            lines.append(f"{fn} | {grid} | {len(ds)} | " + " | ".join(f"{m:.4g}" for m in means))
+        out = os.path.join(args.out, f"counters_{args.tag}_{args.name}.txt")
+    elif args.kind == "mfma":
+        # matrix-core work against the bf16 dense peak: rocprof's MfmaFlopsBF16 (MOPS x 512),
+        # MfmaUtil, VALUBusy and LdsUtil per dispatch, with the dispatch durations of the same run
+        disp = _dispatch_table(args.dir)
+        lines.append(f"peak: {BF16_PEAK_TFLOPS} TFLOP/s bf16 dense (MI355X published)")
+        lines.append("function | grid | dispatches | avg_us | mfma_gflop_per_dispatch | mfma_tflops | "
+                     "pct_bf16_peak | MfmaUtil | VALUBusy | LdsUtil | source_sha256_16")
+
+        def row(label, grid, ds):
+            ns = sum(d.get("ns", 0.0) for d in ds)
+            fl = sum(d.get("MfmaFlopsBF16", 0.0) for d in ds)
+            w = lambda key: (sum(d.get(key, 0.0) * d.get("ns", 0.0) for d in ds) / ns) if ns else float("nan")
+            tf = fl / ns / 1e3 if ns else float("nan")
+            return (f"{label} | {grid} | {len(ds)} | {ns / len(ds) / 1e3:.2f} | {fl / len(ds) / 1e9:.3f} | "
+                    f"{tf:.1f} | {100 * tf / BF16_PEAK_TFLOPS:.2f} | {w('MfmaUtil'):.2f} | {w('VALUBusy'):.2f} | "
+                    f"{w('LdsUtil'):.2f} | {source_digest(label)}")
+        for (fn, grid), ds in sorted(_groups(disp, lambda d: (d["fn"], d["grid"])).items()):
+            lines.append(row(fn, grid, ds))
+        lines.append("# totals per device function (durations summed, utilisations duration-weighted)")
+        for fn, ds in sorted(_groups(disp, lambda d: d["fn"]).items()):
+            lines.append(row(fn, "all", ds))
+        out = os.path.join(args.out, f"mfma_{args.tag}.txt")
     else:
-        fetch = _counter_means(args.fetch, "FETCH_SIZE")
-        write = _counter_means(args.write, "WRITE_SIZE")
+        fetch = _dispatch_table(args.fetch)
+        write = _dispatch_table(args.write)
         sym = args.kernel
-        pick = lambda d, sub: [v for k, v in d.items() if sub in k]
-        copy_f = pick(fetch, "copy") or pick(fetch, "elementwise")
-        copy_w = pick(write, "copy") or pick(write, "elementwise")
-        kf, kw = pick(fetch, sym), pick(write, sym)
+
+        def pick(disp, counter, match):
+            ds = [d for d in disp.values() if match(d) and counter in d]
+            return (len(ds), sum(d[counter] for d in ds) / len(ds)) if ds else None
+        is_copy = lambda d: "copy" in d["name"] or "elementwise" in d["name"]
+        is_k = lambda d: d["fn"] == sym and (not args.grid or d["grid"] == args.grid)
+        copy_f = [d["FETCH_SIZE"] for d in fetch.values() if is_copy(d) and "FETCH_SIZE" in d]
+        copy_w = [d["WRITE_SIZE"] for d in write.values() if is_copy(d) and "WRITE_SIZE" in d]
+        kf, kw = pick(fetch, "FETCH_SIZE", is_k), pick(write, "WRITE_SIZE", is_k)
         if not (copy_f and copy_w and kf and kw):
             raise SystemExit("kernel or calibration copy missing from the counter runs")
         calib_kib = CALIB_BYTES / 1024
-        f_fetch = calib_kib / max(v[1] for v in copy_f)
-        f_write = calib_kib / max(v[1] for v in copy_w)
-        fetch_b = kf[0][1] * f_fetch * 1024
-        write_b = kw[0][1] * f_write * 1024
-        lines += [f"kernel: {args.kernel} (every dispatch whose device function name contains it)",
-                  f"dispatches: {kf[0][0]}",
-                  f"fetch_kib_per_dispatch_raw: {kf[0][1]:.1f}",
-                  f"write_kib_per_dispatch_raw: {kw[0][1]:.1f}",
+        f_fetch = calib_kib / max(copy_f)
+        f_write = calib_kib / max(copy_w)
+        fetch_b = kf[1] * f_fetch * 1024
+        write_b = kw[1] * f_write * 1024
+        lines += [f"kernel: {args.kernel} (dispatches of that device function"
+                  + (f" with grid size {args.grid})" if args.grid else ")"),
+                  f"dispatches: {kf[0]}",
+                  f"fetch_kib_per_dispatch_raw: {kf[1]:.1f}",
+                  f"write_kib_per_dispatch_raw: {kw[1]:.1f}",
                   f"calibration: 1 GiB device copy; FETCH_SIZE scale {f_fetch:.4f}, WRITE_SIZE scale {f_write:.4f}",
                   f"hbm_fetch_bytes_per_launch: {fetch_b:.0f}",
                   f"hbm_write_bytes_per_launch: {write_b:.0f}",
                   f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
                   f"source_sha256_16: {source_digest(args.kernel)}"]
+        if args.alg_bytes:
+            lines.append(f"algorithmic_bytes_per_launch: {args.alg_bytes:.0f}")
+            lines.append(f"measured_over_algorithmic: {(fetch_b + write_b) / args.alg_bytes:.4f}")
         out = os.path.join(args.out, f"{args.kernel}_{args.tag}_traffic.txt")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -595,18 +873,28 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--quick", action="store_true", help="timed steps only (for profiled runs)")
     ap.add_argument("--calib-copy", action="store_true", help="also run a 1 GiB device copy")
+    ap.add_argument("--profile-all", action="store_true",
+                    help="one call of every workload and nothing timed (for rocprofv3 counter runs)")
+    ap.add_argument("--only", default="", help="--profile-all: comma-separated subset of "
+                    "sweep,dlam,fwd2048,train,prefill,decode,serving")
     ap.add_argument("--out", default=PROFILES, help="summarize: output directory")
     ap.add_argument("--fetch", default="", help="summarize --kind traffic: FETCH_SIZE run dir")
     ap.add_argument("--write", default="", help="summarize --kind traffic: WRITE_SIZE run dir")
     ap.add_argument("--kernel", default="k_fwd_dma", help="summarize --kind traffic: device function")
     ap.add_argument("summarize", nargs="?", help=argparse.SUPPRESS)
-    ap.add_argument("--kind", choices=["stats", "fetch", "write", "traffic"], default="stats")
+    ap.add_argument("--kind", choices=["stats", "fetch", "write", "traffic", "pmc", "mfma"], default="stats")
+    ap.add_argument("--name", default="pmc", help="summarize --kind pmc: file name part")
+    ap.add_argument("--grid", type=int, default=0, help="summarize --kind traffic: only dispatches of this grid size")
+    ap.add_argument("--alg-bytes", type=float, default=0.0,
+                    help="summarize --kind traffic: algorithmic bytes per launch, for the ratio")
     ap.add_argument("--dir", default="")
     ap.add_argument("--tag", default="sweep")
     ap.add_argument("--command", default="")
     args = ap.parse_args()
     if args.summarize == "summarize":
         return summarize(args)
+    if args.profile_all:
+        return profile_all(args)
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the library has no multi-GPU "
                                    "path (sequences would shard by batch and head, or by sequence "

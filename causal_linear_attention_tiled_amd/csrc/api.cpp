@@ -316,7 +316,8 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
         else
             rc = launch("chunk_state_generic", s, [&] { la::launch_chunk_state_generic(cs, lam, bf16, s); });
         if (rc) return rc;
-        la::ScanArgs sc{slots, kv_in, kv_in_t, nullptr, N, Lf, static_cast<int>(D), H, chunks_f, pairs, 0};
+        la::ScanArgs sc{slots, kv_in, kv_in_t, nullptr, N, Lf, static_cast<int>(D), H, chunks_f, pairs, 0, 0,
+                        p.agg_k};
         rc = launch("state_scan", s, [&] { la::launch_scan(sc, lam, s); });
         if (rc) return rc;
     }
@@ -341,8 +342,17 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
     a.phi_mask = phi.sweep_mask;
     a.phi_grad = phi.grad;
     a.slot_k = p.agg_k;
-    if (p.mfma && la::fwd_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_FWD", "v1")) {
+    // A 128-token block is stepped as two 64-token blocks by the 64-token kernel: the same
+    // function (the block size only decides which terms pass through a score tile and which
+    // through the carried state), the same bytes, and on this GPU the faster sweep (its LDS
+    // ring holds two 64-token blocks of look-ahead, where the 128-token kernel holds half a
+    // block).  The chunk boundaries stay on multiples of 128.  LA_FWD128=1 selects the
+    // 128-token kernel.
+    const bool step128 = Bk == 128 && env_is("LA_FWD128", "1");
+    const int32_t sweep_bk = (Bk == 128 && !step128) ? 64 : Bk;
+    if (p.mfma && la::fwd_dma_supported(static_cast<int>(D), sweep_bk, N) && !env_is("LA_FWD", "v1")) {
         const int waves = env_is("LA_FWD_WAVES", "8") ? 8 : 4;
+        a.Bk = sweep_bk;
         return launch(tag[0] == 'd' ? "dq_dma" : "fwd_dma", s, [&] { la::launch_fwd_dma(a, lam, waves, s); });
     }
     if (p.mfma && la::fwd_dma128_supported(static_cast<int>(D), Bk, N) && !env_is("LA_FWD", "v1"))
@@ -589,7 +599,7 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
             rc = launch("chunk_state_rev_generic", s, [&] { la::launch_chunk_state_generic(cs, lam, bf16, s); });
         if (rc) return rc;
         la::ScanArgs sc{slots_kv, nullptr, 0, dkv_out, N, Lf, static_cast<int>(D), Hi, chunks_f, pairs, 1,
-                        p.agg_k - 1};
+                        p.agg_k - 1, p.agg_k};
         rc = launch("state_scan_rev", s, [&] { la::launch_scan(sc, lam, s); });
         if (rc) return rc;
     }

@@ -230,60 +230,83 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state_generic(ChunkStateArgs
 constexpr int kScanBatch = 8;  // chunk slots whose loads a scan thread keeps in flight
 
 __global__ __launch_bounds__(kThreads) void k_scan(ScanArgs a, LamArgs lam) {
-    const int DD = a.D * a.D;
-    const int per_pair = (DD + kThreads - 1) / kThreads;
+    // one thread per 4 consecutive elements of the D x D state (D * D is a multiple of 4)
+    const int DD = a.D * a.D, DD4 = DD / 4;
+    const int per_pair = (DD4 + kThreads - 1) / kThreads;
     const int64_t pair = blockIdx.x / per_pair;
-    const int e = (blockIdx.x % per_pair) * kThreads + threadIdx.x;
-    if (e >= DD) return;
+    const int e4 = (blockIdx.x % per_pair) * kThreads + threadIdx.x;
+    if (e4 >= DD4) return;
+    const int e = 4 * e4;
     const float lv = lam.lam[pair % a.H];
     const float lamL = lam_pow(lv, a.L);
     const int n = a.chunks - 1;
-    float* sl = a.slots + pair * n * DD + e;
+    const int keep = a.keep > 1 ? a.keep : 1;
+    float4* sl = reinterpret_cast<float4*>(a.slots + pair * n * DD + e);
+    auto slot = [&](int c) -> float4& { return sl[static_cast<int64_t>(c) * DD4]; };
     // Each batch's loads are issued before any of its stores: the slots are distinct,
     // which the compiler cannot see, and a memory latency per slot would dominate.
-    float x[kScanBatch];
+    float4 x[kScanBatch];
     if (!a.reverse) {
-        float S = 0.f;
+        float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
         if (a.kv_in) {
             const float* src = a.kv_in + pair * DD;
-            S = a.kv_in_transposed ? src[(e % a.D) * a.D + e / a.D] : src[e];
+            if (a.kv_in_transposed) {
+                const int r = e / a.D, col = e % a.D;
+                S = make_float4(src[col * a.D + r], src[(col + 1) * a.D + r], src[(col + 2) * a.D + r],
+                                src[(col + 3) * a.D + r]);
+            } else {
+                S = *reinterpret_cast<const float4*>(src + e);
+            }
         }
         for (int c0 = 0; c0 < n; c0 += kScanBatch) {
 #pragma unroll
-            for (int j = 0; j < kScanBatch; ++j) x[j] = c0 + j < n ? sl[static_cast<int64_t>(c0 + j) * DD] : 0.f;
-#pragma unroll
             for (int j = 0; j < kScanBatch; ++j)
-                if (c0 + j < n) {
-                    S = lamL * S + x[j];
-                    sl[static_cast<int64_t>(c0 + j) * DD] = S;
+                if (c0 + j < n) x[j] = slot(c0 + j);
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j) {
+                const int c = c0 + j;
+                if (c < n) {
+                    S.x = lamL * S.x + x[j].x;
+                    S.y = lamL * S.y + x[j].y;
+                    S.z = lamL * S.z + x[j].z;
+                    S.w = lamL * S.w + x[j].w;
+                    // only the slots a sweep reads: the state entering chunk (c + 1) / keep
+                    if ((c + 1) % keep == 0) slot(c) = S;
                 }
+            }
         }
     } else {
         // the final-state gradient enters at the last token undecayed, so it reaches the
         // start of chunk j decayed over N - 1 - j L tokens
-        const float G = a.g_final ? a.g_final[pair * DD + e] : 0.f;
+        const float4 G = a.g_final ? *reinterpret_cast<const float4*>(a.g_final + pair * DD + e)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
         auto start_of = [&](int c) { return (static_cast<int64_t>(c) + 1 + a.part0) * a.L; };
-        float R = 0.f;
+        float4 R = make_float4(0.f, 0.f, 0.f, 0.f);
         bool started = false;
         for (int c1 = n - 1; c1 >= 0; c1 -= kScanBatch) {
 #pragma unroll
             for (int j = 0; j < kScanBatch; ++j) {
                 const int c = c1 - j;
-                x[j] = (c >= 0 && start_of(c) < a.N) ? sl[static_cast<int64_t>(c) * DD] : 0.f;
+                x[j] = (c >= 0 && start_of(c) < a.N) ? slot(c) : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
             for (int j = 0; j < kScanBatch; ++j) {
                 const int c = c1 - j;
                 if (c < 0) break;
-                float* p = sl + static_cast<int64_t>(c) * DD;
+                const bool store = c % keep == 0;  // the slots a sweep reads: chunk c / keep ends here
                 const int64_t start = start_of(c);
                 if (start >= a.N) {
-                    *p = 0.f;  // a part past the end of the sequence
+                    if (store) slot(c) = make_float4(0.f, 0.f, 0.f, 0.f);  // a part past the end
                     continue;
                 }
-                R = started ? x[j] + lamL * R : x[j] + lam_pow(lv, a.N - 1 - start) * G;
+                const float f = started ? lamL : lam_pow(lv, a.N - 1 - start);
+                const float4 prev = started ? R : G;
+                R.x = x[j].x + f * prev.x;
+                R.y = x[j].y + f * prev.y;
+                R.z = x[j].z + f * prev.z;
+                R.w = x[j].w + f * prev.w;
                 started = true;
-                *p = R;
+                if (store) slot(c) = R;
             }
         }
     }
@@ -408,7 +431,7 @@ void launch_scan_varlen(const ScanArgs& a, const LamArgs& lam, const ScanList& l
 }
 
 void launch_scan(const ScanArgs& a, const LamArgs& lam, hipStream_t s) {
-    const int per_pair = (a.D * a.D + kThreads - 1) / kThreads;
+    const int per_pair = (a.D * a.D / 4 + kThreads - 1) / kThreads;
     dim3 grid(static_cast<unsigned>(a.pairs * per_pair));
     hipLaunchKernelGGL(k_scan, grid, dim3(kThreads), 0, s, a, lam);
 }

@@ -115,6 +115,9 @@ struct ScanArgs {
     int64_t pairs;
     int reverse;
     int part0;
+    int keep;             // k_scan: slots a sweep reads are every keep-th (chunk boundaries of
+                          // aggregates over keep parts per chunk); only those are written
+                          // (0 or 1: every slot)
 };
 
 struct DecodeArgs {
@@ -184,7 +187,8 @@ void launch_fwd_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream
 // The same over a ragged batch: one workgroup per (chunk of a sequence, head), wp[nseq] * H in all.
 void launch_fwd_dma_varlen(const SweepArgs& a, const LamArgs& lam, const VarlenArgs& v, hipStream_t s);
 
-// The same with 128-token blocks (k_fwd_dma128.hip; bf16, D = 128, Bk = 128): a ring of
+// The same with 128-token blocks (k_fwd_dma128.hip; bf16, D = 128, Bk = 128; selected with
+// LA_FWD128=1, otherwise a 128-token block is stepped by the 64-token kernel): a ring of
 // 64-token half blocks, each block computed in two phases.
 bool fwd_dma128_supported(int D, int Bk, int64_t N);
 void launch_fwd_dma128(const SweepArgs& a, const LamArgs& lam, hipStream_t s);

@@ -39,18 +39,19 @@
  *  - Supported: D in {16, 32, 64, 128}, block size Bk in {16, 32, 64, 128,
  *    256}, 1 <= H <= 256, any N >= 1 (the last block may be partial).  The
  *    block size never changes the result beyond float rounding.  For bf16
- *    with D = 128 the forward-direction sweeps (la_fwd, the dQ sweep of
- *    la_bwd) take 64- or 128-token blocks as asked; the dK, dV sweep of
- *    la_bwd and the sweep of la_dlam step a 128-token block as two 64-token
- *    halves (the same function, with the second half's share of the first
- *    half's gradients carried through the state instead of a score tile).
- *    Bk = 256 places the chunk boundaries of the chunked prefix on multiples
- *    of 256 tokens; the kernels then step it as they step Bk = 128.
+ *    with D = 128 every sweep steps 64-token blocks: a 128-token block is
+ *    stepped as two 64-token halves (the same function, with the second
+ *    half's share of the first half's terms carried through the state
+ *    instead of a score tile), and Bk only places the chunk boundaries of the
+ *    chunked prefix on multiples of Bk.  LA_FWD128=1 runs the forward-
+ *    direction sweeps (la_fwd, the dQ sweep of la_bwd) on whole 128-token
+ *    blocks instead.  Bk = 256 is stepped as Bk = 128.
  *  - The environment variable LA_CHUNKS (a positive integer) overrides the
  *    number of chunks a sequence is split into for the chunked prefix over
  *    blocks, LA_AGG_K the number of parts of a chunk the chunk aggregates are
  *    taken over (la_plan); LA_KERNEL=generic forces the generic (non-MFMA)
- *    kernels; LA_FWD_WAVES=8, LA_REV_WAVES=4 and LA_DLAM_WAVES=4 select the
+ *    kernels; LA_FWD128=1 the 128-token-block forward-direction sweep;
+ *    LA_FWD_WAVES=8, LA_REV_WAVES=4 and LA_DLAM_WAVES=4 select the
  *    other wave counts of the bf16 D = 128 direct-to-LDS sweeps (forward and
  *    dQ, dK and dV, decay derivative).  They exist for tests and tuning; a
  *    query of the workspace size must be made under the same setting as the

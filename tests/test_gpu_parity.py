@@ -500,3 +500,26 @@ def test_non_finite_inputs_propagate(kern, kernel):
     assert np.array_equal(ok_[:128], ref[:128])
     assert not np.any(np.isfinite(ok_[130:]).all(axis=1))
     assert not np.all(np.isfinite(got(s_k)))
+
+
+# ------------------------------------------------------------------ the 128-token-block forward kernel
+@pytest.fixture
+def fwd128(monkeypatch):
+    """LA_FWD128=1: forward-direction sweeps with Bk = 128 (and 256) run the 128-token-block kernel
+    instead of stepping each block as two 64-token blocks."""
+    monkeypatch.setenv("LA_FWD128", "1")
+
+
+@pytest.mark.parametrize("Bk,cks,N,with_state", [(128, 1, 1000, True), (128, 3, 128 * 9 + 17, True),
+                                                 (256, 2, 256 * 5 + 17, False), (128, 5, 128 * 9 + 17, False)])
+def test_block128_kernel_parity(fwd128, chunks, Bk, cks, N, with_state):
+    chunks(cks)
+    lam = synth.decay_schedule(3)
+    check_fwd(2, 3, N, 128, Bk, "bf16", lam, seed=N + Bk, with_state=with_state, label="dma128")
+    check_bwd(1, 3, N, 128, Bk, "bf16", lam, seed=N + Bk, with_state=with_state, label="dma128", fwd_ws=True)
+
+
+@pytest.mark.parametrize("lam_val", [1.0, 0.5])
+@pytest.mark.parametrize("Bk,cks", [(128, 3), (256, 2)])
+def test_block128_kernel_impulse(fwd128, lam_val, Bk, cks, chunks, kernel):
+    test_impulse_probe_bit_exact("default", lam_val, Bk, cks, chunks, kernel)

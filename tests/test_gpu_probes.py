@@ -35,11 +35,13 @@ def assert_exact(name, y, ref, pairs=None):
 @pytest.fixture
 def env(monkeypatch):
     """Kernel selection: 'default', 'generic' (plain float32 kernels), 'v1' (register-staged
-    matrix-core kernels), 'w4' (4-wave forward and reverse sweeps), 'w8' (8-wave forward)."""
+    matrix-core kernels), 'w4' (4-wave forward and reverse sweeps), 'w8' (8-wave forward),
+    'dma128' (the 128-token-block forward-direction sweep for Bk = 128 and 256)."""
     def set_(kernel="default", chunks=None, agg=None):
         vals = {"LA_KERNEL": "generic" if kernel == "generic" else None,
                 "LA_FWD": "v1" if kernel == "v1" else None, "LA_REV": "v1" if kernel == "v1" else None,
                 "LA_STATE": "v1" if kernel == "v1" else None,
+                "LA_FWD128": "1" if kernel == "dma128" else None,
                 "LA_FWD_WAVES": {"w4": "4", "w8": "8"}.get(kernel),
                 "LA_REV_WAVES": {"w4": "4", "w8": "8"}.get(kernel),
                 "LA_CHUNKS": chunks, "LA_AGG_K": agg}
@@ -107,6 +109,16 @@ def test_bwd_impulse_kernel_variants(env, kern, lam_val):
     """The register-staged kernels and the 4- and 8-wave sweeps, chunked with parts."""
     env(kernel=kern, chunks=3, agg=2)
     run_bwd_probe(64, lam_val, with_state=True, with_gf=True, use_fwd_ws=True, label=kern)
+
+
+@pytest.mark.parametrize("Bk,cks,agg", [(128, 3, None), (128, 2, 2), (256, 2, None)])
+@pytest.mark.parametrize("lam_val", [0.5, 1.0])
+@pytest.mark.parametrize("use_fwd_ws", [False, True])
+def test_bwd_impulse_block128_kernel(env, Bk, cks, agg, lam_val, use_fwd_ws):
+    """The dQ sweep on the 128-token-block kernel (LA_FWD128=1), with and without the forward's
+    chunk states (the forward then on that kernel too)."""
+    env(kernel="dma128", chunks=cks, agg=agg)
+    run_bwd_probe(Bk, lam_val, with_state=True, with_gf=True, use_fwd_ws=use_fwd_ws, label="dma128")
 
 
 # ------------------------------------------------------------------ la_dlam
