@@ -267,6 +267,38 @@ size_t fwd_slot_bytes(int64_t pairs, const Plan& p, int64_t D) {
 
 size_t round_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// la_fwd's workspace: the chunk states, then (from a 256-byte boundary) the stamp.
+constexpr size_t kStampBytes = 256;
+size_t fwd_ws_bytes(int64_t pairs, const Plan& p, int64_t D) {
+    const size_t slots = fwd_slot_bytes(pairs, p, D);
+    return slots ? round_up(slots) + kStampBytes : 0;
+}
+
+uint32_t fnv1a(uint32_t h, const void* data, size_t n) {
+    const unsigned char* b = static_cast<const unsigned char*>(data);
+    for (size_t i = 0; i < n; ++i) h = (h ^ b[i]) * 16777619u;
+    return h;
+}
+
+// What identifies the chunk states of one forward pass: shape, block size, dtype, feature
+// map, chunk plan, decay values and the addresses of Q, K, V and kv_in.
+la::Stamp make_stamp(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t phi,
+                     const Plan& p, const LamArgs& lam, const void* Q, const void* K, const void* V,
+                     const float* kv_in) {
+    la::Stamp st{};
+    st.w[0] = 0x4c414653u;  // "LAFS"
+    st.w[1] = static_cast<uint32_t>(N) ^ static_cast<uint32_t>(N >> 32);
+    st.w[2] = static_cast<uint32_t>(B * H) ^ static_cast<uint32_t>((B * H) >> 32) ^ (static_cast<uint32_t>(H) << 20);
+    st.w[3] = static_cast<uint32_t>(D) | (static_cast<uint32_t>(Bk) << 8) | (static_cast<uint32_t>(dtype) << 20) |
+              (static_cast<uint32_t>(phi) << 24);
+    st.w[4] = static_cast<uint32_t>(p.chunks) | (static_cast<uint32_t>(p.agg_k) << 24);
+    st.w[5] = static_cast<uint32_t>(p.L) ^ static_cast<uint32_t>(p.L >> 32);
+    st.w[6] = fnv1a(2166136261u, lam.lam, sizeof(float) * static_cast<size_t>(H));
+    const void* ptrs[4] = {Q, K, V, kv_in};
+    st.w[7] = fnv1a(2166136261u, ptrs, sizeof(ptrs));
+    return st;
+}
+
 // Largest workgroup count any launch of a chunked call makes: the sweeps (one per
 // sequence and chunk), the aggregates (agg_k per chunk boundary) and the scans
 // (D * D / 256 per sequence).
@@ -296,10 +328,14 @@ struct PhiUse {
     const void* grad;  // raw tensor whose phi' multiplies the sweep's output, or nullptr
 };
 
+// `stamp_out` (forward pass): where the scan stores `stamp` after the chunk states;
+// `stamp_in` (dQ sweep fed `given`): the stamp stored after those states, checked
+// against `stamp`.
 int run_forward_sweep(const void* q, const void* k, const void* v, void* out, const float* kv_in,
                       int kv_in_t, float* kv_out, float* slots, const float* given, int64_t pairs,
                       int64_t N, int64_t D, int32_t Bk, int32_t H, int bf16, const Plan& p,
-                      const LamArgs& lam, const PhiUse& phi, hipStream_t s, const char* tag) {
+                      const LamArgs& lam, const PhiUse& phi, hipStream_t s, const char* tag,
+                      uint32_t* stamp_out, const uint32_t* stamp_in, const la::Stamp& stamp) {
     int rc;
     // the register-staged kernels have no feature map: with one, the generic kernels run
     const bool v1_ok = phi.kind == 0;
@@ -318,6 +354,8 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
         if (rc) return rc;
         la::ScanArgs sc{slots, kv_in, kv_in_t, nullptr, N, Lf, static_cast<int>(D), H, chunks_f, pairs, 0, 0,
                         p.agg_k};
+        sc.stamp_out = stamp_out;
+        sc.stamp = stamp;
         rc = launch("state_scan", s, [&] { la::launch_scan(sc, lam, s); });
         if (rc) return rc;
     }
@@ -328,6 +366,8 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
     a.out0 = out;
     a.slots = given ? given : slots;
     a.slots_transposed = given ? 1 : 0;
+    a.stamp = given ? stamp_in : nullptr;
+    a.expect = stamp;
     a.kv_in = kv_in;
     a.kv_in_transposed = kv_in_t;
     a.kv_out = kv_out;
@@ -440,8 +480,10 @@ int fwd_entry(const void* Q, const void* K, const void* V, const float* lambda, 
     const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
     if (!plan_grid_ok(B * H, p, D)) return LA_EUNSUPPORTED;
+    const int32_t Bk_call = Bk;  // as asked (the stamp records it)
     Bk = p.bk;  // the block the kernels step
-    const size_t need = fwd_slot_bytes(B * H, p, D);
+    // the static scratch holds the chunk states only; a caller workspace also the stamp
+    const size_t need = use_scratch ? fwd_slot_bytes(B * H, p, D) : fwd_ws_bytes(B * H, p, D);
     if (use_scratch) {
         if (need > kScratchBytes) return LA_ESCRATCH;
     } else if (need && (!ws || ws_bytes < need)) {
@@ -459,8 +501,13 @@ int fwd_entry(const void* Q, const void* K, const void* V, const float* lambda, 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const PhiUse pu{phi, 3, 1, nullptr};  // phi(q), phi(k); the aggregates map k
     const NoEventsGuard quiet(use_scratch);
+    uint32_t* stamp_out = (!use_scratch && need)
+                              ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + round_up(fwd_slot_bytes(B * H, p, D)))
+                              : nullptr;
+    const la::Stamp stamp = make_stamp(B, H, N, D, Bk_call, dtype, phi, p, lam, Q, K, V, kv_in);
     return run_forward_sweep(Q, K, V, O, kv_in, 0, kv_out, static_cast<float*>(ws), nullptr, B * H, N, D,
-                             Bk, static_cast<int32_t>(H), dtype == LA_BF16, p, lam, pu, s, "fwd");
+                             Bk, static_cast<int32_t>(H), dtype == LA_BF16, p, lam, pu, s, "fwd", stamp_out,
+                             nullptr, stamp);
 }
 
 }  // namespace
@@ -504,7 +551,7 @@ size_t la_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_
     int64_t elems;
     if (check_shape(B, H, N, D, Bk, dtype, &elems) != LA_OK) return 0;
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
-    return fwd_slot_bytes(B * H, p, D);
+    return fwd_ws_bytes(B * H, p, D);
 }
 
 size_t la_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype) {
@@ -549,6 +596,7 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
     if (!plan_grid_ok(B * H, p, D)) return LA_EUNSUPPORTED;
+    const la::Stamp stamp = make_stamp(B, H, N, D, Bk, dtype, phi, p, lam, Q, K, V, kv_in);
     Bk = p.bk;  // the block the kernels step
     // chunk states of the dQ sweep (forward direction) and of the dK, dV sweep (reverse
     // direction), both over agg_k parts per chunk boundary
@@ -556,7 +604,7 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     const size_t need = round_up(fq) + round_up(rv);
     if (need && (!ws || ws_bytes < need)) return LA_EWORKSPACE;
     const Range ins[] = {{Q, tb}, {K, tb}, {V, tb}, {dO, tb}, {kv_in, kv_in ? sb : 0},
-                         {dkv_out, dkv_out ? sb : 0}, {fwd_ws, fwd_ws ? fq : 0}};
+                         {dkv_out, dkv_out ? sb : 0}, {fwd_ws, fwd_ws ? fwd_ws_bytes(B * H, p, D) : 0}};
     const Range outs[] = {{dQ, tb}, {dK, tb}, {dV, tb}, {dkv_in, dkv_in ? sb : 0}, {ws, need}};
     constexpr int kOuts = sizeof(outs) / sizeof(outs[0]);
     for (const Range& o : outs)
@@ -579,8 +627,10 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     // the dQ sweep: phi(k) in the value slot, its own aggregates over (v, phi(k)), and
     // phi'(q) on the output
     const PhiUse pu{phi, 4, 2, phi ? Q : nullptr};
+    const uint32_t* stamp_in =
+        (fwd_ws && fq) ? reinterpret_cast<const uint32_t*>(static_cast<const char*>(fwd_ws) + round_up(fq)) : nullptr;
     rc = run_forward_sweep(dO, V, K, dQ, kv_in, 1, nullptr, slots_q, static_cast<const float*>(fwd_ws), pairs,
-                           N, D, Bk, Hi, bf16, p, lam, pu, s, "dq");
+                           N, D, Bk, Hi, bf16, p, lam, pu, s, "dq", nullptr, stamp_in, stamp);
     if (rc) return rc;
 
     // dK, dV: reverse sweep carrying dS, with a chunked suffix over blocks; the aggregates

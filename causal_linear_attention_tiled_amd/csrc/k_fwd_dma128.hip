@@ -123,7 +123,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma128(SweepArgs a, La
     f32x4 S[8][NVT];
     {
         const float* init = nullptr;
-        bool tr = false;
+        bool tr = false, poison = false;
         if (c == 0) {
             if (a.kv_in) {
                 init = a.kv_in + wk.state * D * D;
@@ -132,6 +132,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma128(SweepArgs a, La
         } else {
             init = a.slots + (wk.slot0 + static_cast<int64_t>(c - 1) * wk.slot_step) * D * D;
             tr = a.slots_transposed != 0;
+            poison = !given_states_match(a);
         }
 #pragma unroll
         for (int at = 0; at < 8; ++at)
@@ -149,6 +150,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma128(SweepArgs a, La
                         for (int r = 0; r < 4; ++r) x[r] = init[(row0 + r) * D + col];
                     }
                 }
+                if (poison) x = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
                 S[at][vt] = x;
             }
     }

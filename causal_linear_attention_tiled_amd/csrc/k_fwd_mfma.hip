@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kThreads, (BK == 64) ? 2 : 1) void k_fwd_mfma(Sweep
     f32x4 S[8][2];
     {
         const float* init = nullptr;
-        bool tr = false;
+        bool tr = false, poison = false;
         if (c == 0) {
             if (a.kv_in) {
                 init = a.kv_in + pair * D * D;
@@ -96,6 +96,7 @@ __global__ __launch_bounds__(kThreads, (BK == 64) ? 2 : 1) void k_fwd_mfma(Sweep
         } else {
             init = a.slots + fwd_slot_index(a, pair, c) * D * D;
             tr = a.slots_transposed != 0;
+            poison = !given_states_match(a);
         }
 #pragma unroll
         for (int at = 0; at < 8; ++at)
@@ -112,6 +113,7 @@ __global__ __launch_bounds__(kThreads, (BK == 64) ? 2 : 1) void k_fwd_mfma(Sweep
                         for (int r = 0; r < 4; ++r) x[r] = init[(16 * at + 4 * g + r) * D + col];
                     }
                 }
+                if (poison) x = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
                 S[at][vt] = x;
             }
     }

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs l
     fill_powers(sh.pw, lv, Bk);
 
     const float* init = nullptr;
-    bool transposed = false;
+    bool transposed = false, poison = false;
     if (c == 0) {
         if (a.kv_in) {
             init = a.kv_in + pair * D * D;
@@ -56,11 +56,12 @@ __global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs l
     } else {
         init = a.slots + fwd_slot_index(a, pair, c) * D * D;
         transposed = a.slots_transposed != 0;
+        poison = !given_states_match(a);
     }
     for (int i = tid; i < D * D; i += kThreads) {
         float x = 0.f;
         if (init) x = transposed ? init[(i % D) * D + i / D] : init[i];
-        sh.state[i] = x;
+        sh.state[i] = poison ? __builtin_nanf("") : x;
     }
     __syncthreads();
 
@@ -247,6 +248,8 @@ __global__ __launch_bounds__(kThreads) void k_scan(ScanArgs a, LamArgs lam) {
     // which the compiler cannot see, and a memory latency per slot would dominate.
     float4 x[kScanBatch];
     if (!a.reverse) {
+        if (a.stamp_out && blockIdx.x == 0 && threadIdx.x == 0)
+            for (int i = 0; i < kStampWords; ++i) a.stamp_out[i] = a.stamp.w[i];
         float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
         if (a.kv_in) {
             const float* src = a.kv_in + pair * DD;

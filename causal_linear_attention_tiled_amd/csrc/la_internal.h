@@ -34,6 +34,14 @@ struct VarlenArgs {
 // One sweep over every (sequence, chunk) of a [P][N][D] problem.
 // Sequence p = b * H + h uses decay lam[h].  Chunk c covers tokens
 // [c * L, min(N, (c + 1) * L)); L is a multiple of Bk.
+// Stamp that la_fwd leaves after the chunk states in its workspace: shape, chunk plan,
+// decay values and the identity of the inputs (their addresses).  A dQ sweep fed those
+// states (la_bwd's fwd_ws) compares it with the stamp its own arguments imply.
+constexpr int kStampWords = 8;
+struct Stamp {
+    uint32_t w[kStampWords];
+};
+
 struct SweepArgs {
     const void* a;  // forward: Q      reverse: Q
     const void* b;  // forward: K      reverse: K
@@ -47,6 +55,9 @@ struct SweepArgs {
     int kv_in_transposed; // read kv_in as its transpose (dQ sweep)
     int slots_transposed; // read the slots as their transposes (dQ sweep fed by the
                           // forward pass's chunk states)
+    const uint32_t* stamp;// with slots_transposed: the stamp stored after those states;
+                          // chunks whose words differ from `expect` start from a NaN state
+    Stamp expect;
     float* kv_out;        // [P][D][D] final state (forward only) or nullptr
     const float* g_final; // reverse only: [P][D][D] gradient arriving at the final state, the
                           // dS the last chunk starts from, or nullptr for zero
@@ -118,7 +129,19 @@ struct ScanArgs {
     int keep;             // k_scan: slots a sweep reads are every keep-th (chunk boundaries of
                           // aggregates over keep parts per chunk); only those are written
                           // (0 or 1: every slot)
+    uint32_t* stamp_out;  // forward k_scan: where to store `stamp` (nullptr: nowhere)
+    Stamp stamp;
 };
+
+// False when a sweep is fed a forward pass's chunk states whose stamp is not the one its
+// own arguments imply (a workspace from another call): its state is then NaN.
+__device__ __forceinline__ bool given_states_match(const SweepArgs& a) {
+    if (!a.stamp) return true;
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < kStampWords; ++i) ok &= a.stamp[i] == a.expect.w[i];
+    return ok;
+}
 
 struct DecodeArgs {
     float* state;  // [P][D][D], or the slot pool [pool_slots][H][D][D] when slot_of is set

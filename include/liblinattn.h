@@ -109,8 +109,9 @@ enum {
  *             (may be NULL when that size is 0).  Its contents on entry do
  *             not matter; calls sharing a workspace must be stream-ordered.
  *             On return it holds the key-value state at the end of every
- *             chunk but the last (float32), which la_bwd can take as fwd_ws
- *             instead of computing them again. */
+ *             chunk but the last (float32) and a stamp identifying this call,
+ *             which la_bwd can take as fwd_ws instead of computing the states
+ *             again. */
 int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int64_t B, int64_t H,
            int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t phi, const float* kv_in, void* O,
            float* kv_out, void* ws, size_t ws_bytes, void* hip_stream);
@@ -170,11 +171,18 @@ int la_plan(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtyp
  *             kv_in, also when kv_in is NULL); NULL skips it.  Must not
  *             overlap an input or another output.
  *   fwd_ws  : NULL, or the workspace of an la_fwd call with the same Q, K, V,
- *             lambda, shape, Bk, dtype and kv_in, unchanged since that call
- *             (device, read only; same LA_CHUNKS setting).  The dQ sweep then
- *             reads the chunk states from it rather than making one more
- *             pass over K and V.  Its contents are not checked: a workspace
- *             from any other call gives wrong dQ.
+ *             lambda, shape, Bk, dtype, phi and kv_in, unchanged since that
+ *             call (device, read only; same LA_CHUNKS setting).  The dQ sweep
+ *             then reads the chunk states from it rather than making one more
+ *             pass over K and V.  la_fwd stores a stamp after those states
+ *             (shape, chunk plan, decay values, feature map and the addresses
+ *             of Q, K, V and kv_in); the dQ sweep compares it, on the device,
+ *             with the stamp these arguments imply, and where they differ
+ *             every chunk that would start from those states starts from NaN,
+ *             so its dQ rows come out NaN instead of wrong (chunk 0, dK, dV
+ *             and dkv_in are unaffected).  The stamp cannot see tensors
+ *             rewritten in place at the same addresses since la_fwd: with
+ *             fwd_ws the call is not stateless.
  *   ws      : la_bwd_workspace_bytes(...) bytes, as for la_fwd; must not
  *             overlap fwd_ws.
  *   phi     : the feature map of the forward; dQ and dK are with respect to
