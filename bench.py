@@ -48,7 +48,7 @@ CALIB_BYTES = 1 << 30      # bytes read and written by the calibration copy
 # serves both la_fwd and the dQ pass of la_bwd)
 DEVICE_FN = {
     "fwd_dma": "k_fwd_dma", "dq_dma": "k_fwd_dma", "fwd_mfma": "k_fwd_mfma", "dq_mfma": "k_fwd_mfma",
-    "dkdv_dma": "k_rev_dma", "dkdv_mfma": "k_rev_mfma", "dkdv_generic": "k_rev_generic",
+    "dkdv_dma": "k_rev_dma_split", "dkdv_mfma": "k_rev_mfma", "dkdv_generic": "k_rev_generic",
     "chunk_state_dma": "k_chunk_state_dma", "chunk_state_rev_dma": "k_chunk_state_dma",
     "chunk_state_mfma": "k_chunk_state_mfma", "chunk_state_rev_mfma": "k_chunk_state_mfma",
     "state_scan": "k_scan", "state_scan_rev": "k_scan", "decode": "k_decode",
@@ -131,6 +131,23 @@ def read_traffic(kernel):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def read_mfma(kernel, tag="sweep"):
+    """Matrix-core figures of device function `kernel` from profiles/mfma_<tag>.txt (its totals
+    row), or None when absent or when the kernel's source has changed since."""
+    path = os.path.join(PROFILES, f"mfma_{tag}.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        cols = [c.strip() for c in line.split("|")]
+        if len(cols) == 11 and cols[0] == kernel and cols[1] == "all":
+            if cols[10] != source_digest(kernel):
+                return None
+            return {"mfma_tflops_executed": float(cols[5]), "pct_bf16_peak_executed": float(cols[6]),
+                    "MfmaUtil": float(cols[7]), "VALUBusy": float(cols[8]), "LdsUtil": float(cols[9]),
+                    "source": f"profiles/mfma_{tag}.txt"}
+    return None
 
 
 # ----------------------------------------------------------------------------- inputs
@@ -585,7 +602,8 @@ def bench(args):
         avg_bytes = per_step_bytes / launches_per_step if per_step_bytes else None
         kernels[nm] = {"device_function": DEVICE_FN.get(nm, nm), "launches_per_step": launches_per_step,
                        "avg_ms": round(avg_ms, 5), "share": None, "alg_bytes_per_launch": avg_bytes,
-                       "gbs": (avg_bytes / (avg_ms * 1e-3) / 1e9) if avg_bytes else None}
+                       "gbs": (avg_bytes / (avg_ms * 1e-3) / 1e9) if avg_bytes else None,
+                       "counters": read_mfma(DEVICE_FN.get(nm, nm))}
     total_prof = sum(v[1] for v in prof.values())
     for nm in kernels:
         kernels[nm]["share"] = round(prof[nm][1] / total_prof, 4)
@@ -612,7 +630,8 @@ def bench(args):
                 "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
                 "traffic": read_traffic(dom), "avg_launch_ms": round(avg_ms, 5),
                 "launches_per_step": df["launches"] / args.steps, "alg_bytes_per_launch": avg_bytes,
-                "share": round(df["total_ms"] / total_prof, 4)}
+                "share": round(df["total_ms"] / total_prof, 4),
+                "counters": read_mfma(dom)}
 
     # per sequence length breakdown
     sweep = []
