@@ -18,7 +18,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblinattn.so")
+# LA_SANITIZE=1 loads the build whose host code carries AddressSanitizer and UBSan
+# (tests/sanitize_host.py); its kernels are the same.
+LIB_PATH = os.path.join(_HERE, "liblinattn_san.so" if os.environ.get("LA_SANITIZE") == "1" else "liblinattn.so")
 
 LA_F32, LA_BF16 = 0, 1
 LA_PHI_IDENTITY, LA_PHI_ELU1, LA_PHI_RELU = 0, 1, 2

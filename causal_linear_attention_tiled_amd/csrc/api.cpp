@@ -299,6 +299,24 @@ la::Stamp make_stamp(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int
     return st;
 }
 
+// LA_TRACE=1: every call prints its plan to stderr (one line).
+void trace_plan(const char* call, int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype,
+                const Plan& p, size_t ws_bytes) {
+    const char* e = std::getenv("LA_TRACE");
+    if (!e || std::strcmp(e, "1") != 0) return;
+    const int64_t pairs = B * H;
+    const int64_t agg_wgs = p.chunks > 1 ? pairs * (p.chunks - 1) * p.agg_k : 0;
+    std::fprintf(stderr,
+                 "[liblinattn] %s B=%lld H=%lld N=%lld D=%lld %s Bk=%d (stepped %d) kernels=%s chunks=%d "
+                 "chunk_len=%lld agg_parts=%d sweep_wgs=%lld aggregate_wgs=%lld cus=%lld workspace=%zu\n",
+                 call, static_cast<long long>(B), static_cast<long long>(H), static_cast<long long>(N),
+                 static_cast<long long>(D), dtype == LA_BF16 ? "bf16" : "f32", Bk,
+                 p.mfma ? ((p.bk == 128 && env_is("LA_FWD128", "1")) ? 128 : 64) : p.bk,
+                 p.mfma ? "mfma" : "generic", p.chunks, static_cast<long long>(p.L), p.agg_k,
+                 static_cast<long long>(pairs * p.chunks), static_cast<long long>(agg_wgs),
+                 static_cast<long long>(compute_units()), ws_bytes);
+}
+
 // Largest workgroup count any launch of a chunked call makes: the sweeps (one per
 // sequence and chunk), the aggregates (agg_k per chunk boundary) and the scans
 // (D * D / 256 per sequence).
@@ -489,6 +507,7 @@ int fwd_entry(const void* Q, const void* K, const void* V, const float* lambda, 
     } else if (need && (!ws || ws_bytes < need)) {
         return LA_EWORKSPACE;
     }
+    trace_plan(use_scratch ? "la_fwd_noalloc" : "la_fwd", B, H, N, D, Bk_call, dtype, p, need);
     const Range rq{Q, tb}, rk{K, tb}, rv{V, tb}, ro{O, tb}, rin{kv_in, kv_in ? sb : 0},
         rout{kv_out, kv_out ? sb : 0}, rws{ws, need};
     for (const Range& r : {rq, rk, rv, rin})
@@ -541,6 +560,7 @@ int la_plan(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtyp
     const int rc = check_shape(B, H, N, D, Bk, dtype, &elems);
     if (rc) return rc;
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
+    trace_plan("la_plan", B, H, N, D, Bk, dtype, p, fwd_ws_bytes(B * H, p, D));
     if (chunks) *chunks = p.chunks;
     if (chunk_len) *chunk_len = p.L;
     if (agg_parts) *agg_parts = p.agg_k;
@@ -597,12 +617,14 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
     if (!plan_grid_ok(B * H, p, D)) return LA_EUNSUPPORTED;
     const la::Stamp stamp = make_stamp(B, H, N, D, Bk, dtype, phi, p, lam, Q, K, V, kv_in);
+    const int32_t Bk_call = Bk;
     Bk = p.bk;  // the block the kernels step
     // chunk states of the dQ sweep (forward direction) and of the dK, dV sweep (reverse
     // direction), both over agg_k parts per chunk boundary
     const size_t fq = fwd_slot_bytes(B * H, p, D), rv = fq;
     const size_t need = round_up(fq) + round_up(rv);
     if (need && (!ws || ws_bytes < need)) return LA_EWORKSPACE;
+    trace_plan("la_bwd", B, H, N, D, Bk_call, dtype, p, need);
     const Range ins[] = {{Q, tb}, {K, tb}, {V, tb}, {dO, tb}, {kv_in, kv_in ? sb : 0},
                          {dkv_out, dkv_out ? sb : 0}, {fwd_ws, fwd_ws ? fwd_ws_bytes(B * H, p, D) : 0}};
     const Range outs[] = {{dQ, tb}, {dK, tb}, {dV, tb}, {dkv_in, dkv_in ? sb : 0}, {ws, need}};
@@ -708,9 +730,11 @@ int la_dlam(const void* Q, const void* K, const void* V, const void* dO, const f
     const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
     const Plan p = make_plan(B, H, N, D, Bk, dtype);
     if (!plan_grid_ok(B * H, p, D)) return LA_EUNSUPPORTED;
+    const int32_t Bk_call = Bk;
     Bk = p.bk;  // the block the kernels step
     const size_t need = dlam_ws_bytes(B * H, p, D);
     if (!ws || ws_bytes < need) return LA_EWORKSPACE;
+    trace_plan("la_dlam", B, H, N, D, Bk_call, dtype, p, need);
     const Range ins[] = {{Q, tb}, {K, tb}, {V, tb}, {dO, tb}, {kv_in, kv_in ? sb : 0}, {dkv_out, dkv_out ? sb : 0}};
     const Range rout{dlam, static_cast<size_t>(H) * sizeof(float)}, rws{ws, need};
     for (const Range& i : ins)

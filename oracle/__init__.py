@@ -34,7 +34,10 @@ from .quadratic import (decay_matrix, fwd_quadratic, bwd_quadratic, dlam_quadrat
 from . import feature  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "liboracle.so")
+# LA_SANITIZE=1 (tests/sanitize_host.py): the build with AddressSanitizer and UBSan
+_SANITIZE = os.environ.get("LA_SANITIZE") == "1"
+_SO = os.path.join(_HERE, "liboracle_san.so" if _SANITIZE else "liboracle.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 _lib_handle = None
 
 
@@ -46,8 +49,12 @@ def build() -> str:
     same way."""
     src = os.path.join(_HERE, "oracle.c")
     tmp = _SO + ".tmp"
-    subprocess.run(["gcc", "-O3", "-ffp-contract=off", "-fPIC", "-shared", "-fopenmp", "-o", tmp, src],
-                   check=True)
+    if _SANITIZE:  # clang, so that one sanitizer runtime serves every library in the process
+        cmd = ["/opt/rocm/llvm/bin/clang", "-O1", *_SAN_FLAGS, "-ffp-contract=off", "-fPIC", "-shared",
+               "-fopenmp", "-o", tmp, src]
+    else:
+        cmd = ["gcc", "-O3", "-ffp-contract=off", "-fPIC", "-shared", "-fopenmp", "-o", tmp, src]
+    subprocess.run(cmd, check=True)
     os.replace(tmp, _SO)
     return _SO
 

@@ -19,7 +19,10 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "libsynth.so")
+# LA_SANITIZE=1 (tests/sanitize_host.py): the build with AddressSanitizer and UBSan
+_SANITIZE = os.environ.get("LA_SANITIZE") == "1"
+_SO = os.path.join(_HERE, "libsynth_san.so" if _SANITIZE else "libsynth.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 _lib_handle = None
 
 ID_Q, ID_K, ID_V, ID_DO, ID_STATE = 1, 2, 3, 4, 5
@@ -34,8 +37,12 @@ def build() -> str:
     """Compile libsynth.so with gcc (always recompiles)."""
     src = os.path.join(_HERE, "synth.c")
     tmp = _SO + ".tmp"
-    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-fopenmp", "-o", tmp, src, "-lm"],
-                   check=True)
+    if _SANITIZE:  # clang, so that one sanitizer runtime serves every library in the process
+        cmd = ["/opt/rocm/llvm/bin/clang", "-O1", *_SAN_FLAGS, "-ffp-contract=off", "-fPIC", "-shared",
+               "-fopenmp", "-o", tmp, src, "-lm"]
+    else:
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-fopenmp", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
     os.replace(tmp, _SO)
     return _SO
 

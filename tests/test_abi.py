@@ -317,3 +317,18 @@ def test_noalloc_scratch_limit():
             os.environ.pop("LA_CHUNKS", None)
         else:
             os.environ["LA_CHUNKS"] = old
+
+
+def test_trace_prints_the_plan():
+    """LA_TRACE=1: a call prints its plan (chunks, chunk length, parts, workgroups, workspace)
+    on stderr; host only (la_plan)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); import causal_linear_attention_tiled_amd as la; "
+            "la.la_plan(2, 16, 65536, 128, 64, la.LA_BF16)") % os.path.dirname(os.path.dirname(la.__file__))
+    r = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, LA_TRACE="1"), capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    line = [x for x in r.stderr.splitlines() if x.startswith("[liblinattn] la_plan")]
+    assert line, r.stderr
+    assert "chunks=8 chunk_len=8192 agg_parts=2 sweep_wgs=256 aggregate_wgs=448" in line[0]

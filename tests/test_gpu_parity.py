@@ -523,3 +523,32 @@ def test_block128_kernel_parity(fwd128, chunks, Bk, cks, N, with_state):
 @pytest.mark.parametrize("Bk,cks", [(128, 3), (256, 2)])
 def test_block128_kernel_impulse(fwd128, lam_val, Bk, cks, chunks, kernel):
     test_impulse_probe_bit_exact("default", lam_val, Bk, cks, chunks, kernel)
+
+
+def test_checkpoint_host_roundtrip_bit_identical():
+    """The method's resume point is the fixed-size state (record mechanism field; glossary
+    features list): kv_out saved to host memory and restored continues the sequence bit for bit
+    like the device-resident state, for la_fwd, la_decode_step and la_bwd's kv_in."""
+    B, H, N, D, m = 2, 4, 900, 128, 333
+    lam = synth.decay_schedule(H)
+    _, (q, k, v, g), _ = inputs(23, B, H, N, D, "bf16", with_do=True)
+    first = [x[:, :, :m].contiguous() for x in (q, k, v)]
+    rest = [x[:, :, m:].contiguous() for x in (q, k, v, g)]
+    _, s_mid = la.la_fwd(*first, lam)
+    _sync()
+    saved = s_mid.cpu().numpy().copy()                 # checkpoint on the host
+    restored = torch.from_numpy(saved).cuda()          # resume from it
+    o_dev, s_dev = la.la_fwd(*rest[:3], lam, kv_in=s_mid)
+    o_host, s_host = la.la_fwd(*rest[:3], lam, kv_in=restored)
+    b_dev = la.la_bwd(*rest, lam, kv_in=s_mid)
+    b_host = la.la_bwd(*rest, lam, kv_in=restored)
+    st_dev, st_host = s_dev.clone(), s_host.clone()
+    d_dev = la.la_decode_step(st_dev, rest[0][:, :, 0].contiguous(), rest[1][:, :, 0].contiguous(),
+                              rest[2][:, :, 0].contiguous(), lam)
+    d_host = la.la_decode_step(st_host, rest[0][:, :, 0].contiguous(), rest[1][:, :, 0].contiguous(),
+                               rest[2][:, :, 0].contiguous(), lam)
+    _sync()
+    assert torch.equal(o_dev, o_host) and torch.equal(s_dev, s_host)
+    for x, y in zip(b_dev, b_host):
+        assert torch.equal(x, y)
+    assert torch.equal(d_dev, d_host) and torch.equal(st_dev, st_host)
