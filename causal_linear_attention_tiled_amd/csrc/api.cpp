@@ -529,6 +529,56 @@ int fwd_entry(const void* Q, const void* K, const void* V, const float* lambda, 
                              nullptr, stamp);
 }
 
+// A ragged batch is launched in groups of at most kMaxVarlenSeqs sequences (the batch table
+// travels in the kernel arguments); each group has its own plan, with offsets rebased to its
+// first token, and its own slice of the workspace.
+struct VarGroup {
+    int64_t b0, nb;    // first sequence, sequences
+    int64_t t0;        // first token
+    VarPlan plan;
+    size_t ws_off, ws_bytes;
+};
+
+int varlen_groups(const int64_t* offs, int64_t B, int64_t H, int64_t D, int32_t Bk, std::vector<VarGroup>* out) {
+    if (!offs || B <= 0 || H <= 0 || D <= 0) return LA_EINVAL;
+    if (H > la::kMaxHeads) return LA_EUNSUPPORTED;
+    if (offs[0] != 0) return LA_EINVAL;
+    for (int64_t b = 0; b < B; ++b)
+        if (offs[b + 1] < offs[b]) return LA_EINVAL;
+    size_t off = 0;
+    for (int64_t b0 = 0; b0 < B; b0 += la::kMaxVarlenSeqs) {
+        VarGroup g;
+        g.b0 = b0;
+        g.nb = std::min<int64_t>(la::kMaxVarlenSeqs, B - b0);
+        g.t0 = offs[b0];
+        std::vector<int64_t> rel(static_cast<size_t>(g.nb + 1));
+        for (int64_t i = 0; i <= g.nb; ++i) rel[static_cast<size_t>(i)] = offs[b0 + i] - g.t0;
+        const int rc = make_varplan(rel.data(), g.nb, H, D, Bk, &g.plan);
+        if (rc) return rc;
+        g.ws_off = off;
+        g.ws_bytes = round_up(varlen_slot_bytes(g.plan, H, D));
+        off += g.ws_bytes;
+        out->push_back(g);
+    }
+    return LA_OK;
+}
+
+bool varlen_supported(int32_t dtype, int64_t D, int32_t Bk) {
+    return dtype == LA_BF16 && D == 128 && (Bk == 64 || Bk == 128 || Bk == 256);
+}
+
+// LA_TRACE=1: the plan of one group of a ragged batch.
+void trace_varlen(int64_t nb, int64_t H, const VarPlan& p) {
+    const char* e = std::getenv("LA_TRACE");
+    if (!e || std::strcmp(e, "1") != 0) return;
+    std::fprintf(stderr,
+                 "[liblinattn] la_fwd_varlen group of %lld sequences T=%lld H=%lld chunk_len=%lld sweep_wgs=%lld "
+                 "chunk_states=%lld\n",
+                 static_cast<long long>(nb), static_cast<long long>(p.T), static_cast<long long>(H),
+                 static_cast<long long>(p.L), static_cast<long long>(p.v.wp[nb]) * H,
+                 static_cast<long long>(p.slots_per_head * H));
+}
+
 }  // namespace
 
 // ====================================================================== ABI
@@ -781,10 +831,13 @@ int la_dlam(const void* Q, const void* K, const void* V, const void* dO, const f
 
 size_t la_fwd_varlen_workspace_bytes(const int64_t* seq_offsets, int64_t B, int64_t H, int64_t D, int32_t Bk,
                                      int32_t dtype) {
-    if (dtype != LA_BF16 || D != 128 || Bk != 64) return 0;
-    VarPlan p;
-    if (make_varplan(seq_offsets, B, H, D, Bk, &p) != LA_OK) return 0;
-    return varlen_slot_bytes(p, H, D);
+    if (!varlen_supported(dtype, D, Bk)) return 0;
+    std::vector<VarGroup> groups;
+    if (varlen_groups(seq_offsets, B, H, D, Bk, &groups) != LA_OK) return 0;
+    size_t total = 0;
+    for (const VarGroup& g : groups) total += g.ws_bytes;
+    // a batch whose only group needs no chunk states needs no workspace
+    return total;
 }
 
 int la_fwd_varlen(const void* Q, const void* K, const void* V, const float* lambda, const int64_t* seq_offsets,
@@ -792,20 +845,27 @@ int la_fwd_varlen(const void* Q, const void* K, const void* V, const float* lamb
                   void* O, float* kv_out, void* ws, size_t ws_bytes, void* hip_stream) {
     if (dtype != LA_F32 && dtype != LA_BF16) return LA_EINVAL;
     if (!valid_phi(phi)) return LA_EINVAL;
-    VarPlan p;
-    int rc = make_varplan(seq_offsets, B, H, D, Bk, &p);
+    std::vector<VarGroup> groups;
+    int rc = varlen_groups(seq_offsets, B, H, D, Bk, &groups);
     if (rc) return rc;
-    if (dtype != LA_BF16 || D != 128 || Bk != 64) return LA_EUNSUPPORTED;
-    if (p.T > 0 && (!Q || !K || !V || !O)) return LA_EINVAL;
+    if (!varlen_supported(dtype, D, Bk)) return LA_EUNSUPPORTED;
+    const int64_t T = seq_offsets[B];
+    if (T > 0 && (!Q || !K || !V || !O)) return LA_EINVAL;
     LamArgs lam;
     if ((rc = load_lambda(lambda, H, &lam))) return rc;
     for (const void* ptr : {Q, K, V, static_cast<const void*>(O), static_cast<const void*>(kv_in),
                             static_cast<const void*>(kv_out), static_cast<const void*>(ws)})
         if (ptr && !aligned16(ptr)) return LA_EALIGN;
-    const size_t tb = static_cast<size_t>(p.T * H * D) * 2;
-    const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
-    const size_t need = varlen_slot_bytes(p, H, D);
+    int64_t wgs = 0;
+    size_t need = 0;
+    for (const VarGroup& g : groups) {
+        wgs = std::max<int64_t>(wgs, static_cast<int64_t>(g.plan.v.wp[g.nb]) * H);
+        need += g.ws_bytes;
+    }
+    if (wgs > kMaxWorkgroups) return LA_EUNSUPPORTED;
     if (need && (!ws || ws_bytes < need)) return LA_EWORKSPACE;
+    const size_t tb = static_cast<size_t>(T * H * D) * 2;
+    const size_t sb = static_cast<size_t>(B * H * D * D) * sizeof(float);
     const Range rq{Q, tb}, rk{K, tb}, rv{V, tb}, ro{O, tb}, rin{kv_in, kv_in ? sb : 0},
         rout{kv_out, kv_out ? sb : 0}, rws{ws, need};
     for (const Range& r : {rq, rk, rv, rin})
@@ -816,40 +876,55 @@ int la_fwd_varlen(const void* Q, const void* K, const void* V, const float* lamb
     if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count == 0) return LA_ENODEV;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const int32_t Hi = static_cast<int32_t>(H);
-    float* slots = static_cast<float*>(ws);
-    if (p.slots_per_head > 0) {
-        la::ChunkStateArgs cs{K, V, slots, 0, p.L, static_cast<int>(D), Bk, Hi, 0, 0, 0, phi, 1};
-        rc = launch("chunk_state_varlen_dma", s, [&] { la::launch_chunk_state_dma_varlen(cs, lam, p.v, s); });
-        if (rc) return rc;
-        la::ScanArgs sc{slots, kv_in, 0, nullptr, 0, p.L, static_cast<int>(D), Hi, 0, 0, 0};
-        la::ScanList list;
-        list.count = 0;
-        for (int b = 0; b < p.v.nseq; ++b) {
-            const int n_slots = p.v.wp[b + 1] - p.v.wp[b] - 1;
-            if (n_slots > 0) {
-                list.seq[list.count] = b | (n_slots << 8);
-                list.sbase[list.count] = p.v.wp[b] - b;
-                ++list.count;
+    for (const VarGroup& g : groups) {
+        const VarPlan& p = g.plan;
+        if (p.T == 0 && !kv_out) continue;  // nothing to read or write
+        const int64_t tok = g.t0 * H * D;   // element offset of the group's first token
+        const int64_t st = g.b0 * H * D * D;
+        const void* Qg = static_cast<const uint16_t*>(Q) + tok;
+        const void* Kg = static_cast<const uint16_t*>(K) + tok;
+        const void* Vg = static_cast<const uint16_t*>(V) + tok;
+        void* Og = static_cast<uint16_t*>(O) + tok;
+        const float* kin = kv_in ? kv_in + st : nullptr;
+        float* kout = kv_out ? kv_out + st : nullptr;
+        float* slots = reinterpret_cast<float*>(static_cast<char*>(ws) + g.ws_off);
+        trace_varlen(g.nb, H, p);
+        if (p.slots_per_head > 0) {
+            la::ChunkStateArgs cs{Kg, Vg, slots, 0, p.L, static_cast<int>(D), 64, Hi, 0, 0, 0, phi, 1};
+            rc = launch("chunk_state_varlen_dma", s, [&] { la::launch_chunk_state_dma_varlen(cs, lam, p.v, s); });
+            if (rc) return rc;
+            la::ScanArgs sc{slots, kin, 0, nullptr, 0, p.L, static_cast<int>(D), Hi, 0, 0, 0};
+            la::ScanList list;
+            list.count = 0;
+            for (int b = 0; b < p.v.nseq; ++b) {
+                const int n_slots = p.v.wp[b + 1] - p.v.wp[b] - 1;
+                if (n_slots > 0) {
+                    list.seq[list.count] = b | (n_slots << 8);
+                    list.sbase[list.count] = p.v.wp[b] - b;
+                    ++list.count;
+                }
             }
+            rc = launch("state_scan_varlen", s, [&] { la::launch_scan_varlen(sc, lam, list, s); });
+            if (rc) return rc;
         }
-        rc = launch("state_scan_varlen", s, [&] { la::launch_scan_varlen(sc, lam, list, s); });
+        la::SweepArgs a{};
+        a.a = Qg;
+        a.b = Kg;
+        a.c = Vg;
+        a.out0 = Og;
+        a.slots = slots;
+        a.kv_in = kin;
+        a.kv_out = kout;
+        a.L = p.L;
+        a.D = static_cast<int>(D);
+        a.Bk = 64;  // the kernels step 64-token blocks; the chunk length is a multiple of Bk
+        a.H = Hi;
+        a.phi = phi;
+        a.phi_mask = 3;
+        rc = launch("fwd_varlen_dma", s, [&] { la::launch_fwd_dma_varlen(a, lam, p.v, s); });
         if (rc) return rc;
     }
-    la::SweepArgs a{};
-    a.a = Q;
-    a.b = K;
-    a.c = V;
-    a.out0 = O;
-    a.slots = slots;
-    a.kv_in = kv_in;
-    a.kv_out = kv_out;
-    a.L = p.L;
-    a.D = static_cast<int>(D);
-    a.Bk = Bk;
-    a.H = Hi;
-    a.phi = phi;
-    a.phi_mask = 3;
-    return launch("fwd_varlen_dma", s, [&] { la::launch_fwd_dma_varlen(a, lam, p.v, s); });
+    return LA_OK;
 }
 
 int la_decode_step_paged(float* pool, int64_t pool_slots, const int32_t* slot_of, const void* q, const void* k,

@@ -247,11 +247,15 @@ int la_decode_step(float* state, const void* q, const void* k, const void* v, co
  *                 row t of head h is (t * H + h) * D.
  *   seq_offsets : HOST int64[B + 1], seq_offsets[0] = 0, nondecreasing; read
  *                 during the call only.  Empty sequences are allowed (their
- *                 final state is kv_in, or 0).  1 <= B <= 256.
+ *                 final state is kv_in, or 0).  B >= 1: batches of more than
+ *                 256 sequences are launched as consecutive groups of 256 (one
+ *                 launch per group and stage, all on hip_stream).
  *   kv_in       : [B][H][D][D] float32 device, or NULL for zero.
  *   kv_out      : [B][H][D][D] float32 device, or NULL to skip.
  *   ws          : la_fwd_varlen_workspace_bytes(...) bytes of device memory.
- * Supported: bf16, D = 128, Bk = 64, and T * H * D * 2 < 2^31 (otherwise
+ * Supported: bf16, D = 128, Bk in {64, 128, 256} (chunk boundaries on
+ * multiples of Bk; blocks stepped as 64 tokens, as in la_fwd), and within
+ * every group of 256 sequences T_group * H * D * 2 < 2^31 (otherwise
  * LA_EUNSUPPORTED).  Each sequence's results equal la_fwd over that sequence
  * alone, up to float rounding.  LA_VARLEN_L (a positive multiple of Bk)
  * overrides the chunk length; a size query must see the same setting. */

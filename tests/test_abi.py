@@ -188,10 +188,10 @@ def test_fwd_varlen_rejects():
                                     v(kv_out), v(ws), ws_bytes, None)
     assert call([1, 5, 9]) == la.LA_EINVAL                    # offsets must start at 0
     assert call([0, 9, 5]) == la.LA_EINVAL                    # and not decrease
-    assert call([0] * 258) == la.LA_EUNSUPPORTED              # more than 256 sequences
+    assert call([0, 5, 9] + [9] * 300 + [5]) == la.LA_EINVAL  # also in a later group of 256
     assert call([0, 64], dt=la.LA_F32) == la.LA_EUNSUPPORTED  # bf16 only
     assert call([0, 64], D=64) == la.LA_EUNSUPPORTED
-    assert call([0, 64], Bk=128) == la.LA_EUNSUPPORTED
+    assert call([0, 64], Bk=32) == la.LA_EUNSUPPORTED         # Bk in {64, 128, 256}
     assert call([0, 64], O=Q_) == la.LA_EINVAL                # output aliases Q
     assert call([0, 64], O=O_ + 8) == la.LA_EALIGN
     assert call([0, 1 << 30]) == la.LA_EUNSUPPORTED           # 32-bit buffer offsets
@@ -201,6 +201,14 @@ def test_fwd_varlen_rejects():
     assert call(big, ws=None, ws_bytes=0) == la.LA_EWORKSPACE
     assert call(big, ws_bytes=need - 1) == la.LA_EWORKSPACE
     assert la.la_fwd_varlen_workspace_bytes([0, 10, 20], 2, 128, 64, la.LA_BF16) == 0  # one chunk each
+    # more than 256 sequences: groups of 256, each with its own workspace slice
+    many = [0] + [333 * (i + 1) for i in range(300)]      # 300 short sequences: one chunk each
+    assert la.la_fwd_varlen_workspace_bytes(many, 2, 128, 64, la.LA_BF16) == 0
+    many[-1] = many[-2] + 200000                              # a long last one, in the second group
+    assert la.la_fwd_varlen_workspace_bytes(many, 2, 128, 64, la.LA_BF16) > 0
+    for bk in (128, 256):
+        nb = la.la_fwd_varlen_workspace_bytes(big, 2, 128, bk, la.LA_BF16)
+        assert nb > 0 and call(big, Bk=bk, ws_bytes=nb - 1) == la.LA_EWORKSPACE
 
 
 def test_decode_paged_rejects():

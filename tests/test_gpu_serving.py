@@ -170,3 +170,52 @@ def test_paged_decode_bad_slot_writes_nan():
     for p in (0, 2, 3):
         np.testing.assert_array_equal(pool_h[p], pool0[p])
     assert not np.array_equal(pool_h[1], pool0[1])
+
+
+def check_varlen_against_oracle(lens, H, Bk, seed, with_state):
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T, B = int(offs[-1]), len(lens)
+    lam = synth.decay_schedule(H)
+    (q, k, v), (qh, kh, vh) = packed(seed, T, H)
+    s0 = state_input(seed + 1, B, H, D) if with_state else None
+    kv_in = torch.from_numpy(s0).cuda() if with_state else None
+    o, s = la.la_fwd_varlen(q, k, v, lam, offs, Bk=Bk, kv_in=kv_in)
+    torch.cuda.synchronize()
+    o_h, s_h = got(o), got(s)
+    worst = 0.0
+    for b in range(B):
+        a, e = int(offs[b]), int(offs[b + 1])
+        for h in range(H):
+            init = None if s0 is None else s0[b, h].astype(np.float64)
+            if e > a:
+                o_ref, s_ref = oracle.fwd_recurrent(qh[a:e, h], kh[a:e, h], vh[a:e, h], float(lam[h]), init)
+                err = oracle.rel_l2(o_h[a:e, h], o_ref)
+                worst = max(worst, err)
+                assert err <= BF16_BAR, (b, h, err)
+            else:
+                s_ref = np.zeros((D, D)) if init is None else init
+            assert oracle.rel_l2(s_h[b, h], s_ref) <= BF16_BAR, (b, h)
+    print(f"    worst per-sequence rel-L2 of O {worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("Bk", [128, 256])
+@pytest.mark.parametrize("L", [None, 512])
+def test_varlen_block_sizes(Bk, L, varlen_chunk):
+    """Bk 128 and 256: chunk boundaries on multiples of Bk (forced or planned), blocks stepped as
+    64 tokens; ragged lengths on and next to those boundaries."""
+    varlen_chunk(L)
+    lens = [1, 127, 128, 129, 511, 512, 513, 1500, 0, 2100, 257]
+    print(f"[varlen] Bk={Bk} L={L} lens={lens}", flush=True)
+    check_varlen_against_oracle(lens, 3, Bk, 31 + Bk, with_state=True)
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_varlen_more_than_256_sequences(with_state):
+    """600 sequences (three launch groups of at most 256), seeded lengths 0..300 with a few long
+    ones, every sequence and head against the oracle; group boundaries fall between sequences
+    255/256 and 511/512."""
+    rng = np.random.default_rng(600)
+    lens = rng.integers(0, 301, 600)
+    lens[[3, 255, 256, 511, 599]] = [2000, 1, 1700, 999, 2500]
+    print(f"[varlen] B=600 T={int(lens.sum())} kv_in={with_state}", flush=True)
+    check_varlen_against_oracle(list(lens), 2, 64, 77, with_state)
