@@ -233,12 +233,19 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t d
     p.chunks = static_cast<int>((nb + bpc - 1) / bpc);
     p.bk = std::min(Bk, kMaxKernelBk);
     p.mfma = dtype == LA_BF16 && la::mfma_supported(static_cast<int>(D), p.bk) && !force_generic();
-    // The chunk aggregates (one workgroup each, two per CU) are taken over agg_k equal
-    // parts of every chunk when the chunks alone would leave the pass below 3/4 of a
-    // round of 512 workgroups; the scans then run over the parts, chunk c of a forward
-    // sweep starts from part c * agg_k - 1 and chunk c of a reverse sweep from the
-    // gradient entering part (c + 1) agg_k.  Each part keeps at least kMinBlocksPerChunk
-    // blocks.  LA_AGG_K forces it (dividing the blocks per chunk).
+    // The chunk aggregates are taken over agg_k equal parts of every chunk; the scans then
+    // run over the parts, chunk c of a forward sweep starts from part c * agg_k - 1 and
+    // chunk c of a reverse sweep from the gradient entering part (c + 1) agg_k.  The
+    // aggregate kernels hold one workgroup per CU, so the W = (chunks - 1) agg_k pairs
+    // workgroups run in rounds of CUs.  A round costs its part length plus a pipeline fill
+    // of 256 tokens, scaled by max(1, its workgroups / (7/8 CUs)): about 7/8 of the CUs
+    // streaming already saturate HBM, fewer leave the round bound by one workgroup's rate.
+    // agg_k minimises the summed cost (the smallest on a tie, for the fewest scan steps),
+    // each part keeping at least kMinBlocksPerChunk blocks.  Measured (ms of the forward
+    // aggregates), every choice of this rule the fastest measured: B8 H16 N16384 0.104 at 2
+    // parts (0.111 at 4), B2 H16 N65536 0.163 at 1 (0.177 at 2), B1 H64 N262144 1.108 at 4
+    // (1.179 at 1, 1.278 at 2), B4 H16 N2048 0.0147 at 1 (0.0184 at 2), B2 H32 N8192
+    // 0.039 at 1.  LA_AGG_K forces it (dividing the blocks per chunk).
     p.agg_k = 1;
     if (p.chunks > 1) {
         const char* ek = std::getenv("LA_AGG_K");
@@ -246,9 +253,17 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t d
             const int64_t k = std::atoll(ek);
             if (bpc % k == 0) p.agg_k = static_cast<int>(k);
         } else {
-            while ((p.chunks - 1) * p.agg_k * pairs < 384 && bpc % (2 * p.agg_k) == 0 &&
-                   bpc / (2 * p.agg_k) >= kMinBlocksPerChunk)
-                p.agg_k *= 2;
+            const int64_t cus = compute_units();
+            const double sat = 0.875 * static_cast<double>(cus);
+            auto cost = [&](int64_t k) {
+                const int64_t w = (p.chunks - 1) * k * pairs;
+                const double part = static_cast<double>(p.L / k + 4 * 64);
+                const double full = static_cast<double>(w / cus), rem = static_cast<double>(w % cus);
+                return part * (full * std::max(1.0, static_cast<double>(cus) / sat) +
+                               (rem > 0 ? std::max(1.0, rem / sat) : 0.0));
+            };
+            for (int64_t k = 2; k <= 16 && bpc % k == 0 && bpc / k >= kMinBlocksPerChunk; k *= 2)
+                if (cost(k) < cost(p.agg_k) - 1e-12) p.agg_k = static_cast<int>(k);
         }
     }
     return p;
@@ -364,7 +379,8 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
         la::ChunkStateArgs cs{k, v, slots, N, Lf, static_cast<int>(D), Bk, H, chunks_f, pairs, 0,
                               phi.kind, phi.state_mask};
         if (p.mfma && la::state_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_STATE", "v1"))
-            rc = launch("chunk_state_dma", s, [&] { la::launch_chunk_state_dma(cs, lam, s); });
+            rc = launch("chunk_state_dma", s,
+                        [&] { la::launch_chunk_state_dma(cs, lam, !env_is("LA_STATE", "dma2"), s); });
         else if (p.mfma && v1_ok)
             rc = launch("chunk_state_mfma", s, [&] { la::launch_chunk_state_mfma(cs, lam, s); });
         else
@@ -714,7 +730,8 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
         la::ChunkStateArgs cs{Q, dO, slots_kv, N, Lf, static_cast<int>(D), Bk, Hi, chunks_f, pairs, 1,
                               phi, 1, p.agg_k - 1};
         if (p.mfma && la::state_dma_supported(static_cast<int>(D), Bk, N) && !env_is("LA_STATE", "v1"))
-            rc = launch("chunk_state_rev_dma", s, [&] { la::launch_chunk_state_dma(cs, lam, s); });
+            rc = launch("chunk_state_rev_dma", s,
+                        [&] { la::launch_chunk_state_dma(cs, lam, !env_is("LA_STATE", "dma2"), s); });
         else if (p.mfma && phi == 0)
             rc = launch("chunk_state_rev_mfma", s, [&] { la::launch_chunk_state_mfma(cs, lam, s); });
         else

@@ -211,6 +211,107 @@ __global__ __launch_bounds__(64 * NW, 2) void k_chunk_state_dma(ChunkStateArgs a
     state_body<false, PHI, false>(a, lam, nullptr);
 }
 
+// The same aggregates (forward and reverse, dense [P][N][D] sequences) fed by two loader
+// waves, one per tensor, through a ring of LD_NST 64-token stages at one workgroup per
+// compute unit: LD_NST - 1 blocks are in flight while one computes, against one in the
+// form above, whose ring shares the compute unit between two workgroups.  Each loader
+// issues its tensor's 16 loads of 1 KiB per block, so its vmcnt counts at most 16
+// (LD_NST - 2) loads past the block it waits for.  Compute waves do what state_body
+// does (the same operands, weights and order, so the results are identical).
+constexpr int LD_NST = 3;
+static_assert(LD_NST == 3, "the loaders' vmcnt waits assume one block in flight past the one awaited");
+
+template <bool PHI>
+__global__ __launch_bounds__(64 * (NW + 2), 1) void k_chunk_state_ld(ChunkStateArgs a, LamArgs lam) {
+    __shared__ uint16_t ring[LD_NST][2][TILE];
+    __shared__ float pw[BK + 1];
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int per = a.chunks - 1;
+    const int64_t pair = blockIdx.x / per;
+    const int slot = blockIdx.x % per;
+    const int c = a.reverse ? slot + 1 + a.part0 : slot;
+    const int64_t base = pair * a.N * D;
+    const int64_t t_begin = static_cast<int64_t>(c) * a.L;
+    const int64_t t_end = min(a.N, t_begin + a.L);
+    const int64_t nblk = t_end > t_begin ? (t_end - t_begin + BK - 1) / BK : 0;
+    const float lv = lam.lam[pair % a.H];
+    for (int e = tid; e <= BK; e += 64 * (NW + 2)) pw[e] = lam_pow(lv, e);
+    __syncthreads();
+    // the n-th block of the walk: away from the reference token
+    auto block_of = [&](int64_t n) { return a.reverse ? n : nblk - 1 - n; };
+
+    if (w >= NW) {
+        // loader wave x streams tensor x (0: X, 1: Y); rows at or past the sequence's end read zero
+        const int x = w - NW;
+        const uint32_t bytes = static_cast<uint32_t>(a.N * D * 2);
+        const u32x4 rs = buffer_rsrc(static_cast<const uint16_t*>(x == 0 ? a.x : a.y) + base, bytes);
+        const int sub = lane >> 4, p = lane & 15;
+        auto issue = [&](int64_t n) {
+            const int64_t t0 = t_begin + block_of(n) * BK;
+            uint16_t* dst = ring[n % LD_NST][x];
+#pragma unroll
+            for (int rg = 0; rg < BK / 4; ++rg) {
+                const int r = 4 * rg + sub;
+                const int voff = static_cast<int>(((t0 + r) * D + 8 * (p ^ swz_key(r))) * 2);
+                dma16(rs, dst + 4 * rg * D, voff);
+            }
+        };
+        for (int64_t n = 0; n < min<int64_t>(LD_NST - 1, nblk); ++n) issue(n);
+        for (int64_t n = 0; n < nblk; ++n) {
+            // blocks issued after n that may still be in flight: min(LD_NST - 2, nblk - 1 - n)
+            if (n + 1 < nblk)
+                wait_vmcnt<16 * (LD_NST - 2)>();
+            else
+                wait_vmcnt<0>();
+            __syncthreads();  // A(n): block n landed (both tensors); block n - 1's stage is free
+            if (n + LD_NST - 1 < nblk) issue(n + LD_NST - 1);
+            if constexpr (PHI) __syncthreads();  // T(n)
+        }
+        return;
+    }
+
+    f32x4 S[8];
+#pragma unroll
+    for (int at = 0; at < 8; ++at) S[at] = zero4();
+    double cw = 1.0;  // lam^(tokens walked so far)
+    const double lam_bk = lam_pow64(lv, BK);
+    for (int64_t n = 0; n < nblk; ++n) {
+        const int64_t t0 = t_begin + block_of(n) * BK;
+        const int m = static_cast<int>(min(static_cast<int64_t>(BK), t_end - t0));
+        uint16_t* Xs = ring[n % LD_NST][0];
+        uint16_t* Ys = ring[n % LD_NST][1];
+        __syncthreads();  // A(n)
+        if constexpr (PHI) {
+            if (a.phi_mask & 1) phi_tile(Xs, a.phi, tid, 64 * NW);
+            if (a.phi_mask & 2) phi_tile(Ys, a.phi, tid, 64 * NW);
+            __syncthreads();  // T(n)
+        }
+        const float cf = static_cast<float>(cw);
+        float wx[NKB][8];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int s = 32 * kb + kappa(g, e);
+                wx[kb][e] = cf * masked_pw(pw, a.reverse ? s : m - 1 - s, s < m);
+            }
+        bf16x8 yf[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) yf[kb] = scale8(op_tr_k(Ys, 32 * kb, 16 * w, 4, g, li), wx[kb]);
+#pragma unroll
+        for (int at = 0; at < 8; ++at)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) S[at] = mfma16(op_tr_k(Xs, 32 * kb, 16 * at, 4, g, li), yf[kb], S[at]);
+        cw *= (m == BK) ? lam_bk : lam_pow64(lv, m);
+    }
+    float* dst = a.slots + (pair * per + slot) * D * D;
+#pragma unroll
+    for (int at = 0; at < 8; ++at)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(16 * at + 4 * g + r) * D + 16 * w + li] = S[at][r];
+}
+
 template <bool PHI>
 __global__ __launch_bounds__(64 * NW, 2) void k_chunk_state_dma_varlen(ChunkStateArgs a, LamArgs lam, VarlenArgs v) {
     state_body<true, PHI, false>(a, lam, &v);
@@ -231,8 +332,15 @@ bool state_dma_supported(int d, int bk, int64_t n) {
     return d == 128 && (bk == 64 || bk == 128) && n * d * 2 < (int64_t(1) << 31);
 }
 
-void launch_chunk_state_dma(const ChunkStateArgs& a, const LamArgs& lam, hipStream_t s) {
+void launch_chunk_state_dma(const ChunkStateArgs& a, const LamArgs& lam, bool loader_waves, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(a.pairs * (a.chunks - 1)));
+    if (loader_waves) {
+        if (a.phi)
+            hipLaunchKernelGGL(k_chunk_state_ld<true>, grid, dim3(64 * (NW + 2)), 0, s, a, lam);
+        else
+            hipLaunchKernelGGL(k_chunk_state_ld<false>, grid, dim3(64 * (NW + 2)), 0, s, a, lam);
+        return;
+    }
     if (a.phi)
         hipLaunchKernelGGL(k_chunk_state_dma<true>, grid, dim3(64 * NW), 0, s, a, lam);
     else

@@ -223,7 +223,9 @@ void launch_rev_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream
 
 // Chunk aggregates with direct-to-LDS loads (bf16, D = 128; Bk = 64 or 128, walked in 64-token blocks).
 bool state_dma_supported(int D, int Bk, int64_t N);
-void launch_chunk_state_dma(const ChunkStateArgs& a, const LamArgs& lam, hipStream_t s);
+// loader_waves: the form with two loader waves and a three-stage ring at one workgroup per
+// CU (dense sequences); otherwise every wave loads, two workgroups per CU.
+void launch_chunk_state_dma(const ChunkStateArgs& a, const LamArgs& lam, bool loader_waves, hipStream_t s);
 // Forward chunk aggregates of a ragged batch: one workgroup per (slot, head).
 void launch_chunk_state_dma_varlen(const ChunkStateArgs& a, const LamArgs& lam, const VarlenArgs& v,
                                    hipStream_t s);

@@ -51,6 +51,8 @@
  *    blocks, LA_AGG_K the number of parts of a chunk the chunk aggregates are
  *    taken over (la_plan); LA_KERNEL=generic forces the generic (non-MFMA)
  *    kernels; LA_FWD128=1 the 128-token-block forward-direction sweep;
+ *    LA_STATE=dma2 the chunk aggregates with every wave loading at two
+ *    workgroups per CU (instead of two loader waves at one);
  *    LA_FWD_WAVES=8, LA_REV_WAVES=4 and LA_DLAM_WAVES=4 select the
  *    other wave counts of the bf16 D = 128 direct-to-LDS sweeps (forward and
  *    dQ, dK and dV, decay derivative).  They exist for tests and tuning; a

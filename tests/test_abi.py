@@ -256,13 +256,14 @@ def test_plan():
     chunks of whole blocks, and the forward aggregates over parts of a chunk when the chunks
     alone would leave the aggregate pass short of workgroups."""
     assert la.la_plan(128, 16, 1024, 128, 64, la.LA_BF16) == {"chunks": 1, "chunk_len": 1024, "agg_parts": 1}
-    assert la.la_plan(8, 16, 16384, 128, 64, la.LA_BF16) == {"chunks": 2, "chunk_len": 8192, "agg_parts": 4}
-    assert la.la_plan(2, 16, 65536, 128, 64, la.LA_BF16) == {"chunks": 8, "chunk_len": 8192, "agg_parts": 2}
+    assert la.la_plan(8, 16, 16384, 128, 64, la.LA_BF16) == {"chunks": 2, "chunk_len": 8192, "agg_parts": 2}
+    assert la.la_plan(2, 16, 65536, 128, 64, la.LA_BF16) == {"chunks": 8, "chunk_len": 8192, "agg_parts": 1}
+    assert la.la_plan(1, 64, 262144, 128, 128, la.LA_BF16) == {"chunks": 4, "chunk_len": 65536, "agg_parts": 4}
     p = la.la_plan(1, 2, 1000, 64, 32, la.LA_F32)
     assert p["chunks"] > 1 and p["chunk_len"] % 32 == 0 and (p["chunks"] - 1) * p["chunk_len"] < 1000
     # forward workspace: agg_parts float32 D x D slots per chunk boundary per sequence
     # (then a 256-byte stamp identifying the forward call, checked by la_bwd when given as fwd_ws)
-    assert la.la_fwd_workspace_bytes(2, 16, 65536, 128, 64, la.LA_BF16) == 32 * 7 * 2 * 128 * 128 * 4 + 256
+    assert la.la_fwd_workspace_bytes(2, 16, 65536, 128, 64, la.LA_BF16) == 32 * 7 * 1 * 128 * 128 * 4 + 256
     with pytest.raises(la.LaError):
         la.la_plan(1, 16, 1024, 100, 64, la.LA_BF16)
     # a 256-token block: chunk boundaries on multiples of 256 (the kernels step 128-token blocks)
@@ -339,4 +340,4 @@ def test_trace_prints_the_plan():
     assert r.returncode == 0, r.stderr
     line = [x for x in r.stderr.splitlines() if x.startswith("[liblinattn] la_plan")]
     assert line, r.stderr
-    assert "chunks=8 chunk_len=8192 agg_parts=2 sweep_wgs=256 aggregate_wgs=448" in line[0]
+    assert "chunks=8 chunk_len=8192 agg_parts=1 sweep_wgs=256 aggregate_wgs=224" in line[0]

@@ -335,10 +335,12 @@ def fwd_variant(monkeypatch):
         elif v == "dma8":
             monkeypatch.setenv("LA_FWD_WAVES", "8")
             monkeypatch.setenv("LA_REV_WAVES", "8")
+        elif v == "dma2":
+            monkeypatch.setenv("LA_STATE", "dma2")
     return set_
 
 
-@pytest.mark.parametrize("variant", ["v1", "dma4", "dma8"])
+@pytest.mark.parametrize("variant", ["v1", "dma4", "dma8", "dma2"])
 @pytest.mark.parametrize("N,cks,with_state", [(64, 1, False), (1000, 1, True), (64 * 13 + 5, 3, True),
                                              (64 * 40, 6, False)])
 def test_forward_variants(variant, N, cks, with_state, fwd_variant, chunks):

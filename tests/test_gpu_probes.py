@@ -36,11 +36,12 @@ def assert_exact(name, y, ref, pairs=None):
 def env(monkeypatch):
     """Kernel selection: 'default', 'generic' (plain float32 kernels), 'v1' (register-staged
     matrix-core kernels), 'w4' (4-wave forward and reverse sweeps), 'w8' (8-wave forward),
-    'dma128' (the 128-token-block forward-direction sweep for Bk = 128 and 256)."""
+    'dma128' (the 128-token-block forward-direction sweep for Bk = 128 and 256), 'dma2' (the
+    chunk aggregates with every wave loading, two workgroups per CU)."""
     def set_(kernel="default", chunks=None, agg=None):
         vals = {"LA_KERNEL": "generic" if kernel == "generic" else None,
                 "LA_FWD": "v1" if kernel == "v1" else None, "LA_REV": "v1" if kernel == "v1" else None,
-                "LA_STATE": "v1" if kernel == "v1" else None,
+                "LA_STATE": {"v1": "v1", "dma2": "dma2"}.get(kernel),
                 "LA_FWD128": "1" if kernel == "dma128" else None,
                 "LA_FWD_WAVES": {"w4": "4", "w8": "8"}.get(kernel),
                 "LA_REV_WAVES": {"w4": "4", "w8": "8"}.get(kernel),
@@ -103,10 +104,11 @@ def test_bwd_impulse_state_paths_bit_exact(env, kern, Bk, cks, agg, lam_val, use
                   label=f"{kern} chunks={cks} agg={agg}")
 
 
-@pytest.mark.parametrize("kern", ["v1", "w4", "w8"])
+@pytest.mark.parametrize("kern", ["v1", "w4", "w8", "dma2"])
 @pytest.mark.parametrize("lam_val", [0.5, 1.0])
 def test_bwd_impulse_kernel_variants(env, kern, lam_val):
-    """The register-staged kernels and the 4- and 8-wave sweeps, chunked with parts."""
+    """The register-staged kernels, the 4- and 8-wave sweeps and the chunk aggregates in the
+    two-workgroup form (dma2), chunked with parts."""
     env(kernel=kern, chunks=3, agg=2)
     run_bwd_probe(64, lam_val, with_state=True, with_gf=True, use_fwd_ws=True, label=kern)
 
