@@ -5,6 +5,8 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
+#include <random>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -282,11 +284,54 @@ size_t fwd_slot_bytes(int64_t pairs, const Plan& p, int64_t D) {
 
 size_t round_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// la_fwd's workspace: the chunk states, then (from a 256-byte boundary) the stamp.
+// la_fwd's workspace, each region from a 256-byte boundary: the chunk states; the
+// per-chunk aggregates and their flags of the fused prefix; the stamp.
 constexpr size_t kStampBytes = 256;
-size_t fwd_ws_bytes(int64_t pairs, const Plan& p, int64_t D) {
+struct FwdWs {
+    size_t slots, aggs, flags, stamp, total;  // offsets, and the size
+};
+FwdWs fwd_ws_layout(int64_t pairs, const Plan& p, int64_t D) {
+    FwdWs l{};
     const size_t slots = fwd_slot_bytes(pairs, p, D);
-    return slots ? round_up(slots) + kStampBytes : 0;
+    if (!slots) return l;
+    const size_t chunk_states = static_cast<size_t>(pairs) * static_cast<size_t>(p.chunks - 1);
+    l.aggs = round_up(slots);
+    l.flags = l.aggs + round_up(chunk_states * static_cast<size_t>(D * D) * sizeof(float));
+    l.stamp = l.flags + round_up(chunk_states * 4 * sizeof(uint64_t));
+    l.total = l.stamp + kStampBytes;
+    return l;
+}
+size_t fwd_ws_bytes(int64_t pairs, const Plan& p, int64_t D) { return fwd_ws_layout(pairs, p, D).total; }
+
+// Epochs of fused launches: distinct for every launch of the process (its flags hold the
+// epoch of the launch that set them), starting from a value no earlier process is likely
+// to have left in reused memory.
+std::atomic<uint64_t> g_epoch{0};
+uint64_t next_epoch() {
+    uint64_t e = g_epoch.load(std::memory_order_relaxed);
+    if (e == 0) {
+        std::random_device rd;
+        const uint64_t seed = (static_cast<uint64_t>(rd()) << 32) ^ rd() ^
+                              static_cast<uint64_t>(std::chrono::steady_clock::now().time_since_epoch().count());
+        uint64_t expected = 0;
+        g_epoch.compare_exchange_strong(expected, seed | 1);
+    }
+    uint64_t v;
+    do {
+        v = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    } while (v == 0);
+    return v;
+}
+
+// True when work enqueued on `s` now is being captured into a graph (a graph replays its
+// kernels with the arguments of the capture, so a fused launch's epoch would repeat).
+bool capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;
+    }
+    return st != hipStreamCaptureStatusNone;
 }
 
 uint32_t fnv1a(uint32_t h, const void* data, size_t n) {
@@ -361,18 +406,44 @@ struct PhiUse {
     const void* grad;  // raw tensor whose phi' multiplies the sweep's output, or nullptr
 };
 
-// `stamp_out` (forward pass): where the scan stores `stamp` after the chunk states;
-// `stamp_in` (dQ sweep fed `given`): the stamp stored after those states, checked
-// against `stamp`.
+// The fused chunked prefix (k_fwd_dma_fused: aggregates, their sum and the sweep in one
+// launch) pays off while a chunk has few earlier chunks to sum; LA_FUSED=0 / 1 switches it
+// off / on for every chunk count.
+constexpr int kMaxFusedChunks = 4;
+
+bool fused_wanted(const Plan& p) {
+    if (env_is("LA_FUSED", "0")) return false;
+    if (env_is("LA_FUSED", "1")) return true;
+    // measured faster only with few chunks and no aggregate parts (the fused form walks each
+    // chunk whole, and every chunk sums all earlier aggregates)
+    return p.chunks <= kMaxFusedChunks && p.agg_k == 1;
+}
+
+// `stamp_out` (forward pass): where the scan (or the fused sweep) stores `stamp` after the
+// chunk states; `stamp_in` (dQ sweep fed `given`): the stamp stored after those states,
+// checked against `stamp`.  `fused_aggs` / `fused_flags`: workspace for the fused chunked
+// prefix, or nullptr for the three-launch form.
 int run_forward_sweep(const void* q, const void* k, const void* v, void* out, const float* kv_in,
                       int kv_in_t, float* kv_out, float* slots, const float* given, int64_t pairs,
                       int64_t N, int64_t D, int32_t Bk, int32_t H, int bf16, const Plan& p,
                       const LamArgs& lam, const PhiUse& phi, hipStream_t s, const char* tag,
-                      uint32_t* stamp_out, const uint32_t* stamp_in, const la::Stamp& stamp) {
+                      uint32_t* stamp_out, const uint32_t* stamp_in, const la::Stamp& stamp,
+                      float* fused_aggs = nullptr, uint64_t* fused_flags = nullptr) {
     int rc;
     // the register-staged kernels have no feature map: with one, the generic kernels run
     const bool v1_ok = phi.kind == 0;
-    if (p.chunks > 1 && !given) {
+    // A 128-token block is stepped as two 64-token blocks by the 64-token kernel: the same
+    // function (the block size only decides which terms pass through a score tile and which
+    // through the carried state), the same bytes, and on this GPU the faster sweep (its LDS
+    // ring holds two 64-token blocks of look-ahead, where the 128-token kernel holds half a
+    // block).  The chunk boundaries stay on multiples of 128.  LA_FWD128=1 selects the
+    // 128-token kernel.
+    const bool step128 = Bk == 128 && env_is("LA_FWD128", "1");
+    const int32_t sweep_bk = (Bk == 128 && !step128) ? 64 : Bk;
+    const bool dma = p.mfma && la::fwd_dma_supported(static_cast<int>(D), sweep_bk, N) && !env_is("LA_FWD", "v1");
+    const int waves = env_is("LA_FWD_WAVES", "8") ? 8 : 4;
+    const bool fused = fused_flags && p.chunks > 1 && !given && dma && waves == 4 && fused_wanted(p) && !capturing(s);
+    if (p.chunks > 1 && !given && !fused) {
         // aggregates and scan over the agg_k parts of every chunk but the last
         const int64_t Lf = p.L / p.agg_k;
         const int chunks_f = (p.chunks - 1) * p.agg_k + 1;
@@ -416,18 +487,16 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
     a.phi_mask = phi.sweep_mask;
     a.phi_grad = phi.grad;
     a.slot_k = p.agg_k;
-    // A 128-token block is stepped as two 64-token blocks by the 64-token kernel: the same
-    // function (the block size only decides which terms pass through a score tile and which
-    // through the carried state), the same bytes, and on this GPU the faster sweep (its LDS
-    // ring holds two 64-token blocks of look-ahead, where the 128-token kernel holds half a
-    // block).  The chunk boundaries stay on multiples of 128.  LA_FWD128=1 selects the
-    // 128-token kernel.
-    const bool step128 = Bk == 128 && env_is("LA_FWD128", "1");
-    const int32_t sweep_bk = (Bk == 128 && !step128) ? 64 : Bk;
-    if (p.mfma && la::fwd_dma_supported(static_cast<int>(D), sweep_bk, N) && !env_is("LA_FWD", "v1")) {
-        const int waves = env_is("LA_FWD_WAVES", "8") ? 8 : 4;
+    if (fused) {
+        a.fused_aggs = fused_aggs;
+        a.fused_flags = fused_flags;
+        a.epoch = next_epoch();
+        a.stamp_store = stamp_out;
+    }
+    if (dma) {
         a.Bk = sweep_bk;
-        return launch(tag[0] == 'd' ? "dq_dma" : "fwd_dma", s, [&] { la::launch_fwd_dma(a, lam, waves, s); });
+        return launch(fused ? (tag[0] == 'd' ? "dq_dma_fused" : "fwd_dma_fused") : (tag[0] == 'd' ? "dq_dma" : "fwd_dma"),
+                      s, [&] { la::launch_fwd_dma(a, lam, waves, s); });
     }
     if (p.mfma && la::fwd_dma128_supported(static_cast<int>(D), Bk, N) && !env_is("LA_FWD", "v1"))
         return launch(tag[0] == 'd' ? "dq_dma128" : "fwd_dma128", s, [&] { la::launch_fwd_dma128(a, lam, s); });
@@ -516,8 +585,10 @@ int fwd_entry(const void* Q, const void* K, const void* V, const float* lambda, 
     if (!plan_grid_ok(B * H, p, D)) return LA_EUNSUPPORTED;
     const int32_t Bk_call = Bk;  // as asked (the stamp records it)
     Bk = p.bk;  // the block the kernels step
-    // the static scratch holds the chunk states only; a caller workspace also the stamp
-    const size_t need = use_scratch ? fwd_slot_bytes(B * H, p, D) : fwd_ws_bytes(B * H, p, D);
+    // the static scratch holds the chunk states (and the fused prefix's aggregates and
+    // flags when they fit); a caller workspace also the stamp
+    const FwdWs lay = fwd_ws_layout(B * H, p, D);
+    const size_t need = use_scratch ? fwd_slot_bytes(B * H, p, D) : lay.total;
     if (use_scratch) {
         if (need > kScratchBytes) return LA_ESCRATCH;
     } else if (need && (!ws || ws_bytes < need)) {
@@ -536,13 +607,15 @@ int fwd_entry(const void* Q, const void* K, const void* V, const float* lambda, 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const PhiUse pu{phi, 3, 1, nullptr};  // phi(q), phi(k); the aggregates map k
     const NoEventsGuard quiet(use_scratch);
-    uint32_t* stamp_out = (!use_scratch && need)
-                              ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + round_up(fwd_slot_bytes(B * H, p, D)))
-                              : nullptr;
+    char* wsb = static_cast<char*>(ws);
+    uint32_t* stamp_out = (!use_scratch && need) ? reinterpret_cast<uint32_t*>(wsb + lay.stamp) : nullptr;
+    const bool fused_room = need && (!use_scratch || lay.stamp <= kScratchBytes);
+    float* fused_aggs = fused_room ? reinterpret_cast<float*>(wsb + lay.aggs) : nullptr;
+    uint64_t* fused_flags = fused_room ? reinterpret_cast<uint64_t*>(wsb + lay.flags) : nullptr;
     const la::Stamp stamp = make_stamp(B, H, N, D, Bk_call, dtype, phi, p, lam, Q, K, V, kv_in);
     return run_forward_sweep(Q, K, V, O, kv_in, 0, kv_out, static_cast<float*>(ws), nullptr, B * H, N, D,
                              Bk, static_cast<int32_t>(H), dtype == LA_BF16, p, lam, pu, s, "fwd", stamp_out,
-                             nullptr, stamp);
+                             nullptr, stamp, fused_aggs, fused_flags);
 }
 
 // A ragged batch is launched in groups of at most kMaxVarlenSeqs sequences (the batch table
@@ -716,7 +789,8 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     // phi'(q) on the output
     const PhiUse pu{phi, 4, 2, phi ? Q : nullptr};
     const uint32_t* stamp_in =
-        (fwd_ws && fq) ? reinterpret_cast<const uint32_t*>(static_cast<const char*>(fwd_ws) + round_up(fq)) : nullptr;
+        (fwd_ws && fq) ? reinterpret_cast<const uint32_t*>(static_cast<const char*>(fwd_ws) + fwd_ws_layout(pairs, p, D).stamp)
+                       : nullptr;
     rc = run_forward_sweep(dO, V, K, dQ, kv_in, 1, nullptr, slots_q, static_cast<const float*>(fwd_ws), pairs,
                            N, D, Bk, Hi, bf16, p, lam, pu, s, "dq", nullptr, stamp_in, stamp);
     if (rc) return rc;

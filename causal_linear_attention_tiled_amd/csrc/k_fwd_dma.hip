@@ -55,9 +55,28 @@ struct DmaTiles {
     alignas(16) float wk[2][BK];
 };
 
-template <int NW, bool VARLEN, bool PHI>
+// FUSED: the chunked prefix in the same launch.  A workgroup whose chunk is not the last
+// first walks its chunk's K and V (phase 1: the state update from zero, loads of K and V
+// only) and publishes that chunk aggregate, per compute wave (each wave owns its value
+// columns), followed by a flag holding the call's epoch; then (phase 2) each wave waits for
+// the same wave of every earlier chunk of its sequence and sums their aggregates into its
+// starting state, S = lam^(cL) S0 + sum_j lam^((c-1-j)L) dS_j, stores it where la_fwd
+// keeps the states entering chunks, and sweeps its chunk (phase 3).  A workgroup waits only
+// on lower workgroup indices, which the hardware dispatches first, so every awaited
+// workgroup is running or done; the wait is bounded all the same (kFusedSpinLimit polls),
+// and a wave that gives up starts from NaN instead of hanging.
+// The aggregates and flags travel as agent-scope atomic stores and loads, which the
+// hardware keeps coherent across the XCDs' separate L2 caches line by line.  A wave raises
+// its flag only after its aggregate stores have completed (vmcnt 0), and a waiting wave
+// issues its aggregate loads only after it has read the flag, so the loads see the stores.
+// Agent-scope release/acquire fences would give the same order through a write-back and an
+// invalidate of the whole L2, which cost more than the two launches this form saves.
+constexpr int kFusedSpinLimit = 1 << 17;
+
+template <int NW, bool VARLEN, bool PHI, bool FUSED = false>
 __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam, const VarlenArgs* var) {
     constexpr int NVT = 8 / NW;  // 16-column value tiles per compute wave
+    static_assert(!FUSED || (!VARLEN && NW == 4), "the fused prefix is for dense sequences, 4 compute waves");
     __shared__ DmaTiles sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
     const Work wk = work_item<VARLEN>(a, var, blockIdx.x);
@@ -67,6 +86,11 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
     const int64_t nblk = (t_end - t_begin + BK - 1) / BK;
     const int64_t base = wk.base;
     const int64_t ld = VARLEN ? wk.ld : D;  // elements between token rows
+    // FUSED: blocks 0 .. nblk1 - 1 walk the chunk for its aggregate (every chunk but the last
+    // is whole), blocks nblk1 .. ntot - 1 sweep it
+    const int64_t nblk1 = (FUSED && c < wk.chunks - 1) ? nblk : 0;
+    const int64_t ntot = nblk1 + nblk;
+    const int64_t pair = wk.state;
 
     for (int e = tid; e <= BK; e += 64 * (NW + 1)) sm.pw[e] = lam_pow(lv, e);
     const int m_last = nblk > 0 ? static_cast<int>(t_end - t_begin - (nblk - 1) * BK) : BK;
@@ -87,9 +111,11 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
         const int sub = lane >> 4, p = lane & 15;
         auto issue = [&](int64_t n) {
             const int stage = static_cast<int>(n % NSTAGE);
-            const int64_t t0 = t_begin + n * BK;
+            const bool walk = FUSED && n < nblk1;  // phase 1: K and V only
+            const int64_t t0 = t_begin + (walk ? n : n - nblk1) * BK;
 #pragma unroll
             for (int x = 0; x < 3; ++x)
+                if (!(walk && x == 0))
 #pragma unroll
                 for (int rg = 0; rg < BK / 4; ++rg) {
                     const int r = 4 * rg + sub;
@@ -98,18 +124,23 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[x], (lds_void*)&sm.t[stage][x][4 * rg * D], 16, voff, 0, 0, 0);
                 }
         };
-        if (nblk > 0) issue(0);
-        if (nblk > 1) issue(1);
+        if (ntot > 0) issue(0);
+        if (ntot > 1) issue(1);
         // The loader's own vmcnt wait makes its LDS writes complete before it
         // reaches A(n); a fenced __syncthreads() here would also wait for the
         // loads still in flight, so the loader uses the bare barrier.
-        for (int64_t n = 0; n < nblk; ++n) {
-            if (n + 1 < nblk)
-                wait_vmcnt<DMA_PER_BLOCK>();
-            else
+        for (int64_t n = 0; n < ntot; ++n) {
+            // block n + 1 may still be in flight: 2/3 of a block's loads in phase 1
+            if (n + 1 < ntot) {
+                if (FUSED && n + 1 < nblk1)
+                    wait_vmcnt<2 * BK / 4>();
+                else
+                    wait_vmcnt<DMA_PER_BLOCK>();
+            } else {
                 wait_vmcnt<0>();
+            }
             __builtin_amdgcn_s_barrier();  // A(n): stage n is ready; stage (n+2) % 3 is free
-            if (n + 2 < nblk) issue(n + 2);
+            if (n + 2 < ntot) issue(n + 2);
             if constexpr (PHI) __builtin_amdgcn_s_barrier();  // T(n): feature map applied
             __builtin_amdgcn_s_barrier();  // B(n)
         }
@@ -120,7 +151,12 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
     uint16_t* __restrict__ Og = static_cast<uint16_t*>(a.out0) + base;
     // S[at][vt][r] = S[32 (at/2) + rho(at%2, 4g + r)][16 (NVT w + vt) + li]
     f32x4 S[8][NVT];
-    {
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int at = 0; at < 8; ++at)
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt) S[at][vt] = zero4();
+    } else {
         const float* init = nullptr;
         bool tr = false, poison = false;
         if (c == 0) {
@@ -158,14 +194,142 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
 #pragma unroll
     for (int st = 0; st < NT; ++st) rs[st] = sm.pw[16 * st + li + 1];
 
+    if constexpr (FUSED) {
+        // ---- phase 1: S <- lam^64 S + K^T diag(lam^(63-s)) V over the (whole) chunk, from zero
+        for (int64_t nn = 0; nn < nblk1; ++nn) {
+            const int stage = static_cast<int>(nn % NSTAGE);
+            const uint16_t* Ks = sm.t[stage][1];
+            const uint16_t* Vs = sm.t[stage][2];
+            __syncthreads();  // A(nn)
+            if constexpr (PHI) {
+#pragma unroll
+                for (int x = 1; x < 3; ++x)
+                    if (a.phi_mask & (1 << x)) phi_tile(sm.t[stage][x], a.phi, tid, 64 * NW);
+                __syncthreads();  // T(nn)
+            }
+            __syncthreads();  // B(nn)
+            const float lm = sm.pw[BK];
+            const f32x4 w00 = lane_weights(sm.wk[0], 0, g, 0), w01 = lane_weights(sm.wk[0], 0, g, 1);
+            const f32x4 w10 = lane_weights(sm.wk[0], 1, g, 0), w11 = lane_weights(sm.wk[0], 1, g, 1);
+            const float wkb[NKB][8] = {{w00[0], w00[1], w00[2], w00[3], w01[0], w01[1], w01[2], w01[3]},
+                                       {w10[0], w10[1], w10[2], w10[3], w11[0], w11[1], w11[2], w11[3]}};
+            bf16x8 vw[NVT][NKB];
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+                    vw[vt][kb] = scale8(op_tr_k(Vs, 32 * kb, 16 * (NVT * w + vt), 4, g, li), wkb[kb]);
+#pragma unroll
+            for (int at = 0; at < 8; ++at) {
+#pragma unroll
+                for (int vt = 0; vt < NVT; ++vt) S[at][vt] *= lm;
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const bf16x8 kf = op_tr_k(Ks, 32 * kb, 32 * (at >> 1) + 4 * (at & 1), 8, g, li);
+#pragma unroll
+                    for (int vt = 0; vt < NVT; ++vt) S[at][vt] = mfma16(kf, vw[vt][kb], S[at][vt]);
+                }
+            }
+        }
+        if (nblk1 > 0) {
+            // publish this wave's columns of the chunk aggregate, then its flag
+            float* agg = a.fused_aggs + (pair * (wk.chunks - 1) + c) * D * D;
+#pragma unroll
+            for (int at = 0; at < 8; ++at)
+#pragma unroll
+                for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        __hip_atomic_store(agg + (32 * (at >> 1) + rho(at & 1, 4 * g + r)) * D + 16 * (NVT * w + vt) + li,
+                                           S[at][vt][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // the flag goes out only once every one of those stores has completed
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            wait_vmcnt<0>();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (lane == 0)
+                __hip_atomic_store(a.fused_flags + (pair * (wk.chunks - 1) + c) * NW + w, a.epoch,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+
+        // ---- phase 2: the state entering this chunk, this wave's columns, Horner over the
+        //      earlier chunks: S = lam^L (... (lam^L S0 + dS_0) ...) + dS_(c-1)
+        const float* s0 = a.kv_in ? a.kv_in + pair * D * D : nullptr;
+        const float lamL = lam_pow(lv, a.L);
+#pragma unroll
+        for (int at = 0; at < 8; ++at)
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt) {
+                const int col = 16 * (NVT * w + vt) + li;
+                const int row0 = 32 * (at >> 1) + rho(at & 1, 4 * g);
+                f32x4 x = zero4();
+                if (s0) {
+                    if (a.kv_in_transposed) {
+                        const float4 t4 = *reinterpret_cast<const float4*>(s0 + col * D + row0);
+                        x = f32x4{t4.x, t4.y, t4.z, t4.w};
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) x[r] = s0[(row0 + r) * D + col];
+                    }
+                }
+                S[at][vt] = x;
+            }
+        bool ok = true;
+        for (int j = 0; j < c; ++j) {
+            // wait (bounded) for wave w of chunk j, which was dispatched before this workgroup
+            const uint64_t* flag = a.fused_flags + (pair * (wk.chunks - 1) + j) * NW + w;
+            int spins = 0;
+            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
+                if (++spins >= kFusedSpinLimit) {
+                    ok = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the loads below stay after the flag's
+            const float* agg = a.fused_aggs + (pair * (wk.chunks - 1) + j) * D * D;
+#pragma unroll
+            for (int at = 0; at < 8; ++at)
+#pragma unroll
+                for (int vt = 0; vt < NVT; ++vt) {
+                    const int col = 16 * (NVT * w + vt) + li;
+                    const int row0 = 32 * (at >> 1) + rho(at & 1, 4 * g);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        S[at][vt][r] = lamL * S[at][vt][r] +
+                                       __hip_atomic_load(agg + (row0 + r) * D + col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+        }
+        if (!ok) {
+#pragma unroll
+            for (int at = 0; at < 8; ++at)
+#pragma unroll
+                for (int vt = 0; vt < NVT; ++vt)
+                    S[at][vt] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        }
+        if (c > 0 && a.slots) {
+            // where the three-launch form keeps the states entering chunks (la_bwd's fwd_ws)
+            float* dst = const_cast<float*>(a.slots) + (wk.slot0 + static_cast<int64_t>(c - 1) * wk.slot_step) * D * D;
+#pragma unroll
+            for (int at = 0; at < 8; ++at)
+#pragma unroll
+                for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        dst[(32 * (at >> 1) + rho(at & 1, 4 * g + r)) * D + 16 * (NVT * w + vt) + li] = S[at][vt][r];
+        }
+        if (a.stamp_store && pair == 0 && c == 0 && w == 0 && lane == 0)
+            for (int i = 0; i < kStampWords; ++i) a.stamp_store[i] = a.expect.w[i];
+    }
+
     for (int64_t n = 0; n < nblk; ++n) {
-        const int64_t t0 = t_begin + n * BK;
-        const int m = static_cast<int>(min(static_cast<int64_t>(BK), t_end - t0));
-        const int stage = static_cast<int>(n % NSTAGE);
+        const int64_t nn = n + nblk1;  // the ring counts phase 1's blocks too
+        const int stage = static_cast<int>(nn % NSTAGE);
         const uint16_t* Qs = sm.t[stage][0];
         const uint16_t* Ks = sm.t[stage][1];
         const uint16_t* Vs = sm.t[stage][2];
-        __syncthreads();  // A(n)
+        const int64_t t0 = t_begin + n * BK;
+        const int m = static_cast<int>(min(static_cast<int64_t>(BK), t_end - t0));
+        __syncthreads();  // A(nn)
         if constexpr (PHI) {
             // the feature map on this block's query and key tiles (in the dQ sweep: the keys,
             // which sit in the value slot), once, in place
@@ -326,6 +490,11 @@ __global__ __launch_bounds__(64 * (NW + 1), 1) void k_fwd_dma(SweepArgs a, LamAr
 }
 
 template <bool PHI>
+__global__ __launch_bounds__(64 * 5, 1) void k_fwd_dma_fused(SweepArgs a, LamArgs lam) {
+    fwd_body<4, false, PHI, true>(a, lam, nullptr);
+}
+
+template <bool PHI>
 __global__ __launch_bounds__(64 * 5, 1) void k_fwd_dma_varlen(SweepArgs a, LamArgs lam, VarlenArgs v) {
     fwd_body<4, true, PHI>(a, lam, &v);
 }
@@ -346,6 +515,13 @@ void launch_fwd_dma_varlen(const SweepArgs& a, const LamArgs& lam, const VarlenA
 
 void launch_fwd_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(a.pairs * a.chunks));
+    if (a.fused_flags) {
+        if (a.phi)
+            hipLaunchKernelGGL(k_fwd_dma_fused<true>, grid, dim3(64 * 5), 0, s, a, lam);
+        else
+            hipLaunchKernelGGL(k_fwd_dma_fused<false>, grid, dim3(64 * 5), 0, s, a, lam);
+        return;
+    }
     if (waves == 8) {
         if (a.phi)
             hipLaunchKernelGGL((k_fwd_dma<8, true>), grid, dim3(64 * 9), 0, s, a, lam);

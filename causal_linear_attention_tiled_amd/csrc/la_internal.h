@@ -58,6 +58,13 @@ struct SweepArgs {
     const uint32_t* stamp;// with slots_transposed: the stamp stored after those states;
                           // chunks whose words differ from `expect` start from a NaN state
     Stamp expect;
+    // the fused chunked prefix (k_fwd_dma_fused): per-chunk aggregates [P][chunks-1][D][D],
+    // their flags [P][chunks-1][4] (one per compute wave, set to `epoch`), and where the
+    // first workgroup stores `expect` as the workspace stamp (or nullptr)
+    float* fused_aggs;
+    uint64_t* fused_flags;
+    uint64_t epoch;
+    uint32_t* stamp_store;
     float* kv_out;        // [P][D][D] final state (forward only) or nullptr
     const float* g_final; // reverse only: [P][D][D] gradient arriving at the final state, the
                           // dS the last chunk starts from, or nullptr for zero
@@ -206,6 +213,8 @@ void launch_chunk_state_mfma(const ChunkStateArgs& a, const LamArgs& lam, hipStr
 
 // Forward sweep with direct-to-LDS loads (bf16, D = 128, Bk = 64); `waves` compute waves (4 or 8).
 bool fwd_dma_supported(int D, int Bk, int64_t N);
+// With a.fused_flags set: the fused chunked prefix (4 compute waves), no aggregate or scan
+// launch before it.
 void launch_fwd_dma(const SweepArgs& a, const LamArgs& lam, int waves, hipStream_t s);
 // The same over a ragged batch: one workgroup per (chunk of a sequence, head), wp[nseq] * H in all.
 void launch_fwd_dma_varlen(const SweepArgs& a, const LamArgs& lam, const VarlenArgs& v, hipStream_t s);

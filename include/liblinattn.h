@@ -113,7 +113,18 @@ enum {
  *             On return it holds the key-value state at the end of every
  *             chunk but the last (float32) and a stamp identifying this call,
  *             which la_bwd can take as fwd_ws instead of computing the states
- *             again. */
+ *             again.
+ * When the sequence is split into at most 4 chunks without aggregate parts
+ * (la_plan), on the 64-token sweep, the chunked
+ * prefix runs inside the sweep's own launch: each chunk's workgroup first
+ * aggregates its chunk, publishes it with a flag carrying a number unique to
+ * the call, and sums the aggregates of the earlier chunks of its sequence
+ * before sweeping (a workgroup waits only on workgroups dispatched before
+ * it; the wait is bounded, and a wave that gives up makes its columns NaN).
+ * Under HIP graph capture, and with LA_FUSED=0, the aggregates and their
+ * prefix run as two launches before the sweep instead (LA_FUSED=1 fuses any
+ * chunk count, which is slower with more chunks or with parts).  The two
+ * forms round differently (within float rounding of the same sums). */
 int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int64_t B, int64_t H,
            int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t phi, const float* kv_in, void* O,
            float* kv_out, void* ws, size_t ws_bytes, void* hip_stream);

@@ -96,12 +96,14 @@ def test_workspace_sizes():
     # enough sequences to fill the chip: no chunks, no workspace
     assert la.la_fwd_workspace_bytes(128, 16, 1024, 128, 64, la.LA_BF16) == 0
     assert la.la_bwd_workspace_bytes(128, 16, 1024, 128, 64, la.LA_BF16) == 0
-    # few long sequences: chunked, workspace holds (chunks-1) D x D float32 states per sequence,
-    # then a 256-byte stamp
+    # few long sequences: chunked; the workspace holds (chunks-1) x parts D x D float32 states
+    # per sequence, the fused prefix's (chunks-1) aggregates and 4 flags per sequence, then a
+    # 256-byte stamp (each region from a 256-byte boundary)
     n = la.la_fwd_workspace_bytes(2, 16, 65536, 128, 64, la.LA_BF16)
-    assert n > 256 and (n - 256) % (128 * 128 * 4 * 32) == 0
+    state = 128 * 128 * 4
+    assert n == 32 * 7 * state + 32 * 7 * state + 32 * 7 * 4 * 8 + 256
     # the backward holds the forward direction's slots (for its dQ sweep) and the reverse ones
-    assert la.la_bwd_workspace_bytes(2, 16, 65536, 128, 64, la.LA_BF16) > n
+    assert la.la_bwd_workspace_bytes(2, 16, 65536, 128, 64, la.LA_BF16) == 2 * 32 * 7 * state
     # invalid shapes report 0
     assert la.la_fwd_workspace_bytes(0, 16, 1024, 128, 64, la.LA_BF16) == 0
     assert la.la_fwd_workspace_bytes(1, 16, 1024, 100, 64, la.LA_BF16) == 0
@@ -262,8 +264,10 @@ def test_plan():
     p = la.la_plan(1, 2, 1000, 64, 32, la.LA_F32)
     assert p["chunks"] > 1 and p["chunk_len"] % 32 == 0 and (p["chunks"] - 1) * p["chunk_len"] < 1000
     # forward workspace: agg_parts float32 D x D slots per chunk boundary per sequence
-    # (then a 256-byte stamp identifying the forward call, checked by la_bwd when given as fwd_ws)
-    assert la.la_fwd_workspace_bytes(2, 16, 65536, 128, 64, la.LA_BF16) == 32 * 7 * 1 * 128 * 128 * 4 + 256
+    # (then the fused prefix's aggregates and flags, and a 256-byte stamp identifying the forward
+    # call, checked by la_bwd when given as fwd_ws)
+    assert la.la_fwd_workspace_bytes(2, 16, 65536, 128, 64, la.LA_BF16) == \
+        2 * 32 * 7 * 128 * 128 * 4 + 32 * 7 * 32 + 256
     with pytest.raises(la.LaError):
         la.la_plan(1, 16, 1024, 100, 64, la.LA_BF16)
     # a 256-token block: chunk boundaries on multiples of 256 (the kernels step 128-token blocks)

@@ -554,3 +554,58 @@ def test_checkpoint_host_roundtrip_bit_identical():
     for x, y in zip(b_dev, b_host):
         assert torch.equal(x, y)
     assert torch.equal(d_dev, d_host) and torch.equal(st_dev, st_host)
+
+
+# ------------------------------------------------------------------ the fused chunked prefix
+@pytest.fixture
+def fused(monkeypatch):
+    """LA_FUSED=1: la_fwd's chunked prefix in one launch for every chunk count; 0: never."""
+    def set_(on):
+        monkeypatch.setenv("LA_FUSED", "1" if on else "0")
+    return set_
+
+
+@pytest.mark.parametrize("on", [True, False])
+@pytest.mark.parametrize("cks,N,with_state,Bk", [(2, 64 * 9 + 17, True, 64), (3, 64 * 13 + 5, True, 64),
+                                                 (4, 2048, False, 64), (7, 64 * 21 + 1, True, 64),
+                                                 (16, 64 * 40, True, 64), (3, 128 * 9 + 17, True, 128),
+                                                 (2, 256 * 5 + 17, False, 256)])
+def test_fused_prefix_parity(on, cks, N, with_state, Bk, fused, chunks):
+    """The forward with its chunk aggregates, their sum and the sweep in one launch (or not),
+    and the backward fed that forward's chunk states (fwd_ws), against the oracle."""
+    fused(on)
+    chunks(cks)
+    lam = synth.decay_schedule(3)
+    check_fwd(2, 3, N, 128, Bk, "bf16", lam, seed=N + cks, with_state=with_state, label=f"fused={on}")
+    check_bwd(2, 3, N, 128, Bk, "bf16", lam, seed=N + cks, with_state=with_state, label=f"fused={on}",
+              fwd_ws=True)
+
+
+@pytest.mark.parametrize("lam_val", [1.0, 0.5])
+@pytest.mark.parametrize("Bk,cks", [(64, 2), (64, 4), (64, 7), (128, 3), (256, 2)])
+def test_fused_prefix_impulse(fused, lam_val, Bk, cks, chunks, kernel):
+    """Bit-exact impulse probes through the fused prefix: keys on chunk boundaries and their
+    neighbours, their contributions carried by the aggregates and summed in phase 2."""
+    fused(True)
+    test_impulse_probe_bit_exact("default", lam_val, Bk, cks, chunks, kernel)
+
+
+def test_fused_prefix_repeat_and_reuse(fused, chunks):
+    """Back-to-back fused calls on one workspace (each with its own epoch: no flag of an earlier
+    call may be taken for this one's), bit-identical to each other, with the workspace reused
+    across calls on other inputs in between."""
+    fused(True)
+    chunks(4)
+    B, H, N, D = 2, 4, 2048, 128
+    lam = synth.decay_schedule(H)
+    _, (q, k, v), _ = inputs(91, B, H, N, D, "bf16")
+    _, (q2, k2, v2), _ = inputs(92, B, H, N, D, "bf16")
+    ws = torch.empty(la.la_fwd_workspace_bytes(B, H, N, D, 64, la.LA_BF16), dtype=torch.uint8, device="cuda")
+    o1, s1 = la.la_fwd(q, k, v, lam, ws=ws)
+    o2, s2 = la.la_fwd(q2, k2, v2, lam, ws=ws)
+    o3, s3 = la.la_fwd(q, k, v, lam, ws=ws)
+    o4, s4 = la.la_fwd(q2, k2, v2, lam, ws=ws)
+    _sync()
+    assert torch.equal(o1, o3) and torch.equal(s1, s3)
+    assert torch.equal(o2, o4) and torch.equal(s2, s4)
+    assert not torch.equal(o1, o2)
