@@ -49,12 +49,15 @@ CALIB_BYTES = 1 << 30      # bytes read and written by the calibration copy
 DEVICE_FN = {
     "fwd_dma": "k_fwd_dma", "dq_dma": "k_fwd_dma", "fwd_mfma": "k_fwd_mfma", "dq_mfma": "k_fwd_mfma",
     "dkdv_dma": "k_rev_dma_split", "dkdv_mfma": "k_rev_mfma", "dkdv_generic": "k_rev_generic",
-    "chunk_state_dma": "k_chunk_state_dma", "chunk_state_rev_dma": "k_chunk_state_dma",
+    "fwd_dma_fused": "k_fwd_dma_fused", "dq_dma_fused": "k_fwd_dma_fused",
+    # the chunk aggregates' default form (two loader waves); LA_STATE=dma2 runs k_chunk_state_dma
+    "chunk_state_dma": "k_chunk_state_ld", "chunk_state_rev_dma": "k_chunk_state_ld",
     "chunk_state_mfma": "k_chunk_state_mfma", "chunk_state_rev_mfma": "k_chunk_state_mfma",
     "state_scan": "k_scan", "state_scan_rev": "k_scan", "decode": "k_decode",
 }
 KERNEL_SOURCES = {         # device function -> source file its code lives in
-    "k_fwd_dma": "k_fwd_dma.hip", "k_fwd_mfma": "k_fwd_mfma.hip", "k_rev_dma": "k_bwd_dma.hip",
+    "k_fwd_dma": "k_fwd_dma.hip", "k_fwd_dma_fused": "k_fwd_dma.hip", "k_fwd_mfma": "k_fwd_mfma.hip",
+    "k_rev_dma": "k_bwd_dma.hip", "k_chunk_state_ld": "k_state_dma.hip",
     "k_rev_dma_split": "k_bwd_dma.hip",
     "k_rev_mfma": "k_bwd_mfma.hip", "k_rev_generic": "k_generic.hip", "k_chunk_state_dma": "k_state_dma.hip",
     "k_chunk_state_mfma": "k_fwd_mfma.hip", "k_scan": "k_generic.hip", "k_decode": "k_generic.hip",
