@@ -656,6 +656,68 @@ bool varlen_supported(int32_t dtype, int64_t D, int32_t Bk) {
     return dtype == LA_BF16 && D == 128 && (Bk == 64 || Bk == 128 || Bk == 256);
 }
 
+// The ragged forward for every shape the direct-to-LDS kernels do not take (float32
+// storage, D != 128, Bk of 16 or 32): the generic kernels, one workgroup per (sequence,
+// head) over the whole sequence, in groups of kMaxVarlenSeqs sequences.  No chunks, so no
+// workspace.
+int fwd_varlen_generic(const void* Q, const void* K, const void* V, const float* lambda, const int64_t* offs,
+                       int64_t B, int64_t H, int64_t D, int32_t Bk, int32_t dtype, int32_t phi,
+                       const float* kv_in, void* O, float* kv_out, void* hip_stream) {
+    if (!offs || B <= 0 || H <= 0 || D <= 0) return LA_EINVAL;
+    if (offs[0] != 0) return LA_EINVAL;
+    for (int64_t b = 0; b < B; ++b)
+        if (offs[b + 1] < offs[b]) return LA_EINVAL;
+    if (!supported_D(D) || !supported_Bk(Bk) || H > la::kMaxHeads) return LA_EUNSUPPORTED;
+    const int64_t T = offs[B];
+    if (T >= (int64_t(1) << 31)) return LA_EUNSUPPORTED;  // token offsets travel as int32
+    if (T > 0 && (!Q || !K || !V || !O)) return LA_EINVAL;
+    LamArgs lam;
+    int rc = load_lambda(lambda, H, &lam);
+    if (rc) return rc;
+    for (const void* ptr : {Q, K, V, static_cast<const void*>(O), static_cast<const void*>(kv_in),
+                            static_cast<const void*>(kv_out)})
+        if (ptr && !aligned16(ptr)) return LA_EALIGN;
+    const size_t esize = dtype == LA_BF16 ? 2 : 4;
+    int64_t elems = 0, spairs = 0;
+    if (!mul_ok(T, H * D, &elems) || !mul_ok(B, H, &spairs)) return LA_EINVAL;
+    const size_t tb = static_cast<size_t>(elems) * esize;
+    const size_t sb = static_cast<size_t>(spairs) * static_cast<size_t>(D * D) * sizeof(float);
+    const Range rq{Q, tb}, rk{K, tb}, rv{V, tb}, ro{O, tb}, rin{kv_in, kv_in ? sb : 0},
+        rout{kv_out, kv_out ? sb : 0};
+    for (const Range& r : {rq, rk, rv, rin})
+        if (overlap(ro, r) || overlap(rout, r)) return LA_EINVAL;
+    if (overlap(ro, rout)) return LA_EINVAL;
+
+    int dev_count = 0;
+    if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count == 0) return LA_ENODEV;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    for (int64_t b0 = 0; b0 < B; b0 += la::kMaxVarlenSeqs) {
+        const int64_t nb = std::min<int64_t>(la::kMaxVarlenSeqs, B - b0);
+        const int64_t t0 = offs[b0];
+        if (offs[b0 + nb] == t0 && !kv_out) continue;  // nothing to read or write
+        la::VarlenArgs v{};
+        v.nseq = static_cast<int>(nb);
+        for (int64_t i = 0; i <= nb; ++i) v.cu[i] = static_cast<int>(offs[b0 + i] - t0);
+        const size_t tok = static_cast<size_t>(t0 * H * D) * esize;
+        la::SweepArgs a{};
+        a.a = static_cast<const char*>(Q) + tok;
+        a.b = static_cast<const char*>(K) + tok;
+        a.c = static_cast<const char*>(V) + tok;
+        a.out0 = static_cast<char*>(O) + tok;
+        a.kv_in = kv_in ? kv_in + b0 * H * D * D : nullptr;
+        a.kv_out = kv_out ? kv_out + b0 * H * D * D : nullptr;
+        a.D = static_cast<int>(D);
+        a.Bk = std::min(Bk, kMaxKernelBk);  // the same function at any block size; no chunks here
+        a.H = static_cast<int32_t>(H);
+        a.phi = phi;
+        a.phi_mask = 3;
+        if ((rc = launch("fwd_varlen_generic", s,
+                         [&] { la::launch_fwd_generic_varlen(a, lam, v, dtype == LA_BF16, s); })))
+            return rc;
+    }
+    return LA_OK;
+}
+
 // LA_TRACE=1: the plan of one group of a ragged batch.
 void trace_varlen(int64_t nb, int64_t H, const VarPlan& p) {
     const char* e = std::getenv("LA_TRACE");
@@ -936,10 +998,12 @@ int la_fwd_varlen(const void* Q, const void* K, const void* V, const float* lamb
                   void* O, float* kv_out, void* ws, size_t ws_bytes, void* hip_stream) {
     if (dtype != LA_F32 && dtype != LA_BF16) return LA_EINVAL;
     if (!valid_phi(phi)) return LA_EINVAL;
+    if (!varlen_supported(dtype, D, Bk))
+        return fwd_varlen_generic(Q, K, V, lambda, seq_offsets, B, H, D, Bk, dtype, phi, kv_in, O, kv_out,
+                                  hip_stream);
     std::vector<VarGroup> groups;
     int rc = varlen_groups(seq_offsets, B, H, D, Bk, &groups);
     if (rc) return rc;
-    if (!varlen_supported(dtype, D, Bk)) return LA_EUNSUPPORTED;
     const int64_t T = seq_offsets[B];
     if (T > 0 && (!Q || !K || !V || !O)) return LA_EINVAL;
     LamArgs lam;

@@ -27,25 +27,73 @@ __device__ __forceinline__ void fill_powers(float* pw, float lam, int Bk) {
     for (int e = threadIdx.x; e <= Bk; e += kThreads) pw[e] = lam_pow(lam, e);
 }
 
-// Forward sweep over one chunk:
+// Forward sweep over tokens [t_begin, t_end) of one (sequence, head), whose token rows
+// start at element base and lie pitch elements apart:
 //   O_b = diag(lam^(s+1)) Q_b S + (Q_b K_b^T o M) V_b,  S <- lam^m S + (diag(lam^(m-1-s)) K_b)^T V_b
+// starting from init (or zero; read transposed when `transposed`; NaN when `poison`) and
+// leaving the final state in kv_dst (unless null).
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs lam) {
-    __shared__ Tile sh;
-    const int64_t pair = blockIdx.x / a.chunks;
-    const int c = blockIdx.x % a.chunks;
+__device__ void generic_sweep(const SweepArgs& a, Tile& sh, float lv, int64_t t_begin, int64_t t_end,
+                              int64_t base, int64_t pitch, const float* init, bool transposed, bool poison,
+                              float* kv_dst) {
     const int D = a.D, Bk = a.Bk, tid = threadIdx.x;
-    const float lv = lam.lam[pair % a.H];
-    const int64_t t_begin = static_cast<int64_t>(c) * a.L;
-    const int64_t t_end = min(a.N, t_begin + a.L);
-    const int64_t base = pair * a.N * D;
     // operand x of slot bit (0: a, 1: b, 2: c), through the feature map when that slot takes it
     auto opd = [&](const void* p, int bit, int64_t i) {
         const float x = ld<BF16>(p, i);
         return (a.phi && ((a.phi_mask >> bit) & 1)) ? phi_apply(x, a.phi) : x;
     };
     fill_powers(sh.pw, lv, Bk);
+    for (int i = tid; i < D * D; i += kThreads) {
+        float x = 0.f;
+        if (init) x = transposed ? init[(i % D) * D + i / D] : init[i];
+        sh.state[i] = poison ? __builtin_nanf("") : x;
+    }
+    __syncthreads();
 
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += Bk) {
+        const int m = static_cast<int>(min(static_cast<int64_t>(Bk), t_end - t0));
+        const int64_t r0 = base + t0 * pitch;
+        for (int i = tid; i < m * m; i += kThreads) {
+            const int s = i / m, s2 = i % m;
+            float x = 0.f;
+            if (s2 <= s) {
+                for (int f = 0; f < D; ++f) x += opd(a.a, 0, r0 + s * pitch + f) * opd(a.b, 1, r0 + s2 * pitch + f);
+                x *= sh.pw[s - s2];
+            }
+            sh.score[s * kMaxBk + s2] = x;
+        }
+        __syncthreads();
+        for (int i = tid; i < m * D; i += kThreads) {
+            const int s = i / D, col = i % D;
+            float inter = 0.f, intra = 0.f;
+            for (int f = 0; f < D; ++f) inter += opd(a.a, 0, r0 + s * pitch + f) * sh.state[f * D + col];
+            for (int s2 = 0; s2 <= s; ++s2) intra += sh.score[s * kMaxBk + s2] * opd(a.c, 2, r0 + s2 * pitch + col);
+            const float gr = a.phi_grad ? dphi_of_x(ld<BF16>(a.phi_grad, r0 + s * pitch + col), a.phi) : 1.f;
+            st<BF16>(a.out0, r0 + s * pitch + col, gr * (sh.pw[s + 1] * inter + intra));
+        }
+        __syncthreads();
+        for (int i = tid; i < D * D; i += kThreads) {
+            const int f = i / D, col = i % D;
+            float acc = 0.f;
+            for (int s = 0; s < m; ++s)
+                acc += sh.pw[m - 1 - s] * opd(a.b, 1, r0 + s * pitch + f) * opd(a.c, 2, r0 + s * pitch + col);
+            sh.state[i] = sh.pw[m] * sh.state[i] + acc;
+        }
+        __syncthreads();
+    }
+    if (kv_dst)
+        for (int i = tid; i < D * D; i += kThreads) kv_dst[i] = sh.state[i];
+}
+
+// One workgroup per (sequence, chunk) of a dense [P][N][D] problem.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs lam) {
+    __shared__ Tile sh;
+    const int64_t pair = blockIdx.x / a.chunks;
+    const int c = blockIdx.x % a.chunks;
+    const int D = a.D;
+    const int64_t t_begin = static_cast<int64_t>(c) * a.L;
+    const int64_t t_end = min(a.N, t_begin + a.L);
     const float* init = nullptr;
     bool transposed = false, poison = false;
     if (c == 0) {
@@ -58,48 +106,23 @@ __global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs l
         transposed = a.slots_transposed != 0;
         poison = !given_states_match(a);
     }
-    for (int i = tid; i < D * D; i += kThreads) {
-        float x = 0.f;
-        if (init) x = transposed ? init[(i % D) * D + i / D] : init[i];
-        sh.state[i] = poison ? __builtin_nanf("") : x;
-    }
-    __syncthreads();
+    float* kv_dst = (a.kv_out && c == a.chunks - 1) ? a.kv_out + pair * D * D : nullptr;
+    generic_sweep<BF16>(a, sh, lam.lam[pair % a.H], t_begin, t_end, pair * a.N * D, D, init, transposed, poison,
+                        kv_dst);
+}
 
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += Bk) {
-        const int m = static_cast<int>(min(static_cast<int64_t>(Bk), t_end - t0));
-        const int64_t r0 = base + t0 * D;
-        for (int i = tid; i < m * m; i += kThreads) {
-            const int s = i / m, s2 = i % m;
-            float x = 0.f;
-            if (s2 <= s) {
-                for (int f = 0; f < D; ++f) x += opd(a.a, 0, r0 + s * D + f) * opd(a.b, 1, r0 + s2 * D + f);
-                x *= sh.pw[s - s2];
-            }
-            sh.score[s * kMaxBk + s2] = x;
-        }
-        __syncthreads();
-        for (int i = tid; i < m * D; i += kThreads) {
-            const int s = i / D, col = i % D;
-            float inter = 0.f, intra = 0.f;
-            for (int f = 0; f < D; ++f) inter += opd(a.a, 0, r0 + s * D + f) * sh.state[f * D + col];
-            for (int s2 = 0; s2 <= s; ++s2) intra += sh.score[s * kMaxBk + s2] * opd(a.c, 2, r0 + s2 * D + col);
-            const float gr = a.phi_grad ? dphi_of_x(ld<BF16>(a.phi_grad, r0 + s * D + col), a.phi) : 1.f;
-            st<BF16>(a.out0, r0 + s * D + col, gr * (sh.pw[s + 1] * inter + intra));
-        }
-        __syncthreads();
-        for (int i = tid; i < D * D; i += kThreads) {
-            const int f = i / D, col = i % D;
-            float acc = 0.f;
-            for (int s = 0; s < m; ++s)
-                acc += sh.pw[m - 1 - s] * opd(a.b, 1, r0 + s * D + f) * opd(a.c, 2, r0 + s * D + col);
-            sh.state[i] = sh.pw[m] * sh.state[i] + acc;
-        }
-        __syncthreads();
-    }
-    if (a.kv_out && c == a.chunks - 1) {
-        float* dst = a.kv_out + pair * D * D;
-        for (int i = tid; i < D * D; i += kThreads) dst[i] = sh.state[i];
-    }
+// One workgroup per (sequence, head) of a ragged batch packed token-major [T][H][D]:
+// sequence b holds tokens [v.cu[b], v.cu[b + 1]) and is swept whole from its own initial
+// state (kv_in[b][h]) to its own final state (kv_out[b][h]).
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_fwd_generic_varlen(SweepArgs a, LamArgs lam, VarlenArgs v) {
+    __shared__ Tile sh;
+    const int b = static_cast<int>(blockIdx.x / a.H), h = static_cast<int>(blockIdx.x % a.H);
+    const int64_t DD = static_cast<int64_t>(a.D) * a.D;
+    const int64_t st_off = (static_cast<int64_t>(b) * a.H + h) * DD;
+    generic_sweep<BF16>(a, sh, lam.lam[h], v.cu[b], v.cu[b + 1], static_cast<int64_t>(h) * a.D,
+                        static_cast<int64_t>(a.H) * a.D, a.kv_in ? a.kv_in + st_off : nullptr, false, false,
+                        a.kv_out ? a.kv_out + st_off : nullptr);
 }
 
 // Reverse sweep over one chunk (blocks from last to first), carrying
@@ -409,6 +432,15 @@ void launch_fwd_generic(const SweepArgs& a, const LamArgs& lam, int bf16, hipStr
         hipLaunchKernelGGL(k_fwd_generic<true>, grid, dim3(kThreads), 0, s, a, lam);
     else
         hipLaunchKernelGGL(k_fwd_generic<false>, grid, dim3(kThreads), 0, s, a, lam);
+}
+
+void launch_fwd_generic_varlen(const SweepArgs& a, const LamArgs& lam, const VarlenArgs& v, int bf16,
+                               hipStream_t s) {
+    dim3 grid(static_cast<unsigned>(static_cast<int64_t>(v.nseq) * a.H));
+    if (bf16)
+        hipLaunchKernelGGL(k_fwd_generic_varlen<true>, grid, dim3(kThreads), 0, s, a, lam, v);
+    else
+        hipLaunchKernelGGL(k_fwd_generic_varlen<false>, grid, dim3(kThreads), 0, s, a, lam, v);
 }
 
 void launch_rev_generic(const SweepArgs& a, const LamArgs& lam, int bf16, hipStream_t s) {

@@ -199,6 +199,10 @@ __host__ __device__ inline int64_t dlam_slot_offset(const DlamArgs& a, int64_t p
 
 // Launchers (each enqueues exactly one kernel on `s`; errors are read by the caller).
 void launch_fwd_generic(const SweepArgs& a, const LamArgs& lam, int bf16, hipStream_t s);
+// The ragged forward on the generic kernels: one workgroup per (sequence, head) of the
+// v.nseq sequences (token offsets v.cu), each swept whole.
+void launch_fwd_generic_varlen(const SweepArgs& a, const LamArgs& lam, const VarlenArgs& v, int bf16,
+                               hipStream_t s);
 void launch_rev_generic(const SweepArgs& a, const LamArgs& lam, int bf16, hipStream_t s);
 void launch_chunk_state_generic(const ChunkStateArgs& a, const LamArgs& lam, int bf16, hipStream_t s);
 void launch_scan(const ScanArgs& a, const LamArgs& lam, hipStream_t s);

@@ -256,7 +256,7 @@ int la_decode_step(float* state, const void* q, const void* k, const void* v, co
  * state makes cheap to continue, Lightning Attention-2 record, mechanism
  * field; the same tiling and chunked prefix as la_fwd).  Sequence b holds
  * tokens [seq_offsets[b], seq_offsets[b+1]) of the packed tensors.
- *   Q, K, V, O  : [T][H][D] bf16 device (token-major, T = seq_offsets[B]);
+ *   Q, K, V, O  : [T][H][D] dtype device (token-major, T = seq_offsets[B]);
  *                 row t of head h is (t * H + h) * D.
  *   seq_offsets : HOST int64[B + 1], seq_offsets[0] = 0, nondecreasing; read
  *                 during the call only.  Empty sequences are allowed (their
@@ -266,12 +266,17 @@ int la_decode_step(float* state, const void* q, const void* k, const void* v, co
  *   kv_in       : [B][H][D][D] float32 device, or NULL for zero.
  *   kv_out      : [B][H][D][D] float32 device, or NULL to skip.
  *   ws          : la_fwd_varlen_workspace_bytes(...) bytes of device memory.
- * Supported: bf16, D = 128, Bk in {64, 128, 256} (chunk boundaries on
- * multiples of Bk; blocks stepped as 64 tokens, as in la_fwd), and within
- * every group of 256 sequences T_group * H * D * 2 < 2^31 (otherwise
- * LA_EUNSUPPORTED).  Each sequence's results equal la_fwd over that sequence
- * alone, up to float rounding.  LA_VARLEN_L (a positive multiple of Bk)
- * overrides the chunk length; a size query must see the same setting. */
+ * bf16 with D = 128 and Bk in {64, 128, 256} runs on the direct-to-LDS
+ * kernels (chunk boundaries on multiples of Bk; blocks stepped as 64 tokens,
+ * as in la_fwd; within every group of 256 sequences T_group * H * D * 2 <
+ * 2^31, otherwise LA_EUNSUPPORTED).  Every other shape la_fwd accepts
+ * (float32 storage, D in {16, 32, 64, 128}, Bk in {16, 32, 64, 128, 256})
+ * runs on the generic kernels: one workgroup per (sequence, head) sweeping
+ * the whole sequence in Bk-token blocks (at most 128), no workspace, T <
+ * 2^31.  Each sequence's results equal la_fwd over that sequence alone, up to
+ * float rounding.  LA_VARLEN_L (a positive multiple of Bk) overrides the
+ * chunk length of the direct-to-LDS path; a size query must see the same
+ * setting. */
 int la_fwd_varlen(const void* Q, const void* K, const void* V, const float* lambda,
                   const int64_t* seq_offsets, int64_t B, int64_t H, int64_t D, int32_t Bk,
                   int32_t dtype, int32_t phi, const float* kv_in, void* O, float* kv_out, void* ws,

@@ -191,9 +191,21 @@ def test_fwd_varlen_rejects():
     assert call([1, 5, 9]) == la.LA_EINVAL                    # offsets must start at 0
     assert call([0, 9, 5]) == la.LA_EINVAL                    # and not decrease
     assert call([0, 5, 9] + [9] * 300 + [5]) == la.LA_EINVAL  # also in a later group of 256
-    assert call([0, 64], dt=la.LA_F32) == la.LA_EUNSUPPORTED  # bf16 only
-    assert call([0, 64], D=64) == la.LA_EUNSUPPORTED
-    assert call([0, 64], Bk=32) == la.LA_EUNSUPPORTED         # Bk in {64, 128, 256}
+    # float32 storage, D != 128 and Bk of 16 or 32 take the generic kernels (no workspace):
+    # valid arguments get as far as the device query, invalid ones are rejected before it
+    assert call([0, 64], dt=la.LA_F32) == la.LA_ENODEV
+    assert call([0, 64], D=64) == la.LA_ENODEV
+    assert call([0, 64], Bk=32) == la.LA_ENODEV
+    assert call([0, 64], D=100) == la.LA_EUNSUPPORTED
+    assert call([0, 64], Bk=48) == la.LA_EUNSUPPORTED
+    assert call([0, 64], D=64, H=257) == la.LA_EUNSUPPORTED  # 256 heads at most (checked before lambda is read)
+    assert call([1, 5, 9], D=64) == la.LA_EINVAL
+    assert call([0, 9, 5], dt=la.LA_F32) == la.LA_EINVAL
+    assert call([0, 64], D=64, O=Q_) == la.LA_EINVAL
+    assert call([0, 64], D=64, O=O_ + 8) == la.LA_EALIGN
+    assert call([0, 1 << 31], D=64) == la.LA_EUNSUPPORTED     # int32 token offsets
+    assert la.la_fwd_varlen_workspace_bytes([0, 100000], 2, 64, 64, la.LA_BF16) == 0
+    assert la.la_fwd_varlen_workspace_bytes([0, 100000], 2, 128, 32, la.LA_F32) == 0
     assert call([0, 64], O=Q_) == la.LA_EINVAL                # output aliases Q
     assert call([0, 64], O=O_ + 8) == la.LA_EALIGN
     assert call([0, 1 << 30]) == la.LA_EUNSUPPORTED           # 32-bit buffer offsets

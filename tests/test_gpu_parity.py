@@ -609,3 +609,67 @@ def test_fused_prefix_repeat_and_reuse(fused, chunks):
     assert torch.equal(o1, o3) and torch.equal(s1, s3)
     assert torch.equal(o2, o4) and torch.equal(s2, s4)
     assert not torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("B,H,N,bk,want_fused", [(4, 16, 2048, 64, True), (2, 32, 8192, 64, True),
+                                                 (4, 16, 4096, 128, True), (8, 16, 4096, 64, False),
+                                                 (2, 16, 8192, 64, False), (2, 8, 4096, 128, False)])
+def test_fused_prefix_default_routing(monkeypatch, B, H, N, bk, want_fused):
+    """Without LA_FUSED, the forward of a plan of at most 4 chunks without aggregate parts runs
+    as one launch (fwd_dma_fused) and any other chunked plan as aggregates, scan and sweep; the
+    launches are those the library's own per-launch profiler records.  Under HIP graph capture
+    the three-launch form runs and replays to the eager result."""
+    for name in ("LA_FUSED", "LA_CHUNKS", "LA_AGG_K", "LA_KERNEL", "LA_FWD", "LA_FWD_WAVES", "LA_FWD128"):
+        monkeypatch.delenv(name, raising=False)
+    plan = la.la_plan(B, H, N, 128, bk, la.LA_BF16)
+    print(f"[routing] B={B} H={H} N={N} Bk={bk} plan={plan} fused expected={want_fused}", flush=True)
+    assert (plan["chunks"] > 1 and plan["chunks"] <= 4 and plan["agg_parts"] == 1) == want_fused
+    lam = synth.decay_schedule(H)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    q, k, v = (torch.randn(B, H, N, 128, device="cuda", generator=gen).div(math.sqrt(128)).to(torch.bfloat16)
+               for _ in range(3))
+    o = torch.empty_like(q)
+    s = torch.empty((B, H, 128, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(la.la_fwd_workspace_bytes(B, H, N, 128, bk, la.LA_BF16), 1), dtype=torch.uint8,
+                     device="cuda")
+    _sync()
+    la.la_prof_collect()
+    la.la_prof_enable(True)
+    try:
+        la.la_fwd(q, k, v, lam, bk, out=o, kv_out=s, ws=ws)
+        _sync()
+    finally:
+        prof = la.la_prof_collect()
+        la.la_prof_enable(False)
+    names = set(prof)
+    if want_fused:
+        assert names == {"fwd_dma_fused"}, names
+    else:
+        assert "fwd_dma_fused" not in names and {"chunk_state_dma", "state_scan", "fwd_dma"} <= names, names
+    o_eager, s_eager = o.clone(), s.clone()
+    # graph capture: the three-launch form (its result within float rounding of the fused one's)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        la.la_fwd(q, k, v, lam, bk, out=o, kv_out=s, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    _sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        la.la_fwd(q, k, v, lam, bk, out=o, kv_out=s, ws=ws)
+    outs = []
+    for _ in range(3):
+        o.zero_()
+        s.zero_()
+        g.replay()
+        _sync()
+        outs.append((o.clone(), s.clone()))
+    for og, sg in outs:
+        assert torch.equal(og, outs[0][0]) and torch.equal(sg, outs[0][1])
+    # the two forms round their weighted bf16 key-value operands differently (the fused walk
+    # weights by lam^(63-s) per block, the aggregate kernel by a running product), so they
+    # agree to bf16 rounding, not bit for bit; each is held to the oracle's bar elsewhere
+    e_o = oracle.rel_l2(got(outs[0][0]), got(o_eager))
+    e_s = oracle.rel_l2(got(outs[0][1]), got(s_eager))
+    print(f"    graph (three launches) vs eager: rel-L2 O {e_o:.2e}, kv_out {e_s:.2e}", flush=True)
+    assert e_o <= 1e-2 and e_s <= 2e-3, (e_o, e_s)

@@ -184,3 +184,22 @@ def test_varlen_impulse_bit_exact(monkeypatch, L, with_state):
     e_o, e_s = expected_varlen(offs, lam_vals, j0s, with_state)
     assert_exact("O", got(o), e_o)
     assert_exact("kv_out", got(s), e_s)
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+@pytest.mark.parametrize("Bk", [32, 64])
+def test_varlen_impulse_generic_bit_exact(Bk, with_state):
+    """The same ragged probes in float32 storage, which la_fwd_varlen serves on the generic
+    kernels (one workgroup per sequence and head, no chunks): nothing crosses a sequence
+    boundary, bit for bit."""
+    offs = varlen_offsets(64)
+    lam_vals = [0.5, 1.0]
+    q, k, v, s0, j0s = build_varlen(offs, len(lam_vals), with_state)
+    print(f"[probe varlen generic] Bk={Bk} kv_in={with_state} offsets={offs}", flush=True)
+    qd, kd, vd = (to_dev(x.astype(np.float32), "f32") for x in (q, k, v))
+    kv_in = torch.from_numpy(s0).cuda() if with_state else None
+    o, s = la.la_fwd_varlen(qd, kd, vd, lam_vals, offs, Bk=Bk, kv_in=kv_in)
+    _sync()
+    e_o, e_s = expected_varlen(offs, lam_vals, j0s, with_state)
+    assert_exact("O", got(o), e_o)
+    assert_exact("kv_out", got(s), e_s)

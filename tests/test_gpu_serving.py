@@ -219,3 +219,84 @@ def test_varlen_more_than_256_sequences(with_state):
     lens[[3, 255, 256, 511, 599]] = [2000, 1, 1700, 999, 2500]
     print(f"[varlen] B=600 T={int(lens.sum())} kv_in={with_state}", flush=True)
     check_varlen_against_oracle(list(lens), 2, 64, 77, with_state)
+
+
+# ------------------------------------------------------------------ the generic ragged path
+def packed_any(seed, T, H, Dd, dtype):
+    """Seeded packed [T, H, Dd] Q, K, V of dtype "bf16" or "f32" (device) and their float64
+    values (host)."""
+    from helpers import host_f64, to_dev
+    dev, host = [], []
+    for sid in (synth.ID_Q, synth.ID_K, synth.ID_V):
+        a = synth.normal(seed, sid, (T, H, Dd), 1.0 / math.sqrt(Dd), dtype)
+        dev.append(to_dev(a, dtype))
+        host.append(host_f64(a, dtype))
+    return dev, host
+
+
+@pytest.mark.parametrize("dtype,Dd,Bk,phi", [("f32", 128, 64, "identity"), ("f32", 64, 32, "elu1"),
+                                             ("bf16", 64, 64, "identity"), ("bf16", 32, 16, "relu"),
+                                             ("bf16", 128, 32, "identity"), ("f32", 16, 256, "identity")])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_varlen_generic_matches_oracle(dtype, Dd, Bk, phi, with_state):
+    """Shapes outside the direct-to-LDS kernels (float32 storage, D != 128, Bk of 16 or 32)
+    run the ragged forward on the generic kernels: every sequence and head against the
+    oracle (empty and one-token sequences, block edges), and against la_fwd over the
+    sequence alone."""
+    from helpers import bar
+    lens = [1, 63, 64, 65, 300, 0, 129, 7]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    H, T, B = 3, int(offs[-1]), len(lens)
+    print(f"[varlen generic] {dtype} D={Dd} Bk={Bk} phi={phi} lens={lens} H={H} kv_in={with_state}", flush=True)
+    lam = synth.decay_schedule(H)
+    (q, k, v), (qh, kh, vh) = packed_any(31, T, H, Dd, dtype)
+    s0 = state_input(32, B, H, Dd) if with_state else None
+    kv_in = torch.from_numpy(s0).cuda() if with_state else None
+    assert la.la_fwd_varlen_workspace_bytes(offs, H, Dd, Bk, la.LA_BF16 if dtype == "bf16" else la.LA_F32) == 0
+    o, s = la.la_fwd_varlen(q, k, v, lam, offs, Bk=Bk, kv_in=kv_in, phi=phi)
+    torch.cuda.synchronize()
+    o_h, s_h = got(o), got(s)
+    for b in range(B):
+        a, e = int(offs[b]), int(offs[b + 1])
+        for h in range(H):
+            init = None if s0 is None else s0[b, h].astype(np.float64)
+            if e > a:
+                o_ref, s_ref = oracle.fwd_recurrent(qh[a:e, h], kh[a:e, h], vh[a:e, h], float(lam[h]), init,
+                                                    phi=phi)
+                assert oracle.rel_l2(o_h[a:e, h], o_ref) <= bar(dtype), (b, h)
+            else:
+                s_ref = np.zeros((Dd, Dd)) if init is None else init
+            assert oracle.rel_l2(s_h[b, h], s_ref) <= bar(dtype), (b, h)
+        if e > a:
+            seq = [x[a:e].permute(1, 0, 2).contiguous().unsqueeze(0) for x in (q, k, v)]
+            kin = None if kv_in is None else kv_in[b:b + 1].contiguous()
+            od, sd = la.la_fwd(*seq, lam, Bk=Bk, kv_in=kin, phi=phi)
+            torch.cuda.synchronize()
+            assert oracle.rel_l2(o_h[a:e], got(od)[0].transpose(1, 0, 2)) <= max(bar(dtype), 1e-5)
+            assert oracle.rel_l2(s_h[b], got(sd)[0]) <= max(bar(dtype), 1e-5)
+
+
+def test_varlen_generic_many_sequences():
+    """More than 256 sequences on the generic path (groups of 256), float32 D = 32, each with
+    its own initial state; sampled sequences of both groups against the oracle."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(0, 40, 300)
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    H, T, B, Dd = 2, int(offs[-1]), len(lens), 32
+    print(f"[varlen generic] B={B} T={T} H={H} D={Dd} f32", flush=True)
+    lam = synth.decay_schedule(H)
+    (q, k, v), (qh, kh, vh) = packed_any(41, T, H, Dd, "f32")
+    s0 = state_input(42, B, H, Dd)
+    o, s = la.la_fwd_varlen(q, k, v, lam, offs, Bk=32, kv_in=torch.from_numpy(s0).cuda())
+    torch.cuda.synchronize()
+    o_h, s_h = got(o), got(s)
+    for b in [0, 1, 100, 255, 256, 257, 299]:
+        a, e = int(offs[b]), int(offs[b + 1])
+        for h in range(H):
+            init = s0[b, h].astype(np.float64)
+            if e > a:
+                o_ref, s_ref = oracle.fwd_recurrent(qh[a:e, h], kh[a:e, h], vh[a:e, h], float(lam[h]), init)
+                assert oracle.rel_l2(o_h[a:e, h], o_ref) <= 1e-5, (b, h)
+            else:
+                s_ref = init
+            assert oracle.rel_l2(s_h[b, h], s_ref) <= 1e-5, (b, h)
