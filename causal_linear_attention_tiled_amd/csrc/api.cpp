@@ -410,6 +410,9 @@ struct PhiUse {
 // launch) pays off while a chunk has few earlier chunks to sum; LA_FUSED=0 / 1 switches it
 // off / on for every chunk count.
 constexpr int kMaxFusedChunks = 4;
+// The fused sweep's bound on each wait (polls of about 128 cycles each: a few ms, far beyond
+// any earlier chunk's walk); LA_FUSED_SPIN lowers it for failure-path tests.
+constexpr int kFusedSpinLimit = 1 << 17;
 
 bool fused_wanted(const Plan& p) {
     if (env_is("LA_FUSED", "0")) return false;
@@ -491,6 +494,12 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
         a.fused_aggs = fused_aggs;
         a.fused_flags = fused_flags;
         a.epoch = next_epoch();
+        // LA_FUSED_LOSE_FLAGS=1 (failure-path tests): waiting waves look for a value no wave
+        // publishes, so every wait runs out (LA_FUSED_SPIN polls) and its columns become NaN
+        a.wait_epoch = env_is("LA_FUSED_LOSE_FLAGS", "1") ? ~a.epoch : a.epoch;
+        a.spin_limit = kFusedSpinLimit;
+        if (const char* e = std::getenv("LA_FUSED_SPIN"); e && std::atoi(e) > 0)
+            a.spin_limit = std::min(std::atoi(e), kFusedSpinLimit);
         a.stamp_store = stamp_out;
     }
     if (dma) {

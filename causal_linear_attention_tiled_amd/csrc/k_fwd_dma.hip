@@ -63,7 +63,7 @@ struct DmaTiles {
 // starting state, S = lam^(cL) S0 + sum_j lam^((c-1-j)L) dS_j, stores it where la_fwd
 // keeps the states entering chunks, and sweeps its chunk (phase 3).  A workgroup waits only
 // on lower workgroup indices, which the hardware dispatches first, so every awaited
-// workgroup is running or done; the wait is bounded all the same (kFusedSpinLimit polls),
+// workgroup is running or done; the wait is bounded all the same (a.spin_limit polls),
 // and a wave that gives up starts from NaN instead of hanging.
 // The aggregates and flags travel as agent-scope atomic stores and loads, which the
 // hardware keeps coherent across the XCDs' separate L2 caches line by line.  A wave raises
@@ -71,7 +71,6 @@ struct DmaTiles {
 // issues its aggregate loads only after it has read the flag, so the loads see the stores.
 // Agent-scope release/acquire fences would give the same order through a write-back and an
 // invalidate of the whole L2, which cost more than the two launches this form saves.
-constexpr int kFusedSpinLimit = 1 << 17;
 
 template <int NW, bool VARLEN, bool PHI, bool FUSED = false>
 __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam, const VarlenArgs* var) {
@@ -278,13 +277,14 @@ __device__ __forceinline__ void fwd_body(const SweepArgs& a, const LamArgs& lam,
             // wait (bounded) for wave w of chunk j, which was dispatched before this workgroup
             const uint64_t* flag = a.fused_flags + (pair * (wk.chunks - 1) + j) * NW + w;
             int spins = 0;
-            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
-                if (++spins >= kFusedSpinLimit) {
+            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.wait_epoch) {
+                if (++spins >= a.spin_limit) {
                     ok = false;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(2);
             }
+            if (!ok) break;  // no further waits: this wave's columns become NaN
             __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the loads below stay after the flag's
             const float* agg = a.fused_aggs + (pair * (wk.chunks - 1) + j) * D * D;
 #pragma unroll

@@ -64,6 +64,8 @@ struct SweepArgs {
     float* fused_aggs;
     uint64_t* fused_flags;
     uint64_t epoch;
+    uint64_t wait_epoch;  // the flag value a waiting wave takes as published (normally epoch)
+    int spin_limit;       // polls before a waiting wave gives up and starts from NaN
     uint32_t* stamp_store;
     float* kv_out;        // [P][D][D] final state (forward only) or nullptr
     const float* g_final; // reverse only: [P][D][D] gradient arriving at the final state, the

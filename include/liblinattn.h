@@ -55,7 +55,12 @@
  *    workgroups per CU (instead of two loader waves at one);
  *    LA_FWD_WAVES=8, LA_REV_WAVES=4 and LA_DLAM_WAVES=4 select the
  *    other wave counts of the bf16 D = 128 direct-to-LDS sweeps (forward and
- *    dQ, dK and dV, decay derivative).  They exist for tests and tuning; a
+ *    dQ, dK and dV, decay derivative); LA_FUSED=0 / 1 keeps the chunked
+ *    prefix out of / in the sweep's launch (la_fwd); LA_FUSED_SPIN (polls)
+ *    lowers the bound on the fused prefix's waits and LA_FUSED_LOSE_FLAGS=1
+ *    makes every such wait look for a flag value nobody publishes (both for
+ *    failure-path tests: the waves that give up start from NaN, and the
+ *    kernel ends normally).  They exist for tests and tuning; a
  *    query of the workspace size must be made under the same setting as the
  *    call it sizes.
  */

@@ -673,3 +673,43 @@ def test_fused_prefix_default_routing(monkeypatch, B, H, N, bk, want_fused):
     e_s = oracle.rel_l2(got(outs[0][1]), got(s_eager))
     print(f"    graph (three launches) vs eager: rel-L2 O {e_o:.2e}, kv_out {e_s:.2e}", flush=True)
     assert e_o <= 1e-2 and e_s <= 2e-3, (e_o, e_s)
+
+
+@pytest.mark.parametrize("Bk,cks", [(64, 4), (64, 3), (128, 2)])
+def test_fused_prefix_lost_flags_end_in_nan(monkeypatch, Bk, cks, chunks):
+    """The fused prefix's waits are bounded.  With LA_FUSED_LOSE_FLAGS=1 every waiting wave
+    looks for a flag value no wave publishes and gives up after LA_FUSED_SPIN polls: the
+    kernel still ends, chunk 0 (which waits for nothing) is right, every later chunk's rows
+    and the final state are NaN, and the chunk states left for la_bwd are NaN too.  The next
+    call without the switch is right again on the same workspace."""
+    for name in ("LA_KERNEL", "LA_FWD", "LA_FWD_WAVES", "LA_FWD128", "LA_AGG_K"):
+        monkeypatch.delenv(name, raising=False)
+    monkeypatch.setenv("LA_FUSED", "1")
+    monkeypatch.setenv("LA_FUSED_LOSE_FLAGS", "1")
+    monkeypatch.setenv("LA_FUSED_SPIN", "16")
+    chunks(cks)
+    B, H, N, D = 1, 3, Bk * 4 * cks, 128
+    plan = la.la_plan(B, H, N, D, Bk, la.LA_BF16)
+    assert plan["chunks"] == cks
+    L = plan["chunk_len"]
+    print(f"[lost flags] Bk={Bk} plan={plan}", flush=True)
+    lam = synth.decay_schedule(H)
+    _, (q, k, v), (qh, kh, vh) = inputs(5, B, H, N, D, "bf16")
+    ws = torch.empty(la.la_fwd_workspace_bytes(B, H, N, D, Bk, la.LA_BF16), dtype=torch.uint8, device="cuda")
+    o, s = la.la_fwd(q, k, v, lam, Bk=Bk, ws=ws)
+    _sync()
+    y = got(o)
+    assert np.all(np.isfinite(y[:, :, :L])), "chunk 0 waits for nothing"
+    assert np.all(np.isnan(y[:, :, L:])), "every later chunk starts from NaN"
+    assert np.all(np.isnan(got(s)))
+    o_ref, _ = oracle.fwd_recurrent(qh[0], kh[0], vh[0], lam_pairs(lam, B))
+    assert oracle.rel_l2(y[0, :, :L], o_ref[:, :L]) <= BF16_BAR
+    # the same workspace, flags awaited normally with the default bound (16 polls, about a
+    # microsecond, are too few for a real wait on an earlier chunk's walk)
+    monkeypatch.delenv("LA_FUSED_LOSE_FLAGS")
+    monkeypatch.delenv("LA_FUSED_SPIN")
+    o2, s2 = la.la_fwd(q, k, v, lam, Bk=Bk, ws=ws)
+    _sync()
+    o_ref, s_ref = oracle.fwd_recurrent(qh[0], kh[0], vh[0], lam_pairs(lam, B))
+    assert oracle.rel_l2(got(o2)[0], o_ref) <= BF16_BAR
+    assert oracle.rel_l2(got(s2)[0], s_ref) <= BF16_BAR
