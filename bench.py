@@ -337,6 +337,20 @@ def kernel_breakdown(torch, la, fn, reps):
     return out
 
 
+def median_ms(torch, fn, reps):
+    """Milliseconds per call as the median over reps calls, each bracketed by its own pair of
+    HIP events on the current stream (so launch gaps between calls are left out)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return t[len(t) // 2]
+
+
 def graph_ms(torch, fn, reps):
     """fn captured once in a HIP graph (torch.cuda.CUDAGraph) and replayed: milliseconds per
     replay, which leaves out the host side of every launch."""
@@ -383,14 +397,31 @@ def other_workloads(torch, la, timed):
         byts = 8 * D * B * Hh * N + B * Hh * D * D * 4
         plan = la.la_plan(B, Hh, N, D, bk, la.LA_BF16)
         out[name] = {"workload": f"bf16 forward B{B} H{Hh} N{N} d{D} block {bk}, per-head decay, final state",
-                     "plan": plan, "ms": round(ms, 4), "graph_ms": round(graph_ms(torch, fn, reps), 4),
+                     "plan": plan, "ms": round(ms, 4), "median_ms": round(median_ms(torch, fn, reps), 4),
+                     "graph_ms": round(graph_ms(torch, fn, reps), 4),
                      "tokens_per_s": round(B * N / (ms * 1e-3)),
                      "gbs": round(byts / (ms * 1e-3) / 1e9, 1),
                      "frac_of_8tbs": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "kernels": kernel_breakdown(torch, la, fn, max(3, reps // 4))}
         del q, k, v, o, s, ws
 
-    fwd_case("fwd_b4_h16_n2048", 4, 16, 2048, BK, 50)
+    fwd_case("fwd_b4_h16_n2048", 4, 16, 2048, BK, 200)
+
+    # the float32 correctness shape: latency-bound, its time only (no roofline)
+    Hh, N1, D1 = 2, 256, 16
+    q, k, v = (torch.randn(1, Hh, N1, D1, device="cuda", generator=torch.Generator(device="cuda").manual_seed(sid))
+               .div(math.sqrt(D1)) for sid in (1, 2, 3))
+    o = torch.empty_like(q)
+    s = torch.empty((1, Hh, D1, D1), dtype=torch.float32, device="cuda")
+    fn = lambda: la.la_fwd(q, k, v, [1.0] * Hh, BK, out=o, kv_out=s)
+    for _ in range(20):
+        fn()
+    out["fwd_fp32_b1_h2_n256_d16"] = {
+        "workload": f"float32 forward B1 H{Hh} N{N1} d{D1} block {BK}, no decay (lambda = 1), final state; "
+                    "generic kernels, latency-bound (time only)",
+        "plan": la.la_plan(1, Hh, N1, D1, BK, la.LA_F32), "median_ms": round(median_ms(torch, fn, 200), 4),
+        "ms": round(timed(fn, 200), 4), "kernels": kernel_breakdown(torch, la, fn, 20)}
+    del q, k, v, o, s
 
     B, Hh, N = 2, 32, 8192
     lam_h = synth.decay_schedule(Hh)
