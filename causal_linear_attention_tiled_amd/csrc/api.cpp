@@ -855,20 +855,12 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
     const int64_t pairs = B * H;
     const int32_t Hi = static_cast<int32_t>(H);
 
-    // dQ: the forward sweep with (q, k, v) = (dO, V, K) and the transposed initial state.
-    // the dQ sweep: phi(k) in the value slot, its own aggregates over (v, phi(k)), and
-    // phi'(q) on the output
-    const PhiUse pu{phi, 4, 2, phi ? Q : nullptr};
-    const uint32_t* stamp_in =
-        (fwd_ws && fq) ? reinterpret_cast<const uint32_t*>(static_cast<const char*>(fwd_ws) + fwd_ws_layout(pairs, p, D).stamp)
-                       : nullptr;
-    rc = run_forward_sweep(dO, V, K, dQ, kv_in, 1, nullptr, slots_q, static_cast<const float*>(fwd_ws), pairs,
-                           N, D, Bk, Hi, bf16, p, lam, pu, s, "dq", nullptr, stamp_in, stamp);
-    if (rc) return rc;
-
     // dK, dV: reverse sweep carrying dS, with a chunked suffix over blocks; the aggregates
     // are taken over the agg_k parts of every chunk but the first (a part past the end of
-    // the sequence aggregates nothing)
+    // the sequence aggregates nothing).  They run first: they read Q and dO, so the dQ sweep
+    // after them finds part of dO still in the infinity cache (measured, fwd + bwd with the
+    // forward's chunk states: B2 H32 N8192 470 against 477 us with the dQ sweep first,
+    // B8 H16 N16384 1.676 against 1.686 ms).
     if (p.chunks > 1) {
         const int64_t Lf = p.L / p.agg_k;
         const int chunks_f = (p.chunks - 1) * p.agg_k + 1;
@@ -887,6 +879,17 @@ int la_bwd(const void* Q, const void* K, const void* V, const void* dO, const fl
         rc = launch("state_scan_rev", s, [&] { la::launch_scan(sc, lam, s); });
         if (rc) return rc;
     }
+    // dQ: the forward sweep with (q, k, v) = (dO, V, K) and the transposed initial state.
+    // the dQ sweep: phi(k) in the value slot, its own aggregates over (v, phi(k)), and
+    // phi'(q) on the output
+    const PhiUse pu{phi, 4, 2, phi ? Q : nullptr};
+    const uint32_t* stamp_in =
+        (fwd_ws && fq) ? reinterpret_cast<const uint32_t*>(static_cast<const char*>(fwd_ws) + fwd_ws_layout(pairs, p, D).stamp)
+                       : nullptr;
+    rc = run_forward_sweep(dO, V, K, dQ, kv_in, 1, nullptr, slots_q, static_cast<const float*>(fwd_ws), pairs,
+                           N, D, Bk, Hi, bf16, p, lam, pu, s, "dq", nullptr, stamp_in, stamp);
+    if (rc) return rc;
+
     la::SweepArgs a{};
     a.a = Q;
     a.b = K;
