@@ -78,3 +78,36 @@ def test_noalloc_binding_and_limit(monkeypatch):
     assert e.value.code == la.LA_ESCRATCH
     torch.cuda.synchronize()
     assert bool((ob == 7.0).all())
+
+
+def test_noalloc_fused_prefix_falls_back(monkeypatch):
+    """Chunk states that fit the static scratch while the fused prefix's aggregates and flags
+    would not (4 chunks over 256 sequences: 48 MiB of states, 96 MiB with the aggregates):
+    la_fwd_noalloc runs the three-launch prefix instead, bit-identical to la_fwd with
+    LA_FUSED=0, within float rounding of la_fwd's fused form, and within the bar of the oracle
+    on sampled sequences."""
+    monkeypatch.setenv("LA_CHUNKS", "4")
+    monkeypatch.delenv("LA_FUSED", raising=False)
+    monkeypatch.delenv("LA_AGG_K", raising=False)
+    B, H, N, D = 16, 16, 1024, 128
+    plan = la.la_plan(B, H, N, D, 64, la.LA_BF16)
+    states = B * H * (plan["chunks"] - 1) * D * D * 4
+    need = la.la_fwd_workspace_bytes(B, H, N, D, 64, la.LA_BF16)
+    print(f"[noalloc fallback] plan={plan} chunk states {states} B, fused workspace {need} B, "
+          f"scratch {la.la_scratch_bytes()} B", flush=True)
+    assert plan["chunks"] == 4 and plan["agg_parts"] == 1
+    assert states <= la.la_scratch_bytes() < need
+    lam = synth.decay_schedule(H)
+    _, (q, k, v), (qh, kh, vh) = inputs(12, B, H, N, D, "bf16")
+    o_n, s_n = noalloc_via_abi(q, k, v, lam, 64)
+    monkeypatch.setenv("LA_FUSED", "0")
+    o_3, s_3 = la.la_fwd(q, k, v, lam, Bk=64)
+    monkeypatch.delenv("LA_FUSED")
+    o_f, s_f = la.la_fwd(q, k, v, lam, Bk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o_n, o_3) and torch.equal(s_n, s_3)
+    assert oracle.rel_l2(got(o_f), got(o_n)) <= 1e-2 and oracle.rel_l2(got(s_f), got(s_n)) <= 2e-3
+    for b, h in [(0, 0), (7, 5), (15, 15)]:
+        o_ref, s_ref = oracle.fwd_recurrent(qh[b, h], kh[b, h], vh[b, h], float(lam[h]))
+        assert oracle.rel_l2(got(o_n[b, h]), o_ref) <= BF16_BAR, (b, h)
+        assert oracle.rel_l2(got(s_n[b, h]), s_ref) <= BF16_BAR, (b, h)
