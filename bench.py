@@ -402,7 +402,11 @@ def other_workloads(torch, la, timed):
         ms = timed(fn, reps)
         byts = 8 * D * B * Hh * N + B * Hh * D * D * 4
         plan = la.la_plan(B, Hh, N, D, bk, la.LA_BF16)
-        out[name] = {"workload": f"bf16 forward B{B} H{Hh} N{N} d{D} block {bk}, per-head decay, final state",
+        stepped = 64 if bk >= 64 and D == 128 and os.environ.get("LA_FWD128") != "1" else bk
+        out[name] = {"workload": f"bf16 forward B{B} H{Hh} N{N} d{D} block {bk}, per-head decay, final state"
+                                 + (f" (chunk boundaries on multiples of {bk}; the kernel steps {stepped}-token "
+                                    "blocks, the same function)" if stepped != bk else ""),
+                     "kernel_block": stepped,
                      "plan": plan, "ms": round(ms, 4), "median_ms": round(median_ms(torch, fn, reps), 4),
                      "graph_ms": round(graph_ms(torch, fn, reps), 4),
                      "tokens_per_s": round(B * N / (ms * 1e-3)),
