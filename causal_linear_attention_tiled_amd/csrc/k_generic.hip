@@ -6,8 +6,9 @@
 // MFMA kernels do not cover, and for float32 storage.
 //
 // One workgroup handles one (sequence, chunk).  The D x D float32 state and
-// one Bk x Bk score tile live in LDS; operands are read from global memory
-// (through the caches) as they are needed.
+// one Bk x Bk score tile live in LDS; the forward also stages each block's Q, K
+// and V rows there, the other kernels read operands from global memory (through
+// the caches) as they are needed.
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -27,68 +28,93 @@ __device__ __forceinline__ void fill_powers(float* pw, float lam, int Bk) {
     for (int e = threadIdx.x; e <= Bk; e += kThreads) pw[e] = lam_pow(lam, e);
 }
 
+// The forward's LDS: the D x D state, one block's score tile, the block's Q, K and V rows
+// (feature map applied) and its decay powers, for blocks of Bs tokens, the largest block
+// that divides the call's Bk and fits (fwd_generic_block; the block only decides which
+// terms pass through a score tile and which through the state, never the function).
+constexpr int kFwdPoolFloats = 30 * 1024;  // 120 KiB
+// (the staged rows are D + 1 floats apart, so that threads reading one column of
+// consecutive rows hit distinct LDS banks)
+__host__ __device__ constexpr int fwd_pool_floats(int D, int Bs) { return D * D + Bs * Bs + 3 * Bs * (D + 1) + Bs + 1; }
+static_assert(fwd_pool_floats(kMaxD, 16) <= kFwdPoolFloats, "every D fits at the smallest block");
+
 // Forward sweep over tokens [t_begin, t_end) of one (sequence, head), whose token rows
-// start at element base and lie pitch elements apart:
+// start at element base and lie pitch elements apart, in blocks of a.Bk tokens:
 //   O_b = diag(lam^(s+1)) Q_b S + (Q_b K_b^T o M) V_b,  S <- lam^m S + (diag(lam^(m-1-s)) K_b)^T V_b
 // starting from init (or zero; read transposed when `transposed`; NaN when `poison`) and
-// leaving the final state in kv_dst (unless null).
+// leaving the final state in kv_dst (unless null).  Each block's rows are read from
+// global memory once, into LDS.
 template <bool BF16>
-__device__ void generic_sweep(const SweepArgs& a, Tile& sh, float lv, int64_t t_begin, int64_t t_end,
+__device__ void generic_sweep(const SweepArgs& a, float* pool, float lv, int64_t t_begin, int64_t t_end,
                               int64_t base, int64_t pitch, const float* init, bool transposed, bool poison,
                               float* kv_dst) {
     const int D = a.D, Bk = a.Bk, tid = threadIdx.x;
+    float* state = pool;             // [D][D]
+    float* score = state + D * D;    // [Bk][Bk]
+    const int rp = D + 1;            // staged row pitch
+    float* qs = score + Bk * Bk;     // [Bk][D + 1] each
+    float* ks = qs + Bk * rp;
+    float* vs = ks + Bk * rp;
+    float* pw = vs + Bk * rp;        // lam^e, e = 0..Bk
     // operand x of slot bit (0: a, 1: b, 2: c), through the feature map when that slot takes it
     auto opd = [&](const void* p, int bit, int64_t i) {
         const float x = ld<BF16>(p, i);
         return (a.phi && ((a.phi_mask >> bit) & 1)) ? phi_apply(x, a.phi) : x;
     };
-    fill_powers(sh.pw, lv, Bk);
+    fill_powers(pw, lv, Bk);
     for (int i = tid; i < D * D; i += kThreads) {
         float x = 0.f;
         if (init) x = transposed ? init[(i % D) * D + i / D] : init[i];
-        sh.state[i] = poison ? __builtin_nanf("") : x;
+        state[i] = poison ? __builtin_nanf("") : x;
     }
-    __syncthreads();
 
     for (int64_t t0 = t_begin; t0 < t_end; t0 += Bk) {
         const int m = static_cast<int>(min(static_cast<int64_t>(Bk), t_end - t0));
         const int64_t r0 = base + t0 * pitch;
+        __syncthreads();  // the previous block's rows and the state update are done with
+        for (int i = tid; i < m * D; i += kThreads) {
+            const int row = i / D, col = i % D;
+            const int64_t at = r0 + row * pitch + col;
+            qs[row * rp + col] = opd(a.a, 0, at);
+            ks[row * rp + col] = opd(a.b, 1, at);
+            vs[row * rp + col] = opd(a.c, 2, at);
+        }
+        __syncthreads();
         for (int i = tid; i < m * m; i += kThreads) {
             const int s = i / m, s2 = i % m;
             float x = 0.f;
             if (s2 <= s) {
-                for (int f = 0; f < D; ++f) x += opd(a.a, 0, r0 + s * pitch + f) * opd(a.b, 1, r0 + s2 * pitch + f);
-                x *= sh.pw[s - s2];
+                for (int f = 0; f < D; ++f) x += qs[s * rp + f] * ks[s2 * rp + f];
+                x *= pw[s - s2];
             }
-            sh.score[s * kMaxBk + s2] = x;
+            score[s * Bk + s2] = x;
         }
         __syncthreads();
         for (int i = tid; i < m * D; i += kThreads) {
             const int s = i / D, col = i % D;
             float inter = 0.f, intra = 0.f;
-            for (int f = 0; f < D; ++f) inter += opd(a.a, 0, r0 + s * pitch + f) * sh.state[f * D + col];
-            for (int s2 = 0; s2 <= s; ++s2) intra += sh.score[s * kMaxBk + s2] * opd(a.c, 2, r0 + s2 * pitch + col);
+            for (int f = 0; f < D; ++f) inter += qs[s * rp + f] * state[f * D + col];
+            for (int s2 = 0; s2 <= s; ++s2) intra += score[s * Bk + s2] * vs[s2 * rp + col];
             const float gr = a.phi_grad ? dphi_of_x(ld<BF16>(a.phi_grad, r0 + s * pitch + col), a.phi) : 1.f;
-            st<BF16>(a.out0, r0 + s * pitch + col, gr * (sh.pw[s + 1] * inter + intra));
+            st<BF16>(a.out0, r0 + s * pitch + col, gr * (pw[s + 1] * inter + intra));
         }
         __syncthreads();
         for (int i = tid; i < D * D; i += kThreads) {
             const int f = i / D, col = i % D;
             float acc = 0.f;
-            for (int s = 0; s < m; ++s)
-                acc += sh.pw[m - 1 - s] * opd(a.b, 1, r0 + s * pitch + f) * opd(a.c, 2, r0 + s * pitch + col);
-            sh.state[i] = sh.pw[m] * sh.state[i] + acc;
+            for (int s = 0; s < m; ++s) acc += pw[m - 1 - s] * ks[s * rp + f] * vs[s * rp + col];
+            state[i] = pw[m] * state[i] + acc;
         }
-        __syncthreads();
     }
+    __syncthreads();
     if (kv_dst)
-        for (int i = tid; i < D * D; i += kThreads) kv_dst[i] = sh.state[i];
+        for (int i = tid; i < D * D; i += kThreads) kv_dst[i] = state[i];
 }
 
 // One workgroup per (sequence, chunk) of a dense [P][N][D] problem.
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs lam) {
-    __shared__ Tile sh;
+    __shared__ float pool[kFwdPoolFloats];
     const int64_t pair = blockIdx.x / a.chunks;
     const int c = blockIdx.x % a.chunks;
     const int D = a.D;
@@ -107,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs l
         poison = !given_states_match(a);
     }
     float* kv_dst = (a.kv_out && c == a.chunks - 1) ? a.kv_out + pair * D * D : nullptr;
-    generic_sweep<BF16>(a, sh, lam.lam[pair % a.H], t_begin, t_end, pair * a.N * D, D, init, transposed, poison,
+    generic_sweep<BF16>(a, pool, lam.lam[pair % a.H], t_begin, t_end, pair * a.N * D, D, init, transposed, poison,
                         kv_dst);
 }
 
@@ -116,11 +142,11 @@ __global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs l
 // state (kv_in[b][h]) to its own final state (kv_out[b][h]).
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_fwd_generic_varlen(SweepArgs a, LamArgs lam, VarlenArgs v) {
-    __shared__ Tile sh;
+    __shared__ float pool[kFwdPoolFloats];
     const int b = static_cast<int>(blockIdx.x / a.H), h = static_cast<int>(blockIdx.x % a.H);
     const int64_t DD = static_cast<int64_t>(a.D) * a.D;
     const int64_t st_off = (static_cast<int64_t>(b) * a.H + h) * DD;
-    generic_sweep<BF16>(a, sh, lam.lam[h], v.cu[b], v.cu[b + 1], static_cast<int64_t>(h) * a.D,
+    generic_sweep<BF16>(a, pool, lam.lam[h], v.cu[b], v.cu[b + 1], static_cast<int64_t>(h) * a.D,
                         static_cast<int64_t>(a.H) * a.D, a.kv_in ? a.kv_in + st_off : nullptr, false, false,
                         a.kv_out ? a.kv_out + st_off : nullptr);
 }
@@ -426,21 +452,30 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a, LamArgs lam) 
 
 }  // namespace
 
+// The block the generic forward steps: the largest of Bk, Bk/2, ... whose LDS pool fits.
+SweepArgs fwd_generic_block(const SweepArgs& a) {
+    SweepArgs b = a;
+    while (b.Bk > 16 && fwd_pool_floats(b.D, b.Bk) > kFwdPoolFloats) b.Bk /= 2;
+    return b;
+}
+
 void launch_fwd_generic(const SweepArgs& a, const LamArgs& lam, int bf16, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(a.pairs * a.chunks));
+    const SweepArgs b = fwd_generic_block(a);
     if (bf16)
-        hipLaunchKernelGGL(k_fwd_generic<true>, grid, dim3(kThreads), 0, s, a, lam);
+        hipLaunchKernelGGL(k_fwd_generic<true>, grid, dim3(kThreads), 0, s, b, lam);
     else
-        hipLaunchKernelGGL(k_fwd_generic<false>, grid, dim3(kThreads), 0, s, a, lam);
+        hipLaunchKernelGGL(k_fwd_generic<false>, grid, dim3(kThreads), 0, s, b, lam);
 }
 
 void launch_fwd_generic_varlen(const SweepArgs& a, const LamArgs& lam, const VarlenArgs& v, int bf16,
                                hipStream_t s) {
     dim3 grid(static_cast<unsigned>(static_cast<int64_t>(v.nseq) * a.H));
+    const SweepArgs b = fwd_generic_block(a);
     if (bf16)
-        hipLaunchKernelGGL(k_fwd_generic_varlen<true>, grid, dim3(kThreads), 0, s, a, lam, v);
+        hipLaunchKernelGGL(k_fwd_generic_varlen<true>, grid, dim3(kThreads), 0, s, b, lam, v);
     else
-        hipLaunchKernelGGL(k_fwd_generic_varlen<false>, grid, dim3(kThreads), 0, s, a, lam, v);
+        hipLaunchKernelGGL(k_fwd_generic_varlen<false>, grid, dim3(kThreads), 0, s, b, lam, v);
 }
 
 void launch_rev_generic(const SweepArgs& a, const LamArgs& lam, int bf16, hipStream_t s) {
