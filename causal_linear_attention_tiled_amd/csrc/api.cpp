@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <limits>
 #include <atomic>
 #include <chrono>
 #include <random>
@@ -359,6 +360,33 @@ la::Stamp make_stamp(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int
     return st;
 }
 
+// The fused chunked prefix (k_fwd_dma_fused: aggregates, their sum and the sweep in one
+// launch) pays off while a chunk has few earlier chunks to sum; LA_FUSED=0 / 1 switches it
+// off / on for every chunk count.
+constexpr int kMaxFusedChunks = 4;
+// The fused sweep's bound on each wait, in polls of at least 128 cycles (a sleep and a load):
+// a base of 2^17 polls (several ms) plus 4096 polls (over 200 us) per 64-token block of the
+// awaited chunk's walk, so a wait gives up only when that walk runs about a hundred times
+// slower than a block's measured 1.5 us, whatever the chunk length.  Plans without aggregate
+// parts can have long chunks (an odd number of blocks per chunk admits no parts), whose walk
+// takes tens of ms.  LA_FUSED_SPIN lowers the bound for failure-path tests.
+constexpr int64_t kFusedSpinBase = int64_t(1) << 17;
+constexpr int64_t kFusedSpinPerBlock = 4096;
+
+int fused_spin_limit(const Plan& p) {
+    const int64_t blocks = (p.L + 63) / 64;
+    return static_cast<int>(std::min<int64_t>(std::numeric_limits<int>::max(),
+                                              kFusedSpinBase + kFusedSpinPerBlock * blocks));
+}
+
+bool fused_wanted(const Plan& p) {
+    if (env_is("LA_FUSED", "0")) return false;
+    if (env_is("LA_FUSED", "1")) return true;
+    // measured faster only with few chunks and no aggregate parts (the fused form walks each
+    // chunk whole, and every chunk sums all earlier aggregates)
+    return p.chunks <= kMaxFusedChunks && p.agg_k == 1;
+}
+
 // LA_TRACE=1: every call prints its plan to stderr (one line).
 void trace_plan(const char* call, int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t dtype,
                 const Plan& p, size_t ws_bytes) {
@@ -368,13 +396,15 @@ void trace_plan(const char* call, int64_t B, int64_t H, int64_t N, int64_t D, in
     const int64_t agg_wgs = p.chunks > 1 ? pairs * (p.chunks - 1) * p.agg_k : 0;
     std::fprintf(stderr,
                  "[liblinattn] %s B=%lld H=%lld N=%lld D=%lld %s Bk=%d (stepped %d) kernels=%s chunks=%d "
-                 "chunk_len=%lld agg_parts=%d sweep_wgs=%lld aggregate_wgs=%lld cus=%lld workspace=%zu\n",
+                 "chunk_len=%lld agg_parts=%d sweep_wgs=%lld aggregate_wgs=%lld cus=%lld workspace=%zu "
+                 "fused=%d fused_spin=%d\n",
                  call, static_cast<long long>(B), static_cast<long long>(H), static_cast<long long>(N),
                  static_cast<long long>(D), dtype == LA_BF16 ? "bf16" : "f32", Bk,
                  p.mfma ? ((p.bk == 128 && env_is("LA_FWD128", "1")) ? 128 : 64) : p.bk,
                  p.mfma ? "mfma" : "generic", p.chunks, static_cast<long long>(p.L), p.agg_k,
                  static_cast<long long>(pairs * p.chunks), static_cast<long long>(agg_wgs),
-                 static_cast<long long>(compute_units()), ws_bytes);
+                 static_cast<long long>(compute_units()), ws_bytes, p.chunks > 1 && fused_wanted(p) ? 1 : 0,
+                 fused_spin_limit(p));
 }
 
 // Largest workgroup count any launch of a chunked call makes: the sweeps (one per
@@ -405,22 +435,6 @@ struct PhiUse {
     int state_mask;    // operands of the chunk aggregates over (k, v) it maps (bit 0: k, 1: v)
     const void* grad;  // raw tensor whose phi' multiplies the sweep's output, or nullptr
 };
-
-// The fused chunked prefix (k_fwd_dma_fused: aggregates, their sum and the sweep in one
-// launch) pays off while a chunk has few earlier chunks to sum; LA_FUSED=0 / 1 switches it
-// off / on for every chunk count.
-constexpr int kMaxFusedChunks = 4;
-// The fused sweep's bound on each wait (polls of about 128 cycles each: a few ms, far beyond
-// any earlier chunk's walk); LA_FUSED_SPIN lowers it for failure-path tests.
-constexpr int kFusedSpinLimit = 1 << 17;
-
-bool fused_wanted(const Plan& p) {
-    if (env_is("LA_FUSED", "0")) return false;
-    if (env_is("LA_FUSED", "1")) return true;
-    // measured faster only with few chunks and no aggregate parts (the fused form walks each
-    // chunk whole, and every chunk sums all earlier aggregates)
-    return p.chunks <= kMaxFusedChunks && p.agg_k == 1;
-}
 
 // `stamp_out` (forward pass): where the scan (or the fused sweep) stores `stamp` after the
 // chunk states; `stamp_in` (dQ sweep fed `given`): the stamp stored after those states,
@@ -497,9 +511,9 @@ int run_forward_sweep(const void* q, const void* k, const void* v, void* out, co
         // LA_FUSED_LOSE_FLAGS=1 (failure-path tests): waiting waves look for a value no wave
         // publishes, so every wait runs out (LA_FUSED_SPIN polls) and its columns become NaN
         a.wait_epoch = env_is("LA_FUSED_LOSE_FLAGS", "1") ? ~a.epoch : a.epoch;
-        a.spin_limit = kFusedSpinLimit;
+        a.spin_limit = fused_spin_limit(p);
         if (const char* e = std::getenv("LA_FUSED_SPIN"); e && std::atoi(e) > 0)
-            a.spin_limit = std::min(std::atoi(e), kFusedSpinLimit);
+            a.spin_limit = std::min(std::atoi(e), a.spin_limit);
         a.stamp_store = stamp_out;
     }
     if (dma) {

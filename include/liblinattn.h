@@ -125,7 +125,9 @@ enum {
  * aggregates its chunk, publishes it with a flag carrying a number unique to
  * the call, and sums the aggregates of the earlier chunks of its sequence
  * before sweeping (a workgroup waits only on workgroups dispatched before
- * it; the wait is bounded, and a wave that gives up makes its columns NaN).
+ * it; the wait is bounded, in proportion to the awaited chunk's length
+ * (about 200 us per 64-token block on top of several ms), and a wave that
+ * gives up makes its columns NaN).
  * Under HIP graph capture, and with LA_FUSED=0, the aggregates and their
  * prefix run as two launches before the sweep instead (LA_FUSED=1 fuses any
  * chunk count, which is slower with more chunks or with parts).  The two

@@ -357,3 +357,29 @@ def test_trace_prints_the_plan():
     line = [x for x in r.stderr.splitlines() if x.startswith("[liblinattn] la_plan")]
     assert line, r.stderr
     assert "chunks=8 chunk_len=8192 agg_parts=1 sweep_wgs=256 aggregate_wgs=224" in line[0]
+    assert " fused=0 " in line[0]
+
+
+def test_fused_wait_bound_scales_with_the_chunk():
+    """A plan of 4 chunks whose block count per chunk is odd admits no aggregate parts, so the
+    fused prefix takes it however long its chunks are (here 16385 blocks, a walk of tens of
+    ms): the bound on each wait grows with the awaited walk (4096 polls per block on a base
+    of 2^17), where a fixed bound would let the waiting chunks give up and return NaN.
+    Host only (la_plan under LA_TRACE=1)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(la.__file__))
+    code = ("import sys; sys.path.insert(0, %r); import causal_linear_attention_tiled_amd as la; "
+            "la.la_plan(1, 64, 4 * 16385 * 64 - 3 * 64, 128, 64, la.LA_BF16); "
+            "la.la_plan(4, 16, 2048, 128, 64, la.LA_BF16)") % root
+    r = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, LA_TRACE="1"), capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    lines = [x for x in r.stderr.splitlines() if x.startswith("[liblinattn] la_plan")]
+    assert len(lines) == 2, r.stderr
+    fields = [dict(f.split("=", 1) for f in x.split() if "=" in f) for x in lines]
+    long_, short = fields
+    assert (long_["chunks"], long_["chunk_len"], long_["agg_parts"], long_["fused"]) == ("4", str(16385 * 64), "1", "1")
+    assert int(long_["fused_spin"]) == (1 << 17) + 4096 * 16385
+    assert (short["chunks"], short["chunk_len"], short["fused"]) == ("4", "512", "1")
+    assert int(short["fused_spin"]) == (1 << 17) + 4096 * 8
