@@ -57,6 +57,9 @@ constexpr int64_t kMaxWorkgroups = ((int64_t(1) << 32) - 1) / 1024;
 // A chunk should span at least this many blocks, so the per-chunk state
 // traffic (a few D x D float32 matrices) stays small next to its tokens.
 constexpr int64_t kMinBlocksPerChunk = 4;
+// The fixed cost of a round of aggregate workgroups, in tokens of one workgroup's stream
+// (the chunk plan's cost model).
+constexpr int64_t kRoundFill = 896;
 
 thread_local char g_err[256];
 
@@ -240,34 +243,63 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int32_t d
     // run over the parts, chunk c of a forward sweep starts from part c * agg_k - 1 and
     // chunk c of a reverse sweep from the gradient entering part (c + 1) agg_k.  The
     // aggregate kernels hold one workgroup per CU, so the W = (chunks - 1) agg_k pairs
-    // workgroups run in rounds of CUs.  A round costs its part length plus a pipeline fill
-    // of 256 tokens, scaled by max(1, its workgroups / (7/8 CUs)): about 7/8 of the CUs
-    // streaming already saturate HBM, fewer leave the round bound by one workgroup's rate.
-    // agg_k minimises the summed cost (the smallest on a tie, for the fewest scan steps),
-    // each part keeping at least kMinBlocksPerChunk blocks.  Measured (ms of the forward
-    // aggregates), every choice of this rule the fastest measured: B8 H16 N16384 0.104 at 2
-    // parts (0.111 at 4), B2 H16 N65536 0.163 at 1 (0.177 at 2), B1 H64 N262144 1.108 at 4
-    // (1.179 at 1, 1.278 at 2), B4 H16 N2048 0.0147 at 1 (0.0184 at 2), B2 H32 N8192
-    // 0.039 at 1.  LA_AGG_K forces it (dividing the blocks per chunk).
+    // workgroups run in rounds of CUs.  A round costs its part length plus kRoundFill tokens
+    // (its launch, pipeline fill and drain, and the spread of its workgroups' finishing
+    // times), scaled by max(1, its workgroups / (7/8 CUs)): about 7/8 of the CUs streaming
+    // already saturate HBM, fewer leave the round bound by one workgroup's rate.  agg_k
+    // minimises the summed cost (the smallest on a tie, for the fewest scan steps), each part
+    // keeping at least kMinBlocksPerChunk blocks.  Measured, every choice of this rule the
+    // fastest measured: ms of the forward aggregates, B8 H16 N16384 0.104 at 2 parts (0.111
+    // at 4), B2 H16 N65536 0.163 at 1 (0.177 at 2), B1 H64 N262144 1.108 at 4 (1.179 at 1,
+    // 1.278 at 2), B4 H16 N2048 0.0147 at 1 (0.0184 at 2), B2 H32 N8192 0.039 at 1; and ms
+    // of la_fwd + la_bwd at B2 H32 (4 chunks), 1 part against 4: N40960 2.30 against 2.33,
+    // N81920 4.56 against 4.54, N163840 9.44 against 9.31 (the fill of 256 tokens assumed
+    // before switched to 4 parts at chunks of 7K tokens, 900 at 15K, between these two
+    // measured crossings).  Parts need a chunk of a whole number of parts: where the blocks per chunk
+    // do not divide by k, the chunks grow to the next multiple of k blocks if the chunk count
+    // stays the same (the last chunk takes what is left), and the cost adds the sweep's
+    // longer chunks at twice an aggregate token (a sweep streams four tensors, an aggregate
+    // two).  LA_AGG_K forces k (when such a chunk length exists).
     p.agg_k = 1;
     if (p.chunks > 1) {
+        // blocks per chunk with k parts, or 0 where rounding up would change the chunk count
+        auto blocks_for = [&](int64_t k) -> int64_t {
+            const int64_t b = (bpc + k - 1) / k * k;
+            return (nb + b - 1) / b == p.chunks ? b : 0;
+        };
+        int64_t best_b = bpc;
         const char* ek = std::getenv("LA_AGG_K");
         if (ek && std::atoll(ek) > 0) {
             const int64_t k = std::atoll(ek);
-            if (bpc % k == 0) p.agg_k = static_cast<int>(k);
+            if (const int64_t b = blocks_for(k)) {
+                p.agg_k = static_cast<int>(k);
+                best_b = b;
+            }
         } else {
             const int64_t cus = compute_units();
             const double sat = 0.875 * static_cast<double>(cus);
-            auto cost = [&](int64_t k) {
+            auto cost = [&](int64_t k, int64_t b) {
                 const int64_t w = (p.chunks - 1) * k * pairs;
-                const double part = static_cast<double>(p.L / k + 4 * 64);
+                const double part = static_cast<double>(b / k * Bk + kRoundFill);
                 const double full = static_cast<double>(w / cus), rem = static_cast<double>(w % cus);
                 return part * (full * std::max(1.0, static_cast<double>(cus) / sat) +
-                               (rem > 0 ? std::max(1.0, rem / sat) : 0.0));
+                               (rem > 0 ? std::max(1.0, rem / sat) : 0.0)) +
+                       2.0 * static_cast<double>((b - bpc) * Bk);
             };
-            for (int64_t k = 2; k <= 16 && bpc % k == 0 && bpc / k >= kMinBlocksPerChunk; k *= 2)
-                if (cost(k) < cost(p.agg_k) - 1e-12) p.agg_k = static_cast<int>(k);
+            double best = cost(1, bpc);
+            for (int64_t k = 2; k <= 16; k *= 2) {
+                const int64_t b = blocks_for(k);
+                if (!b) continue;
+                if (b / k < kMinBlocksPerChunk) break;
+                const double c = cost(k, b);
+                if (c < best - 1e-12) {
+                    best = c;
+                    best_b = b;
+                    p.agg_k = static_cast<int>(k);
+                }
+            }
         }
+        p.L = best_b * Bk;
     }
     return p;
 }
@@ -361,9 +393,14 @@ la::Stamp make_stamp(int64_t B, int64_t H, int64_t N, int64_t D, int32_t Bk, int
 }
 
 // The fused chunked prefix (k_fwd_dma_fused: aggregates, their sum and the sweep in one
-// launch) pays off while a chunk has few earlier chunks to sum; LA_FUSED=0 / 1 switches it
-// off / on for every chunk count.
+// launch) pays off while a chunk has few earlier chunks to sum and is short enough that the
+// launches it saves count; LA_FUSED=0 / 1 switches it off / on for every plan.  Measured
+// (us of la_fwd, one aggregate part, fused against three launches): B4 H16 N2048 (512-token
+// chunks) 48 against 53, B4 H16 N4096 (1024) 80 against 81, B2 H32 N8192 (2048) 152
+// against 154; B2 H32 N12288 (3072) 240-257 against 238, N20480 (5120) 385 against 374,
+// N40960 (10240) 744-752 against 737.
 constexpr int kMaxFusedChunks = 4;
+constexpr int64_t kMaxFusedChunkLen = 2048;
 // The fused sweep's bound on each wait, in polls of at least 128 cycles (a sleep and a load):
 // a base of 2^17 polls (several ms) plus 4096 polls (over 200 us) per 64-token block of the
 // awaited chunk's walk, so a wait gives up only when that walk runs about a hundred times
@@ -382,9 +419,9 @@ int fused_spin_limit(const Plan& p) {
 bool fused_wanted(const Plan& p) {
     if (env_is("LA_FUSED", "0")) return false;
     if (env_is("LA_FUSED", "1")) return true;
-    // measured faster only with few chunks and no aggregate parts (the fused form walks each
-    // chunk whole, and every chunk sums all earlier aggregates)
-    return p.chunks <= kMaxFusedChunks && p.agg_k == 1;
+    // measured faster only with few, short chunks and no aggregate parts (the fused form
+    // walks each chunk whole, and every chunk sums all earlier aggregates)
+    return p.chunks <= kMaxFusedChunks && p.L <= kMaxFusedChunkLen && p.agg_k == 1;
 }
 
 // LA_TRACE=1: every call prints its plan to stderr (one line).

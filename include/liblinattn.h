@@ -49,7 +49,8 @@
  *  - The environment variable LA_CHUNKS (a positive integer) overrides the
  *    number of chunks a sequence is split into for the chunked prefix over
  *    blocks, LA_AGG_K the number of parts of a chunk the chunk aggregates are
- *    taken over (la_plan); LA_KERNEL=generic forces the generic (non-MFMA)
+ *    taken over (la_plan; the chunks grow to a whole number of parts where the
+ *    chunk count stays the same, else it is ignored); LA_KERNEL=generic forces the generic (non-MFMA)
  *    kernels; LA_FWD128=1 the 128-token-block forward-direction sweep;
  *    LA_STATE=dma2 the chunk aggregates with every wave loading at two
  *    workgroups per CU (instead of two loader waves at one);
@@ -119,8 +120,8 @@ enum {
  *             chunk but the last (float32) and a stamp identifying this call,
  *             which la_bwd can take as fwd_ws instead of computing the states
  *             again.
- * When the sequence is split into at most 4 chunks without aggregate parts
- * (la_plan), on the 64-token sweep, the chunked
+ * When the sequence is split into at most 4 chunks of at most 2048 tokens
+ * without aggregate parts (la_plan), on the 64-token sweep, the chunked
  * prefix runs inside the sweep's own launch: each chunk's workgroup first
  * aggregates its chunk, publishes it with a flag carrying a number unique to
  * the call, and sums the aggregates of the earlier chunks of its sequence

@@ -273,6 +273,15 @@ def test_plan():
     assert la.la_plan(8, 16, 16384, 128, 64, la.LA_BF16) == {"chunks": 2, "chunk_len": 8192, "agg_parts": 2}
     assert la.la_plan(2, 16, 65536, 128, 64, la.LA_BF16) == {"chunks": 8, "chunk_len": 8192, "agg_parts": 1}
     assert la.la_plan(1, 64, 262144, 128, 128, la.LA_BF16) == {"chunks": 4, "chunk_len": 65536, "agg_parts": 4}
+    # 4097 blocks: chunks of 1025 blocks admit no parts, so they grow to 1028 (4 parts of 257),
+    # the last chunk keeping 1013
+    assert la.la_plan(1, 64, 262208, 128, 64, la.LA_BF16) == {"chunks": 4, "chunk_len": 65792, "agg_parts": 4}
+    # whatever the rounding, the chunks cover the sequence, the last one non-empty, in whole parts
+    for B, H, N, Bk in [(1, 64, 100000, 64), (1, 64, 262272, 128), (2, 32, 8000, 64), (8, 16, 16320, 64),
+                        (1, 16, 77777, 64), (3, 7, 54321, 128), (1, 64, 4 * 16385 * 64 - 192, 64)]:
+        p = la.la_plan(B, H, N, 128, Bk, la.LA_BF16)
+        assert (p["chunks"] - 1) * p["chunk_len"] < N <= p["chunks"] * p["chunk_len"], (B, H, N, p)
+        assert p["chunk_len"] % (p["agg_parts"] * Bk) == 0, (B, H, N, p)
     p = la.la_plan(1, 2, 1000, 64, 32, la.LA_F32)
     assert p["chunks"] > 1 and p["chunk_len"] % 32 == 0 and (p["chunks"] - 1) * p["chunk_len"] < 1000
     # forward workspace: agg_parts float32 D x D slots per chunk boundary per sequence
@@ -361,25 +370,33 @@ def test_trace_prints_the_plan():
 
 
 def test_fused_wait_bound_scales_with_the_chunk():
-    """A plan of 4 chunks whose block count per chunk is odd admits no aggregate parts, so the
-    fused prefix takes it however long its chunks are (here 16385 blocks, a walk of tens of
-    ms): the bound on each wait grows with the awaited walk (4096 polls per block on a base
-    of 2^17), where a fixed bound would let the waiting chunks give up and return NaN.
-    Host only (la_plan under LA_TRACE=1)."""
+    """The bound on each wait of the fused prefix grows with the awaited chunk's walk (4096
+    polls per 64-token block on a base of 2^17): LA_FUSED=1 fuses chunks of any length, here
+    16388 blocks (a walk of tens of ms), where a fixed bound would let the waiting chunks give
+    up and return NaN.  By default the fused form takes the plans whose cost model keeps one
+    aggregate part, chunks of a few thousand tokens.  Host only (la_plan under LA_TRACE=1)."""
     import subprocess
     import sys
     root = os.path.dirname(os.path.dirname(la.__file__))
     code = ("import sys; sys.path.insert(0, %r); import causal_linear_attention_tiled_amd as la; "
             "la.la_plan(1, 64, 4 * 16385 * 64 - 3 * 64, 128, 64, la.LA_BF16); "
             "la.la_plan(4, 16, 2048, 128, 64, la.LA_BF16)") % root
-    r = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, LA_TRACE="1"), capture_output=True,
-                       text=True, timeout=120)
-    assert r.returncode == 0, r.stderr
-    lines = [x for x in r.stderr.splitlines() if x.startswith("[liblinattn] la_plan")]
-    assert len(lines) == 2, r.stderr
-    fields = [dict(f.split("=", 1) for f in x.split() if "=" in f) for x in lines]
-    long_, short = fields
-    assert (long_["chunks"], long_["chunk_len"], long_["agg_parts"], long_["fused"]) == ("4", str(16385 * 64), "1", "1")
-    assert int(long_["fused_spin"]) == (1 << 17) + 4096 * 16385
-    assert (short["chunks"], short["chunk_len"], short["fused"]) == ("4", "512", "1")
+    env = dict(os.environ, LA_TRACE="1")
+    for name in ("LA_FUSED", "LA_CHUNKS", "LA_AGG_K"):
+        env.pop(name, None)
+    fields = {}
+    for fused in (None, "1"):
+        if fused:
+            env["LA_FUSED"] = fused
+        r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+        assert r.returncode == 0, r.stderr
+        lines = [x for x in r.stderr.splitlines() if x.startswith("[liblinattn] la_plan")]
+        assert len(lines) == 2, r.stderr
+        fields[fused] = [dict(f.split("=", 1) for f in x.split() if "=" in f) for x in lines]
+    (long_, short), (long_forced, _) = fields[None], fields["1"]
+    # the long chunks: 4 parts (the chunk grown from 16385 to 16388 blocks), not fused by default
+    assert (long_["chunks"], long_["chunk_len"], long_["agg_parts"], long_["fused"]) == ("4", str(16388 * 64), "4", "0")
+    assert long_forced["fused"] == "1"
+    assert int(long_forced["fused_spin"]) == (1 << 17) + 4096 * 16388
+    assert (short["chunks"], short["chunk_len"], short["agg_parts"], short["fused"]) == ("4", "512", "1", "1")
     assert int(short["fused_spin"]) == (1 << 17) + 4096 * 8

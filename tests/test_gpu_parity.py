@@ -233,15 +233,46 @@ def test_impulse_probe_fine_aggregates(kern, lam_val, agg, chunks, kernel, monke
 
 
 @pytest.mark.parametrize("kern", ["generic", "default"])
-@pytest.mark.parametrize("cks,agg", [(2, 2), (2, 4), (3, 2)])
-def test_fine_aggregates_parity(kern, cks, agg, chunks, kernel, monkeypatch):
+@pytest.mark.parametrize("lam_val", [1.0, 0.5])
+def test_impulse_probe_grown_chunks(kern, lam_val, chunks, kernel, monkeypatch):
+    """27 blocks in 3 chunks of 9 blocks admit no 2 parts; the plan grows the chunks to 10
+    blocks (the last keeping 7) and takes the aggregates over parts of 5.  Keys on part,
+    chunk and block boundaries and their neighbours: O_t = lam^(t-j0) e_c exactly."""
+    kernel(kern)
+    chunks(3)
+    monkeypatch.setenv("LA_AGG_K", "2")
+    N, D, c, Bk = 64 * 26 + 17, 128, 3, 64
+    assert la.la_plan(1, 1, N, D, Bk, la.LA_BF16) == {"chunks": 3, "chunk_len": 640, "agg_parts": 2}
+    t = np.arange(N)
+    for j0 in sorted({0, 319, 320, 321, 639, 640, 641, 959, 960, 961, 1279, 1280, 1281, N - 1}):
+        print(f"[impulse grown] kern={kern} lam={lam_val} j0={j0}", flush=True)
+        qa, ka, va = impulse_inputs(N, D, j0, c, "bf16")
+        o, s = la.la_fwd(to_dev(qa, "bf16"), to_dev(ka, "bf16"), to_dev(va, "bf16"), [lam_val], Bk=Bk)
+        _sync()
+        rel = t - j0
+        keep = rel <= 100 if lam_val < 1 else np.ones(N, bool)
+        expect = np.zeros((N, D))
+        expect[rel >= 0, c] = np.float64(lam_val) ** rel[rel >= 0]
+        np.testing.assert_array_equal(got(o)[0, 0][keep], expect[keep], err_msg=f"j0={j0}")
+        if lam_val == 1 or N - 1 - j0 <= 100:
+            s_exp = np.zeros((D, D))
+            s_exp[0, c] = np.float64(lam_val) ** (N - 1 - j0)
+            np.testing.assert_array_equal(got(s)[0, 0], s_exp, err_msg=f"state j0={j0}")
+
+
+@pytest.mark.parametrize("kern", ["generic", "default"])
+@pytest.mark.parametrize("cks,agg,N", [(2, 2, 64 * 15 + 17), (2, 4, 64 * 15 + 17), (3, 2, 64 * 15 + 17),
+                                       (3, 2, 64 * 14 + 17)])
+def test_fine_aggregates_parity(kern, cks, agg, N, chunks, kernel, monkeypatch):
     """Forward and backward (the backward also fed the forward's states) with the forward
-    aggregates over agg parts of each chunk, ragged tail, initial state."""
+    aggregates over agg parts of each chunk, ragged tail, initial state.  At N = 64*14+17
+    (15 blocks in 3 chunks of 5) the chunks grow to 6 blocks for 2 parts, the last keeping 3."""
     kernel(kern)
     chunks(cks)
     monkeypatch.setenv("LA_AGG_K", str(agg))
     lam = synth.decay_schedule(3)
-    N = 64 * 15 + 17
+    if N == 64 * 14 + 17:
+        assert la.la_plan(2, 3, N, 128, 64, la.LA_BF16) == {"chunks": 3, "chunk_len": 384, "agg_parts": 2}
     check_fwd(2, 3, N, 128, 64, "bf16", lam, seed=40 + agg, with_state=True, label=f"{kern} agg={agg}")
     check_bwd(2, 3, N, 128, 64, "bf16", lam, seed=40 + agg, with_state=True, label=f"{kern} agg={agg}", fwd_ws=True)
 
@@ -613,17 +644,19 @@ def test_fused_prefix_repeat_and_reuse(fused, chunks):
 
 @pytest.mark.parametrize("B,H,N,bk,want_fused", [(4, 16, 2048, 64, True), (2, 32, 8192, 64, True),
                                                  (4, 16, 4096, 128, True), (8, 16, 4096, 64, False),
-                                                 (2, 16, 8192, 64, False), (2, 8, 4096, 128, False)])
+                                                 (2, 16, 8192, 64, False), (2, 8, 4096, 128, False),
+                                                 (2, 32, 12288, 64, False)])
 def test_fused_prefix_default_routing(monkeypatch, B, H, N, bk, want_fused):
-    """Without LA_FUSED, the forward of a plan of at most 4 chunks without aggregate parts runs
-    as one launch (fwd_dma_fused) and any other chunked plan as aggregates, scan and sweep; the
-    launches are those the library's own per-launch profiler records.  Under HIP graph capture
-    the three-launch form runs and replays to the eager result."""
+    """Without LA_FUSED, the forward of a plan of at most 4 chunks of at most 2048 tokens without
+    aggregate parts runs as one launch (fwd_dma_fused) and any other chunked plan (here also
+    3072-token chunks with one part) as aggregates, scan and sweep; the launches are those the
+    library's own per-launch profiler records.  Under HIP graph capture the three-launch form
+    runs and replays to the eager result."""
     for name in ("LA_FUSED", "LA_CHUNKS", "LA_AGG_K", "LA_KERNEL", "LA_FWD", "LA_FWD_WAVES", "LA_FWD128"):
         monkeypatch.delenv(name, raising=False)
     plan = la.la_plan(B, H, N, 128, bk, la.LA_BF16)
     print(f"[routing] B={B} H={H} N={N} Bk={bk} plan={plan} fused expected={want_fused}", flush=True)
-    assert (plan["chunks"] > 1 and plan["chunks"] <= 4 and plan["agg_parts"] == 1) == want_fused
+    assert (1 < plan["chunks"] <= 4 and plan["chunk_len"] <= 2048 and plan["agg_parts"] == 1) == want_fused
     lam = synth.decay_schedule(H)
     gen = torch.Generator(device="cuda").manual_seed(7)
     q, k, v = (torch.randn(B, H, N, 128, device="cuda", generator=gen).div(math.sqrt(128)).to(torch.bfloat16)

@@ -54,8 +54,8 @@ def env(monkeypatch):
     return set_
 
 
-def run_bwd_probe(Bk, lam_val, with_state, with_gf, use_fwd_ws, label):
-    N, H = 64 * 23 + 17, PROBES
+def run_bwd_probe(Bk, lam_val, with_state, with_gf, use_fwd_ws, label, N=64 * 23 + 17):
+    H = PROBES
     plan = la.la_plan(1, H, N, D, Bk, la.LA_BF16)
     pairs = probe_pairs(N, Bk, plan, lam_val, limit=H)
     print(f"[probe bwd] {label} Bk={Bk} lam={lam_val} kv_in={with_state} dkv_out={with_gf} "
@@ -123,12 +123,28 @@ def test_bwd_impulse_block128_kernel(env, Bk, cks, agg, lam_val, use_fwd_ws):
     run_bwd_probe(Bk, lam_val, with_state=True, with_gf=True, use_fwd_ws=use_fwd_ws, label="dma128")
 
 
+# 27 blocks in 3 chunks of 9 admit no 2 parts: the plan grows the chunks to 10 blocks (the
+# last keeping 7), the aggregates taken over parts of 5
+GROWN_N = 64 * 26 + 17
+GROWN_PLAN = {"chunks": 3, "chunk_len": 640, "agg_parts": 2}
+
+
+@pytest.mark.parametrize("kern", ["default", "generic"])
+@pytest.mark.parametrize("lam_val", [0.5, 1.0])
+@pytest.mark.parametrize("use_fwd_ws", [False, True])
+def test_bwd_impulse_grown_chunks(env, kern, lam_val, use_fwd_ws):
+    env(kernel=kern, chunks=3, agg=2)
+    assert la.la_plan(1, PROBES, GROWN_N, D, 64, la.LA_BF16) == GROWN_PLAN
+    run_bwd_probe(64, lam_val, with_state=True, with_gf=True, use_fwd_ws=use_fwd_ws,
+                  label=f"{kern} grown chunks", N=GROWN_N)
+
+
 # ------------------------------------------------------------------ la_dlam
-def run_dlam_probe(Bk, lam_val, with_terms, label):
+def run_dlam_probe(Bk, lam_val, with_terms, label, N=64 * 23 + 17):
     """lam = 1/2 without S0 and F: dL/dlam = (i0-j0) 2^-(i0-j0-1) (0 for i0 = j0), one exact
     term.  lam = 1 with S0 = e_a e_c2^T and F = e0 e_c^T + e_a e_c2^T: the four terms
     (i0-j0) + (i0+1) + (N-1-j0) + N are integers, exact in float32."""
-    N, H = 64 * 23 + 17, PROBES
+    H = PROBES
     plan = la.la_plan(1, H, N, D, Bk, la.LA_BF16)
     pairs = probe_pairs(N, Bk, plan, lam_val, limit=H)
     print(f"[probe dlam] {label} Bk={Bk} lam={lam_val} terms={with_terms} plan={plan} probes={H}", flush=True)
@@ -160,6 +176,19 @@ def test_dlam_impulse_bit_exact(monkeypatch, kern, Bk, cks, agg, lam_val, with_t
         else:
             monkeypatch.setenv(name, str(val))
     run_dlam_probe(Bk, lam_val, with_terms, label=f"{kern} chunks={cks} agg={agg}")
+
+
+@pytest.mark.parametrize("kern", ["default", "generic"])
+@pytest.mark.parametrize("lam_val,with_terms", [(0.5, False), (1.0, True)])
+def test_dlam_impulse_grown_chunks(monkeypatch, kern, lam_val, with_terms):
+    for name, val in (("LA_KERNEL", "generic" if kern == "generic" else None), ("LA_DLAM", None),
+                      ("LA_DLAM_WAVES", None), ("LA_CHUNKS", 3), ("LA_AGG_K", 2)):
+        if val is None:
+            monkeypatch.delenv(name, raising=False)
+        else:
+            monkeypatch.setenv(name, str(val))
+    assert la.la_plan(1, PROBES, GROWN_N, D, 64, la.LA_BF16) == GROWN_PLAN
+    run_dlam_probe(64, lam_val, with_terms, label=f"{kern} grown chunks", N=GROWN_N)
 
 
 # ------------------------------------------------------------------ la_fwd_varlen
