@@ -207,6 +207,68 @@ def test_impulse_probe_bit_exact(kern, lam_val, Bk, cks, chunks, kernel):
             np.testing.assert_array_equal(got(s)[0, 0], s_exp, err_msg=f"state j0={j0}")
 
 
+MAX_HEADS = 256  # per-head decays travel in the kernel arguments, 256 at most
+
+
+def max_heads_decays():
+    """Every head decays by 1 except head 0 (1/4), head 128 (0) and the last head (1/2): a
+    head reading its neighbour's value, or a value past the table, shows."""
+    lam = np.ones(MAX_HEADS, np.float32)
+    lam[0], lam[128], lam[MAX_HEADS - 1] = 0.25, 0.0, 0.5
+    return lam
+
+
+@pytest.mark.parametrize("kern", ["generic", "default"])
+@pytest.mark.parametrize("cks", [None, 2])
+def test_max_heads_decay_per_head_bit_exact(kern, cks, chunks, kernel):
+    """B1 H256 (the most heads a call takes): q_t = e0, one key e0 with value e_c at j0 in
+    every head, so O_t = lam_h^(t-j0) e_c and S_N = lam_h^(N-1-j0) e0 e_c^T exactly, each
+    head with its own decay (one chunk, and two chunks, which also runs the aggregates)."""
+    kernel(kern)
+    chunks(cks)
+    H, N, D, c, j0 = MAX_HEADS, 70, 128, 7, 30
+    lam = max_heads_decays()
+    q = np.zeros((1, H, N, D), np.float32)
+    q[..., 0] = 1.0
+    k, v = np.zeros_like(q), np.zeros_like(q)
+    k[0, :, j0, 0] = 1.0
+    v[0, :, j0, c] = 1.0
+    dev = [to_dev(synth.f32_to_bf16_bits(x), "bf16") for x in (q, k, v)]
+    print(f"[max heads] kern={kern} chunks={cks} plan={la.la_plan(1, H, N, D, 64, la.LA_BF16)}", flush=True)
+    o, s = la.la_fwd(*dev, lam, Bk=64)
+    _sync()
+    t = np.arange(N)
+    lam64 = lam.astype(np.float64)
+    exp_o = np.zeros((H, N, D))
+    rel = t - j0
+    exp_o[:, rel >= 0, c] = lam64[:, None] ** rel[None, rel >= 0]
+    exp_s = np.zeros((H, D, D))
+    exp_s[:, 0, c] = lam64 ** (N - 1 - j0)
+    np.testing.assert_array_equal(got(o)[0], exp_o)
+    np.testing.assert_array_equal(got(s)[0], exp_s)
+
+
+def test_max_heads_decode_decay_per_head_bit_exact():
+    """A decode step at B2 H256: from S = e0 e_c^T with k = v = 0, the step leaves
+    S = lam_h e0 e_c^T and o = q S = lam_h e_c (q = e0), each head with its own decay."""
+    Bs, H, D, c = 2, MAX_HEADS, 128, 5
+    lam = max_heads_decays()
+    state = torch.zeros((Bs, H, D, D), dtype=torch.float32, device="cuda")
+    state[:, :, 0, c] = 1.0
+    q = torch.zeros((Bs, H, D), dtype=torch.bfloat16, device="cuda")
+    q[..., 0] = 1.0
+    k, v = torch.zeros_like(q), torch.zeros_like(q)
+    o = la.la_decode_step(state, q, k, v, lam)
+    _sync()
+    lam64 = lam.astype(np.float64)
+    exp_o = np.zeros((Bs, H, D))
+    exp_o[:, :, c] = lam64[None, :]
+    exp_s = np.zeros((Bs, H, D, D))
+    exp_s[:, :, 0, c] = lam64[None, :]
+    np.testing.assert_array_equal(got(o), exp_o)
+    np.testing.assert_array_equal(got(state), exp_s)
+
+
 @pytest.mark.parametrize("kern", ["generic", "default"])
 @pytest.mark.parametrize("lam_val", [1.0, 0.5])
 @pytest.mark.parametrize("agg", [2, 4])
