@@ -43,12 +43,15 @@ static_assert(fwd_pool_floats(kMaxD, 16) <= kFwdPoolFloats, "every D fits at the
 //   O_b = diag(lam^(s+1)) Q_b S + (Q_b K_b^T o M) V_b,  S <- lam^m S + (diag(lam^(m-1-s)) K_b)^T V_b
 // starting from init (or zero; read transposed when `transposed`; NaN when `poison`) and
 // leaving the final state in kv_dst (unless null).  Each block's rows are read from
-// global memory once, into LDS.
-template <bool BF16>
+// global memory once, into LDS.  D (= a.D) is a compile-time constant, so the loops over
+// features unroll and their LDS reads issue back to back instead of one dependent read
+// per step (the float32 correctness shape B1 H2 N256 d16 runs on two workgroups, where
+// that latency is the whole run time).
+template <bool BF16, int D>
 __device__ void generic_sweep(const SweepArgs& a, float* pool, float lv, int64_t t_begin, int64_t t_end,
                               int64_t base, int64_t pitch, const float* init, bool transposed, bool poison,
                               float* kv_dst) {
-    const int D = a.D, Bk = a.Bk, tid = threadIdx.x;
+    const int Bk = a.Bk, tid = threadIdx.x;
     float* state = pool;             // [D][D]
     float* score = state + D * D;    // [Bk][Bk]
     const int rp = D + 1;            // staged row pitch
@@ -84,6 +87,7 @@ __device__ void generic_sweep(const SweepArgs& a, float* pool, float lv, int64_t
             const int s = i / m, s2 = i % m;
             float x = 0.f;
             if (s2 <= s) {
+#pragma unroll
                 for (int f = 0; f < D; ++f) x += qs[s * rp + f] * ks[s2 * rp + f];
                 x *= pw[s - s2];
             }
@@ -93,7 +97,9 @@ __device__ void generic_sweep(const SweepArgs& a, float* pool, float lv, int64_t
         for (int i = tid; i < m * D; i += kThreads) {
             const int s = i / D, col = i % D;
             float inter = 0.f, intra = 0.f;
+#pragma unroll
             for (int f = 0; f < D; ++f) inter += qs[s * rp + f] * state[f * D + col];
+#pragma unroll 8
             for (int s2 = 0; s2 <= s; ++s2) intra += score[s * Bk + s2] * vs[s2 * rp + col];
             const float gr = a.phi_grad ? dphi_of_x(ld<BF16>(a.phi_grad, r0 + s * pitch + col), a.phi) : 1.f;
             st<BF16>(a.out0, r0 + s * pitch + col, gr * (pw[s + 1] * inter + intra));
@@ -102,6 +108,7 @@ __device__ void generic_sweep(const SweepArgs& a, float* pool, float lv, int64_t
         for (int i = tid; i < D * D; i += kThreads) {
             const int f = i / D, col = i % D;
             float acc = 0.f;
+#pragma unroll 8
             for (int s = 0; s < m; ++s) acc += pw[m - 1 - s] * ks[s * rp + f] * vs[s * rp + col];
             state[i] = pw[m] * state[i] + acc;
         }
@@ -111,13 +118,12 @@ __device__ void generic_sweep(const SweepArgs& a, float* pool, float lv, int64_t
         for (int i = tid; i < D * D; i += kThreads) kv_dst[i] = state[i];
 }
 
-// One workgroup per (sequence, chunk) of a dense [P][N][D] problem.
-template <bool BF16>
+// One workgroup per (sequence, chunk) of a dense [P][N][D] problem (D = a.D).
+template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs lam) {
     __shared__ float pool[kFwdPoolFloats];
     const int64_t pair = blockIdx.x / a.chunks;
     const int c = blockIdx.x % a.chunks;
-    const int D = a.D;
     const int64_t t_begin = static_cast<int64_t>(c) * a.L;
     const int64_t t_end = min(a.N, t_begin + a.L);
     const float* init = nullptr;
@@ -133,22 +139,22 @@ __global__ __launch_bounds__(kThreads) void k_fwd_generic(SweepArgs a, LamArgs l
         poison = !given_states_match(a);
     }
     float* kv_dst = (a.kv_out && c == a.chunks - 1) ? a.kv_out + pair * D * D : nullptr;
-    generic_sweep<BF16>(a, pool, lam.lam[pair % a.H], t_begin, t_end, pair * a.N * D, D, init, transposed, poison,
-                        kv_dst);
+    generic_sweep<BF16, D>(a, pool, lam.lam[pair % a.H], t_begin, t_end, pair * a.N * D, D, init, transposed,
+                           poison, kv_dst);
 }
 
 // One workgroup per (sequence, head) of a ragged batch packed token-major [T][H][D]:
 // sequence b holds tokens [v.cu[b], v.cu[b + 1]) and is swept whole from its own initial
-// state (kv_in[b][h]) to its own final state (kv_out[b][h]).
-template <bool BF16>
+// state (kv_in[b][h]) to its own final state (kv_out[b][h]) (D = a.D).
+template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void k_fwd_generic_varlen(SweepArgs a, LamArgs lam, VarlenArgs v) {
     __shared__ float pool[kFwdPoolFloats];
     const int b = static_cast<int>(blockIdx.x / a.H), h = static_cast<int>(blockIdx.x % a.H);
-    const int64_t DD = static_cast<int64_t>(a.D) * a.D;
+    const int64_t DD = static_cast<int64_t>(D) * D;
     const int64_t st_off = (static_cast<int64_t>(b) * a.H + h) * DD;
-    generic_sweep<BF16>(a, pool, lam.lam[h], v.cu[b], v.cu[b + 1], static_cast<int64_t>(h) * a.D,
-                        static_cast<int64_t>(a.H) * a.D, a.kv_in ? a.kv_in + st_off : nullptr, false, false,
-                        a.kv_out ? a.kv_out + st_off : nullptr);
+    generic_sweep<BF16, D>(a, pool, lam.lam[h], v.cu[b], v.cu[b + 1], static_cast<int64_t>(h) * D,
+                           static_cast<int64_t>(a.H) * D, a.kv_in ? a.kv_in + st_off : nullptr, false, false,
+                           a.kv_out ? a.kv_out + st_off : nullptr);
 }
 
 // Reverse sweep over one chunk (blocks from last to first), carrying
@@ -459,23 +465,41 @@ SweepArgs fwd_generic_block(const SweepArgs& a) {
     return b;
 }
 
+namespace {
+// the dense kernel for the storage type and D (16, 32, 64 or 128: what the library accepts)
+template <bool BF16>
+void (*fwd_generic_kernel(int D))(SweepArgs, LamArgs) {
+    switch (D) {
+        case 16: return k_fwd_generic<BF16, 16>;
+        case 32: return k_fwd_generic<BF16, 32>;
+        case 64: return k_fwd_generic<BF16, 64>;
+        default: return k_fwd_generic<BF16, 128>;
+    }
+}
+template <bool BF16>
+void (*fwd_generic_varlen_kernel(int D))(SweepArgs, LamArgs, VarlenArgs) {
+    switch (D) {
+        case 16: return k_fwd_generic_varlen<BF16, 16>;
+        case 32: return k_fwd_generic_varlen<BF16, 32>;
+        case 64: return k_fwd_generic_varlen<BF16, 64>;
+        default: return k_fwd_generic_varlen<BF16, 128>;
+    }
+}
+}  // namespace
+
 void launch_fwd_generic(const SweepArgs& a, const LamArgs& lam, int bf16, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(a.pairs * a.chunks));
     const SweepArgs b = fwd_generic_block(a);
-    if (bf16)
-        hipLaunchKernelGGL(k_fwd_generic<true>, grid, dim3(kThreads), 0, s, b, lam);
-    else
-        hipLaunchKernelGGL(k_fwd_generic<false>, grid, dim3(kThreads), 0, s, b, lam);
+    auto kern = bf16 ? fwd_generic_kernel<true>(b.D) : fwd_generic_kernel<false>(b.D);
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, b, lam);
 }
 
 void launch_fwd_generic_varlen(const SweepArgs& a, const LamArgs& lam, const VarlenArgs& v, int bf16,
                                hipStream_t s) {
     dim3 grid(static_cast<unsigned>(static_cast<int64_t>(v.nseq) * a.H));
     const SweepArgs b = fwd_generic_block(a);
-    if (bf16)
-        hipLaunchKernelGGL(k_fwd_generic_varlen<true>, grid, dim3(kThreads), 0, s, b, lam, v);
-    else
-        hipLaunchKernelGGL(k_fwd_generic_varlen<false>, grid, dim3(kThreads), 0, s, b, lam, v);
+    auto kern = bf16 ? fwd_generic_varlen_kernel<true>(b.D) : fwd_generic_varlen_kernel<false>(b.D);
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, b, lam, v);
 }
 
 void launch_rev_generic(const SweepArgs& a, const LamArgs& lam, int bf16, hipStream_t s) {
