@@ -5,10 +5,10 @@
 // through the carried key-value state) and serve as the path for shapes the
 // MFMA kernels do not cover, and for float32 storage.
 //
-// One workgroup handles one (sequence, chunk).  The D x D float32 state and
-// one Bk x Bk score tile live in LDS; the forward also stages each block's Q, K
-// and V rows there, the other kernels read operands from global memory (through
-// the caches) as they are needed.
+// One workgroup handles one (sequence, chunk).  The sweeps keep the D x D float32
+// state and one block's score tile in LDS and stage each block's rows there (read
+// from global memory once); the chunk aggregates stage their rows and keep the state
+// in registers.  D is a compile-time constant of every kernel that loops over features.
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -16,13 +16,6 @@ namespace la {
 namespace {
 
 constexpr int kMaxD = 128;
-constexpr int kMaxBk = 128;
-
-struct Tile {
-    float state[kMaxD * kMaxD];  // running state, [D][D]
-    float score[kMaxBk * kMaxBk];  // masked, decayed scores of one block, [Bk][Bk]
-    float pw[kMaxBk + 1];        // lam^e, e = 0..Bk
-};
 
 __device__ __forceinline__ void fill_powers(float* pw, float lam, int Bk) {
     for (int e = threadIdx.x; e <= Bk; e += kThreads) pw[e] = lam_pow(lam, e);
@@ -157,6 +150,17 @@ __global__ __launch_bounds__(kThreads) void k_fwd_generic_varlen(SweepArgs a, La
                            a.kv_out ? a.kv_out + st_off : nullptr);
 }
 
+// The reverse sweep's LDS: the D x D gradient state (rows padded to D + 1 floats, so that
+// threads reading one column of consecutive rows hit distinct banks), one block's score
+// tile, the block's Q, K, V and dO rows (feature map applied to Q and K; padded rows) and
+// its decay powers, for blocks of Bs tokens, the largest block dividing the call's Bk that
+// fits (rev_generic_block).
+constexpr int kRevPoolFloats = 34 * 1024;  // 136 KiB
+__host__ __device__ constexpr int rev_pool_floats(int D, int Bs) {
+    return D * (D + 1) + Bs * Bs + 4 * Bs * (D + 1) + Bs + 2;
+}
+static_assert(rev_pool_floats(kMaxD, 16) <= kRevPoolFloats, "every D fits at the smallest block");
+
 // Reverse sweep over one chunk (blocks from last to first), carrying
 // dS = sum_{i >= end of block} lam^(i - end) q_i dO_i^T:
 //   dK_b = (G o M)^T Q_b + diag(lam^(m-s)) V_b dS^T,   G = dO_b V_b^T
@@ -165,12 +169,22 @@ __global__ __launch_bounds__(kThreads) void k_fwd_generic_varlen(SweepArgs a, La
 // A gradient F arriving at the final state enters as the last chunk's dS with the
 // exponents of the sequence's last block lowered by one (F reaches token j as
 // lam^(N-1-j) F, not lam^(N-j)); chunk 0 ends with lam dS = the gradient of S0.
-template <bool BF16>
+// Each block's rows are read from global memory once, into LDS; D (= a.D) is a
+// compile-time constant, so the loops over features unroll.
+template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs lam) {
-    __shared__ Tile sh;
+    __shared__ float pool[kRevPoolFloats];
+    constexpr int rp = D + 1;  // row pitch of the state and the staged rows
     const int64_t pair = blockIdx.x / a.chunks;
     const int c = blockIdx.x % a.chunks;
-    const int D = a.D, Bk = a.Bk, tid = threadIdx.x;
+    const int Bk = a.Bk, tid = threadIdx.x;
+    float* state = pool;             // [D][D + 1]
+    float* score = state + D * rp;   // [Bk][Bk]
+    float* qs = score + Bk * Bk;     // [Bk][D + 1] each: phi(Q), phi(K), V, dO
+    float* ks = qs + Bk * rp;
+    float* vs = ks + Bk * rp;
+    float* gs = vs + Bk * rp;
+    float* pw = gs + Bk * rp;        // lam^e, e = 0..Bk
     const float lv = lam.lam[pair % a.H];
     const int64_t t_begin = static_cast<int64_t>(c) * a.L;
     const int64_t t_end = min(a.N, t_begin + a.L);
@@ -180,12 +194,11 @@ __global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs l
         const float x = ld<BF16>(p, i);
         return (a.phi && ((a.phi_mask >> bit) & 1)) ? phi_apply(x, a.phi) : x;
     };
-    fill_powers(sh.pw, lv, Bk);
+    fill_powers(pw, lv, Bk);
     const bool last = c == a.chunks - 1;
     const float* init = !last ? a.slots + rev_slot_index(a, pair, c) * D * D
                               : (a.g_final ? a.g_final + pair * D * D : nullptr);
-    for (int i = tid; i < D * D; i += kThreads) sh.state[i] = init ? init[i] : 0.f;
-    __syncthreads();
+    for (int i = tid; i < D * D; i += kThreads) state[(i / D) * rp + i % D] = init ? init[i] : 0.f;
 
     const int64_t nblk = (t_end - t_begin + Bk - 1) / Bk;
     for (int64_t bi = nblk - 1; bi >= 0; --bi) {
@@ -193,24 +206,37 @@ __global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs l
         const int m = static_cast<int>(min(static_cast<int64_t>(Bk), t_end - t0));
         const int shift = (last && a.g_final && bi == nblk - 1) ? 1 : 0;
         const int64_t r0 = base + t0 * D;
+        __syncthreads();  // the previous block's rows, scores and state update are done with
+        for (int i = tid; i < m * D; i += kThreads) {
+            const int row = i / D, col = i % D;
+            const int64_t at = r0 + row * D + col;
+            qs[row * rp + col] = opd(a.a, 0, at);
+            ks[row * rp + col] = opd(a.b, 1, at);
+            vs[row * rp + col] = ld<BF16>(a.c, at);
+            gs[row * rp + col] = ld<BF16>(a.g, at);
+        }
+        __syncthreads();
         // G[i][j] = lam^(i-j) dO_i . v_j for i >= j
         for (int idx = tid; idx < m * m; idx += kThreads) {
             const int i = idx / m, j = idx % m;
             float x = 0.f;
             if (j <= i) {
-                for (int f = 0; f < D; ++f) x += ld<BF16>(a.g, r0 + i * D + f) * ld<BF16>(a.c, r0 + j * D + f);
-                x *= sh.pw[i - j];
+#pragma unroll
+                for (int f = 0; f < D; ++f) x += gs[i * rp + f] * vs[j * rp + f];
+                x *= pw[i - j];
             }
-            sh.score[i * kMaxBk + j] = x;
+            score[i * Bk + j] = x;
         }
         __syncthreads();
         for (int idx = tid; idx < m * D; idx += kThreads) {
             const int j = idx / D, f = idx % D;
             float intra = 0.f, inter = 0.f;
-            for (int i = j; i < m; ++i) intra += sh.score[i * kMaxBk + j] * opd(a.a, 0, r0 + i * D + f);
-            for (int col = 0; col < D; ++col) inter += sh.state[f * D + col] * ld<BF16>(a.c, r0 + j * D + col);
+#pragma unroll 8
+            for (int i = j; i < m; ++i) intra += score[i * Bk + j] * qs[i * rp + f];
+#pragma unroll
+            for (int col = 0; col < D; ++col) inter += state[f * rp + col] * vs[j * rp + col];
             const float gr = a.phi ? dphi_of_x(ld<BF16>(a.b, r0 + j * D + f), a.phi) : 1.f;
-            st<BF16>(a.out0, r0 + j * D + f, gr * (intra + sh.pw[m - shift - j] * inter));
+            st<BF16>(a.out0, r0 + j * D + f, gr * (intra + pw[m - shift - j] * inter));
         }
         __syncthreads();
         // P[i][j] = lam^(i-j) q_i . k_j for i >= j
@@ -218,69 +244,95 @@ __global__ __launch_bounds__(kThreads) void k_rev_generic(SweepArgs a, LamArgs l
             const int i = idx / m, j = idx % m;
             float x = 0.f;
             if (j <= i) {
-                for (int f = 0; f < D; ++f) x += opd(a.a, 0, r0 + i * D + f) * opd(a.b, 1, r0 + j * D + f);
-                x *= sh.pw[i - j];
+#pragma unroll
+                for (int f = 0; f < D; ++f) x += qs[i * rp + f] * ks[j * rp + f];
+                x *= pw[i - j];
             }
-            sh.score[i * kMaxBk + j] = x;
+            score[i * Bk + j] = x;
         }
         __syncthreads();
         for (int idx = tid; idx < m * D; idx += kThreads) {
             const int j = idx / D, col = idx % D;
             float intra = 0.f, inter = 0.f;
-            for (int i = j; i < m; ++i) intra += sh.score[i * kMaxBk + j] * ld<BF16>(a.g, r0 + i * D + col);
-            for (int f = 0; f < D; ++f) inter += opd(a.b, 1, r0 + j * D + f) * sh.state[f * D + col];
-            st<BF16>(a.out1, r0 + j * D + col, intra + sh.pw[m - shift - j] * inter);
+#pragma unroll 8
+            for (int i = j; i < m; ++i) intra += score[i * Bk + j] * gs[i * rp + col];
+#pragma unroll
+            for (int f = 0; f < D; ++f) inter += ks[j * rp + f] * state[f * rp + col];
+            st<BF16>(a.out1, r0 + j * D + col, intra + pw[m - shift - j] * inter);
         }
         __syncthreads();
         for (int idx = tid; idx < D * D; idx += kThreads) {
             const int f = idx / D, col = idx % D;
             float acc = 0.f;
-            for (int s = 0; s < m; ++s)
-                acc += sh.pw[s] * opd(a.a, 0, r0 + s * D + f) * ld<BF16>(a.g, r0 + s * D + col);
-            sh.state[idx] = sh.pw[m - shift] * sh.state[idx] + acc;
+#pragma unroll 8
+            for (int s2 = 0; s2 < m; ++s2) acc += pw[s2] * qs[s2 * rp + f] * gs[s2 * rp + col];
+            state[f * rp + col] = pw[m - shift] * state[f * rp + col] + acc;
         }
-        __syncthreads();
     }
+    __syncthreads();
     if (c == 0 && a.ds_out)
-        for (int i = tid; i < D * D; i += kThreads) a.ds_out[pair * D * D + i] = lv * sh.state[i];
+        for (int i = tid; i < D * D; i += kThreads) a.ds_out[pair * D * D + i] = lv * state[(i / D) * rp + i % D];
 }
 
-// Aggregate state of one chunk, started from zero (see ChunkStateArgs).
-template <bool BF16>
+// Aggregate state of one chunk, started from zero (see ChunkStateArgs), in blocks of at
+// most 64 tokens (the aggregate is the same at any block size): each block's x and y rows
+// are read from global memory once, into LDS (feature map applied, rows padded to D + 1
+// floats); each thread keeps its D * D / kThreads entries of the state in registers.
+constexpr int kStateRows = 64;
+template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void k_chunk_state_generic(ChunkStateArgs a, LamArgs lam) {
-    __shared__ float state[kMaxD * kMaxD];
-    __shared__ float pw[kMaxBk + 1];
+    constexpr int rp = D + 1;
+    constexpr int NE = (D * D + kThreads - 1) / kThreads;  // state entries per thread
+    __shared__ float xs[kStateRows * (kMaxD + 1)];
+    __shared__ float ys[kStateRows * (kMaxD + 1)];
+    __shared__ float pw[kStateRows + 1];
     const int per = a.chunks - 1;
     const int64_t pair = blockIdx.x / per;
     const int slot = blockIdx.x % per;
     const int c = a.reverse ? slot + 1 + a.part0 : slot;
-    const int D = a.D, Bk = a.Bk, tid = threadIdx.x;
-    fill_powers(pw, lam.lam[pair % a.H], Bk);
-    for (int i = tid; i < D * D; i += kThreads) state[i] = 0.f;
-    __syncthreads();
+    const int Bs = min(a.Bk, kStateRows), tid = threadIdx.x;
+    fill_powers(pw, lam.lam[pair % a.H], Bs);
+    float acc[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = 0.f;
     const int64_t t_begin = static_cast<int64_t>(c) * a.L;
     const int64_t t_end = min(a.N, t_begin + a.L);
     const int64_t base = pair * a.N * D;
-    const int64_t nblk = (t_end - t_begin + Bk - 1) / Bk;
+    const int64_t nblk = t_end > t_begin ? (t_end - t_begin + Bs - 1) / Bs : 0;
     for (int64_t n = 0; n < nblk; ++n) {
         const int64_t bi = a.reverse ? nblk - 1 - n : n;
-        const int64_t t0 = t_begin + bi * Bk;
-        const int m = static_cast<int>(min(static_cast<int64_t>(Bk), t_end - t0));
+        const int64_t t0 = t_begin + bi * Bs;
+        const int m = static_cast<int>(min(static_cast<int64_t>(Bs), t_end - t0));
         const int64_t r0 = base + t0 * D;
-        for (int i = tid; i < D * D; i += kThreads) {
-            const int f = i / D, col = i % D;
-            float acc = 0.f;
-            for (int s = 0; s < m; ++s) {
-                const float w = a.reverse ? pw[s] : pw[m - 1 - s];
-                const float x = ld<BF16>(a.x, r0 + s * D + f), y = ld<BF16>(a.y, r0 + s * D + col);
-                acc += w * ((a.phi_mask & 1) ? phi_apply(x, a.phi) : x) * ((a.phi_mask & 2) ? phi_apply(y, a.phi) : y);
-            }
-            state[i] = pw[m] * state[i] + acc;
+        __syncthreads();  // the previous block's rows are done with (and the powers are in)
+        for (int i = tid; i < m * D; i += kThreads) {
+            const int row = i / D, col = i % D;
+            const float x = ld<BF16>(a.x, r0 + row * D + col), y = ld<BF16>(a.y, r0 + row * D + col);
+            xs[row * rp + col] = (a.phi_mask & 1) ? phi_apply(x, a.phi) : x;
+            ys[row * rp + col] = (a.phi_mask & 2) ? phi_apply(y, a.phi) : y;
         }
         __syncthreads();
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int i = tid + e * kThreads;
+            if (i < D * D) {
+                const int f = i / D, col = i % D;
+                float sum = 0.f;
+#pragma unroll 8
+                for (int s2 = 0; s2 < m; ++s2) {
+                    const float w = a.reverse ? pw[s2] : pw[m - 1 - s2];
+                    sum += w * xs[s2 * rp + f] * ys[s2 * rp + col];
+                }
+                acc[e] = pw[m] * acc[e] + sum;
+            }
+        }
     }
     float* dst = a.slots + (pair * per + slot) * D * D;
-    for (int i = tid; i < D * D; i += kThreads) dst[i] = state[i];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        const int i = tid + e * kThreads;
+        if (i < D * D) dst[i] = acc[e];
+    }
 }
 
 constexpr int kScanBatch = 8;  // chunk slots whose loads a scan thread keeps in flight
@@ -502,20 +554,45 @@ void launch_fwd_generic_varlen(const SweepArgs& a, const LamArgs& lam, const Var
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, b, lam, v);
 }
 
+namespace {
+template <bool BF16>
+void (*rev_generic_kernel(int D))(SweepArgs, LamArgs) {
+    switch (D) {
+        case 16: return k_rev_generic<BF16, 16>;
+        case 32: return k_rev_generic<BF16, 32>;
+        case 64: return k_rev_generic<BF16, 64>;
+        default: return k_rev_generic<BF16, 128>;
+    }
+}
+template <bool BF16>
+void (*chunk_state_generic_kernel(int D))(ChunkStateArgs, LamArgs) {
+    switch (D) {
+        case 16: return k_chunk_state_generic<BF16, 16>;
+        case 32: return k_chunk_state_generic<BF16, 32>;
+        case 64: return k_chunk_state_generic<BF16, 64>;
+        default: return k_chunk_state_generic<BF16, 128>;
+    }
+}
+}  // namespace
+
+// The block the generic reverse sweep steps: the largest of Bk, Bk/2, ... whose LDS pool fits.
+SweepArgs rev_generic_block(const SweepArgs& a) {
+    SweepArgs b = a;
+    while (b.Bk > 16 && rev_pool_floats(b.D, b.Bk) > kRevPoolFloats) b.Bk /= 2;
+    return b;
+}
+
 void launch_rev_generic(const SweepArgs& a, const LamArgs& lam, int bf16, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(a.pairs * a.chunks));
-    if (bf16)
-        hipLaunchKernelGGL(k_rev_generic<true>, grid, dim3(kThreads), 0, s, a, lam);
-    else
-        hipLaunchKernelGGL(k_rev_generic<false>, grid, dim3(kThreads), 0, s, a, lam);
+    const SweepArgs b = rev_generic_block(a);
+    auto kern = bf16 ? rev_generic_kernel<true>(b.D) : rev_generic_kernel<false>(b.D);
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, b, lam);
 }
 
 void launch_chunk_state_generic(const ChunkStateArgs& a, const LamArgs& lam, int bf16, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(a.pairs * (a.chunks - 1)));
-    if (bf16)
-        hipLaunchKernelGGL(k_chunk_state_generic<true>, grid, dim3(kThreads), 0, s, a, lam);
-    else
-        hipLaunchKernelGGL(k_chunk_state_generic<false>, grid, dim3(kThreads), 0, s, a, lam);
+    auto kern = bf16 ? chunk_state_generic_kernel<true>(a.D) : chunk_state_generic_kernel<false>(a.D);
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, a, lam);
 }
 
 void launch_scan_varlen(const ScanArgs& a, const LamArgs& lam, const ScanList& list, hipStream_t s) {
