@@ -123,6 +123,20 @@ def test_bwd_ragged_bf16(kern, D, Bk, kernel):
     check_bwd(1, 4, 777, D, Bk, "bf16", lam, seed=3, label=kern)
 
 
+@pytest.mark.parametrize("D,Bk", [(16, 128), (32, 128), (64, 64), (128, 16), (128, 128)])
+def test_fp32_generic_backward_block_regimes(D, Bk, chunks):
+    """float32 forward and backward on the generic kernels, two chunks, ragged tail, initial
+    state, with the forward's chunk states: the reverse sweep stages its block rows in LDS and
+    steps the largest block dividing Bk that fits (128 tokens at D = 16 and 32, 64 at D = 64,
+    32 at D = 128, 16 for Bk = 16), the chunk aggregates step 64-token blocks (or Bk when
+    smaller), the forward its own largest fitting block."""
+    chunks(2)
+    lam = synth.decay_schedule(2)
+    N = 2 * Bk + 37 if Bk >= 64 else 300
+    check_fwd(1, 2, N, D, Bk, "f32", lam, seed=60 + D, with_state=True, label=f"f32 D={D} Bk={Bk}")
+    check_bwd(1, 2, N, D, Bk, "f32", lam, seed=60 + D, with_state=True, label=f"f32 D={D} Bk={Bk}", fwd_ws=True)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_initial_state(dtype):
     lam = synth.decay_schedule(4)
