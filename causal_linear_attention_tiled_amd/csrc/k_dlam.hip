@@ -18,7 +18,7 @@
 // kernel adds the partials of every sequence and chunk of a head.
 //
 // Generic kernels (any supported D, Bk, float32 or bfloat16 storage) work in
-// float32 from LDS states; the matrix-core kernels (bf16, D = 128, Bk = 64) keep
+// float32 on rows staged in LDS; the matrix-core kernels (bf16, D = 128, Bk = 64) keep
 // both states in MFMA accumulators, with the same operand layouts as the
 // register-staged forward kernel.  Partial sums are accumulated in double.
 #include "la_device.h"
@@ -45,47 +45,70 @@ __device__ __forceinline__ double block_sum(double x, double* red) {
 // ------------------------------------------------------------------ generic kernels
 // Chunk aggregates of (S, T) over chunk c = blockIdx % (chunks - 1) of sequence
 // blockIdx / (chunks - 1), both started from zero; x = k (through the feature map
-// when phi_mask bit 0 is set), y = v.  Thread i owns state elements i, i + 256, ...
-template <bool BF16>
+// when phi_mask bit 0 is set), y = v.  Each block (at most 64 tokens: the aggregate is
+// the same at any block size) has its rows read from global memory once, into LDS
+// (rows padded to DG + 1 floats); thread i owns state elements i, i + 256, ... of both,
+// in registers.  DG (= a.D) is a compile-time constant, so the loops over features unroll.
+constexpr int kStateRows = 64;
+template <bool BF16, int DG>
 __global__ __launch_bounds__(kThreads) void k_dlam_state_generic(ChunkStateArgs a, LamArgs lam) {
-    __shared__ float S[kMaxD * kMaxD];
-    __shared__ float T[kMaxD * kMaxD];
-    __shared__ float pw[kMaxBk + 1], dpw[kMaxBk + 1];
+    constexpr int rp = DG + 1, DD = DG * DG;
+    constexpr int NE = (DD + kThreads - 1) / kThreads;
+    __shared__ float xs[kStateRows * (kMaxD + 1)];
+    __shared__ float ys[kStateRows * (kMaxD + 1)];
+    __shared__ float pw[kStateRows + 1], dpw[kStateRows + 1];
     const int per = a.chunks - 1;
     const int64_t pair = blockIdx.x / per;
     const int c = blockIdx.x % per;
-    const int D = a.D, DD = D * D, Bk = a.Bk, tid = threadIdx.x;
+    const int Bs = min(a.Bk, kStateRows), tid = threadIdx.x;
     const float lv = lam.lam[pair % a.H];
     const int phi = (a.phi_mask & 1) ? a.phi : 0;
-    for (int e = tid; e <= Bk; e += kThreads) {
+    for (int e = tid; e <= Bs; e += kThreads) {
         pw[e] = lam_pow(lv, e);
         dpw[e] = lam_dpow(lv, e);
     }
-    for (int i = tid; i < DD; i += kThreads) S[i] = T[i] = 0.f;
-    __syncthreads();
+    float S[NE], T[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) S[e] = T[e] = 0.f;
     const int64_t t_begin = static_cast<int64_t>(c) * a.L;
     const int64_t t_end = min(a.N, t_begin + a.L);
-    const int64_t base = pair * a.N * D;
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += Bk) {
-        const int m = static_cast<int>(min(static_cast<int64_t>(Bk), t_end - t0));
-        const int64_t r0 = base + t0 * D;
-        for (int i = tid; i < DD; i += kThreads) {
-            const int f = i / D, col = i % D;
-            float a1 = 0.f, a2 = 0.f;
-            for (int s = 0; s < m; ++s) {
-                const float xy = phi_apply(ld<BF16>(a.x, r0 + s * D + f), phi) * ld<BF16>(a.y, r0 + s * D + col);
-                a1 += pw[m - 1 - s] * xy;
-                a2 += dpw[m - 1 - s] * xy;
+    const int64_t base = pair * a.N * DG;
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += Bs) {
+        const int m = static_cast<int>(min(static_cast<int64_t>(Bs), t_end - t0));
+        const int64_t r0 = base + t0 * DG;
+        __syncthreads();  // the previous block's rows are done with (and the powers are in)
+        for (int i = tid; i < m * DG; i += kThreads) {
+            const int row = i / DG, col = i % DG;
+            xs[row * rp + col] = phi_apply(ld<BF16>(a.x, r0 + row * DG + col), phi);
+            ys[row * rp + col] = ld<BF16>(a.y, r0 + row * DG + col);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int i = tid + e * kThreads;
+            if (i < DD) {
+                const int f = i / DG, col = i % DG;
+                float a1 = 0.f, a2 = 0.f;
+#pragma unroll 8
+                for (int s2 = 0; s2 < m; ++s2) {
+                    const float xy = xs[s2 * rp + f] * ys[s2 * rp + col];
+                    a1 += pw[m - 1 - s2] * xy;
+                    a2 += dpw[m - 1 - s2] * xy;
+                }
+                const float s_old = S[e];
+                T[e] = pw[m] * T[e] + dpw[m] * s_old + a2;
+                S[e] = pw[m] * s_old + a1;
             }
-            const float s_old = S[i];
-            T[i] = pw[m] * T[i] + dpw[m] * s_old + a2;
-            S[i] = pw[m] * s_old + a1;
         }
     }
     float* dst = a.slots + (pair * per + c) * 2 * static_cast<int64_t>(DD);
-    for (int i = tid; i < DD; i += kThreads) {
-        dst[i] = S[i];
-        dst[DD + i] = T[i];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        const int i = tid + e * kThreads;
+        if (i < DD) {
+            dst[i] = S[e];
+            dst[DD + i] = T[e];
+        }
     }
 }
 
@@ -123,18 +146,36 @@ __global__ __launch_bounds__(kThreads) void k_dlam_scan(ScanArgs a, LamArgs lam)
     }
 }
 
-// The sweep over one (sequence, chunk): states in LDS, operands read through the caches.
-template <bool BF16>
+// The sweep's LDS: S and T ([DG][DG]; every access runs along a row, one column per
+// thread, so they need no padding), the block's q, k, v and dO rows (feature map applied to
+// q and k; rows padded to DG + 1 floats) and the decay powers and their derivatives, for
+// blocks of Bs tokens, the largest block dividing the call's Bk that fits
+// (dlam_generic_block: 8 tokens at D = 128, where the two states take 128 KiB).
+constexpr int kDlamPoolFloats = 37 * 1024;  // 148 KiB
+constexpr int kDlamMinBlock = 8;
+__host__ __device__ constexpr int dlam_pool_floats(int D, int Bs) { return 2 * D * D + 4 * Bs * (D + 1) + 2 * (Bs + 2); }
+static_assert(dlam_pool_floats(kMaxD, kDlamMinBlock) <= kDlamPoolFloats, "every D fits at the smallest block");
+
+// The sweep over one (sequence, chunk): states in LDS, each block's rows read from global
+// memory once, into LDS; DG (= a.D) a compile-time constant, so the loops over features unroll.
+template <bool BF16, int DG>
 __global__ __launch_bounds__(kThreads) void k_dlam_generic(DlamArgs a, LamArgs lam) {
-    __shared__ float S[kMaxD * kMaxD];
-    __shared__ float T[kMaxD * kMaxD];
-    __shared__ float pw[kMaxBk + 2], dpw[kMaxBk + 2];
+    __shared__ float pool[kDlamPoolFloats];
     __shared__ double red[kThreads];
+    constexpr int rp = DG + 1, DD = DG * DG;
     const int64_t pair = blockIdx.x / a.chunks;
     const int c = blockIdx.x % a.chunks;
-    const int D = a.D, DD = D * D, Bk = a.Bk, tid = threadIdx.x;
+    const int Bk = a.Bk, tid = threadIdx.x;
+    float* S = pool;              // [DG][DG]
+    float* T = S + DD;
+    float* qs = T + DD;           // [Bk][DG + 1] each: phi(q), phi(k), v, dO
+    float* ks = qs + Bk * rp;
+    float* vs = ks + Bk * rp;
+    float* gs = vs + Bk * rp;
+    float* pw = gs + Bk * rp;     // lam^e, e = 0..Bk + 1
+    float* dpw = pw + Bk + 2;     // d(lam^e)/dlam
     const float lv = lam.lam[pair % a.H];
-    const int64_t base = pair * a.N * D;
+    const int64_t base = pair * a.N * DG;
     const int64_t t_begin = static_cast<int64_t>(c) * a.L;
     const int64_t t_end = min(a.N, t_begin + a.L);
     for (int e = tid; e <= Bk + 1; e += kThreads) {
@@ -154,48 +195,58 @@ __global__ __launch_bounds__(kThreads) void k_dlam_generic(DlamArgs a, LamArgs l
             T[i] = src[DD + i];
         }
     }
-    __syncthreads();
-    auto qv = [&](int64_t i) { return phi_apply(ld<BF16>(a.q, i), a.phi); };
-    auto kv = [&](int64_t i) { return phi_apply(ld<BF16>(a.k, i), a.phi); };
     double acc = 0.0;
     for (int64_t t0 = t_begin; t0 < t_end; t0 += Bk) {
         const int m = static_cast<int>(min(static_cast<int64_t>(Bk), t_end - t0));
-        const int64_t r0 = base + t0 * D;
-        for (int i = tid; i < m * m; i += kThreads) {
-            const int s = i / m, s2 = i % m;
-            if (s2 >= s) continue;
-            float qk = 0.f, gv = 0.f;
-            for (int f = 0; f < D; ++f) {
-                qk += qv(r0 + s * D + f) * kv(r0 + s2 * D + f);
-                gv += ld<BF16>(a.g, r0 + s * D + f) * ld<BF16>(a.v, r0 + s2 * D + f);
-            }
-            acc += static_cast<double>(dpw[s - s2] * qk * gv);
-        }
-        for (int i = tid; i < m * D; i += kThreads) {
-            const int s = i / D, col = i % D;
-            float u = 0.f, w = 0.f;
-            for (int f = 0; f < D; ++f) {
-                const float x = qv(r0 + s * D + f);
-                u += x * S[f * D + col];
-                w += x * T[f * D + col];
-            }
-            acc += static_cast<double>(ld<BF16>(a.g, r0 + s * D + col) * (dpw[s + 1] * u + pw[s + 1] * w));
+        const int64_t r0 = base + t0 * DG;
+        __syncthreads();  // the previous block's rows and state update are done with
+        for (int i = tid; i < m * DG; i += kThreads) {
+            const int row = i / DG, col = i % DG;
+            const int64_t at = r0 + row * DG + col;
+            qs[row * rp + col] = phi_apply(ld<BF16>(a.q, at), a.phi);
+            ks[row * rp + col] = phi_apply(ld<BF16>(a.k, at), a.phi);
+            vs[row * rp + col] = ld<BF16>(a.v, at);
+            gs[row * rp + col] = ld<BF16>(a.g, at);
         }
         __syncthreads();
+        for (int i = tid; i < m * m; i += kThreads) {
+            const int s1 = i / m, s2 = i % m;
+            if (s2 >= s1) continue;
+            float qk = 0.f, gv = 0.f;
+#pragma unroll
+            for (int f = 0; f < DG; ++f) {
+                qk += qs[s1 * rp + f] * ks[s2 * rp + f];
+                gv += gs[s1 * rp + f] * vs[s2 * rp + f];
+            }
+            acc += static_cast<double>(dpw[s1 - s2] * qk * gv);
+        }
+        for (int i = tid; i < m * DG; i += kThreads) {
+            const int s1 = i / DG, col = i % DG;
+            float u = 0.f, w = 0.f;
+#pragma unroll
+            for (int f = 0; f < DG; ++f) {
+                const float x = qs[s1 * rp + f];
+                u += x * S[f * DG + col];
+                w += x * T[f * DG + col];
+            }
+            acc += static_cast<double>(gs[s1 * rp + col] * (dpw[s1 + 1] * u + pw[s1 + 1] * w));
+        }
+        __syncthreads();  // S and T are read above and rewritten below
         for (int i = tid; i < DD; i += kThreads) {
-            const int f = i / D, col = i % D;
+            const int f = i / DG, col = i % DG;
             float a1 = 0.f, a2 = 0.f;
-            for (int s = 0; s < m; ++s) {
-                const float xy = kv(r0 + s * D + f) * ld<BF16>(a.v, r0 + s * D + col);
-                a1 += pw[m - 1 - s] * xy;
-                a2 += dpw[m - 1 - s] * xy;
+#pragma unroll 8
+            for (int s2 = 0; s2 < m; ++s2) {
+                const float xy = ks[s2 * rp + f] * vs[s2 * rp + col];
+                a1 += pw[m - 1 - s2] * xy;
+                a2 += dpw[m - 1 - s2] * xy;
             }
             const float s_old = S[i];
             T[i] = pw[m] * T[i] + dpw[m] * s_old + a2;
             S[i] = pw[m] * s_old + a1;
         }
-        __syncthreads();
     }
+    __syncthreads();
     if (a.g_final && c == a.chunks - 1) {
         const float* F = a.g_final + pair * DD;
         for (int i = tid; i < DD; i += kThreads) acc += static_cast<double>(F[i] * T[i]);
@@ -634,12 +685,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_dlam_mfma(DlamArgs a, LamArgs l
 
 }  // namespace
 
+namespace {
+template <bool BF16>
+void (*dlam_state_generic_kernel(int d))(ChunkStateArgs, LamArgs) {
+    switch (d) {
+        case 16: return k_dlam_state_generic<BF16, 16>;
+        case 32: return k_dlam_state_generic<BF16, 32>;
+        case 64: return k_dlam_state_generic<BF16, 64>;
+        default: return k_dlam_state_generic<BF16, 128>;
+    }
+}
+template <bool BF16>
+void (*dlam_generic_kernel(int d))(DlamArgs, LamArgs) {
+    switch (d) {
+        case 16: return k_dlam_generic<BF16, 16>;
+        case 32: return k_dlam_generic<BF16, 32>;
+        case 64: return k_dlam_generic<BF16, 64>;
+        default: return k_dlam_generic<BF16, 128>;
+    }
+}
+}  // namespace
+
 void launch_dlam_state_generic(const ChunkStateArgs& a, const LamArgs& lam, int bf16, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(a.pairs * (a.chunks - 1)));
-    if (bf16)
-        hipLaunchKernelGGL(k_dlam_state_generic<true>, grid, dim3(kThreads), 0, s, a, lam);
-    else
-        hipLaunchKernelGGL(k_dlam_state_generic<false>, grid, dim3(kThreads), 0, s, a, lam);
+    auto kern = bf16 ? dlam_state_generic_kernel<true>(a.D) : dlam_state_generic_kernel<false>(a.D);
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, a, lam);
 }
 
 void launch_dlam_state_mfma(const ChunkStateArgs& a, const LamArgs& lam, hipStream_t s) {
@@ -653,12 +723,19 @@ void launch_dlam_scan(const ScanArgs& a, const LamArgs& lam, hipStream_t s) {
     hipLaunchKernelGGL(k_dlam_scan, grid, dim3(kThreads), 0, s, a, lam);
 }
 
+// The block the generic sweep steps: the largest of Bk, Bk/2, ... that fits (the block only
+// decides which terms pass through the in-block sum and which through the carried states).
+DlamArgs dlam_generic_block(const DlamArgs& a) {
+    DlamArgs b = a;
+    while (b.Bk > kDlamMinBlock && dlam_pool_floats(b.D, b.Bk) > kDlamPoolFloats) b.Bk /= 2;
+    return b;
+}
+
 void launch_dlam_generic(const DlamArgs& a, const LamArgs& lam, int bf16, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(a.pairs * a.chunks));
-    if (bf16)
-        hipLaunchKernelGGL(k_dlam_generic<true>, grid, dim3(kThreads), 0, s, a, lam);
-    else
-        hipLaunchKernelGGL(k_dlam_generic<false>, grid, dim3(kThreads), 0, s, a, lam);
+    const DlamArgs b = dlam_generic_block(a);
+    auto kern = bf16 ? dlam_generic_kernel<true>(b.D) : dlam_generic_kernel<false>(b.D);
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, b, lam);
 }
 
 bool dlam_mfma_supported(int d, int bk) { return d == D && bk == 64; }
