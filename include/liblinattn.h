@@ -49,9 +49,10 @@
  *  - The environment variable LA_CHUNKS (a positive integer) overrides the
  *    number of chunks a sequence is split into for the chunked prefix over
  *    blocks, LA_AGG_K the number of parts of a chunk the chunk aggregates are
- *    taken over (la_plan; the chunks grow to a whole number of parts where the
- *    chunk count stays the same, else it is ignored); LA_KERNEL=generic forces the generic (non-MFMA)
- *    kernels; LA_FWD128=1 the 128-token-block forward-direction sweep;
+ *    taken over (la_plan; the chunks grow to a whole number of parts where
+ *    the chunk count stays the same, else it is ignored); LA_KERNEL=generic
+ *    forces the generic (non-MFMA) kernels; LA_FWD128=1 the 128-token-block
+ *    forward-direction sweep;
  *    LA_STATE=dma2 the chunk aggregates with every wave loading at two
  *    workgroups per CU (instead of two loader waves at one);
  *    LA_FWD_WAVES=8, LA_REV_WAVES=4 and LA_DLAM_WAVES=4 select the
@@ -131,7 +132,7 @@ enum {
  * gives up makes its columns NaN).
  * Under HIP graph capture, and with LA_FUSED=0, the aggregates and their
  * prefix run as two launches before the sweep instead (LA_FUSED=1 fuses any
- * chunk count, which is slower with more chunks or with parts).  The two
+ * plan, which is slower with more chunks, longer chunks or parts).  The two
  * forms round differently (within float rounding of the same sums). */
 int la_fwd(const void* Q, const void* K, const void* V, const float* lambda, int64_t B, int64_t H,
            int64_t N, int64_t D, int32_t Bk, int32_t dtype, int32_t phi, const float* kv_in, void* O,
@@ -280,7 +281,7 @@ int la_decode_step(float* state, const void* q, const void* k, const void* v, co
  * 2^31, otherwise LA_EUNSUPPORTED).  Every other shape la_fwd accepts
  * (float32 storage, D in {16, 32, 64, 128}, Bk in {16, 32, 64, 128, 256})
  * runs on the generic kernels: one workgroup per (sequence, head) sweeping
- * the whole sequence in Bk-token blocks (at most 128), no workspace, T <
+ * the whole sequence in blocks of at most Bk and 128 tokens, no workspace, T <
  * 2^31.  Each sequence's results equal la_fwd over that sequence alone, up to
  * float rounding.  LA_VARLEN_L (a positive multiple of Bk) overrides the
  * chunk length of the direct-to-LDS path; a size query must see the same
